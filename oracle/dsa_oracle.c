@@ -1,0 +1,246 @@
+/* dsa_oracle.c -- plain, slow, double-precision CPU statement of the DeepSeek Sparse
+ * Attention (DSA) hot path: Lightning Indexer scores, exact top-k, sparse attention on
+ * the selected latent rows, and dense causal attention.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke check and the benchmark's CPU
+ * baseline, never by the GPU library. No code here is shared with the GPU path.
+ *
+ * Page references:
+ *   [DSA-blog]  "DeepSeek Sparse Attention：从 SWA 到稀疏 Attention 计算" (kevinye.org)
+ *   [Handbook]  "MTP 与稀疏注意力：NSA 与 DSA" (anrans.github.io, ai-infra-handbooks)
+ *
+ * The method is exact (no approximation, no iteration), so each function is the plain
+ * definition written out with double accumulation and one final rounding to float.
+ * Readings taken where the pages leave a step open are listed beside the code.
+ *
+ * Pins: every function here is checked against values fixed independently of this file
+ * (the worked example, closed forms, library routines, brute force); see tests/test_oracle.py.
+ */
+#include "dsa_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- element decoders ------------------------------------------------------------- */
+
+/* OCP 8-bit floating point, E4M3FN: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits;
+ * exponent field 0 encodes subnormals m/8 * 2^-6; S.1111.111 is NaN; no infinities. */
+double oracle_e4m3_to_double(uint8_t code) {
+  int sign = code >> 7;
+  int expo = (code >> 3) & 0xF;
+  int mant = code & 0x7;
+  double mag;
+  if (expo == 0xF && mant == 0x7) return NAN;
+  if (expo == 0)
+    mag = ldexp((double)mant / 8.0, -6);
+  else
+    mag = ldexp(1.0 + (double)mant / 8.0, expo - 7);
+  return sign ? -mag : mag;
+}
+
+/* bfloat16 is the upper 16 bits of an IEEE binary32. */
+double oracle_bf16_to_double(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double elem(const void* base, int64_t i, int fmt) {
+  if (fmt == ORACLE_E4M3) return oracle_e4m3_to_double(((const uint8_t*)base)[i]);
+  return (double)((const float*)base)[i];
+}
+
+/* Physical row of position p of sequence s in a paged cache; -1 if the page id is invalid. */
+static int64_t phys_row(const int32_t* page_table, int64_t ld_pt, int page_size, int num_pages,
+                        int s, int64_t p) {
+  int32_t page = page_table[(int64_t)s * ld_pt + p / page_size];
+  if (page < 0 || page >= num_pages) return -1;
+  return (int64_t)page * page_size + p % page_size;
+}
+
+static int bad_common(int n_seq, int q_per_seq, int row_begin, int row_end) {
+  if (n_seq < 0 || q_per_seq < 1) return 1;
+  if (row_begin < 0 || row_end > n_seq * q_per_seq || row_begin > row_end) return 1;
+  return 0;
+}
+
+/* ---- Lightning Indexer ------------------------------------------------------------ */
+
+/* [DSA-blog] "Lightning Indexer": I_tj = sum over indexer heads r of
+ * w_tr * ReLU(q_tr . k_j), for every visible j <= t, one key k_j shared by all heads.
+ * Reading (key scale): the cached key is k_j = k_scale_j * k8_j, dequantised before the
+ * dot product exactly as written here. */
+int oracle_indexer_scores(const void* q, const float* w, const void* k_cache, const float* k_scale,
+                          const int32_t* page_table, int64_t ld_pt, int page_size, int num_pages,
+                          const int32_t* q_pos, int n_seq, int q_per_seq, int Hi, int Di, int fmt,
+                          float* scores, int64_t ld_scores, int row_begin, int row_end) {
+  if (bad_common(n_seq, q_per_seq, row_begin, row_end)) return 1;
+  if (Hi < 1 || Di < 1 || page_size < 1 || (fmt != ORACLE_E4M3 && fmt != ORACLE_F32)) return 1;
+  double* key = (double*)malloc(sizeof(double) * (size_t)Di);
+  if (!key) return 2;
+  for (int r = row_begin; r < row_end; ++r) {
+    int s = r / q_per_seq;
+    int64_t t = q_pos[r];
+    for (int64_t j = 0; j <= t; ++j) {
+      int64_t row = phys_row(page_table, ld_pt, page_size, num_pages, s, j);
+      if (row < 0) { free(key); return 3; }
+      double scale = k_scale ? (double)k_scale[row] : 1.0;
+      for (int c = 0; c < Di; ++c) key[c] = scale * elem(k_cache, row * Di + c, fmt);
+      double score = 0.0;
+      for (int h = 0; h < Hi; ++h) {
+        double dot = 0.0;
+        for (int c = 0; c < Di; ++c) dot += elem(q, ((int64_t)r * Hi + h) * Di + c, fmt) * key[c];
+        double relu = dot > 0.0 ? dot : 0.0;
+        score += (double)w[(int64_t)r * Hi + h] * relu;
+      }
+      scores[(int64_t)r * ld_scores + j] = (float)score;
+    }
+  }
+  free(key);
+  return 0;
+}
+
+/* ---- top-k ------------------------------------------------------------------------ */
+
+typedef struct {
+  float v;
+  int32_t j;
+} cand_t;
+
+/* Larger score first; equal scores (by value, so -0 == +0) by smaller position first. */
+static int cmp_rank(const void* a, const void* b) {
+  const cand_t* x = (const cand_t*)a;
+  const cand_t* y = (const cand_t*)b;
+  if (x->v > y->v) return -1;
+  if (x->v < y->v) return 1;
+  return (x->j > y->j) - (x->j < y->j);
+}
+
+static int cmp_i32(const void* a, const void* b) {
+  int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+/* [DSA-blog] "Lightning Indexer": S_t = TopK over j <= t of I_tj with k positions;
+ * [Handbook] cost model: k = min(L, 2048), i.e. a prefix shorter than k keeps every
+ * position. Reading (ties): equal scores rank the smaller position first. */
+int oracle_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int rows, int k,
+                int32_t* idx, int64_t ld_idx, int row_begin, int row_end) {
+  if (k < 1 || rows < 0 || row_begin < 0 || row_end > rows || row_begin > row_end) return 1;
+  for (int r = row_begin; r < row_end; ++r) {
+    int64_t n = (int64_t)q_pos[r] + 1;
+    if (n < 0) n = 0;
+    cand_t* c = (cand_t*)malloc(sizeof(cand_t) * (size_t)(n > 0 ? n : 1));
+    if (!c) return 2;
+    for (int64_t j = 0; j < n; ++j) {
+      c[j].v = scores[(int64_t)r * ld_scores + j];
+      c[j].j = (int32_t)j;
+    }
+    qsort(c, (size_t)n, sizeof(cand_t), cmp_rank);
+    int64_t m = n < k ? n : k;
+    int32_t* out = idx + (int64_t)r * ld_idx;
+    for (int64_t i = 0; i < m; ++i) out[i] = c[i].j;
+    qsort(out, (size_t)m, sizeof(int32_t), cmp_i32);
+    for (int64_t i = m; i < k; ++i) out[i] = -1;
+    free(c);
+  }
+  return 0;
+}
+
+/* ---- attention over a position set -------------------------------------------------- */
+
+/* Softmax attention of one query row over the listed positions ([DSA-blog] "Sparse
+ * Attention": softmax(q K^T / sqrt(d_h) + M) V with M = 0 on S_t and -inf elsewhere, which
+ * on S_t alone is an ordinary softmax). Two passes: logits and their maximum, then the
+ * normalised weighted sum of value rows. */
+static int attend_row(const uint16_t* q_row /* [H, Dqk] */, const uint16_t* kv_cache,
+                      const int64_t* rows_of_set, int64_t n_set, int H, int Dqk, int Dv,
+                      int kv_dim, int v_col0, double sm_scale, float* out /* [H, Dv] */,
+                      float* lse /* [H] or NULL */) {
+  double* logit = (double*)malloc(sizeof(double) * (size_t)(n_set > 0 ? n_set : 1));
+  double* acc = (double*)malloc(sizeof(double) * (size_t)Dv);
+  if (!logit || !acc) { free(logit); free(acc); return 2; }
+  for (int h = 0; h < H; ++h) {
+    const uint16_t* qh = q_row + (int64_t)h * Dqk;
+    double mx = -INFINITY;
+    for (int64_t i = 0; i < n_set; ++i) {
+      const uint16_t* kr = kv_cache + rows_of_set[i] * kv_dim;
+      double dot = 0.0;
+      for (int c = 0; c < Dqk; ++c) dot += oracle_bf16_to_double(qh[c]) * oracle_bf16_to_double(kr[c]);
+      logit[i] = sm_scale * dot;
+      if (logit[i] > mx) mx = logit[i];
+    }
+    for (int c = 0; c < Dv; ++c) acc[c] = 0.0;
+    double denom = 0.0;
+    for (int64_t i = 0; i < n_set; ++i) {
+      double p = exp(logit[i] - mx);
+      const uint16_t* vr = kv_cache + rows_of_set[i] * kv_dim + v_col0;
+      denom += p;
+      for (int c = 0; c < Dv; ++c) acc[c] += p * oracle_bf16_to_double(vr[c]);
+    }
+    for (int c = 0; c < Dv; ++c) out[(int64_t)h * Dv + c] = n_set > 0 ? (float)(acc[c] / denom) : 0.0f;
+    if (lse) lse[h] = n_set > 0 ? (float)(mx + log(denom)) : -INFINITY;
+  }
+  free(logit);
+  free(acc);
+  return 0;
+}
+
+static int bad_attn(int H, int Dqk, int Dv, int kv_dim, int v_col0, int page_size) {
+  if (H < 1 || Dqk < 1 || Dv < 1 || page_size < 1) return 1;
+  if (Dqk > kv_dim || v_col0 < 0 || v_col0 + Dv > kv_dim) return 1;
+  return 0;
+}
+
+int oracle_sparse_mla(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
+                      int64_t ld_pt, int page_size, int num_pages, const int32_t* q_pos, int n_seq,
+                      int q_per_seq, const int32_t* idx, int64_t ld_idx, int k, int H, int Dqk,
+                      int Dv, int kv_dim, int v_col0, double sm_scale, float* out, float* lse,
+                      int row_begin, int row_end) {
+  if (bad_common(n_seq, q_per_seq, row_begin, row_end) || k < 0) return 1;
+  if (bad_attn(H, Dqk, Dv, kv_dim, v_col0, page_size)) return 1;
+  int64_t* set = (int64_t*)malloc(sizeof(int64_t) * (size_t)(k > 0 ? k : 1));
+  if (!set) return 2;
+  for (int r = row_begin; r < row_end; ++r) {
+    int s = r / q_per_seq;
+    int64_t t = q_pos[r], n_set = 0;
+    for (int i = 0; i < k; ++i) {
+      int64_t j = idx[(int64_t)r * ld_idx + i];
+      if (j < 0 || j > t) continue; /* not a visible position, so not in S_t */
+      int64_t row = phys_row(page_table, ld_pt, page_size, num_pages, s, j);
+      if (row < 0) { free(set); return 3; }
+      set[n_set++] = row;
+    }
+    int rc = attend_row(q + (int64_t)r * H * Dqk, kv_cache, set, n_set, H, Dqk, Dv, kv_dim, v_col0,
+                        sm_scale, out + (int64_t)r * H * Dv, lse ? lse + (int64_t)r * H : NULL);
+    if (rc) { free(set); return rc; }
+  }
+  free(set);
+  return 0;
+}
+
+int oracle_dense_mla(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
+                     int64_t ld_pt, int page_size, int num_pages, const int32_t* q_pos, int n_seq,
+                     int q_per_seq, int H, int Dqk, int Dv, int kv_dim, int v_col0,
+                     double sm_scale, float* out, float* lse, int row_begin, int row_end) {
+  if (bad_common(n_seq, q_per_seq, row_begin, row_end)) return 1;
+  if (bad_attn(H, Dqk, Dv, kv_dim, v_col0, page_size)) return 1;
+  for (int r = row_begin; r < row_end; ++r) {
+    int s = r / q_per_seq;
+    int64_t n_set = (int64_t)q_pos[r] + 1;
+    if (n_set < 0) n_set = 0;
+    int64_t* set = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_set > 0 ? n_set : 1));
+    if (!set) return 2;
+    for (int64_t j = 0; j < n_set; ++j) {
+      set[j] = phys_row(page_table, ld_pt, page_size, num_pages, s, j);
+      if (set[j] < 0) { free(set); return 3; }
+    }
+    int rc = attend_row(q + (int64_t)r * H * Dqk, kv_cache, set, n_set, H, Dqk, Dv, kv_dim, v_col0,
+                        sm_scale, out + (int64_t)r * H * Dv, lse ? lse + (int64_t)r * H : NULL);
+    free(set);
+    if (rc) return rc;
+  }
+  return 0;
+}

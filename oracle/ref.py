@@ -1,0 +1,198 @@
+"""ctypes wrapper of the C oracle (``liboracle.so``), built with plain gcc.
+
+TEST INFRASTRUCTURE ONLY (tests, smoke check, the benchmark's CPU baseline). Arrays are
+numpy; every call can split rows over host threads (ctypes drops the GIL during a call).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dsa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+E4M3 = 0
+F32 = 1
+
+_lib = None
+_lock = threading.Lock()
+
+
+def build_oracle(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, so every double operation is IEEE)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
+             "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"],
+            check=True,
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                build_oracle(force=True)
+            lib = ctypes.CDLL(_LIB_PATH)
+            vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+            lib.oracle_e4m3_to_double.restype = dbl
+            lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+            lib.oracle_bf16_to_double.restype = dbl
+            lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+            lib.oracle_indexer_scores.restype = i32
+            lib.oracle_indexer_scores.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, vp, i32, i32, i32,
+                                                  i32, i32, vp, i64, i32, i32]
+            lib.oracle_topk.restype = i32
+            lib.oracle_topk.argtypes = [vp, i64, vp, i32, i32, vp, i64, i32, i32]
+            lib.oracle_sparse_mla.restype = i32
+            lib.oracle_sparse_mla.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, i32, vp, i64, i32, i32,
+                                              i32, i32, i32, i32, dbl, vp, vp, i32, i32]
+            lib.oracle_dense_mla.restype = i32
+            lib.oracle_dense_mla.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, i32, i32, i32, i32,
+                                             i32, i32, dbl, vp, vp, i32, i32]
+            _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _run_rows(fn, rows, threads, row_subset=None):
+    """Call fn(row_begin, row_end) over [0, rows) (or over the given sorted row subset)
+    split across `threads` host threads; raise on a nonzero return code."""
+    if row_subset is not None:
+        spans = [(int(r), int(r) + 1) for r in row_subset]
+    else:
+        threads = max(1, min(threads, rows)) if rows > 0 else 1
+        step = (rows + threads - 1) // threads if rows > 0 else 0
+        spans = [(b, min(rows, b + step)) for b in range(0, rows, step)] if rows > 0 else []
+    errors = []
+
+    def work(chunk):
+        for b, e in chunk:
+            rc = fn(b, e)
+            if rc != 0:
+                errors.append(rc)
+
+    n = max(1, min(threads, len(spans)))
+    chunks = [spans[i::n] for i in range(n)]
+    ts = [threading.Thread(target=work, args=(c,)) for c in chunks]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    if errors:
+        raise ValueError(f"oracle call failed with code {errors[0]}")
+
+
+def e4m3_to_double(code: int) -> float:
+    return _load().oracle_e4m3_to_double(code)
+
+
+def bf16_to_double(bits: int) -> float:
+    return _load().oracle_bf16_to_double(bits)
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == dtype, (a.dtype, dtype)
+    return a
+
+
+def indexer_scores(q, w, k_cache, k_scale, page_table, page_size, q_pos, n_seq, q_per_seq, fmt,
+                   ld_scores, scores=None, threads=1, rows=None):
+    """Scores [n_seq*q_per_seq, ld_scores] float32; entries j > q_pos[r] are left as given
+    (NaN in a fresh array). `rows` optionally restricts the computed rows."""
+    lib = _load()
+    qdt = np.uint8 if fmt == E4M3 else np.float32
+    q = _c(q, qdt)
+    k_cache = _c(k_cache, qdt)
+    w = _c(w, np.float32)
+    pt = _c(page_table, np.int32)
+    q_pos = _c(q_pos, np.int32)
+    ks = None if k_scale is None else _c(k_scale, np.float32)
+    nrows = n_seq * q_per_seq
+    Hi, Di = q.shape[-2], q.shape[-1]
+    num_pages = k_cache.shape[0]
+    if scores is None:
+        scores = np.full((nrows, ld_scores), np.nan, dtype=np.float32)
+
+    def fn(b, e):
+        return lib.oracle_indexer_scores(_ptr(q), _ptr(w), _ptr(k_cache), _ptr(ks), _ptr(pt), pt.shape[1],
+                                         page_size, num_pages, _ptr(q_pos), n_seq, q_per_seq, Hi, Di, fmt,
+                                         _ptr(scores), ld_scores, b, e)
+
+    _run_rows(fn, nrows, threads, rows)
+    return scores
+
+
+def topk(scores, q_pos, k, threads=1, rows=None, idx=None):
+    lib = _load()
+    scores = _c(scores, np.float32)
+    q_pos = _c(q_pos, np.int32)
+    nrows = scores.shape[0]
+    if idx is None:
+        idx = np.full((nrows, k), -2, dtype=np.int32)
+
+    def fn(b, e):
+        return lib.oracle_topk(_ptr(scores), scores.shape[1], _ptr(q_pos), nrows, k, _ptr(idx), k, b, e)
+
+    _run_rows(fn, nrows, threads, rows)
+    return idx
+
+
+def sparse_mla(q, kv_cache, page_table, page_size, q_pos, n_seq, q_per_seq, idx, Dqk, Dv, v_col0,
+               sm_scale, threads=1, rows=None, with_lse=True):
+    """q: uint16 (bf16 bits) [rows, H, Dqk]; kv_cache: uint16 [P, page, kv_dim];
+    returns (out float32 [rows, H, Dv], lse float32 [rows, H])."""
+    lib = _load()
+    q = _c(q, np.uint16)
+    kv = _c(kv_cache, np.uint16)
+    pt = _c(page_table, np.int32)
+    q_pos = _c(q_pos, np.int32)
+    idx = _c(idx, np.int32)
+    nrows, H = q.shape[0], q.shape[1]
+    kv_dim = kv.shape[-1]
+    num_pages = kv.shape[0]
+    out = np.full((nrows, H, Dv), np.nan, dtype=np.float32)
+    lse = np.full((nrows, H), np.nan, dtype=np.float32) if with_lse else None
+
+    def fn(b, e):
+        return lib.oracle_sparse_mla(_ptr(q), _ptr(kv), _ptr(pt), pt.shape[1], page_size, num_pages,
+                                     _ptr(q_pos), n_seq, q_per_seq, _ptr(idx), idx.shape[1], idx.shape[1],
+                                     H, Dqk, Dv, kv_dim, v_col0, float(sm_scale), _ptr(out), _ptr(lse), b, e)
+
+    _run_rows(fn, nrows, threads, rows)
+    return out, lse
+
+
+def dense_mla(q, kv_cache, page_table, page_size, q_pos, n_seq, q_per_seq, Dqk, Dv, v_col0, sm_scale,
+              threads=1, rows=None, with_lse=True):
+    lib = _load()
+    q = _c(q, np.uint16)
+    kv = _c(kv_cache, np.uint16)
+    pt = _c(page_table, np.int32)
+    q_pos = _c(q_pos, np.int32)
+    nrows, H = q.shape[0], q.shape[1]
+    kv_dim = kv.shape[-1]
+    num_pages = kv.shape[0]
+    out = np.full((nrows, H, Dv), np.nan, dtype=np.float32)
+    lse = np.full((nrows, H), np.nan, dtype=np.float32) if with_lse else None
+
+    def fn(b, e):
+        return lib.oracle_dense_mla(_ptr(q), _ptr(kv), _ptr(pt), pt.shape[1], page_size, num_pages,
+                                    _ptr(q_pos), n_seq, q_per_seq, H, Dqk, Dv, kv_dim, v_col0,
+                                    float(sm_scale), _ptr(out), _ptr(lse), b, e)
+
+    _run_rows(fn, nrows, threads, rows)
+    return out, lse

@@ -1,0 +1,395 @@
+"""Pins of the CPU oracle against facts fixed independently of it (CPU only).
+
+Each test checks the oracle against something other than itself: the worked example printed
+on the DSA blog page, library routines (torch's FP8/bf16 decoders, torch.topk, numpy einsum,
+torch's float64 scaled_dot_product_attention), closed forms and brute force. The cases are
+chosen so that a plausible slip (a dropped ReLU, a sign, a transposed operand, a wrong tie
+rule, a missing scale, an off-by-one in causality) fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _golden():
+    with open(os.path.join(HERE, "golden", "worked_example.json")) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- decoders
+
+
+def test_e4m3_decode_matches_torch_for_all_codes(oracle_lib):
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        got = oracle_lib.e4m3_to_double(c)
+        if math.isnan(ref[c]):
+            assert math.isnan(got), c
+        else:
+            assert got == ref[c] and math.copysign(1, got) == math.copysign(1, ref[c]), (c, got, ref[c])
+
+
+def test_e4m3_spec_values(oracle_lib):
+    # OCP E4M3FN: bias 7, max normal 448, min subnormal 2^-9, S.1111.111 = NaN
+    d = oracle_lib.e4m3_to_double
+    assert d(0x38) == 1.0 and d(0x40) == 2.0 and d(0x7E) == 448.0 and d(0xFE) == -448.0
+    assert d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9 and d(0x08) == 2.0 ** -6
+    assert d(0x80) == 0.0 and math.copysign(1, d(0x80)) == -1.0
+    assert math.isnan(d(0x7F)) and math.isnan(d(0xFF))
+
+
+def test_bf16_decode_matches_torch(oracle_lib):
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 1 << 16, size=4000, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    for b, r in zip(bits, ref):
+        got = oracle_lib.bf16_to_double(int(b))
+        assert (math.isnan(got) and math.isnan(r)) or got == r
+
+
+# ---------------------------------------------------------------- indexer helpers
+
+
+def _one_page_table(n_seq, pages_per_seq):
+    return np.arange(n_seq * pages_per_seq, dtype=np.int32).reshape(n_seq, pages_per_seq)
+
+
+def _worked_inputs(coeff, head_w, heads, dims, extra_head=None):
+    """Query at 0-based position 7 of one sequence; keys k_j = coeff_j * e_1."""
+    T = len(coeff)
+    q = np.zeros((1, heads, dims), np.float32)
+    q[0, :, 0] = 1.0
+    w = np.full((1, heads), head_w, np.float32)
+    k = np.zeros((1, 64, dims), np.float32)   # one 64-token page
+    k[0, :T, 0] = coeff
+    if extra_head is not None:   # (head, weight, {pos: value}) on component 1
+        h, wv, comps = extra_head
+        q[0, h, :] = 0.0
+        q[0, h, 1] = 1.0
+        w[0, h] = wv
+        for p, v in comps.items():
+            k[0, p, 1] = v
+    return q, w, k, np.array([T - 1], np.int32)
+
+
+def _select(oracle_lib, q, w, k, q_pos, kk, fmt=1, k_scale=None):
+    pt = _one_page_table(1, k.shape[0])
+    s = oracle_lib.indexer_scores(q, w, k, k_scale, pt, 64, q_pos, 1, len(q_pos), fmt, 64 * k.shape[0])
+    idx = oracle_lib.topk(s, q_pos, kk)
+    return s, idx
+
+
+def test_worked_example_from_golden(oracle_lib):
+    g = _golden()
+    q, w, k, q_pos = _worked_inputs(g["key_coeff_by_position_1based"], g["head_weight"], g["heads"], g["dims"])
+    s, idx = _select(oracle_lib, q, w, k, q_pos, g["k"])
+    # the construction gives I_8j = c_j exactly (4 * 1/4 * c_j)
+    np.testing.assert_array_equal(s[0, :8], np.float32(g["key_coeff_by_position_1based"]))
+    assert [int(i) + 1 for i in idx[0]] == g["expected_1based"]
+
+
+def test_worked_example_relu_not_abs(oracle_lib):
+    g = _golden()
+    c = list(g["key_coeff_by_position_1based"])
+    c[0] = -5.0   # largest magnitude, but ReLU clips it to 0
+    q, w, k, q_pos = _worked_inputs(c, g["head_weight"], g["heads"], g["dims"])
+    s, idx = _select(oracle_lib, q, w, k, q_pos, g["k"])
+    assert s[0, 0] == 0.0
+    assert [int(i) + 1 for i in idx[0]] == [2, 5, 8]
+
+
+def test_worked_example_negative_head_weight_demotes(oracle_lib):
+    g = _golden()
+    c = g["key_coeff_by_position_1based"]
+    # head 3 looks at component 1, weight -1; only position 5 (1-based) has that component
+    q, w, k, q_pos = _worked_inputs(c, g["head_weight"], g["heads"], g["dims"], extra_head=(3, -1.0, {4: 1.0}))
+    s, idx = _select(oracle_lib, q, w, k, q_pos, g["k"])
+    expect = [0.75 * x for x in c]
+    expect[4] -= 1.0
+    np.testing.assert_allclose(s[0, :8], expect, rtol=1e-6)
+    assert [int(i) + 1 for i in idx[0]] == [2, 7, 8]
+
+
+def test_worked_example_causality_excludes_future(oracle_lib):
+    # the same query at position 8 (1-based) must not see a huge score at position 9
+    g = _golden()
+    c = list(g["key_coeff_by_position_1based"]) + [100.0]
+    q, w, k, _ = _worked_inputs(c, g["head_weight"], g["heads"], g["dims"])
+    s, idx = _select(oracle_lib, q, w, k, np.array([7], np.int32), g["k"])
+    assert [int(i) + 1 for i in idx[0]] == [2, 5, 8]
+
+
+def _np_scores(q, w, keys_by_pos, q_pos, q_per_seq, seq_keys):
+    out = {}
+    for r in range(q.shape[0]):
+        s = r // q_per_seq
+        K = seq_keys[s][: q_pos[r] + 1]                                      # [t+1, Di]
+        dots = np.einsum("hd,jd->hj", q[r].astype(np.float64), K)            # [Hi, t+1]
+        out[r] = np.einsum("h,hj->j", w[r].astype(np.float64), np.maximum(dots, 0.0))
+    return out
+
+
+def test_indexer_f32_matches_numpy_einsum_with_permuted_pages(oracle_lib):
+    rng = np.random.default_rng(1)
+    n_seq, qps, Hi, Di, ps = 2, 3, 5, 12, 64
+    pps = 3
+    P = n_seq * pps + 2
+    perm = rng.permutation(P)[: n_seq * pps].astype(np.int32).reshape(n_seq, pps)
+    k_cache = rng.standard_normal((P, ps, Di)).astype(np.float32)
+    q = rng.standard_normal((n_seq * qps, Hi, Di)).astype(np.float32)
+    w = rng.standard_normal((n_seq * qps, Hi)).astype(np.float32)
+    q_pos = np.array([0, 70, 191, 5, 64, 150], np.int32)
+    s = oracle_lib.indexer_scores(q, w, k_cache, None, perm, ps, q_pos, n_seq, qps, 1, 192)
+    seq_keys = [np.concatenate([k_cache[perm[b, p]] for p in range(pps)]).astype(np.float64) for b in range(n_seq)]
+    ref = _np_scores(q, w, None, q_pos, qps, seq_keys)
+    for r, v in ref.items():
+        np.testing.assert_allclose(s[r, : q_pos[r] + 1], v.astype(np.float32), rtol=2e-6, atol=1e-6)
+        assert np.isnan(s[r, q_pos[r] + 1:]).all()      # nothing written past the visible prefix
+
+
+def test_indexer_e4m3_matches_torch_decode_and_einsum(oracle_lib):
+    w = workloads.make_random(1, 2, [100, 127], 128, Hi=8, Di=32, H=2, Dqk=16, Dv=8, seed=7)
+    s = oracle_lib.indexer_scores(w.iq, w.iw, w.ik, w.iks, w.page_table, 64, w.q_pos, 1, 2, 0, 128)
+    dec = lambda b: torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    keys = dec(w.ik).reshape(-1, 32) * w.iks.reshape(-1, 1).astype(np.float64)
+    qd = dec(w.iq)
+    ref = _np_scores(qd, w.iw, None, w.q_pos, 2, [keys])
+    for r, v in ref.items():
+        np.testing.assert_allclose(s[r, : w.q_pos[r] + 1], v.astype(np.float32), rtol=1e-6, atol=1e-7)
+
+
+def test_indexer_key_scale_homogeneity_exact(oracle_lib):
+    # ReLU is positively homogeneous: scaling one key's scale by 4 scales its score by exactly 4
+    w = workloads.make_random(1, 1, [63], 64, Hi=8, Di=32, H=2, Dqk=16, Dv=8, seed=9)
+    s1 = oracle_lib.indexer_scores(w.iq, w.iw, w.ik, w.iks, w.page_table, 64, w.q_pos, 1, 1, 0, 64)
+    ks = w.iks.copy()
+    ks[0, 10] *= 4.0
+    s2 = oracle_lib.indexer_scores(w.iq, w.iw, w.ik, ks, w.page_table, 64, w.q_pos, 1, 1, 0, 64)
+    assert s2[0, 10] == np.float32(4.0) * s1[0, 10]
+    others = [j for j in range(64) if j != 10]
+    np.testing.assert_array_equal(s2[0, others], s1[0, others])
+
+
+# ---------------------------------------------------------------- top-k
+
+
+def _rank_key(v, j):
+    return (-v, j)
+
+
+def test_topk_brute_force_small_rows_with_ties(oracle_lib):
+    rng = np.random.default_rng(2)
+    values = np.array([-1.0, -0.0, 0.0, 0.5, 1.0, 2.0], np.float32)
+    for trial in range(300):
+        n = int(rng.integers(1, 11))
+        k = int(rng.integers(1, 13))
+        sc = rng.choice(values, size=n).astype(np.float32)
+        row = np.full((1, 16), np.nan, np.float32)
+        row[0, :n] = sc
+        idx = oracle_lib.topk(row, np.array([n - 1], np.int32), k)[0]
+        m = min(k, n)
+        # brute force: the unique m-subset whose members all outrank (value desc, position asc)
+        # every non-member
+        winners = []
+        for sub in itertools.combinations(range(n), m):
+            rest = [j for j in range(n) if j not in sub]
+            if all(_rank_key(float(sc[a]), a) < _rank_key(float(sc[b]), b) for a in sub for b in rest):
+                winners.append(sub)
+        assert len(winners) == 1
+        assert list(idx[:m]) == list(winners[0])
+        assert list(idx[m:]) == [-1] * (k - m)
+
+
+def test_topk_values_match_torch_topk(oracle_lib):
+    rng = np.random.default_rng(3)
+    sc = rng.standard_normal((3, 5000)).astype(np.float32)
+    q_pos = np.array([4999, 3000, 100], np.int32)
+    idx = oracle_lib.topk(sc, q_pos, 512)
+    for r in range(3):
+        n = q_pos[r] + 1
+        m = min(512, n)
+        ref = torch.topk(torch.from_numpy(sc[r, :n]), m).values.numpy()
+        got = np.sort(sc[r, idx[r, :m]])[::-1]
+        np.testing.assert_array_equal(got, ref)
+        assert (np.diff(idx[r, :m]) > 0).all()       # ascending, no duplicates
+
+
+def test_topk_short_prefix_keeps_everything(oracle_lib):
+    sc = np.random.default_rng(4).standard_normal((2, 64)).astype(np.float32)
+    idx = oracle_lib.topk(sc, np.array([9, 0], np.int32), 32)
+    assert list(idx[0, :10]) == list(range(10)) and (idx[0, 10:] == -1).all()
+    assert idx[1, 0] == 0 and (idx[1, 1:] == -1).all()
+
+
+def test_topk_signed_zero_ties_by_position(oracle_lib):
+    sc = np.array([[0.0, -0.0, 0.0, -0.0, -1.0, 0.0]], np.float32)
+    idx = oracle_lib.topk(sc, np.array([5], np.int32), 3)
+    assert list(idx[0]) == [0, 1, 2]
+
+
+# ---------------------------------------------------------------- attention
+
+
+def _bf16(x):
+    return workloads.bf16_bits(torch.as_tensor(x, dtype=torch.float32))
+
+
+def _dec_bf16(bits):
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64)
+
+
+def _attn_case(seed=5, rows=4, H=3, Dqk=16, Dv=8, kv_dim=24, v_col0=8, T=100):
+    rng = np.random.default_rng(seed)
+    q = _bf16(rng.standard_normal((rows, H, Dqk)))
+    kv = _bf16(rng.standard_normal((2, 64, kv_dim)))
+    pt = np.array([[1, 0]], np.int32)         # non-identity paging
+    q_pos = np.array(sorted(rng.integers(0, T, rows)), np.int32)
+    return q, kv, pt, q_pos
+
+
+def _rows_of(kv, pt, n):
+    flat = kv.reshape(-1, kv.shape[-1])
+    return np.stack([flat[pt[0, p // 64] * 64 + p % 64] for p in range(n)])
+
+
+def test_sparse_attention_matches_torch_sdpa_with_mask(oracle_lib):
+    q, kv, pt, q_pos = _attn_case()
+    rows, H, Dqk = q.shape
+    Dv, v0, T = 8, 8, 128
+    rng = np.random.default_rng(6)
+    k = 12
+    idx = np.full((rows, k), -1, np.int32)
+    for r in range(rows):
+        m = min(k, q_pos[r] + 1)
+        idx[r, :m] = np.sort(rng.choice(q_pos[r] + 1, m, replace=False))
+    scale = 0.37
+    out, lse = oracle_lib.sparse_mla(q, kv, pt, 64, q_pos, 1, rows, idx, Dqk, Dv, v0, scale)
+    allrows = _dec_bf16(_rows_of(kv, pt, T))                          # [T, kv_dim]
+    K, V = allrows[:, :Dqk], allrows[:, v0: v0 + Dv]
+    Q = _dec_bf16(q)                                                  # [rows, H, Dqk]
+    mask = torch.zeros(rows, T, dtype=torch.bool)
+    for r in range(rows):
+        for j in idx[r]:
+            if j >= 0:
+                mask[r, j] = True
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        Q.transpose(0, 1), K.expand(H, T, Dqk), V.expand(H, T, Dv),
+        attn_mask=mask.unsqueeze(0).expand(H, rows, T), scale=scale).transpose(0, 1)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-6, atol=1e-6)
+    logits = scale * torch.einsum("rhd,jd->rhj", Q, K)
+    ref_lse = torch.logsumexp(logits.masked_fill(~mask.unsqueeze(1), -math.inf), dim=-1)
+    np.testing.assert_allclose(lse, ref_lse.numpy(), rtol=1e-6, atol=1e-6)
+
+
+def test_dense_attention_matches_torch_sdpa_causal(oracle_lib):
+    q, kv, pt, q_pos = _attn_case(seed=8)
+    rows, H, Dqk = q.shape
+    out, lse = oracle_lib.dense_mla(q, kv, pt, 64, q_pos, 1, rows, Dqk, 8, 8, 0.25)
+    T = 128
+    allrows = _dec_bf16(_rows_of(kv, pt, T))
+    K, V = allrows[:, :Dqk], allrows[:, 8:16]
+    Q = _dec_bf16(q)
+    mask = torch.arange(T).unsqueeze(0) <= torch.from_numpy(q_pos).long().unsqueeze(1)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        Q.transpose(0, 1), K.expand(H, T, Dqk), V.expand(H, T, 8),
+        attn_mask=mask.unsqueeze(0).expand(H, rows, T), scale=0.25).transpose(0, 1)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-6, atol=1e-6)
+
+
+def test_sparse_with_full_set_equals_dense_bitwise(oracle_lib):
+    # k >= t: DSA is dense causal attention (the handbook's k = min(L, 2048))
+    q, kv, pt, q_pos = _attn_case(seed=10)
+    rows, H, Dqk = q.shape
+    k = 128
+    idx = np.full((rows, k), -1, np.int32)
+    for r in range(rows):
+        idx[r, : q_pos[r] + 1] = np.arange(q_pos[r] + 1)
+    o1, l1 = oracle_lib.sparse_mla(q, kv, pt, 64, q_pos, 1, rows, idx, Dqk, 8, 8, 0.3)
+    o2, l2 = oracle_lib.dense_mla(q, kv, pt, 64, q_pos, 1, rows, Dqk, 8, 8, 0.3)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_sparse_single_position_returns_its_value_row(oracle_lib):
+    q, kv, pt, q_pos = _attn_case(seed=11)
+    rows, H, Dqk = q.shape
+    idx = np.full((rows, 4), -1, np.int32)
+    idx[:, 0] = q_pos // 2
+    out, lse = oracle_lib.sparse_mla(q, kv, pt, 64, q_pos, 1, rows, idx, Dqk, 8, 8, 0.5)
+    allrows = _dec_bf16(_rows_of(kv, pt, 128)).numpy()
+    Q = _dec_bf16(q).numpy()
+    for r in range(rows):
+        j = idx[r, 0]
+        np.testing.assert_array_equal(out[r], np.broadcast_to(allrows[j, 8:16].astype(np.float32), (H, 8)))
+        np.testing.assert_allclose(lse[r], 0.5 * Q[r] @ allrows[j, :Dqk], rtol=1e-6)
+
+
+def test_sparse_zero_query_averages_values(oracle_lib):
+    q, kv, pt, q_pos = _attn_case(seed=12)
+    q[:] = 0
+    rows, H, Dqk = q.shape
+    idx = np.full((rows, 6), -1, np.int32)
+    for r in range(rows):
+        m = min(6, q_pos[r] + 1)
+        idx[r, :m] = np.arange(q_pos[r] + 1 - m, q_pos[r] + 1)
+    out, lse = oracle_lib.sparse_mla(q, kv, pt, 64, q_pos, 1, rows, idx, Dqk, 8, 8, 1.0)
+    allrows = _dec_bf16(_rows_of(kv, pt, 128)).numpy()
+    for r in range(rows):
+        sel = idx[r][idx[r] >= 0]
+        np.testing.assert_allclose(out[r], np.broadcast_to(allrows[sel, 8:16].mean(0), (H, 8)), rtol=1e-6, atol=1e-7)
+        np.testing.assert_allclose(lse[r], math.log(len(sel)), rtol=1e-6)
+
+
+def test_sparse_ignores_padding_and_invisible_entries(oracle_lib):
+    q, kv, pt, q_pos = _attn_case(seed=13)
+    rows, H, Dqk = q.shape
+    base = np.full((rows, 5), -1, np.int32)
+    noisy = np.full((rows, 8), -1, np.int32)
+    for r in range(rows):
+        sel = np.arange(min(3, q_pos[r] + 1))
+        base[r, : len(sel)] = sel
+        noisy[r, : len(sel)] = sel
+        noisy[r, 5] = q_pos[r] + 1          # a future position is not visible
+        noisy[r, 6] = -7
+    o1, l1 = oracle_lib.sparse_mla(q, kv, pt, 64, q_pos, 1, rows, base, Dqk, 8, 8, 0.3)
+    o2, l2 = oracle_lib.sparse_mla(q, kv, pt, 64, q_pos, 1, rows, noisy, Dqk, 8, 8, 0.3)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_sparse_empty_set(oracle_lib):
+    q, kv, pt, q_pos = _attn_case(seed=14)
+    rows, H, Dqk = q.shape
+    idx = np.full((rows, 4), -1, np.int32)
+    out, lse = oracle_lib.sparse_mla(q, kv, pt, 64, q_pos, 1, rows, idx, Dqk, 8, 8, 0.3)
+    assert (out == 0).all() and np.isneginf(lse).all()
+
+
+def test_tiny_workload_end_to_end_invariants(oracle_lib):
+    """The tiny prefill workload: every row with t + 1 <= k reproduces dense attention, and the
+    selected sets obey the score order."""
+    w = workloads.make_tiny()
+    s = oracle_lib.indexer_scores(w.iq, w.iw, w.ik, None, w.page_table, 64, w.q_pos, 1, w.rows, 1, w.max_ctx)
+    idx = oracle_lib.topk(s, w.q_pos, w.topk)
+    out, lse = oracle_lib.sparse_mla(w.q, w.kv, w.page_table, 64, w.q_pos, 1, w.rows, idx, w.Dqk, w.Dv, w.v_col0, w.sm_scale)
+    dout, dlse = oracle_lib.dense_mla(w.q, w.kv, w.page_table, 64, w.q_pos, 1, w.rows, w.Dqk, w.Dv, w.v_col0, w.sm_scale)
+    short = w.q_pos + 1 <= w.topk
+    np.testing.assert_array_equal(out[short], dout[short])
+    assert not np.allclose(out[~short], dout[~short])   # sparse differs once the prefix exceeds k
+    for r in range(w.rows):
+        n = w.q_pos[r] + 1
+        sel = idx[r][idx[r] >= 0]
+        assert len(sel) == min(n, w.topk)
+        if n > w.topk:
+            rest = np.setdiff1d(np.arange(n), sel)
+            assert s[r, sel].min() >= s[r, rest].max()
