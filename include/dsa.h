@@ -1,0 +1,177 @@
+/* dsa.h -- C ABI of libdsa.so: the DeepSeek Sparse Attention (DSA) hot path on gfx950.
+ *
+ * Page references:
+ *   [DSA-blog]  "DeepSeek Sparse Attention：从 SWA 到稀疏 Attention 计算" (kevinye.org)
+ *   [Handbook]  "MTP 与稀疏注意力：NSA 与 DSA" (anrans.github.io, ai-infra-handbooks)
+ *
+ * The path, per query row: the Lightning Indexer scores every visible position
+ * (dsa_indexer_scores), an exact top-k picks the index set S_t (dsa_topk), and attention runs
+ * over the latent rows in S_t only (dsa_sparse_mla_decode / dsa_sparse_mla_prefill). A dense
+ * causal attention (dsa_dense_mla_prefill) serves short prefill, where it equals DSA exactly
+ * whenever every prefix is no longer than k.
+ *
+ * Common conventions
+ * ------------------
+ * Pointers: every array argument is a DEVICE pointer (HIP global memory) unless stated
+ *   otherwise; `stream` is a hipStream_t passed as void* (NULL = the null stream). The caller
+ *   owns all memory. The library never allocates, frees or synchronises: each call validates
+ *   its host-side arguments, then only enqueues kernels on `stream` and returns. Arrays must
+ *   stay valid until that work completes. Calls on different streams are independent.
+ * Rows: a call processes rows = n_seq * q_per_seq query rows; row r belongs to sequence
+ *   s = r / q_per_seq and sits at 0-based position q_pos[r] (device int32 [rows]). It sees
+ *   positions j in [0, q_pos[r]], itself included ([DSA-blog] "Lightning Indexer": j <= t; the
+ *   worked example selects the query's own position 8). Decode uses q_per_seq = 1, MTP
+ *   verification q_per_seq = 2 (both rows of a request share one scan of its keys), a prefill
+ *   chunk n_seq = 1 and q_per_seq = chunk length.
+ * Paging: both caches are paged. Position p of sequence s is physical row
+ *   page_table[s * ld_pt + p / page_size] * page_size + p % page_size
+ *   of a cache holding num_pages * page_size rows. page_table is device int32 [n_seq, ld_pt].
+ *   A contiguous cache is the identity table.
+ * Host bound: max_ctx (host int) must exceed every q_pos; it sizes grids so that no call has
+ *   to read device memory on the host. Page ids and positions outside their ranges never cause
+ *   an out-of-bounds access (kernels bound-check them); the affected results are unspecified.
+ * Errors: DSA_ERR_INVALID_ARG for a bad host argument (null pointer, 16-byte misalignment of
+ *   a cache or activation array, non-positive size, inconsistent dims), DSA_ERR_WORKSPACE for
+ *   a missing or small workspace, DSA_ERR_UNSUPPORTED for a shape no kernel here handles (the
+ *   library never substitutes a different computation), DSA_ERR_HIP when a launch fails. On
+ *   any error nothing is enqueued (a DSA_ERR_HIP may follow partial work of the same call).
+ *   dsa_last_error() gives a message for the calling thread's last failed call.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1,
+  DSA_ERR_UNSUPPORTED = 2,
+  DSA_ERR_WORKSPACE = 3,
+  DSA_ERR_HIP = 4
+} dsa_status_t;
+
+/* Element format of the indexer operands. */
+typedef enum {
+  DSA_E4M3 = 0, /* OCP FP8 E4M3FN bytes (gfx950's native FP8) */
+  DSA_F32 = 1   /* IEEE binary32 */
+} dsa_dtype_t;
+
+/* Kernel variants reported by dsa_last_path() (observability only, never a control). */
+enum {
+  DSA_PATH_NONE = 0,
+  DSA_PATH_INDEXER_GENERIC = 1,       /* any Hi, Di, dtype: one thread per (row, key), VALU */
+  DSA_PATH_INDEXER_SCAN_MFMA = 2,     /* Hi=64, Di=128, E4M3, q_per_seq <= 2: key scan */
+  DSA_PATH_INDEXER_PREFILL_MFMA = 3,  /* Hi=64, Di=128, E4M3, q_per_seq > 2: query x key tiles */
+  DSA_PATH_TOPK_COPY = 10,            /* every row no longer than k: all positions kept */
+  DSA_PATH_TOPK_RADIX = 11,           /* radix select, one workgroup per row */
+  DSA_PATH_MLA_GENERIC = 20,          /* any shape: one wave per (row, head), VALU */
+  DSA_PATH_MLA_MFMA = 21,             /* H=128, Dqk=576, Dv=512: bf16 MFMA, one pass */
+  DSA_PATH_MLA_MFMA_SPLIT = 22        /* as 21, key set split over workgroups + combine */
+};
+
+const char* dsa_status_string(dsa_status_t status);
+/* Message of the calling thread's most recent failed call ("" if none). */
+const char* dsa_last_error(void);
+/* DSA_PATH_* of the kernel variant used by the calling thread's most recent successful call. */
+int dsa_last_path(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * dsa_indexer_scores -- Lightning Indexer ([DSA-blog] "Lightning Indexer", the equation for
+ * I_tj; [Handbook] "稀疏注意力：NSA 与 DSA", index score with 64 heads of 128 dims, FP8):
+ *     scores[r, j] = k_scale[j] * sum_h w[r, h] * ReLU( q[r, h, :] . k8[j, :] ),  j <= q_pos[r]
+ * i.e. the page's I_tj with the dequantised key k_j = k_scale_j * k8_j (k_scale > 0, so the
+ * scale commutes with ReLU).
+ *   q        [rows, Hi, Di]        E4M3 bytes or f32 (per dtype), 16-byte aligned
+ *   w        [rows, Hi]            f32 head weights
+ *   k_cache  [num_pages, page_size, Di]  E4M3 or f32, 16-byte aligned
+ *   k_scale  [num_pages, page_size] f32 per-token key scale, or NULL for 1
+ *   scores   [rows, ld_scores] f32, ld_scores >= max_ctx; entries j <= q_pos[r] are written,
+ *            entries q_pos[r] < j < max_ctx may be written with -inf, nothing beyond.
+ * Accumulation is exact up to fp32 rounding: FP8 operands are widened exactly to f16 and
+ * contracted on the f16 matrix cores with fp32 accumulation.
+ * ------------------------------------------------------------------------------------------- */
+dsa_status_t dsa_indexer_scores(const void* q, const float* w, const void* k_cache,
+                                const float* k_scale, const int32_t* page_table, int64_t ld_pt,
+                                int page_size, int num_pages, const int32_t* q_pos, int n_seq,
+                                int q_per_seq, int max_ctx, int Hi, int Di, dsa_dtype_t dtype,
+                                float* scores, int64_t ld_scores, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * dsa_topk -- S_t = TopK_{j <= t}(I_tj, k) ([DSA-blog] "Lightning Indexer", the TopK equation);
+ * a row whose prefix holds fewer than k positions keeps all of them ([Handbook] cost model,
+ * k = min(L, 2048)).
+ *   scores [rows, ld_scores] f32 from dsa_indexer_scores; row r uses entries 0..q_pos[r]
+ *   idx    [rows, ld_idx] int32 out, ld_idx >= k: the min(k, q_pos[r]+1) selected positions in
+ *          ASCENDING order, then -1 up to slot k-1.
+ * Ranking: larger score first; equal scores (by value: -0 == +0) rank the smaller position
+ * first, so the result is unique. NaN scores are not supported (their rank is unspecified).
+ * Needs no workspace (ws may be NULL; dsa_topk_workspace_size returns 0); the arguments are
+ * kept so that future variants can use one without an ABI change.
+ * ------------------------------------------------------------------------------------------- */
+size_t dsa_topk_workspace_size(int rows, int max_ctx, int k);
+dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int rows,
+                      int max_ctx, int k, int32_t* idx, int64_t ld_idx, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * dsa_sparse_mla_decode / dsa_sparse_mla_prefill -- attention over the selected rows only
+ * ([DSA-blog] "Sparse Attention": softmax(QK^T/sqrt(d_h) + M^DSA)V with M = 0 on S_t and -inf
+ * elsewhere, computed by reading only the indexed rows; [Handbook] absorbed MLA: one latent row
+ * of 512+64 bf16 per position is the key of all 128 heads, its first 512 columns the value).
+ * For row r and head h, with S = the entries of idx[r, 0..k-1] lying in [0, q_pos[r]] (so the
+ * -1 padding and any invisible position are skipped):
+ *     l_j    = sm_scale * q[r, h, 0:Dqk] . kv[j, 0:Dqk]
+ *     out[r, h, :] = sum_{j in S} softmax(l)_j * kv[j, v_col0 : v_col0 + Dv]
+ *     lse[r, h]    = log sum_{j in S} exp(l_j)         (natural log; -inf for an empty S)
+ * An empty S gives out = 0.
+ *   q        [rows, H, Dqk] bf16 bits, 16-byte aligned
+ *   kv_cache [num_pages, page_size, kv_dim] bf16 bits, 16-byte aligned; kv_dim >= Dqk and
+ *            kv_dim >= v_col0 + Dv (absorbed MLA: kv_dim = Dqk = 576, Dv = 512, v_col0 = 0)
+ *   idx      [rows, ld_idx] int32, k entries per row (e.g. from dsa_topk)
+ *   out      [rows, H, Dv] bf16 bits out (fp32 accumulation, one rounding)
+ *   lse      [rows, H] f32 out, or NULL
+ *   ws       device workspace of at least dsa_sparse_mla_workspace_size(...) bytes (may be
+ *            NULL when that size is 0); its contents on entry do not matter
+ * Softmax runs in fp32 with the probabilities rounded to bf16 for the value product.
+ * Tuned shape: H=128, Dqk=576, Dv=512, kv_dim=576, v_col0=0 (bf16 MFMA). Other shapes with
+ * Dqk <= 1024 and Dv <= 512 run a generic VALU kernel (reported by dsa_last_path()).
+ * The decode entry point may split each row's index set over several workgroups and combine
+ * the partial results (workspace); the prefill entry point does one pass per row.
+ * ------------------------------------------------------------------------------------------- */
+size_t dsa_sparse_mla_workspace_size(int rows, int H, int Dv, int k);
+dsa_status_t dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* kv_cache,
+                                   const int32_t* page_table, int64_t ld_pt, int page_size,
+                                   int num_pages, const int32_t* q_pos, int n_seq, int q_per_seq,
+                                   const int32_t* idx, int64_t ld_idx, int k, int H, int Dqk,
+                                   int Dv, int kv_dim, int v_col0, float sm_scale, uint16_t* out,
+                                   float* lse, void* ws, size_t ws_bytes, void* stream);
+dsa_status_t dsa_sparse_mla_prefill(const uint16_t* q, const uint16_t* kv_cache,
+                                    const int32_t* page_table, int64_t ld_pt, int page_size,
+                                    int num_pages, const int32_t* q_pos, int n_seq, int q_per_seq,
+                                    const int32_t* idx, int64_t ld_idx, int k, int H, int Dqk,
+                                    int Dv, int kv_dim, int v_col0, float sm_scale, uint16_t* out,
+                                    float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * dsa_dense_mla_prefill -- dense causal attention: the computation above with S = {0..q_pos[r]}
+ * ([DSA-blog] "SWA" section, the causal set C_t). It equals DSA exactly when q_pos[r] + 1 <= k
+ * for every row ([Handbook]: short prefill falls back to dense). Arguments as above, without
+ * idx; max_ctx (> every q_pos) sizes the key loop. Workspace: dsa_dense_mla_workspace_size.
+ * ------------------------------------------------------------------------------------------- */
+size_t dsa_dense_mla_workspace_size(int rows, int H, int Dv, int max_ctx);
+dsa_status_t dsa_dense_mla_prefill(const uint16_t* q, const uint16_t* kv_cache,
+                                   const int32_t* page_table, int64_t ld_pt, int page_size,
+                                   int num_pages, const int32_t* q_pos, int n_seq, int q_per_seq,
+                                   int max_ctx, int H, int Dqk, int Dv, int kv_dim, int v_col0,
+                                   float sm_scale, uint16_t* out, float* lse, void* ws,
+                                   size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

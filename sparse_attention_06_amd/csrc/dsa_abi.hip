@@ -1,0 +1,227 @@
+// dsa_abi.hip -- the extern "C" entry points of libdsa.so: host-side argument checks, kernel
+// choice and launch. No allocation, no synchronisation: every call only enqueues on `stream`.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local int g_path = DSA_PATH_NONE;
+
+dsa_status_t fail(dsa_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+dsa_status_t ok(int path) {
+  g_path = path;
+  return DSA_OK;
+}
+
+dsa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DSA_OK;
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+#define REQUIRE(cond, ...) \
+  do {                     \
+    if (!(cond)) return fail(DSA_ERR_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+
+dsa_status_t check_paging(const int32_t* page_table, int64_t ld_pt, int page_size, int num_pages,
+                          int max_ctx) {
+  REQUIRE(page_table != nullptr, "page_table is NULL");
+  REQUIRE(page_size >= 1, "page_size must be >= 1 (got %d)", page_size);
+  REQUIRE(num_pages >= 1, "num_pages must be >= 1 (got %d)", num_pages);
+  REQUIRE(max_ctx >= 1, "max_ctx must be >= 1 (got %d)", max_ctx);
+  REQUIRE(ld_pt >= ((int64_t)max_ctx + page_size - 1) / page_size,
+          "ld_pt (%lld) must cover max_ctx / page_size pages", (long long)ld_pt);
+  REQUIRE((int64_t)num_pages * page_size < ((int64_t)1 << 31), "cache larger than 2^31 rows");
+  return DSA_OK;
+}
+
+bool mla_tuned(int H, int Dqk, int Dv, int kv_dim, int v_col0) {
+  return H == 128 && Dqk == 576 && Dv == 512 && kv_dim == 576 && v_col0 == 0;
+}
+
+dsa_status_t check_attn(const uint16_t* q, const uint16_t* kv_cache, const int32_t* q_pos,
+                        int n_seq, int q_per_seq, int H, int Dqk, int Dv, int kv_dim, int v_col0,
+                        uint16_t* out) {
+  REQUIRE(n_seq >= 0 && q_per_seq >= 1, "need n_seq >= 0 and q_per_seq >= 1");
+  if (n_seq == 0) return DSA_OK;  // nothing to do; the caller returns before any launch
+  REQUIRE(q && kv_cache && q_pos && out, "q, kv_cache, q_pos and out must be non-NULL");
+  REQUIRE((int64_t)n_seq * q_per_seq < ((int64_t)1 << 31), "too many rows");
+  REQUIRE(H >= 1 && Dqk >= 1 && Dv >= 1, "H, Dqk and Dv must be >= 1");
+  REQUIRE(kv_dim >= Dqk && v_col0 >= 0 && v_col0 + Dv <= kv_dim,
+          "need Dqk <= kv_dim and v_col0 + Dv <= kv_dim");
+  REQUIRE(!misaligned(q) && !misaligned(kv_cache) && !misaligned(out),
+          "q, kv_cache and out must be 16-byte aligned");
+  if (!mla_tuned(H, Dqk, Dv, kv_dim, v_col0) && (Dqk > 1024 || Dv > 512))
+    return fail(DSA_ERR_UNSUPPORTED, "attention shape Dqk=%d Dv=%d not supported (Dqk<=1024, Dv<=512)", Dqk, Dv);
+  return DSA_OK;
+}
+
+dsa_status_t run_sparse(bool decode, const uint16_t* q, const uint16_t* kv_cache,
+                        const int32_t* page_table, int64_t ld_pt, int page_size, int num_pages,
+                        const int32_t* q_pos, int n_seq, int q_per_seq, const int32_t* idx,
+                        int64_t ld_idx, int k, int H, int Dqk, int Dv, int kv_dim, int v_col0,
+                        float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                        void* stream) {
+  dsa_status_t s = check_attn(q, kv_cache, q_pos, n_seq, q_per_seq, H, Dqk, Dv, kv_dim, v_col0, out);
+  if (s != DSA_OK) return s;
+  REQUIRE(k >= 1 && ld_idx >= k, "need k >= 1 and ld_idx >= k");
+  const int rows = n_seq * q_per_seq;
+  if (rows == 0) return ok(DSA_PATH_NONE);
+  REQUIRE(idx != nullptr, "idx is NULL");
+  s = check_paging(page_table, ld_pt, page_size, num_pages, 1);
+  if (s != DSA_OK) return s;
+  dsa::AttnArgs a{q, {kv_cache, page_table, ld_pt, page_size, num_pages}, q_pos, n_seq, q_per_seq,
+                  idx, ld_idx, k, H, Dqk, Dv, kv_dim, v_col0, sm_scale, out, lse};
+  hipStream_t st = (hipStream_t)stream;
+  if (!mla_tuned(H, Dqk, Dv, kv_dim, v_col0)) {
+    s = hip_status(dsa::launch_mla_generic(a, st), "mla_generic launch");
+    return s == DSA_OK ? ok(DSA_PATH_MLA_GENERIC) : s;
+  }
+  const int splits = decode ? dsa::mla_mfma_pick_splits(rows, k) : 1;
+  const size_t need = dsa::mla_mfma_ws_bytes(rows, splits);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  if (need > 0 && misaligned(ws)) return fail(DSA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+  s = hip_status(dsa::launch_mla_mfma(a, splits, ws, st), "mla_mfma launch");
+  return s == DSA_OK ? ok(splits > 1 ? DSA_PATH_MLA_MFMA_SPLIT : DSA_PATH_MLA_MFMA) : s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status_t status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+  }
+  return "unknown dsa_status_t";
+}
+
+const char* dsa_last_error(void) { return g_err; }
+int dsa_last_path(void) { return g_path; }
+
+dsa_status_t dsa_indexer_scores(const void* q, const float* w, const void* k_cache,
+                                const float* k_scale, const int32_t* page_table, int64_t ld_pt,
+                                int page_size, int num_pages, const int32_t* q_pos, int n_seq,
+                                int q_per_seq, int max_ctx, int Hi, int Di, dsa_dtype_t dtype,
+                                float* scores, int64_t ld_scores, void* stream) {
+  REQUIRE(n_seq >= 0 && q_per_seq >= 1, "need n_seq >= 0 and q_per_seq >= 1");
+  if (n_seq == 0) return ok(DSA_PATH_NONE);  // nothing to do; pointers may be NULL
+  REQUIRE(q && w && k_cache && q_pos && scores, "q, w, k_cache, q_pos and scores must be non-NULL");
+  REQUIRE((int64_t)n_seq * q_per_seq < ((int64_t)1 << 31), "too many rows");
+  REQUIRE(Hi >= 1 && Di >= 1, "Hi and Di must be >= 1");
+  REQUIRE(dtype == DSA_E4M3 || dtype == DSA_F32, "dtype must be DSA_E4M3 or DSA_F32");
+  REQUIRE(!misaligned(q) && !misaligned(k_cache), "q and k_cache must be 16-byte aligned");
+  dsa_status_t s = check_paging(page_table, ld_pt, page_size, num_pages, max_ctx);
+  if (s != DSA_OK) return s;
+  REQUIRE(ld_scores >= max_ctx, "ld_scores (%lld) must be >= max_ctx (%d)", (long long)ld_scores, max_ctx);
+  if (n_seq == 0) return ok(DSA_PATH_NONE);
+  dsa::PagedCache kc{k_cache, page_table, ld_pt, page_size, num_pages};
+  hipStream_t st = (hipStream_t)stream;
+  if (Hi == 64 && Di == 128 && dtype == DSA_E4M3) {
+    if (q_per_seq <= 2) {
+      s = hip_status(dsa::launch_indexer_scan((const uint8_t*)q, w, kc, k_scale, q_pos, n_seq, q_per_seq,
+                                              max_ctx, scores, ld_scores, st), "indexer_scan launch");
+      return s == DSA_OK ? ok(DSA_PATH_INDEXER_SCAN_MFMA) : s;
+    }
+    s = hip_status(dsa::launch_indexer_prefill((const uint8_t*)q, w, kc, k_scale, q_pos, n_seq, q_per_seq,
+                                               max_ctx, scores, ld_scores, st), "indexer_prefill launch");
+    return s == DSA_OK ? ok(DSA_PATH_INDEXER_PREFILL_MFMA) : s;
+  }
+  s = hip_status(dsa::launch_indexer_generic(q, w, kc, k_scale, q_pos, n_seq, q_per_seq, max_ctx, Hi, Di,
+                                             dtype == DSA_F32, scores, ld_scores, st), "indexer_generic launch");
+  return s == DSA_OK ? ok(DSA_PATH_INDEXER_GENERIC) : s;
+}
+
+size_t dsa_topk_workspace_size(int rows, int max_ctx, int k) {
+  (void)rows; (void)max_ctx; (void)k;
+  return 0;
+}
+
+dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int rows,
+                      int max_ctx, int k, int32_t* idx, int64_t ld_idx, void* ws, size_t ws_bytes,
+                      void* stream) {
+  (void)ws; (void)ws_bytes;
+  REQUIRE(rows >= 0 && k >= 1 && max_ctx >= 1, "need rows >= 0, k >= 1, max_ctx >= 1");
+  if (rows == 0) return ok(DSA_PATH_NONE);  // nothing to do; pointers may be NULL
+  REQUIRE(scores && q_pos && idx, "scores, q_pos and idx must be non-NULL");
+  REQUIRE(ld_scores >= max_ctx, "ld_scores (%lld) must be >= max_ctx (%d)", (long long)ld_scores, max_ctx);
+  REQUIRE(ld_idx >= k, "ld_idx (%lld) must be >= k (%d)", (long long)ld_idx, k);
+  if (rows == 0) return ok(DSA_PATH_NONE);
+  int path = DSA_PATH_NONE;
+  dsa_status_t s = hip_status(dsa::launch_topk(scores, ld_scores, q_pos, rows, max_ctx, k, idx, ld_idx,
+                                               (hipStream_t)stream, &path), "topk launch");
+  return s == DSA_OK ? ok(path) : s;
+}
+
+size_t dsa_sparse_mla_workspace_size(int rows, int H, int Dv, int k) {
+  if (rows <= 0 || H != 128 || Dv != 512 || k < 1) return 0;
+  return dsa::mla_mfma_ws_bytes(rows, dsa::mla_mfma_pick_splits(rows, k));
+}
+
+dsa_status_t dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* kv_cache,
+                                   const int32_t* page_table, int64_t ld_pt, int page_size,
+                                   int num_pages, const int32_t* q_pos, int n_seq, int q_per_seq,
+                                   const int32_t* idx, int64_t ld_idx, int k, int H, int Dqk,
+                                   int Dv, int kv_dim, int v_col0, float sm_scale, uint16_t* out,
+                                   float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return run_sparse(true, q, kv_cache, page_table, ld_pt, page_size, num_pages, q_pos, n_seq, q_per_seq,
+                    idx, ld_idx, k, H, Dqk, Dv, kv_dim, v_col0, sm_scale, out, lse, ws, ws_bytes, stream);
+}
+
+dsa_status_t dsa_sparse_mla_prefill(const uint16_t* q, const uint16_t* kv_cache,
+                                    const int32_t* page_table, int64_t ld_pt, int page_size,
+                                    int num_pages, const int32_t* q_pos, int n_seq, int q_per_seq,
+                                    const int32_t* idx, int64_t ld_idx, int k, int H, int Dqk,
+                                    int Dv, int kv_dim, int v_col0, float sm_scale, uint16_t* out,
+                                    float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return run_sparse(false, q, kv_cache, page_table, ld_pt, page_size, num_pages, q_pos, n_seq, q_per_seq,
+                    idx, ld_idx, k, H, Dqk, Dv, kv_dim, v_col0, sm_scale, out, lse, ws, ws_bytes, stream);
+}
+
+size_t dsa_dense_mla_workspace_size(int rows, int H, int Dv, int max_ctx) {
+  (void)rows; (void)H; (void)Dv; (void)max_ctx;
+  return 0;
+}
+
+dsa_status_t dsa_dense_mla_prefill(const uint16_t* q, const uint16_t* kv_cache,
+                                   const int32_t* page_table, int64_t ld_pt, int page_size,
+                                   int num_pages, const int32_t* q_pos, int n_seq, int q_per_seq,
+                                   int max_ctx, int H, int Dqk, int Dv, int kv_dim, int v_col0,
+                                   float sm_scale, uint16_t* out, float* lse, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  dsa_status_t s = check_attn(q, kv_cache, q_pos, n_seq, q_per_seq, H, Dqk, Dv, kv_dim, v_col0, out);
+  if (s != DSA_OK) return s;
+  const int rows = n_seq * q_per_seq;
+  if (rows == 0) return ok(DSA_PATH_NONE);
+  s = check_paging(page_table, ld_pt, page_size, num_pages, max_ctx);
+  if (s != DSA_OK) return s;
+  dsa::AttnArgs a{q, {kv_cache, page_table, ld_pt, page_size, num_pages}, q_pos, n_seq, q_per_seq,
+                  nullptr, 0, max_ctx, H, Dqk, Dv, kv_dim, v_col0, sm_scale, out, lse};
+  hipStream_t st = (hipStream_t)stream;
+  if (!mla_tuned(H, Dqk, Dv, kv_dim, v_col0)) {
+    s = hip_status(dsa::launch_mla_generic(a, st), "mla_generic launch");
+    return s == DSA_OK ? ok(DSA_PATH_MLA_GENERIC) : s;
+  }
+  s = hip_status(dsa::launch_mla_mfma(a, 1, nullptr, st), "mla_mfma launch");
+  return s == DSA_OK ? ok(DSA_PATH_MLA_MFMA) : s;
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// dsa_internal.h -- device helpers and kernel launchers shared by the gfx950 kernels of libdsa.
+// Internal to the library; the public interface is include/dsa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsa.h"
+
+namespace dsa {
+
+// ---------------------------------------------------------------- vector types
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- numeric helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Round-to-nearest-even float -> bf16 bits (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Two OCP E4M3 bytes (the low or high 16-bit half of `word`) -> two f16, exact (hardware convert).
+__device__ __forceinline__ f16x2 e4m3x2_to_f16(uint32_t word, bool high) {
+  return high ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)word, 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)word, 1.0f, false);
+}
+
+// 16 E4M3 bytes (4 dwords) -> 16 f16 (two MFMA operands of 8).
+__device__ __forceinline__ void e4m3x16_to_f16(i32x4 raw, f16x8& lo, f16x8& hi) {
+  f16x2 a = e4m3x2_to_f16((uint32_t)raw[0], false), b = e4m3x2_to_f16((uint32_t)raw[0], true);
+  f16x2 c = e4m3x2_to_f16((uint32_t)raw[1], false), d = e4m3x2_to_f16((uint32_t)raw[1], true);
+  f16x2 e = e4m3x2_to_f16((uint32_t)raw[2], false), f = e4m3x2_to_f16((uint32_t)raw[2], true);
+  f16x2 g = e4m3x2_to_f16((uint32_t)raw[3], false), h = e4m3x2_to_f16((uint32_t)raw[3], true);
+  lo = f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  hi = f16x8{e[0], e[1], f[0], f[1], g[0], g[1], h[0], h[1]};
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Physical row of position p of sequence s, or -1 if p lies outside the page table's
+// [0, ld_pt * page_size) or the page id outside [0, num_pages).
+__device__ __forceinline__ int64_t phys_row(const int32_t* __restrict__ page_table, int64_t ld_pt,
+                                            int page_size, int num_pages, int s, int p) {
+  if (p < 0 || p / page_size >= ld_pt) return -1;
+  int32_t page = page_table[(int64_t)s * ld_pt + p / page_size];
+  if (page < 0 || page >= num_pages) return -1;
+  return (int64_t)page * page_size + p % page_size;
+}
+
+// ---------------------------------------------------------------- launchers (one per kernel family)
+struct PagedCache {
+  const void* base;
+  const int32_t* page_table;
+  int64_t ld_pt;
+  int page_size;
+  int num_pages;
+};
+
+hipError_t launch_indexer_generic(const void* q, const float* w, PagedCache kc, const float* k_scale,
+                                  const int32_t* q_pos, int n_seq, int q_per_seq, int max_ctx, int Hi,
+                                  int Di, int is_f32, float* scores, int64_t ld_scores,
+                                  hipStream_t stream);
+hipError_t launch_indexer_scan(const uint8_t* q, const float* w, PagedCache kc, const float* k_scale,
+                               const int32_t* q_pos, int n_seq, int q_per_seq, int max_ctx,
+                               float* scores, int64_t ld_scores, hipStream_t stream);
+hipError_t launch_indexer_prefill(const uint8_t* q, const float* w, PagedCache kc,
+                                  const float* k_scale, const int32_t* q_pos, int n_seq,
+                                  int q_per_seq, int max_ctx, float* scores, int64_t ld_scores,
+                                  hipStream_t stream);
+
+hipError_t launch_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int rows,
+                       int max_ctx, int k, int32_t* idx, int64_t ld_idx, hipStream_t stream,
+                       int* path);
+
+struct AttnArgs {
+  const uint16_t* q;
+  PagedCache kv;
+  const int32_t* q_pos;
+  int n_seq, q_per_seq;
+  const int32_t* idx;  // NULL => dense causal set {0..q_pos}
+  int64_t ld_idx;
+  int k;               // entries per idx row (dense: max_ctx)
+  int H, Dqk, Dv, kv_dim, v_col0;
+  float sm_scale;
+  uint16_t* out;
+  float* lse;
+};
+
+hipError_t launch_mla_generic(const AttnArgs& a, hipStream_t stream);
+// splits: number of workgroups sharing one row's set (1 = single pass). ws: splits > 1 partials.
+hipError_t launch_mla_mfma(const AttnArgs& a, int splits, void* ws, hipStream_t stream);
+size_t mla_mfma_ws_bytes(int rows, int splits);
+int mla_mfma_pick_splits(int rows, int k);
+
+}  // namespace dsa

@@ -1,0 +1,212 @@
+"""Python binding of libdsa.so (include/dsa.h): argument marshalling only.
+
+Every function takes torch tensors on the GPU, checks their dtype/shape/contiguity, and calls
+the C entry point of the same name on the current HIP stream. All computation runs in the
+library's kernels; there is no fallback of any kind: without the built library every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
+
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
+DSA_E4M3, DSA_F32 = 0, 1
+PATHS = {
+    0: "none", 1: "indexer_generic", 2: "indexer_scan_mfma", 3: "indexer_prefill_mfma",
+    10: "topk_copy", 11: "topk_radix", 20: "mla_generic", 21: "mla_mfma", 22: "mla_mfma_split",
+}
+
+EXPORTS = [
+    "dsa_status_string", "dsa_last_error", "dsa_last_path",
+    "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk",
+    "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
+    "dsa_dense_mla_workspace_size", "dsa_dense_mla_prefill",
+]
+
+
+class DSAError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed: {status} ({msg})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libdsa.so (raises if it has not been built) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build() or "
+                           "python -m sparse_attention_06_amd.build")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    lib.dsa_status_string.restype = ctypes.c_char_p
+    lib.dsa_status_string.argtypes = [i32]
+    lib.dsa_last_error.restype = ctypes.c_char_p
+    lib.dsa_last_error.argtypes = []
+    lib.dsa_last_path.restype = i32
+    lib.dsa_last_path.argtypes = []
+    lib.dsa_indexer_scores.restype = i32
+    lib.dsa_indexer_scores.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, vp, i32, i32, i32, i32, i32, i32,
+                                       vp, i64, vp]
+    lib.dsa_topk_workspace_size.restype = sz
+    lib.dsa_topk_workspace_size.argtypes = [i32, i32, i32]
+    lib.dsa_topk.restype = i32
+    lib.dsa_topk.argtypes = [vp, i64, vp, i32, i32, i32, vp, i64, vp, sz, vp]
+    lib.dsa_sparse_mla_workspace_size.restype = sz
+    lib.dsa_sparse_mla_workspace_size.argtypes = [i32, i32, i32, i32]
+    attn = [vp, vp, vp, i64, i32, i32, vp, i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, sz, vp]
+    lib.dsa_sparse_mla_decode.restype = i32
+    lib.dsa_sparse_mla_decode.argtypes = attn
+    lib.dsa_sparse_mla_prefill.restype = i32
+    lib.dsa_sparse_mla_prefill.argtypes = attn
+    lib.dsa_dense_mla_workspace_size.restype = sz
+    lib.dsa_dense_mla_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.dsa_dense_mla_prefill.restype = i32
+    lib.dsa_dense_mla_prefill.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                          f32, vp, vp, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def last_path() -> str:
+    return PATHS.get(load().dsa_last_path(), "unknown")
+
+
+def _check(fn, status):
+    if status != DSA_OK:
+        lib = load()
+        raise DSAError(fn, lib.dsa_status_string(status).decode(), lib.dsa_last_error().decode())
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, dim=None):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims (got {t.dim()})")
+
+
+def indexer_scores(q, w, k_cache, k_scale, page_table, q_pos, n_seq, q_per_seq, max_ctx, scores=None,
+                   stream=None):
+    """q [rows, Hi, Di] uint8 (E4M3 bytes) or float32; w [rows, Hi] f32; k_cache [P, page, Di];
+    k_scale [P, page] f32 or None; page_table [n_seq, ld_pt] i32; q_pos [rows] i32.
+    Returns scores [rows, max_ctx] f32 (entries j > q_pos[r] are -inf or unspecified)."""
+    dtype = DSA_E4M3 if q.dtype == torch.uint8 else DSA_F32
+    _need(q, "q", q.dtype, 3)
+    _need(k_cache, "k_cache", q.dtype, 3)
+    _need(w, "w", torch.float32, 2)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(q_pos, "q_pos", torch.int32, 1)
+    if k_scale is not None:
+        _need(k_scale, "k_scale", torch.float32)
+    rows, Hi, Di = q.shape
+    if rows != n_seq * q_per_seq or q_pos.numel() != rows:
+        raise ValueError("rows must equal n_seq * q_per_seq")
+    if scores is None:
+        scores = torch.empty(rows, max_ctx, dtype=torch.float32, device=q.device)
+    _need(scores, "scores", torch.float32, 2)
+    st = load().dsa_indexer_scores(_p(q), _p(w), _p(k_cache), _p(k_scale), _p(page_table), page_table.shape[1],
+                                   k_cache.shape[1], k_cache.shape[0], _p(q_pos), n_seq, q_per_seq, max_ctx, Hi, Di,
+                                   dtype, _p(scores), scores.shape[1], _stream(stream))
+    _check("dsa_indexer_scores", st)
+    return scores
+
+
+def topk(scores, q_pos, max_ctx, k, idx=None, stream=None):
+    """Top-k positions per row, ascending, -1 padded: idx [rows, k] int32."""
+    _need(scores, "scores", torch.float32, 2)
+    _need(q_pos, "q_pos", torch.int32, 1)
+    rows = scores.shape[0]
+    if idx is None:
+        idx = torch.empty(rows, k, dtype=torch.int32, device=scores.device)
+    _need(idx, "idx", torch.int32, 2)
+    st = load().dsa_topk(_p(scores), scores.shape[1], _p(q_pos), rows, max_ctx, k, _p(idx), idx.shape[1], None, 0,
+                         _stream(stream))
+    _check("dsa_topk", st)
+    return idx
+
+
+def sparse_mla_workspace_size(rows, H, Dv, k) -> int:
+    return int(load().dsa_sparse_mla_workspace_size(rows, H, Dv, k))
+
+
+def _attn_common(q, kv_cache, page_table, q_pos, out, lse, Dv):
+    _need(q, "q", torch.uint16 if q.dtype == torch.uint16 else torch.bfloat16, 3)
+    _need(kv_cache, "kv_cache", kv_cache.dtype, 3)
+    if kv_cache.dtype not in (torch.bfloat16, torch.uint16):
+        raise ValueError("kv_cache must be bf16 (or its uint16 bits)")
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(q_pos, "q_pos", torch.int32, 1)
+    rows, H, _ = q.shape
+    if out is None:
+        out = torch.empty(rows, H, Dv, dtype=torch.bfloat16, device=q.device)
+    if out.dtype not in (torch.bfloat16, torch.uint16):
+        raise ValueError("out must be bf16")
+    _need(out, "out", out.dtype, 3)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2)
+    return out
+
+
+def _sparse(fn_name, q, kv_cache, page_table, q_pos, n_seq, q_per_seq, idx, Dqk, Dv, v_col0, sm_scale,
+            out=None, lse=None, ws=None, stream=None):
+    out = _attn_common(q, kv_cache, page_table, q_pos, out, lse, Dv)
+    _need(idx, "idx", torch.int32, 2)
+    rows, H, _ = q.shape
+    k = idx.shape[1]
+    lib = load()
+    need = lib.dsa_sparse_mla_workspace_size(rows, H, Dv, k) if fn_name == "dsa_sparse_mla_decode" else 0
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    fn = getattr(lib, fn_name)
+    st = fn(_p(q), _p(kv_cache), _p(page_table), page_table.shape[1], kv_cache.shape[1], kv_cache.shape[0],
+            _p(q_pos), n_seq, q_per_seq, _p(idx), idx.shape[1], k, H, Dqk, Dv, kv_cache.shape[2], v_col0,
+            float(sm_scale), _p(out), _p(lse), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+            _stream(stream))
+    _check(fn_name, st)
+    return out
+
+
+def sparse_mla_decode(*args, **kw):
+    return _sparse("dsa_sparse_mla_decode", *args, **kw)
+
+
+def sparse_mla_prefill(*args, **kw):
+    return _sparse("dsa_sparse_mla_prefill", *args, **kw)
+
+
+def dense_mla_prefill(q, kv_cache, page_table, q_pos, n_seq, q_per_seq, max_ctx, Dqk, Dv, v_col0, sm_scale,
+                      out=None, lse=None, stream=None):
+    out = _attn_common(q, kv_cache, page_table, q_pos, out, lse, Dv)
+    rows, H, _ = q.shape
+    st = load().dsa_dense_mla_prefill(_p(q), _p(kv_cache), _p(page_table), page_table.shape[1], kv_cache.shape[1],
+                                      kv_cache.shape[0], _p(q_pos), n_seq, q_per_seq, max_ctx, H, Dqk, Dv,
+                                      kv_cache.shape[2], v_col0, float(sm_scale), _p(out), _p(lse), None, 0,
+                                      _stream(stream))
+    _check("dsa_dense_mla_prefill", st)
+    return out

@@ -1,0 +1,90 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point that
+include/dsa.h declares, and rejects bad host arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_06_amd import dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dsa.lib_path()):
+        pytest.fail("libdsa.so is not built (run __graft_entry__.build())")
+    return dsa.load()
+
+
+def test_header_declares_the_hot_path():
+    names = _declared()
+    for n in ["dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
+              "dsa_dense_mla_prefill"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(dsa.lib_path())
+    for n in _declared():
+        assert hasattr(raw, n), f"{n} declared in include/dsa.h but not exported"
+    assert sorted(dsa.EXPORTS) == _declared()
+
+
+def test_status_strings(lib):
+    assert lib.dsa_status_string(0) == b"DSA_OK"
+    assert lib.dsa_status_string(3) == b"DSA_ERR_WORKSPACE"
+
+
+NULL = None
+
+
+def test_indexer_rejects_null_and_bad_dims(lib):
+    st = lib.dsa_indexer_scores(NULL, NULL, NULL, NULL, NULL, 1, 64, 1, NULL, 1, 1, 64, 64, 128, 0, NULL, 64, NULL)
+    assert st == dsa.DSA_ERR_INVALID_ARG
+    assert b"non-NULL" in lib.dsa_last_error()
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    st = lib.dsa_indexer_scores(fake, fake, fake, NULL, fake, 1, 64, 1, fake, 1, 1, 64, 64, 128, 7, fake, 64, NULL)
+    assert st == dsa.DSA_ERR_INVALID_ARG and b"dtype" in lib.dsa_last_error()
+    st = lib.dsa_indexer_scores(fake, fake, fake, NULL, fake, 1, 64, 1, fake, 1, 1, 128, 64, 128, 0, fake, 64, NULL)
+    assert st == dsa.DSA_ERR_INVALID_ARG    # ld_pt too small for max_ctx = 128
+    st = lib.dsa_indexer_scores(fake, fake, fake, NULL, fake, 2, 64, 1, fake, 1, 1, 128, 64, 128, 0, fake, 64, NULL)
+    assert st == dsa.DSA_ERR_INVALID_ARG    # ld_scores < max_ctx
+    mis = ctypes.c_void_p(0x1004)
+    st = lib.dsa_indexer_scores(mis, fake, fake, NULL, fake, 2, 64, 1, fake, 1, 1, 128, 64, 128, 0, fake, 128, NULL)
+    assert st == dsa.DSA_ERR_INVALID_ARG and b"aligned" in lib.dsa_last_error()
+
+
+def test_topk_rejects_bad_k(lib):
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.dsa_topk(fake, 64, fake, 4, 64, 0, fake, 64, NULL, 0, NULL) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk(fake, 64, fake, 4, 64, 32, fake, 16, NULL, 0, NULL) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk_workspace_size(128, 16384, 2048) == 0
+
+
+def test_attention_rejects_unsupported_and_inconsistent(lib):
+    fake = ctypes.c_void_p(0x1000)
+    # v_col0 + Dv beyond the row
+    st = lib.dsa_sparse_mla_decode(fake, fake, fake, 1, 64, 1, fake, 1, 1, fake, 8, 8, 128, 576, 512, 576, 65,
+                                   ctypes.c_float(0.1), fake, NULL, NULL, 0, NULL)
+    assert st == dsa.DSA_ERR_INVALID_ARG
+    # a shape no kernel handles is reported, never substituted
+    st = lib.dsa_sparse_mla_decode(fake, fake, fake, 1, 64, 1, fake, 1, 1, fake, 8, 8, 4, 2048, 64, 2048, 0,
+                                   ctypes.c_float(0.1), fake, NULL, NULL, 0, NULL)
+    assert st == dsa.DSA_ERR_UNSUPPORTED
+    # the tuned decode path needs its split workspace for small batches
+    need = lib.dsa_sparse_mla_workspace_size(4, 128, 512, 2048)
+    assert need > 0
+    st = lib.dsa_sparse_mla_decode(fake, fake, fake, 64, 64, 64, fake, 4, 1, fake, 2048, 2048, 128, 576, 512, 576, 0,
+                                   ctypes.c_float(0.1), fake, NULL, NULL, 0, NULL)
+    assert st == dsa.DSA_ERR_WORKSPACE
+    st = lib.dsa_dense_mla_prefill(fake, fake, fake, 1, 64, 1, fake, 1, 4, 0, 128, 576, 512, 576, 0,
+                                   ctypes.c_float(0.1), fake, NULL, NULL, 0, NULL)
+    assert st == dsa.DSA_ERR_INVALID_ARG    # max_ctx = 0
