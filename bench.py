@@ -311,6 +311,21 @@ def run_crossover(args):
     print(json.dumps({"crossover": res, "sparse_wins_from_T": cross}), flush=True)
 
 
+def run_copy_calibration(args):
+    """A plain device copy of known size (1 GiB read + 1 GiB written per launch): the reference
+    for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+
+    n = 1 << 28  # float32 elements = 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(max(args.steps, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4,
+                                           "launches": max(args.steps, 1)}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -320,13 +335,16 @@ def main():
                     choices=["decode_mtp_b64_16k", "decode_b16_4k", "decode_b4_128k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--crossover", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); the DSA "
               "hot path here is a single-GPU library with no collectives.", file=sys.stderr)
         raise SystemExit(2)
-    if args.crossover:
+    if args.copy_calibration:
+        run_copy_calibration(args)
+    elif args.crossover:
         run_crossover(args)
     else:
         run_decode_bench(args)

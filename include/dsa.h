@@ -140,8 +140,9 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_p
  * Softmax runs in fp32 with the probabilities rounded to bf16 for the value product.
  * Tuned shape: H=128, Dqk=576, Dv=512, kv_dim=576, v_col0=0 (bf16 MFMA). Other shapes with
  * Dqk <= 1024 and Dv <= 512 run a generic VALU kernel (reported by dsa_last_path()).
- * The decode entry point may split each row's index set over several workgroups and combine
- * the partial results (workspace); the prefill entry point does one pass per row.
+ * The decode entry point may split each row's index set over several workgroups and merge
+ * their partial results, kept in the workspace as fp16 outputs normalised per split plus an
+ * fp32 (max, sum) pair per head; the prefill entry point does one pass per row.
  * ------------------------------------------------------------------------------------------- */
 size_t dsa_sparse_mla_workspace_size(int rows, int H, int Dv, int k);
 dsa_status_t dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* kv_cache,

@@ -78,20 +78,23 @@ hipError_t launch_mla_generic(const AttnArgs& a, hipStream_t stream) {
 // ------------------------------------------------------------------ tuned MFMA kernel
 
 constexpr int kH = 128, kDqk = 576, kDv = 512;
-constexpr int kHG = 64;                          // heads per workgroup (two workgroups per row)
 constexpr int kNK = 32;                          // positions per tile
 constexpr int kRowBytes = kDqk * 2;              // 1152 = 1024 latent + 128 rope
 constexpr int kLatBytes = 1024;                  // dims 0..511: one wave-wide 16-byte load
+constexpr int kLatStride = 1280;                 // LDS line of a latent row: 1 KB + rotation room
 constexpr int kRopeBytes = 128;                  // dims 512..575: 8 chunks of 16 bytes
-constexpr int kRopeOff = kNK * kLatBytes;        // 32768: rope region of a tile
-constexpr int kTileBytes = kRopeOff + kNK * kRopeBytes;  // 36864
+constexpr int kRopeOff = kNK * kLatStride;       // 40960: rope region of a tile
+constexpr int kTileBytes = kRopeOff + kNK * kRopeBytes;  // 45056
 constexpr int kRowsPerWave = kNK / 4;            // 8 rows gathered by each wave
 constexpr int kInstrPerWave = kRowsPerWave + 1;  // 8 latent loads + 1 rope load
-constexpr int kNBuf = 3;
+constexpr int kNBuf = 3;                         // tile buffers: kNBuf - 1 tiles in flight
+static_assert(kNBuf >= 2 && kNBuf <= 4, "wait_gathers covers up to two younger tiles");
 constexpr int kListCap = 2048;                   // resolved entries held in LDS at a time
-constexpr int kListOff = kNBuf * kTileBytes;     // 110592
-constexpr int kLdsBytes = kListOff + 4 * kListCap;  // 118784
-static_assert(kHG * kDv * 2 <= kLdsBytes, "output staging");
+constexpr int kListOff = kNBuf * kTileBytes;
+constexpr int kQRopeOff = kListOff + 4 * kListCap; // rope dims of the 128 query heads (16 KB)
+constexpr int kLdsBytes = kQRopeOff + kH * kRopeBytes;
+static_assert(kH * kDv * 2 <= kLdsBytes, "output staging");
+static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
 constexpr float kLog2e = 1.4426950408889634f;
 // The softmax reference of a head moves only when a logit exceeds it by 2^64 (log2 units):
 // fp32 and bf16 share an exponent range of 2^+-126, so probabilities up to 2^64 and sums of
@@ -99,13 +102,17 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 64.0f;
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// LDS swizzles (64 banks of 4 bytes). Latent part: tile row r keeps 16-byte chunk c at position
-// c ^ lat_swz(r) of its 1 KB line, so the 16 rows read together by a QK^T operand fetch, and the
-// 4 rows x 2 chunks of a transpose read, fall on distinct banks. Rope part: row r keeps chunk
-// c (0..7) at position c ^ rope_swz(r) of its 128-byte line.
-__device__ __forceinline__ int lat_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// LDS layout of a tile. Latent row r (1 KB) starts 16 * lat_rot(r) bytes into its 1280-byte line,
+// i.e. its 16-byte chunks are rotated over the 64 banks (4 bytes each): lat_rot is a permutation
+// of 0..15 over any 16 consecutive rows (the 16 rows of a QK^T operand fetch hit distinct banks)
+// and steps by 4 chunks across each aligned group of 4 rows (the 4 rows x 32 bytes served
+// together in a PV transpose read hit distinct banks). The lane offsets of both operand fetches
+// are then one base per lane plus immediates. Rope part: 128-byte rows, row r keeps chunk c
+// (0..7) at c ^ rope_swz(r).
+__device__ __forceinline__ int lat_rot(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 __device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
 
 // Physical row of entry e of row r (sparse: position idx[r, e]; dense: position e), or -1 when
@@ -136,8 +143,8 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
 }
 
 // This wave's share of one tile gather: tile rows 8w..8w+7, as 8 wave-wide latent loads (lane l
-// fetches chunk l ^ lat_swz(row)) and one rope load (lane l: row 8w + l/8, chunk
-// (l%8) ^ rope_swz(row)). Every lane is active in every load, so each wave has exactly
+// fetches chunk l, into the row's rotated position) and one rope load (lane l: row 8w + l/8,
+// chunk (l%8) ^ rope_swz(row)). Every lane is active in every load, so each wave has exactly
 // kInstrPerWave loads in flight per tile. Rows of invalid entries load the tile's first valid
 // row instead (finite data; their probability is 0).
 __device__ __forceinline__ void gather_tile(const uint8_t* __restrict__ kv_base, lds_u8* buf,
@@ -154,43 +161,79 @@ __device__ __forceinline__ void gather_tile(const uint8_t* __restrict__ kv_base,
   for (int i = 0; i < kRowsPerWave; ++i) {
     const int row = kRowsPerWave * wave + i;
     const int rid = __builtin_amdgcn_readfirstlane(__shfl(my_rid, 8 * i));
-    const uint8_t* src = kv_base + (int64_t)rid * kRowBytes + 16 * (lane ^ lat_swz(row));
-    lds_dma16(src, (uint32_t)(uintptr_t)(buf + row * kLatBytes));
+    const uint8_t* src = kv_base + (int64_t)rid * kRowBytes + 16 * lane;
+    lds_dma16(src, (uint32_t)(uintptr_t)(buf + row * kLatStride + 16 * lat_rot(row)));
   }
   const uint8_t* src = kv_base + (int64_t)my_rid * kRowBytes + kLatBytes + 16 * ((lane & 7) ^ rope_swz(my_slot));
   lds_dma16(src, (uint32_t)(uintptr_t)(buf + kRopeOff + kRowsPerWave * wave * kRopeBytes));
 }
 
-__device__ __forceinline__ void wait_gathers(bool keep_one_tile) {
-  // vmcnt(kInstrPerWave) leaves the younger tile's loads in flight; vmcnt(0) drains
-  if (keep_one_tile) __builtin_amdgcn_s_waitcnt(0x0F70 | kInstrPerWave);
-  else __builtin_amdgcn_s_waitcnt(0x0F70);
+// Wait until this wave's loads of the oldest tile in flight have landed, leaving the loads of
+// `younger` later tiles in flight (each tile is kInstrPerWave loads per wave, issued in order).
+__device__ __forceinline__ void wait_gathers(int younger) {
+  // s_waitcnt immediate: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt
+  // left at their maxima (no wait)
+  constexpr int kBase = 0x0F70;
+  if (younger >= 2) __builtin_amdgcn_s_waitcnt(kBase | ((2 * kInstrPerWave) & 15) | (((2 * kInstrPerWave) >> 4) << 14));
+  else if (younger == 1) __builtin_amdgcn_s_waitcnt(kBase | (kInstrPerWave & 15) | ((kInstrPerWave >> 4) << 14));
+  else __builtin_amdgcn_s_waitcnt(kBase);
 }
 
-// Rare path (a head's maximum grew past its reference by more than the threshold): scale the
-// running output. Out of line, so that the hot loop keeps its accumulators in AGPRs.
-__device__ __attribute__((noinline)) void rescale_acc(f32x4* o, float alpha) {
-  for (int mt = 0; mt < kDv / 16; ++mt) o[mt] *= alpha;
+// Workspace of the split path: fp16 partial outputs [unit][head][column] and (reference, sum)
+// per (unit, head), each part 256-byte aligned.
+struct MlaSplitWs {
+  uint16_t* part;
+  f32x2* ml;
+};
+__host__ __device__ inline size_t mla_align256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ __device__ inline size_t mla_split_ws_bytes(int units) {
+  return mla_align256((size_t)units * kH * kDv * 2) + mla_align256((size_t)units * kH * 8);
+}
+__host__ __device__ inline MlaSplitWs mla_split_ws(void* ws, int units) {
+  uint8_t* p = (uint8_t*)ws;
+  MlaSplitWs w;
+  w.part = (uint16_t*)p;
+  w.ml = (f32x2*)(p + mla_align256((size_t)units * kH * kDv * 2));
+  return w;
 }
 
-// Block -> (unit, head half): the two halves of a unit (row, split) get block ids b and b + 8,
-// which the dispatcher places on the same XCD back to back, so the second gather of each
-// latent row is an L2 hit.
-__device__ __forceinline__ void block_unit(int b, int units, int& unit, int& half) {
-  const int grp = b >> 4, in = b & 15;
-  unit = grp * 8 + (in & 7);
-  half = in >> 3;
-  (void)units;
+__device__ __forceinline__ uint32_t pack_f16x2(float x, float y) {
+  const f16x2 h = {(_Float16)x, (_Float16)y};
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ f32x2 unpack_f16x2(uint32_t v) {
+  const f16x2 h = __builtin_bit_cast(f16x2, v);
+  return f32x2{(float)h[0], (float)h[1]};
 }
 
-template <bool kSplit>
+// How a workgroup finishes: the whole row (no split), or a partial for the merge kernel.
+constexpr int kMlaNoSplit = 0, kMlaSplitCombine = 1;
+
+// Rare path (the lane's head moved its reference maximum): scale its running output by alpha.
+// Out of line, so that the hot loop keeps its accumulators in AGPRs.
+__device__ __attribute__((noinline)) void rescale_acc(f32x16* o, float alpha) {
+  for (int mt = 0; mt < kDv / 32; ++mt) o[mt] *= alpha;
+}
+
+// Workgroup: 4 waves, all 128 heads of one (row, split); wave w owns heads 32w..32w+31 for the
+// whole computation, so the tiles are the only thing the waves share. Per tile of 32 positions
+// (v_mfma_f32_32x32x16_bf16 throughout):
+//   S^T = K Q^T: key tile rows as the A operand from LDS, the wave's 32 query heads as the B
+//     operand (latent dims resident in 128 VGPRs, rope dims from LDS); lane l ends up with head
+//     l%32 and 16 of the 32 keys
+//   softmax bookkeeping per head in the log2 domain, probabilities rounded to bf16 in registers
+//   O^T += V^T P: V^T from LDS through ds_read_b64_tr_b16 as the A operand, P straight from the
+//     registers as the B operand (the K steps take the keys in the order the S layout holds them),
+//     512 value columns x 32 heads in 256 AGPRs
+template <int kMode>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, float* __restrict__ ws) {
+mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int per_xcd, void* __restrict__ ws) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int unit, half;
-  block_unit(blockIdx.x, units, unit, half);
+  // Workgroups are dispatched to the 8 XCDs round robin; give each XCD a contiguous range of
+  // units, so the rows of one sequence share that XCD's L2.
+  const int unit = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (unit >= units) return;
   const int r = unit / splits, sp = unit % splits;
   const int seq = r / a.q_per_seq;
@@ -200,255 +243,423 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, float*
   const int e_end = min(n_entries, e_begin + entries_per_split);
   lds_u8* lds = (lds_u8*)smem;
   int* list = (int*)(smem + kListOff);
-  const int head0 = kHG * half + 16 * wave;  // this wave's 16 heads
+  const int hl = lane & 31, half = lane >> 5;  // lane's head within the wave, key half
 
-  // query heads as B operands: lane holds head head0 + lane%16, dims 32*ks + 8*(lane/16) .. +8
-  bf16x8 qf[kDqk / 32];
+  // query heads as B operands: lane holds head 32w + lane%32, dims 16*ks + 8*(lane/32) .. +8 of
+  // the latent part in registers; the rope dims of all heads go to LDS (head h keeps chunk c at
+  // c ^ rope_swz(h) of its 128-byte row). The loads are issued here and complete while the
+  // first chunk of the index list is resolved.
+  bf16x8 qf[kDv / 16];
+  i32x4 qr[kH * 8 / 256];
   {
-    const uint16_t* qh = a.q + ((int64_t)r * kH + head0 + (lane & 15)) * kDqk + 8 * (lane >> 4);
+    const uint16_t* qh = a.q + ((int64_t)r * kH + 32 * wave + hl) * kDqk + 8 * half;
 #pragma unroll
-    for (int ks = 0; ks < kDqk / 32; ++ks) qf[ks] = *(const bf16x8*)(qh + 32 * ks);
-    // consume the fragments here, so their loads are complete before the tile loop and no wait
-    // for them lands inside it (where it would also drain the in-flight tile gathers)
+    for (int ks = 0; ks < kDv / 16; ++ks) qf[ks] = *(const bf16x8*)(qh + 16 * ks);
 #pragma unroll
-    for (int ks = 0; ks < kDqk / 32; ++ks) asm volatile("" ::"v"(qf[ks]));
+    for (int j = 0; j < kH * 8 / 256; ++j) {
+      const int i = threadIdx.x + 256 * j, h = i >> 3, c = i & 7;
+      qr[j] = *(const i32x4*)(a.q + ((int64_t)r * kH + h) * kDqk + kDv + 8 * c);
+    }
   }
-  f32x4 o[kDv / 16];
+  // O^T accumulators: o[mt] = value columns 32mt .. 32mt+31 of head 32w + lane%32
+  f32x16 o[kDv / 32];
 #pragma unroll
-  for (int mt = 0; mt < kDv / 16; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // l_part sums the bf16-rounded probabilities the PV product uses (it normalises the output);
-  // l_exact sums them unrounded (it gives the log-sum-exp)
-  float m_ref = -INFINITY, l_part = 0.f, l_exact = 0.f;
+  for (int i = 0; i < kDv / 32; ++i) o[i] = f32x16{};
+  float m_ref = -INFINITY, l_sum = 0.f;
   const float c_scale = a.sm_scale * kLog2e;
   const uint8_t* kv_base = (const uint8_t*)a.kv.base;
 
-  // Per-lane LDS byte offsets of the operand fetches within a tile. The swizzles only touch the
-  // low bits of the K step / column block, the rest folds into immediates.
-  int g1_base[4], rope_base[2], tr_base[8];
+  // Per-lane LDS byte offsets of the operand fetches within a tile
+  int g1_base, rope_base, qr_base, tr_base[2];
+  const int rope_x = rope_swz(hl) >> 1;
   {
-    const int g = lane >> 4, j = lane & 15;
-    const int S = lat_swz(j);              // rows j and 16 + j share the swizzle
-    // QK^T: row 16*st + j, chunk 4*ks + g
+    // QK^T A operand: key row lane%32, chunk 2*ks + lane/32
+    g1_base = hl * kLatStride + 16 * lat_rot(hl) + 16 * half;
+    // rope k-step k: chunk 2k + half of key row lane%32 / of query head 32w + lane%32, both at
+    // position (2k + half) ^ rope_swz = 2 * (k ^ rope_x) + (half ^ (rope_swz & 1))
+    rope_base = kRopeOff + hl * kRopeBytes + 16 * (half ^ (rope_swz(hl) & 1));
+    qr_base = kQRopeOff + (32 * wave + hl) * kRopeBytes + 16 * (half ^ (rope_swz(hl) & 1));
+    // PV transpose reads (read a of K step ks, lane group G = lane/16, lane j in the group): key
+    // row 16*ks + 4*(G/2) + 8*a + j/4, value columns 32*mt + 16*(G%2) + 4*(j%4) .. +4; the
+    // row's rotation is 4*(j/4) + G/2 + 2*a
+    const int G = lane >> 4, j = lane & 15;
 #pragma unroll
-    for (int k3 = 0; k3 < 4; ++k3) g1_base[k3] = j * kLatBytes + 16 * (4 * (k3 ^ (S >> 2)) + (g ^ (S & 3)));
-    const int R = rope_swz(j);
-#pragma unroll
-    for (int k1 = 0; k1 < 2; ++k1) rope_base[k1] = kRopeOff + j * kRopeBytes + 16 * ((4 * k1 + g) ^ R);
-    // transpose reads: row 16*a + 4*g + j/4, column chunk 2*mt + (j%4)/2, half (j%2)
-    const int rr = 4 * g + (j >> 2);
-    const int T = lat_swz(rr);
-#pragma unroll
-    for (int m7 = 0; m7 < 8; ++m7)
-      tr_base[m7] = rr * kLatBytes + 16 * (2 * (m7 ^ (T >> 1)) + (((j & 3) >> 1) ^ (T & 1))) + 8 * (j & 1);
+    for (int a8 = 0; a8 < 2; ++a8)
+      tr_base[a8] = (4 * (G >> 1) + 8 * a8 + (j >> 2)) * kLatStride + 16 * (4 * (j >> 2) + (G >> 1) + 2 * a8) +
+                    32 * (G & 1) + 8 * (j & 3);
   }
 
   for (int cb = e_begin; cb < e_end; cb += kListCap) {
     const int ce = min(e_end, cb + kListCap);
     __syncthreads();  // the previous chunk is done with the list and the buffers
     for (int e = cb + threadIdx.x; e < ce; e += 256) list[e - cb] = resolve_entry(a, r, seq, t, e);
+    if (cb == e_begin) {
+#pragma unroll
+      for (int j = 0; j < kH * 8 / 256; ++j) {
+        const int i = threadIdx.x + 256 * j, h = i >> 3, c = i & 7;
+        *(__attribute__((address_space(3))) i32x4*)(lds + kQRopeOff + h * kRopeBytes + 16 * (c ^ rope_swz(h))) = qr[j];
+      }
+      // consume the fragments here, so their loads are complete before the tile loop and no
+      // wait for them lands inside it (where it would also drain the in-flight tile gathers)
+#pragma unroll
+      for (int ks = 0; ks < kDv / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
+    }
     __syncthreads();
     const int n_list = ce - cb;
     const int ntiles = (n_list + kNK - 1) / kNK;
-    uint32_t vmask[kNBuf];
+    // vm[d] = valid-entry mask of tile it + d (0 past the end); only constant indices, so the
+    // masks stay in scalar registers
+    uint32_t vm[kNBuf];
     auto tile_mask = [&](int ti) -> uint32_t {
       const int e = ti * kNK + lane;
       const bool v = lane < kNK && e < n_list && list[e] >= 0;
       return (uint32_t)__ballot(v);
     };
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
-      if (pt < ntiles) {
-        vmask[pt] = tile_mask(pt);
-        if (vmask[pt]) gather_tile(kv_base, lds + pt * kTileBytes, list + pt * kNK, n_list - pt * kNK, vmask[pt], wave, lane);
+    for (int pt = 0; pt < kNBuf; ++pt) {
+      vm[pt] = 0u;
+      if (pt < kNBuf - 1 && pt < ntiles) {
+        vm[pt] = tile_mask(pt);
+        if (vm[pt]) gather_tile(kv_base, lds + pt * kTileBytes, list + pt * kNK, n_list - pt * kNK, vm[pt], wave, lane);
       }
     }
+    int b = 0;  // buffer of tile it (it % kNBuf, kept as a rotating counter)
     for (int it = 0; it < ntiles; ++it) {
-      const int b = it % kNBuf;
-      const bool next_in_flight = it + 1 < ntiles && vmask[(it + 1) % kNBuf] != 0u;
-      wait_gathers(next_in_flight);
-      // Every wave's share of tile `it` has landed once all waves pass this barrier, and all of
-      // tile it-1's LDS reads were consumed by MFMAs already. A bare s_barrier: the fence of
-      // __syncthreads would also drain the younger tile's loads that are meant to stay in flight.
+      int younger = 0;  // later tiles whose gathers are in flight
+#pragma unroll
+      for (int d = 1; d + 1 < kNBuf; ++d) younger += vm[d] != 0u ? 1 : 0;
+      wait_gathers(younger);
+      // Every wave's share of tile `it` has landed once all waves pass this barrier, and every
+      // wave has consumed its reads of tile it-1 (into MFMAs). A bare s_barrier: the fence of
+      // __syncthreads would also drain the younger tiles' loads that are meant to stay in flight.
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      if (it + 2 < ntiles) {
-        const int nb = (it + 2) % kNBuf;
-        vmask[nb] = tile_mask(it + 2);
-        if (vmask[nb]) gather_tile(kv_base, lds + nb * kTileBytes, list + (it + 2) * kNK, n_list - (it + 2) * kNK, vmask[nb], wave, lane);
+      const int b_cur = b;
+      b = b + 1 == kNBuf ? 0 : b + 1;
+      if (it + kNBuf - 1 < ntiles) {
+        // tile it + kNBuf - 1 goes to the buffer tile it - 1 used
+        const int nt = it + kNBuf - 1, nb = b_cur == 0 ? kNBuf - 1 : b_cur - 1;
+        vm[kNBuf - 1] = tile_mask(nt);
+        if (vm[kNBuf - 1]) gather_tile(kv_base, lds + nb * kTileBytes, list + nt * kNK, n_list - nt * kNK, vm[kNBuf - 1], wave, lane);
       }
-      const uint32_t valid = vmask[b];
-      if (valid == 0u) continue;
-      const lds_u8* tile = lds + b * kTileBytes;
+      const uint32_t valid = vm[0];
+#pragma unroll
+      for (int d = 0; d + 1 < kNBuf; ++d) vm[d] = vm[d + 1];
+      vm[kNBuf - 1] = 0u;
+      if (valid == 0u) continue;  // uniform across the workgroup
+      const lds_u8* tile = lds + b_cur * kTileBytes;
 
-      // ---- S = K Q^T for two 16-key halves: lane holds head lane%16,
-      //      keys 16*st + 4*(lane/16) + i, i = 0..3
-      f32x4 s[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < kDv / 32; ++ks) {
-          const lds_u8* p = tile + g1_base[ks & 3] + 16384 * st + 64 * (ks & 12);
-          const bf16x8 af = *(const __attribute__((address_space(3))) bf16x8*)p;
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[ks], acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int ks = kDv / 32; ks < kDqk / 32; ++ks) {
-          const lds_u8* p = tile + rope_base[ks - kDv / 32] + 2048 * st;
-          const bf16x8 af = *(const __attribute__((address_space(3))) bf16x8*)p;
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[ks], acc, 0, 0, 0);
-        }
-        s[st] = acc;
+      // ---- S^T = K Q^T: lane holds head lane%32, keys 8*(i/4) + 4*(lane/32) + i%4, i = 0..15
+      // S^T for this tile, with the operand fetches issued four MFMAs ahead: written as one asm
+      // block so that S is accumulated in VGPRs (the AGPRs hold the output) and the fetches are
+      // not reordered. Rope k-steps first (both operands from LDS), then the 32 latent k-steps.
+      // LDS reads complete in order, so each wait counts only the younger reads of this block.
+      // Dependent MFMAs chain through srcC directly; the trailing s_nops cover the MFMA-result
+      // to VALU-read latency for the softmax that follows.
+      f32x16 s;
+      {
+        const uint32_t al = (uint32_t)(uintptr_t)(tile + g1_base);
+        const uint32_t kb = (uint32_t)(uintptr_t)(tile + rope_base), qb = (uint32_t)(uintptr_t)(lds + qr_base);
+        const uint32_t x0 = 32 * (0 ^ rope_x), x1 = 32 * (1 ^ rope_x), x2 = 32 * (2 ^ rope_x), x3 = 32 * (3 ^ rope_x);
+        bf16x8 t0, t1, t2, t3;
+        asm volatile(
+          "ds_read_b128 %[t0], %[k0]\n"
+          "ds_read_b128 %[t1], %[r0]\n"
+          "ds_read_b128 %[t2], %[k1]\n"
+          "ds_read_b128 %[t3], %[r1]\n"
+          "s_waitcnt lgkmcnt(2)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[t1], 0\n"
+          "ds_read_b128 %[t0], %[k2]\n"
+          "ds_read_b128 %[t1], %[r2]\n"
+          "s_waitcnt lgkmcnt(2)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[t3], %[s]\n"
+          "ds_read_b128 %[t2], %[k3]\n"
+          "ds_read_b128 %[t3], %[r3]\n"
+          "s_waitcnt lgkmcnt(2)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[t1], %[s]\n"
+          "ds_read_b128 %[t0], %[al]\n"
+          "ds_read_b128 %[t1], %[al] offset:32\n"
+          "s_waitcnt lgkmcnt(2)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[t3], %[s]\n"
+          "ds_read_b128 %[t2], %[al] offset:64\n"
+          "ds_read_b128 %[t3], %[al] offset:96\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q0], %[s]\n"
+          "ds_read_b128 %[t0], %[al] offset:128\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q1], %[s]\n"
+          "ds_read_b128 %[t1], %[al] offset:160\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q2], %[s]\n"
+          "ds_read_b128 %[t2], %[al] offset:192\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q3], %[s]\n"
+          "ds_read_b128 %[t3], %[al] offset:224\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q4], %[s]\n"
+          "ds_read_b128 %[t0], %[al] offset:256\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q5], %[s]\n"
+          "ds_read_b128 %[t1], %[al] offset:288\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q6], %[s]\n"
+          "ds_read_b128 %[t2], %[al] offset:320\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q7], %[s]\n"
+          "ds_read_b128 %[t3], %[al] offset:352\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q8], %[s]\n"
+          "ds_read_b128 %[t0], %[al] offset:384\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q9], %[s]\n"
+          "ds_read_b128 %[t1], %[al] offset:416\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q10], %[s]\n"
+          "ds_read_b128 %[t2], %[al] offset:448\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q11], %[s]\n"
+          "ds_read_b128 %[t3], %[al] offset:480\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q12], %[s]\n"
+          "ds_read_b128 %[t0], %[al] offset:512\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q13], %[s]\n"
+          "ds_read_b128 %[t1], %[al] offset:544\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q14], %[s]\n"
+          "ds_read_b128 %[t2], %[al] offset:576\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q15], %[s]\n"
+          "ds_read_b128 %[t3], %[al] offset:608\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q16], %[s]\n"
+          "ds_read_b128 %[t0], %[al] offset:640\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q17], %[s]\n"
+          "ds_read_b128 %[t1], %[al] offset:672\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q18], %[s]\n"
+          "ds_read_b128 %[t2], %[al] offset:704\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q19], %[s]\n"
+          "ds_read_b128 %[t3], %[al] offset:736\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q20], %[s]\n"
+          "ds_read_b128 %[t0], %[al] offset:768\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q21], %[s]\n"
+          "ds_read_b128 %[t1], %[al] offset:800\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q22], %[s]\n"
+          "ds_read_b128 %[t2], %[al] offset:832\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q23], %[s]\n"
+          "ds_read_b128 %[t3], %[al] offset:864\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q24], %[s]\n"
+          "ds_read_b128 %[t0], %[al] offset:896\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q25], %[s]\n"
+          "ds_read_b128 %[t1], %[al] offset:928\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q26], %[s]\n"
+          "ds_read_b128 %[t2], %[al] offset:960\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q27], %[s]\n"
+          "ds_read_b128 %[t3], %[al] offset:992\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q28], %[s]\n"
+          "s_waitcnt lgkmcnt(2)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q29], %[s]\n"
+          "s_waitcnt lgkmcnt(1)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q30], %[s]\n"
+          "s_waitcnt lgkmcnt(0)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q31], %[s]\n"
+          "s_nop 7\n"
+          "s_nop 7\n"
+          "s_nop 7\n"
+          : [s] "=&v"(s), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3)
+          : [al] "v"(al), [k0] "v"(kb + x0), [k1] "v"(kb + x1), [k2] "v"(kb + x2), [k3] "v"(kb + x3),
+            [r0] "v"(qb + x0), [r1] "v"(qb + x1), [r2] "v"(qb + x2), [r3] "v"(qb + x3),
+            [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]), [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]), [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]), [q14] "v"(qf[14]), [q15] "v"(qf[15]), [q16] "v"(qf[16]), [q17] "v"(qf[17]), [q18] "v"(qf[18]), [q19] "v"(qf[19]), [q20] "v"(qf[20]), [q21] "v"(qf[21]), [q22] "v"(qf[22]), [q23] "v"(qf[23]), [q24] "v"(qf[24]), [q25] "v"(qf[25]), [q26] "v"(qf[26]), [q27] "v"(qf[27]), [q28] "v"(qf[28]), [q29] "v"(qf[29]), [q30] "v"(qf[30]), [q31] "v"(qf[31])
+          : "memory");
       }
-      // ---- softmax bookkeeping (log2 domain)
+      // ---- softmax bookkeeping (log2 domain); the two lanes of a head see all 32 keys
       float mx = -INFINITY;
+      const uint32_t vh = valid >> (4 * half);  // bit 8*(i/4) + i%4: key of s[i] is valid
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 16 * st + 4 * (lane >> 4) + i;
-          const float v = ((valid >> key) & 1u) ? s[st][i] * c_scale : -INFINITY;
-          s[st][i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      for (int i = 0; i < 16; ++i) {
+        const float v = ((vh >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] * c_scale : -INFINITY;
+        s[i] = v;
+        mx = fmaxf(mx, v);
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool need = mx > m_ref + kRescaleThreshold;
-      if (__any(need)) {
-        const float nref = need ? mx : m_ref;
-        const float alpha = need ? exp2f(m_ref - nref) : 1.f;  // m_ref = -inf gives 0
-        if (__any(alpha != 1.f && l_part != 0.f)) {
-          f32x4 tmp[kDv / 16];
+      if (mx > m_ref + kRescaleThreshold) {
+        // nothing accumulated yet (m_ref = -inf): the output is still zero, just adopt mx
+        const float alpha = (m_ref == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - mx);
+        m_ref = mx;
+        l_sum *= alpha;
+        if (__any(alpha != 1.f)) {
+          f32x16 tmp[kDv / 32];
 #pragma unroll
-          for (int mt = 0; mt < kDv / 16; ++mt) tmp[mt] = o[mt];
+          for (int i = 0; i < kDv / 32; ++i) tmp[i] = o[i];
           rescale_acc(tmp, alpha);
 #pragma unroll
-          for (int mt = 0; mt < kDv / 16; ++mt) o[mt] = tmp[mt];
+          for (int i = 0; i < kDv / 32; ++i) o[i] = tmp[i];
           // settle the reloads here, so no wait for them is left on the hot path after the join
           __builtin_amdgcn_s_waitcnt(0x0F70);
         }
-        l_part *= alpha;
-        l_exact *= alpha;
-        m_ref = nref;
       }
-      bf16x8 pf;
+      // probabilities, packed to bf16 pairs: pk[ks] is the B operand of K step ks
+      bf16x8 pk[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int ks = 0; ks < 2; ++ks) {
+        float pv[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = (m_ref == -INFINITY) ? 0.f : exp2f(s[st][i] - m_ref);
-          const __bf16 pb = (__bf16)p;
-          l_part += (float)pb;
-          l_exact += p;
-          pf[4 * st + i] = pb;
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(s[8 * ks + e] - m_ref);  // exp2(-inf) = 0 for invalid keys
+          l_sum += pv[e];
         }
-      // ---- O^T += V^T P : A = V^T via transpose reads; lane group g reads keys 4g..4g+3
-      //      and 16+4g..16+4g+3, matching the key order of the P fragment
 #pragma unroll
-      for (int mt = 0; mt < kDv / 16; ++mt) {
-        const lds_u8* p0 = tile + tr_base[mt & 7] + 32 * (mt & 24);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0 + 16 * kLatBytes));
-        // whole-vector reinterpretation (element-wise bit casts of the 16-bit lanes were
-        // miscompiled into a broadcast of element 0)
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[mt], 0, 0, 0);
+        for (int e = 0; e < 8; ++e) pk[ks][e] = (__bf16)pv[e];
+      }
+      // ---- O^T += V^T P. K step ks takes keys 16*ks + 8*(e/4) + 4*h + e%4 in slot 8*h + e, the
+      //      order in which lane half h holds them in pk[ks]
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int mt = 0; mt < kDv / 32; ++mt) {
+          const int off = 64 * mt + 16 * kLatStride * ks;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(tile + tr_base[0] + off));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(tile + tr_base[1] + off));
+          // whole-vector reinterpretation (element-wise bit casts of the 16-bit lanes were
+          // miscompiled into a broadcast of element 0)
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[ks], o[mt], 0, 0, 0);
+        }
       }
     }
   }
 
-  float l_tot = l_part + __shfl_xor(l_part, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  float l_ex = l_exact + __shfl_xor(l_exact, 16);
-  l_ex += __shfl_xor(l_ex, 32);
-  const int hl = 16 * wave + (lane & 15);   // head within this workgroup's 64
-  const int head = kHG * half + hl;
-  if (!kSplit) {
-    // normalise, stage [head][vdim] bf16 in LDS (64 KB), then coalesced 16-byte stores
+  // per-head totals: the two lanes of a head hold the sums over their key halves
+  const float l_tot = l_sum + __shfl_xor(l_sum, 32);
+  const int head = 32 * wave + hl;
+  // Output layout: lane holds columns 32mt + 8(i/4) + 4*half + i%4 of head 32w + lane%32. Results
+  // are staged [head][column] in LDS (8-byte unit u of a head's 1 KB line at u ^ 2*(head%32), i.e.
+  // 16-byte chunk c at c ^ (head%32)) and stored with coalesced 16-byte writes.
+  auto stage = [&](auto cvt4) {
+    lds_u8* st = lds + head * (kDv * 2);
+#pragma unroll
+    for (int mt = 0; mt < kDv / 32; ++mt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int u = 8 * mt + 2 * q + half;
+        *(__attribute__((address_space(3))) u32x2*)(st + 8 * (u ^ (2 * hl))) = cvt4(mt, q);
+      }
+  };
+  auto store_staged = [&](uint16_t* dst16) {
+    i32x4* dst = (i32x4*)dst16;
+    for (int i = threadIdx.x; i < kH * kDv / 8; i += 256) {
+      const int h = i >> 6, c = i & 63;
+      dst[i] = *(const __attribute__((address_space(3))) i32x4*)(lds + h * (kDv * 2) + 16 * (c ^ (h & 31)));
+    }
+  };
+  auto bf16x4_of = [](float x0, float x1, float x2, float x3) {
+    return u32x2{(uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16),
+                 (uint32_t)f32_to_bf16(x2) | ((uint32_t)f32_to_bf16(x3) << 16)};
+  };
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  float lse2 = l_tot > 0.f ? m_ref + __log2f(l_tot) : -INFINITY;  // log-sum-exp, log2 units
+  __syncthreads();  // every wave is done with the tile buffers
+  if (kMode == kMlaNoSplit) {
+    if (a.lse && half == 0) a.lse[(int64_t)r * kH + head] = lse2 / kLog2e;
+    stage([&](int mt, int q) {
+      return bf16x4_of(o[mt][4 * q] * inv, o[mt][4 * q + 1] * inv, o[mt][4 * q + 2] * inv, o[mt][4 * q + 3] * inv);
+    });
     __syncthreads();
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* st = (uint16_t*)smem;
-#pragma unroll
-    for (int mt = 0; mt < kDv / 16; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st[hl * kDv + 16 * mt + 4 * (lane >> 4) + i] = f32_to_bf16(o[mt][i] * inv);
-    __syncthreads();
-    i32x4* dst = (i32x4*)(a.out + ((int64_t)r * kH + kHG * half) * kDv);
-    for (int i = threadIdx.x; i < kHG * kDv / 8; i += 256) dst[i] = ((const i32x4*)smem)[i];
-    if (a.lse && lane < 16) a.lse[(int64_t)r * kH + head] = l_ex > 0.f ? (m_ref + __log2f(l_ex)) / kLog2e : -INFINITY;
-  } else {
-    // partial result of this split: unnormalised O as [unit][head][vdim] fp32, plus
-    // (m_ref, rounded sum, exact sum) per head
-    float* po = ws + ((int64_t)unit * kH + head) * kDv;
-#pragma unroll
-    for (int mt = 0; mt < kDv / 16; ++mt)
-      *(f32x4*)(po + 16 * mt + 4 * (lane >> 4)) = o[mt];
-    float* pm = ws + (int64_t)units * kH * kDv + ((int64_t)unit * kH + head) * 4;
-    if (lane < 16) { pm[0] = m_ref; pm[1] = l_tot; pm[2] = l_ex; }
+    store_staged(a.out + (int64_t)r * kH * kDv);
+    return;
   }
+  // Partial result of this split: the normalised output in fp16 ([unit][head][column]) and
+  // (reference, sum) per head.
+  MlaSplitWs w = mla_split_ws(ws, units);
+  stage([&](int mt, int q) {
+    return u32x2{pack_f16x2(o[mt][4 * q] * inv, o[mt][4 * q + 1] * inv), pack_f16x2(o[mt][4 * q + 2] * inv, o[mt][4 * q + 3] * inv)};
+  });
+  if (half == 0) w.ml[(int64_t)unit * kH + head] = f32x2{m_ref, l_tot};
+  __syncthreads();
+  store_staged(w.part + (int64_t)unit * kH * kDv);
 }
 
-// Merge the splits of each row: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// One thread per (row, head, 8 output columns).
-__global__ void __launch_bounds__(256) mla_combine_kernel(AttnArgs a, int splits, int units, const float* __restrict__ ws) {
+// Merge the splits of each row from their fp16 partials: out = sum_s w_s N_s / sum_s w_s with
+// w_s = l_s 2^(m_s - M). One thread per (row, head, 8 output columns).
+__global__ void __launch_bounds__(256) mla_combine_kernel(AttnArgs a, int splits, int units, void* __restrict__ ws) {
   const int r = blockIdx.y;
   const int item = blockIdx.x * 256 + threadIdx.x;  // head * 64 + column group
   if (item >= kH * (kDv / 8)) return;
   const int head = item / (kDv / 8), cg = item % (kDv / 8);
-  const float* pm = ws + (int64_t)units * kH * kDv;
+  MlaSplitWs w = mla_split_ws(ws, units);
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, pm[((int64_t)(r * splits + s) * kH + head) * 4]);
-  float den = 0.f, den_ex = 0.f, acc[8];
+  for (int s2 = 0; s2 < splits; ++s2) {
+    const f32x2 ml = w.ml[(int64_t)(r * splits + s2) * kH + head];
+    if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
+  }
+  float L = 0.f, acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const int64_t u = (int64_t)(r * splits + s) * kH + head;
-    const float m = pm[u * 4], l = pm[u * 4 + 1];
-    if (l <= 0.f) continue;
-    const float f = exp2f(m - M);
-    den += f * l;
-    den_ex += f * pm[u * 4 + 2];
-    const f32x4* po = (const f32x4*)(ws + u * kDv + 8 * cg);
-    const f32x4 v0 = po[0], v1 = po[1];
+  for (int s2 = 0; s2 < splits; ++s2) {
+    const int64_t u = (int64_t)(r * splits + s2) * kH + head;
+    const f32x2 ml = w.ml[u];
+    if (!(ml[1] > 0.f)) continue;
+    const float f = ml[1] * exp2f(ml[0] - M);
+    L += f;
+    const i32x4 v = *(const i32x4*)(w.part + u * kDv + 8 * cg);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { acc[e] = fmaf(f, v0[e], acc[e]); acc[e + 4] = fmaf(f, v1[e], acc[e + 4]); }
+    for (int e = 0; e < 4; ++e) {
+      const f32x2 x = unpack_f16x2((uint32_t)v[e]);
+      acc[2 * e] = fmaf(f, x[0], acc[2 * e]);
+      acc[2 * e + 1] = fmaf(f, x[1], acc[2 * e + 1]);
+    }
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* dst = a.out + ((int64_t)r * kH + head) * kDv + 8 * cg;
-  uint32_t w[4];
+  uint32_t wd[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) w[e] = (uint32_t)f32_to_bf16(acc[2 * e] * inv) | ((uint32_t)f32_to_bf16(acc[2 * e + 1] * inv) << 16);
-  *(i32x4*)dst = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-  if (a.lse && cg == 0) a.lse[(int64_t)r * kH + head] = den_ex > 0.f ? (M + __log2f(den_ex)) / kLog2e : -INFINITY;
+  for (int e = 0; e < 4; ++e) wd[e] = (uint32_t)f32_to_bf16(acc[2 * e] * inv) | ((uint32_t)f32_to_bf16(acc[2 * e + 1] * inv) << 16);
+  *(i32x4*)dst = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+  if (a.lse && cg == 0) a.lse[(int64_t)r * kH + head] = L > 0.f ? (M + __log2f(L)) / kLog2e : -INFINITY;
 }
 
 size_t mla_mfma_ws_bytes(int rows, int splits) {
   if (splits <= 1) return 0;
-  return (size_t)rows * splits * kH * (kDv + 4) * sizeof(float);
+  return mla_split_ws_bytes(rows * splits);
 }
 
 int mla_mfma_pick_splits(int rows, int k) {
-  // aim for >= 256 workgroups (two per (row, split)), at least 2 tiles per split
+  // aim for >= 256 workgroups (one per (row, split)), at least 2 tiles per split
   int s = 1;
-  while (2 * rows * s < 256 && (k / (s * 2)) >= 2 * kNK) s *= 2;
+  while (rows * s < 256 && (k / (s * 2)) >= 2 * kNK) s *= 2;
   return s;
 }
 
 hipError_t launch_mla_mfma(const AttnArgs& a, int splits, void* ws, hipStream_t stream) {
   const int rows = a.n_seq * a.q_per_seq;
   const int units = rows * (splits > 1 ? splits : 1);
-  const int blocks = ((units + 7) / 8) * 16;  // groups of 8 units x 2 head halves
+  const int per_xcd = (units + 7) / 8;
+  const int blocks = 8 * per_xcd;
   if (splits <= 1) {
     const int per = a.idx ? a.k : 1 << 30;
-    hipLaunchKernelGGL(mla_mfma_kernel<false>, dim3(blocks), dim3(256), 0, stream, a, 1, per, units, (float*)nullptr);
+    hipLaunchKernelGGL(mla_mfma_kernel<kMlaNoSplit>, dim3(blocks), dim3(256), 0, stream, a, 1, per, units, per_xcd, nullptr);
     return hipGetLastError();
   }
   const int per = ((a.k + splits - 1) / splits + kNK - 1) / kNK * kNK;
-  hipLaunchKernelGGL(mla_mfma_kernel<true>, dim3(blocks), dim3(256), 0, stream, a, splits, per, units, (float*)ws);
+  hipLaunchKernelGGL(mla_mfma_kernel<kMlaSplitCombine>, dim3(blocks), dim3(256), 0, stream, a, splits, per, units, per_xcd, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((kH * (kDv / 8) + 255) / 256, rows), dim3(256), 0, stream, a, splits, units, (const float*)ws);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3((kH * (kDv / 8) + 255) / 256, rows), dim3(256), 0, stream, a, splits, units, ws);
   return hipGetLastError();
 }
 
