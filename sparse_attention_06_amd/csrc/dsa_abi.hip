@@ -47,8 +47,10 @@ dsa_status_t check_paging(const int32_t* page_table, int64_t ld_pt, int page_siz
   return DSA_OK;
 }
 
-bool mla_tuned(int H, int Dqk, int Dv, int kv_dim, int v_col0) {
-  return H == 128 && Dqk == 576 && Dv == 512 && kv_dim == 576 && v_col0 == 0;
+// The MFMA kernels take the absorbed-MLA shape with a positive softmax scale (they track the
+// running maximum on the unscaled scores).
+bool mla_tuned(int H, int Dqk, int Dv, int kv_dim, int v_col0, float sm_scale = 1.f) {
+  return H == 128 && Dqk == 576 && Dv == 512 && kv_dim == 576 && v_col0 == 0 && sm_scale > 0.f;
 }
 
 dsa_status_t check_attn(const uint16_t* q, const uint16_t* kv_cache, const int32_t* q_pos,
@@ -85,7 +87,7 @@ dsa_status_t run_sparse(bool decode, const uint16_t* q, const uint16_t* kv_cache
   dsa::AttnArgs a{q, {kv_cache, page_table, ld_pt, page_size, num_pages}, q_pos, n_seq, q_per_seq,
                   idx, ld_idx, k, H, Dqk, Dv, kv_dim, v_col0, sm_scale, out, lse};
   hipStream_t st = (hipStream_t)stream;
-  if (!mla_tuned(H, Dqk, Dv, kv_dim, v_col0)) {
+  if (!mla_tuned(H, Dqk, Dv, kv_dim, v_col0, sm_scale)) {
     s = hip_status(dsa::launch_mla_generic(a, st), "mla_generic launch");
     return s == DSA_OK ? ok(DSA_PATH_MLA_GENERIC) : s;
   }
@@ -216,7 +218,7 @@ dsa_status_t dsa_dense_mla_prefill(const uint16_t* q, const uint16_t* kv_cache,
   dsa::AttnArgs a{q, {kv_cache, page_table, ld_pt, page_size, num_pages}, q_pos, n_seq, q_per_seq,
                   nullptr, 0, max_ctx, H, Dqk, Dv, kv_dim, v_col0, sm_scale, out, lse};
   hipStream_t st = (hipStream_t)stream;
-  if (!mla_tuned(H, Dqk, Dv, kv_dim, v_col0)) {
+  if (!mla_tuned(H, Dqk, Dv, kv_dim, v_col0, sm_scale)) {
     s = hip_status(dsa::launch_mla_generic(a, st), "mla_generic launch");
     return s == DSA_OK ? ok(DSA_PATH_MLA_GENERIC) : s;
   }

@@ -142,30 +142,37 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
       : "memory");
 }
 
-// This wave's share of one tile gather: tile rows 8w..8w+7, as 8 wave-wide latent loads (lane l
-// fetches chunk l, into the row's rotated position) and one rope load (lane l: row 8w + l/8,
-// chunk (l%8) ^ rope_swz(row)). Every lane is active in every load, so each wave has exactly
-// kInstrPerWave loads in flight per tile. Rows of invalid entries load the tile's first valid
-// row instead (finite data; their probability is 0).
-__device__ __forceinline__ void gather_tile(const uint8_t* __restrict__ kv_base, lds_u8* buf,
-                                            const int* list, int n_in_tile, uint32_t vmask,
-                                            int wave, int lane) {
+// This wave's share of one tile gather (tile entries tl[0 .. n_in_tile), at most kNK): tile rows
+// 8w..8w+7 as 8 wave-wide latent loads (lane l fetches chunk l, into the row's rotated position)
+// and one rope load (lane l: row 8w + l/8, chunk (l%8) ^ rope_swz(row)). Returns the mask of
+// valid entries (bit e: entry e is a visible position with a valid page); loads nothing when it
+// is 0. Otherwise every lane is active in every load, so each wave has exactly kInstrPerWave
+// loads in flight per tile; rows of invalid entries load the tile's first valid row instead
+// (finite data; their probability is 0). Lanes 0..31 read the tile's entries once and the row ids
+// are taken from them with v_readlane (no LDS round trips between the loads).
+__device__ __forceinline__ uint32_t issue_tile(const uint8_t* __restrict__ kv_base, lds_u8* buf,
+                                               const int* tl, int n_in_tile, int wave, int lane) {
   // An opaque copy of the lane id: the per-lane offsets below are recomputed per tile (a few
   // VALU ops) instead of being hoisted out of the tile loop into long-lived registers.
   asm volatile("" : "+v"(lane));
-  const int dummy = __builtin_amdgcn_readfirstlane(list[__ffs(vmask) - 1]);
+  const int ent = (lane < kNK && lane < n_in_tile) ? tl[lane] : -1;
   const int my_slot = kRowsPerWave * wave + (lane >> 3);
-  int my_rid = my_slot < n_in_tile ? list[my_slot] : -1;
-  my_rid = my_rid < 0 ? dummy : my_rid;
+  const int my_ent = my_slot < n_in_tile ? tl[my_slot] : -1;
+  const uint32_t vmask = (uint32_t)__ballot(ent >= 0);
+  if (vmask == 0u) return 0u;
+  const int dummy = __builtin_amdgcn_readlane(ent, __ffs(vmask) - 1);
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i) {
     const int row = kRowsPerWave * wave + i;
-    const int rid = __builtin_amdgcn_readfirstlane(__shfl(my_rid, 8 * i));
+    int rid = __builtin_amdgcn_readlane(ent, row);
+    rid = rid < 0 ? dummy : rid;
     const uint8_t* src = kv_base + (int64_t)rid * kRowBytes + 16 * lane;
     lds_dma16(src, (uint32_t)(uintptr_t)(buf + row * kLatStride + 16 * lat_rot(row)));
   }
+  const int my_rid = my_ent < 0 ? dummy : my_ent;
   const uint8_t* src = kv_base + (int64_t)my_rid * kRowBytes + kLatBytes + 16 * ((lane & 7) ^ rope_swz(my_slot));
   lds_dma16(src, (uint32_t)(uintptr_t)(buf + kRopeOff + kRowsPerWave * wave * kRopeBytes));
+  return vmask;
 }
 
 // Wait until this wave's loads of the oldest tile in flight have landed, leaving the loads of
@@ -310,18 +317,11 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
     // vm[d] = valid-entry mask of tile it + d (0 past the end); only constant indices, so the
     // masks stay in scalar registers
     uint32_t vm[kNBuf];
-    auto tile_mask = [&](int ti) -> uint32_t {
-      const int e = ti * kNK + lane;
-      const bool v = lane < kNK && e < n_list && list[e] >= 0;
-      return (uint32_t)__ballot(v);
-    };
 #pragma unroll
     for (int pt = 0; pt < kNBuf; ++pt) {
       vm[pt] = 0u;
-      if (pt < kNBuf - 1 && pt < ntiles) {
-        vm[pt] = tile_mask(pt);
-        if (vm[pt]) gather_tile(kv_base, lds + pt * kTileBytes, list + pt * kNK, n_list - pt * kNK, vm[pt], wave, lane);
-      }
+      if (pt < kNBuf - 1 && pt < ntiles)
+        vm[pt] = issue_tile(kv_base, lds + pt * kTileBytes, list + pt * kNK, n_list - pt * kNK, wave, lane);
     }
     int b = 0;  // buffer of tile it (it % kNBuf, kept as a rotating counter)
     for (int it = 0; it < ntiles; ++it) {
@@ -340,161 +340,169 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
       if (it + kNBuf - 1 < ntiles) {
         // tile it + kNBuf - 1 goes to the buffer tile it - 1 used
         const int nt = it + kNBuf - 1, nb = b_cur == 0 ? kNBuf - 1 : b_cur - 1;
-        vm[kNBuf - 1] = tile_mask(nt);
-        if (vm[kNBuf - 1]) gather_tile(kv_base, lds + nb * kTileBytes, list + nt * kNK, n_list - nt * kNK, vm[kNBuf - 1], wave, lane);
+        vm[kNBuf - 1] = issue_tile(kv_base, lds + nb * kTileBytes, list + nt * kNK, n_list - nt * kNK, wave, lane);
       }
       const uint32_t valid = vm[0];
 #pragma unroll
-      for (int d = 0; d + 1 < kNBuf; ++d) vm[d] = vm[d + 1];
+      for (int q = 0; q + 1 < kNBuf; ++q) vm[q] = vm[q + 1];
       vm[kNBuf - 1] = 0u;
       if (valid == 0u) continue;  // uniform across the workgroup
       const lds_u8* tile = lds + b_cur * kTileBytes;
 
       // ---- S^T = K Q^T: lane holds head lane%32, keys 8*(i/4) + 4*(lane/32) + i%4, i = 0..15
-      // S^T for this tile, with the operand fetches issued four MFMAs ahead: written as one asm
-      // block so that S is accumulated in VGPRs (the AGPRs hold the output) and the fetches are
-      // not reordered. Rope k-steps first (both operands from LDS), then the 32 latent k-steps.
-      // LDS reads complete in order, so each wait counts only the younger reads of this block.
-      // Dependent MFMAs chain through srcC directly; the trailing s_nops cover the MFMA-result
-      // to VALU-read latency for the softmax that follows.
+      // S^T for this tile: the 4 rope k-steps (both operands from LDS) and the 32 latent k-steps,
+      // alternating between two accumulation chains, with 8 operand fetches in flight ahead of
+      // the MFMAs (into v224..v255); when a gather is due, its loads are issued between the
+      // MFMAs. Written as one asm block so that S stays in VGPRs (the AGPRs hold the output) and
+      // the fetches are not reordered. LDS reads complete in order, so each wait counts only the
+      // younger reads of this block; the trailing s_nops cover the MFMA-result to VALU-read
+      // latency of the softmax that follows.
       f32x16 s;
       {
         const uint32_t al = (uint32_t)(uintptr_t)(tile + g1_base);
         const uint32_t kb = (uint32_t)(uintptr_t)(tile + rope_base), qb = (uint32_t)(uintptr_t)(lds + qr_base);
         const uint32_t x0 = 32 * (0 ^ rope_x), x1 = 32 * (1 ^ rope_x), x2 = 32 * (2 ^ rope_x), x3 = 32 * (3 ^ rope_x);
-        bf16x8 t0, t1, t2, t3;
+        f32x16 s0, s1;
         asm volatile(
-          "ds_read_b128 %[t0], %[k0]\n"
-          "ds_read_b128 %[t1], %[r0]\n"
-          "ds_read_b128 %[t2], %[k1]\n"
-          "ds_read_b128 %[t3], %[r1]\n"
+          "ds_read_b128 v[224:227], %[k0]\n"
+          "ds_read_b128 v[228:231], %[r0]\n"
+          "ds_read_b128 v[232:235], %[k1]\n"
+          "ds_read_b128 v[236:239], %[r1]\n"
+          "ds_read_b128 v[240:243], %[k2]\n"
+          "ds_read_b128 v[244:247], %[r2]\n"
+          "ds_read_b128 v[248:251], %[k3]\n"
+          "ds_read_b128 v[252:255], %[r3]\n"
+          "s_waitcnt lgkmcnt(6)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[224:227], v[228:231], 0\n"
+          "ds_read_b128 v[224:227], %[al]\n"
+          "ds_read_b128 v[228:231], %[al] offset:32\n"
+          "s_waitcnt lgkmcnt(6)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[232:235], v[236:239], 0\n"
+          "ds_read_b128 v[232:235], %[al] offset:64\n"
+          "ds_read_b128 v[236:239], %[al] offset:96\n"
+          "s_waitcnt lgkmcnt(6)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[240:243], v[244:247], %[s0]\n"
+          "ds_read_b128 v[240:243], %[al] offset:128\n"
+          "ds_read_b128 v[244:247], %[al] offset:160\n"
+          "s_waitcnt lgkmcnt(6)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[248:251], v[252:255], %[s1]\n"
+          "ds_read_b128 v[248:251], %[al] offset:192\n"
+          "ds_read_b128 v[252:255], %[al] offset:224\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[224:227], %[q0], %[s0]\n"
+          "ds_read_b128 v[224:227], %[al] offset:256\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[228:231], %[q1], %[s1]\n"
+          "ds_read_b128 v[228:231], %[al] offset:288\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[232:235], %[q2], %[s0]\n"
+          "ds_read_b128 v[232:235], %[al] offset:320\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[236:239], %[q3], %[s1]\n"
+          "ds_read_b128 v[236:239], %[al] offset:352\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[240:243], %[q4], %[s0]\n"
+          "ds_read_b128 v[240:243], %[al] offset:384\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[244:247], %[q5], %[s1]\n"
+          "ds_read_b128 v[244:247], %[al] offset:416\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[248:251], %[q6], %[s0]\n"
+          "ds_read_b128 v[248:251], %[al] offset:448\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[252:255], %[q7], %[s1]\n"
+          "ds_read_b128 v[252:255], %[al] offset:480\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[224:227], %[q8], %[s0]\n"
+          "ds_read_b128 v[224:227], %[al] offset:512\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[228:231], %[q9], %[s1]\n"
+          "ds_read_b128 v[228:231], %[al] offset:544\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[232:235], %[q10], %[s0]\n"
+          "ds_read_b128 v[232:235], %[al] offset:576\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[236:239], %[q11], %[s1]\n"
+          "ds_read_b128 v[236:239], %[al] offset:608\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[240:243], %[q12], %[s0]\n"
+          "ds_read_b128 v[240:243], %[al] offset:640\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[244:247], %[q13], %[s1]\n"
+          "ds_read_b128 v[244:247], %[al] offset:672\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[248:251], %[q14], %[s0]\n"
+          "ds_read_b128 v[248:251], %[al] offset:704\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[252:255], %[q15], %[s1]\n"
+          "ds_read_b128 v[252:255], %[al] offset:736\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[224:227], %[q16], %[s0]\n"
+          "ds_read_b128 v[224:227], %[al] offset:768\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[228:231], %[q17], %[s1]\n"
+          "ds_read_b128 v[228:231], %[al] offset:800\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[232:235], %[q18], %[s0]\n"
+          "ds_read_b128 v[232:235], %[al] offset:832\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[236:239], %[q19], %[s1]\n"
+          "ds_read_b128 v[236:239], %[al] offset:864\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[240:243], %[q20], %[s0]\n"
+          "ds_read_b128 v[240:243], %[al] offset:896\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[244:247], %[q21], %[s1]\n"
+          "ds_read_b128 v[244:247], %[al] offset:928\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[248:251], %[q22], %[s0]\n"
+          "ds_read_b128 v[248:251], %[al] offset:960\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[252:255], %[q23], %[s1]\n"
+          "ds_read_b128 v[252:255], %[al] offset:992\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[224:227], %[q24], %[s0]\n"
+          "s_waitcnt lgkmcnt(6)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[228:231], %[q25], %[s1]\n"
+          "s_waitcnt lgkmcnt(5)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[232:235], %[q26], %[s0]\n"
+          "s_waitcnt lgkmcnt(4)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[236:239], %[q27], %[s1]\n"
+          "s_waitcnt lgkmcnt(3)\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[240:243], %[q28], %[s0]\n"
           "s_waitcnt lgkmcnt(2)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[t1], 0\n"
-          "ds_read_b128 %[t0], %[k2]\n"
-          "ds_read_b128 %[t1], %[r2]\n"
-          "s_waitcnt lgkmcnt(2)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[t3], %[s]\n"
-          "ds_read_b128 %[t2], %[k3]\n"
-          "ds_read_b128 %[t3], %[r3]\n"
-          "s_waitcnt lgkmcnt(2)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[t1], %[s]\n"
-          "ds_read_b128 %[t0], %[al]\n"
-          "ds_read_b128 %[t1], %[al] offset:32\n"
-          "s_waitcnt lgkmcnt(2)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[t3], %[s]\n"
-          "ds_read_b128 %[t2], %[al] offset:64\n"
-          "ds_read_b128 %[t3], %[al] offset:96\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q0], %[s]\n"
-          "ds_read_b128 %[t0], %[al] offset:128\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q1], %[s]\n"
-          "ds_read_b128 %[t1], %[al] offset:160\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q2], %[s]\n"
-          "ds_read_b128 %[t2], %[al] offset:192\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q3], %[s]\n"
-          "ds_read_b128 %[t3], %[al] offset:224\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q4], %[s]\n"
-          "ds_read_b128 %[t0], %[al] offset:256\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q5], %[s]\n"
-          "ds_read_b128 %[t1], %[al] offset:288\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q6], %[s]\n"
-          "ds_read_b128 %[t2], %[al] offset:320\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q7], %[s]\n"
-          "ds_read_b128 %[t3], %[al] offset:352\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q8], %[s]\n"
-          "ds_read_b128 %[t0], %[al] offset:384\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q9], %[s]\n"
-          "ds_read_b128 %[t1], %[al] offset:416\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q10], %[s]\n"
-          "ds_read_b128 %[t2], %[al] offset:448\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q11], %[s]\n"
-          "ds_read_b128 %[t3], %[al] offset:480\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q12], %[s]\n"
-          "ds_read_b128 %[t0], %[al] offset:512\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q13], %[s]\n"
-          "ds_read_b128 %[t1], %[al] offset:544\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q14], %[s]\n"
-          "ds_read_b128 %[t2], %[al] offset:576\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q15], %[s]\n"
-          "ds_read_b128 %[t3], %[al] offset:608\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q16], %[s]\n"
-          "ds_read_b128 %[t0], %[al] offset:640\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q17], %[s]\n"
-          "ds_read_b128 %[t1], %[al] offset:672\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q18], %[s]\n"
-          "ds_read_b128 %[t2], %[al] offset:704\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q19], %[s]\n"
-          "ds_read_b128 %[t3], %[al] offset:736\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q20], %[s]\n"
-          "ds_read_b128 %[t0], %[al] offset:768\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q21], %[s]\n"
-          "ds_read_b128 %[t1], %[al] offset:800\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q22], %[s]\n"
-          "ds_read_b128 %[t2], %[al] offset:832\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q23], %[s]\n"
-          "ds_read_b128 %[t3], %[al] offset:864\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q24], %[s]\n"
-          "ds_read_b128 %[t0], %[al] offset:896\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q25], %[s]\n"
-          "ds_read_b128 %[t1], %[al] offset:928\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q26], %[s]\n"
-          "ds_read_b128 %[t2], %[al] offset:960\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q27], %[s]\n"
-          "ds_read_b128 %[t3], %[al] offset:992\n"
-          "s_waitcnt lgkmcnt(3)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q28], %[s]\n"
-          "s_waitcnt lgkmcnt(2)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q29], %[s]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[244:247], %[q29], %[s1]\n"
           "s_waitcnt lgkmcnt(1)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q30], %[s]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[248:251], %[q30], %[s0]\n"
           "s_waitcnt lgkmcnt(0)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q31], %[s]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s1], v[252:255], %[q31], %[s1]\n"
           "s_nop 7\n"
           "s_nop 7\n"
           "s_nop 7\n"
-          : [s] "=&v"(s), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3)
+          : [s0] "=&v"(s0), [s1] "=&v"(s1)
           : [al] "v"(al), [k0] "v"(kb + x0), [k1] "v"(kb + x1), [k2] "v"(kb + x2), [k3] "v"(kb + x3),
             [r0] "v"(qb + x0), [r1] "v"(qb + x1), [r2] "v"(qb + x2), [r3] "v"(qb + x3),
             [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]), [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]), [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]), [q14] "v"(qf[14]), [q15] "v"(qf[15]), [q16] "v"(qf[16]), [q17] "v"(qf[17]), [q18] "v"(qf[18]), [q19] "v"(qf[19]), [q20] "v"(qf[20]), [q21] "v"(qf[21]), [q22] "v"(qf[22]), [q23] "v"(qf[23]), [q24] "v"(qf[24]), [q25] "v"(qf[25]), [q26] "v"(qf[26]), [q27] "v"(qf[27]), [q28] "v"(qf[28]), [q29] "v"(qf[29]), [q30] "v"(qf[30]), [q31] "v"(qf[31])
-          : "memory");
+          : "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
+        s = s0 + s1;
       }
-      // ---- softmax bookkeeping (log2 domain); the two lanes of a head see all 32 keys
-      float mx = -INFINITY;
-      const uint32_t vh = valid >> (4 * half);  // bit 8*(i/4) + i%4: key of s[i] is valid
+      // ---- softmax bookkeeping in the log2 domain; the two lanes of a head see all 32 keys.
+      //      c_scale > 0, so the largest raw score gives the largest logit.
+      if (valid != 0xffffffffu) {  // uniform: a partial tile, mask its invalid keys
+        const uint32_t vh = valid >> (4 * half);  // bit 8*(i/4) + i%4: key of s[i] is valid
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float v = ((vh >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] * c_scale : -INFINITY;
-        s[i] = v;
-        mx = fmaxf(mx, v);
+        for (int i = 0; i < 16; ++i)
+          if (!((vh >> (8 * (i >> 2) + (i & 3))) & 1u)) s[i] = -INFINITY;
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float mx = s[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+      {
+        // the other lane of the head is lane ^ 32: v_permlane32_swap exchanges the wave halves
+        // (one result holds the lane's own value, the other its partner's)
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]))) * c_scale;
+      }
       if (mx > m_ref + kRescaleThreshold) {
         // nothing accumulated yet (m_ref = -inf): the output is still zero, just adopt mx
         const float alpha = (m_ref == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - mx);
@@ -518,32 +526,160 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(s[8 * ks + e] - m_ref);  // exp2(-inf) = 0 for invalid keys
+          // exp2(-inf) = 0 for invalid keys
+          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * ks + e], c_scale, -m_ref));
           l_sum += pv[e];
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) pk[ks][e] = (__bf16)pv[e];
       }
-      // ---- O^T += V^T P. K step ks takes keys 16*ks + 8*(e/4) + 4*h + e%4 in slot 8*h + e, the
-      //      order in which lane half h holds them in pk[ks]
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int mt = 0; mt < kDv / 32; ++mt) {
-          const int off = 64 * mt + 16 * kLatStride * ks;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(tile + tr_base[0] + off));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(tile + tr_base[1] + off));
-          // whole-vector reinterpretation (element-wise bit casts of the 16-bit lanes were
-          // miscompiled into a broadcast of element 0)
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[ks], o[mt], 0, 0, 0);
-        }
+      // ---- O^T += V^T P, 32 MFMAs (K step ks = j / 16, column block mt = j % 16) with the two
+      //      transpose reads of each A operand issued eight MFMAs ahead into v224..v255. K step
+      //      ks takes keys 16*ks + 8*(e/4) + 4*h + e%4 in slot 8*h + e, the order in which lane
+      //      half h holds them in pk[ks]; the read of key row 16*ks + 4*(G/2) + 8*a + j/4 sits at
+      //      tr_base[a] = tr_base[0] + 10272*a, plus 64*mt + 20480*ks. The output accumulators
+      //      stay in AGPRs; their readers after the tile loop are separated by s_nops.
+      {
+        const uint32_t ta = (uint32_t)(uintptr_t)(tile + tr_base[0]);
+        asm volatile(
+          "ds_read_b64_tr_b16 v[224:225], %[ta]\n"
+          "ds_read_b64_tr_b16 v[226:227], %[ta] offset:10272\n"
+          "ds_read_b64_tr_b16 v[228:229], %[ta] offset:64\n"
+          "ds_read_b64_tr_b16 v[230:231], %[ta] offset:10336\n"
+          "ds_read_b64_tr_b16 v[232:233], %[ta] offset:128\n"
+          "ds_read_b64_tr_b16 v[234:235], %[ta] offset:10400\n"
+          "ds_read_b64_tr_b16 v[236:237], %[ta] offset:192\n"
+          "ds_read_b64_tr_b16 v[238:239], %[ta] offset:10464\n"
+          "ds_read_b64_tr_b16 v[240:241], %[ta] offset:256\n"
+          "ds_read_b64_tr_b16 v[242:243], %[ta] offset:10528\n"
+          "ds_read_b64_tr_b16 v[244:245], %[ta] offset:320\n"
+          "ds_read_b64_tr_b16 v[246:247], %[ta] offset:10592\n"
+          "ds_read_b64_tr_b16 v[248:249], %[ta] offset:384\n"
+          "ds_read_b64_tr_b16 v[250:251], %[ta] offset:10656\n"
+          "ds_read_b64_tr_b16 v[252:253], %[ta] offset:448\n"
+          "ds_read_b64_tr_b16 v[254:255], %[ta] offset:10720\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o0], v[224:227], %[p0], %[o0]\n"
+          "ds_read_b64_tr_b16 v[224:225], %[ta] offset:512\n"
+          "ds_read_b64_tr_b16 v[226:227], %[ta] offset:10784\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o1], v[228:231], %[p0], %[o1]\n"
+          "ds_read_b64_tr_b16 v[228:229], %[ta] offset:576\n"
+          "ds_read_b64_tr_b16 v[230:231], %[ta] offset:10848\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o2], v[232:235], %[p0], %[o2]\n"
+          "ds_read_b64_tr_b16 v[232:233], %[ta] offset:640\n"
+          "ds_read_b64_tr_b16 v[234:235], %[ta] offset:10912\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o3], v[236:239], %[p0], %[o3]\n"
+          "ds_read_b64_tr_b16 v[236:237], %[ta] offset:704\n"
+          "ds_read_b64_tr_b16 v[238:239], %[ta] offset:10976\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o4], v[240:243], %[p0], %[o4]\n"
+          "ds_read_b64_tr_b16 v[240:241], %[ta] offset:768\n"
+          "ds_read_b64_tr_b16 v[242:243], %[ta] offset:11040\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o5], v[244:247], %[p0], %[o5]\n"
+          "ds_read_b64_tr_b16 v[244:245], %[ta] offset:832\n"
+          "ds_read_b64_tr_b16 v[246:247], %[ta] offset:11104\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o6], v[248:251], %[p0], %[o6]\n"
+          "ds_read_b64_tr_b16 v[248:249], %[ta] offset:896\n"
+          "ds_read_b64_tr_b16 v[250:251], %[ta] offset:11168\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o7], v[252:255], %[p0], %[o7]\n"
+          "ds_read_b64_tr_b16 v[252:253], %[ta] offset:960\n"
+          "ds_read_b64_tr_b16 v[254:255], %[ta] offset:11232\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o8], v[224:227], %[p0], %[o8]\n"
+          "ds_read_b64_tr_b16 v[224:225], %[ta] offset:20480\n"
+          "ds_read_b64_tr_b16 v[226:227], %[ta] offset:30752\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o9], v[228:231], %[p0], %[o9]\n"
+          "ds_read_b64_tr_b16 v[228:229], %[ta] offset:20544\n"
+          "ds_read_b64_tr_b16 v[230:231], %[ta] offset:30816\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o10], v[232:235], %[p0], %[o10]\n"
+          "ds_read_b64_tr_b16 v[232:233], %[ta] offset:20608\n"
+          "ds_read_b64_tr_b16 v[234:235], %[ta] offset:30880\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o11], v[236:239], %[p0], %[o11]\n"
+          "ds_read_b64_tr_b16 v[236:237], %[ta] offset:20672\n"
+          "ds_read_b64_tr_b16 v[238:239], %[ta] offset:30944\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o12], v[240:243], %[p0], %[o12]\n"
+          "ds_read_b64_tr_b16 v[240:241], %[ta] offset:20736\n"
+          "ds_read_b64_tr_b16 v[242:243], %[ta] offset:31008\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o13], v[244:247], %[p0], %[o13]\n"
+          "ds_read_b64_tr_b16 v[244:245], %[ta] offset:20800\n"
+          "ds_read_b64_tr_b16 v[246:247], %[ta] offset:31072\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o14], v[248:251], %[p0], %[o14]\n"
+          "ds_read_b64_tr_b16 v[248:249], %[ta] offset:20864\n"
+          "ds_read_b64_tr_b16 v[250:251], %[ta] offset:31136\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o15], v[252:255], %[p0], %[o15]\n"
+          "ds_read_b64_tr_b16 v[252:253], %[ta] offset:20928\n"
+          "ds_read_b64_tr_b16 v[254:255], %[ta] offset:31200\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o0], v[224:227], %[p1], %[o0]\n"
+          "ds_read_b64_tr_b16 v[224:225], %[ta] offset:20992\n"
+          "ds_read_b64_tr_b16 v[226:227], %[ta] offset:31264\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o1], v[228:231], %[p1], %[o1]\n"
+          "ds_read_b64_tr_b16 v[228:229], %[ta] offset:21056\n"
+          "ds_read_b64_tr_b16 v[230:231], %[ta] offset:31328\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o2], v[232:235], %[p1], %[o2]\n"
+          "ds_read_b64_tr_b16 v[232:233], %[ta] offset:21120\n"
+          "ds_read_b64_tr_b16 v[234:235], %[ta] offset:31392\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o3], v[236:239], %[p1], %[o3]\n"
+          "ds_read_b64_tr_b16 v[236:237], %[ta] offset:21184\n"
+          "ds_read_b64_tr_b16 v[238:239], %[ta] offset:31456\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o4], v[240:243], %[p1], %[o4]\n"
+          "ds_read_b64_tr_b16 v[240:241], %[ta] offset:21248\n"
+          "ds_read_b64_tr_b16 v[242:243], %[ta] offset:31520\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o5], v[244:247], %[p1], %[o5]\n"
+          "ds_read_b64_tr_b16 v[244:245], %[ta] offset:21312\n"
+          "ds_read_b64_tr_b16 v[246:247], %[ta] offset:31584\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o6], v[248:251], %[p1], %[o6]\n"
+          "ds_read_b64_tr_b16 v[248:249], %[ta] offset:21376\n"
+          "ds_read_b64_tr_b16 v[250:251], %[ta] offset:31648\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o7], v[252:255], %[p1], %[o7]\n"
+          "ds_read_b64_tr_b16 v[252:253], %[ta] offset:21440\n"
+          "ds_read_b64_tr_b16 v[254:255], %[ta] offset:31712\n"
+          "s_waitcnt lgkmcnt(14)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o8], v[224:227], %[p1], %[o8]\n"
+          "s_waitcnt lgkmcnt(12)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o9], v[228:231], %[p1], %[o9]\n"
+          "s_waitcnt lgkmcnt(10)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o10], v[232:235], %[p1], %[o10]\n"
+          "s_waitcnt lgkmcnt(8)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o11], v[236:239], %[p1], %[o11]\n"
+          "s_waitcnt lgkmcnt(6)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o12], v[240:243], %[p1], %[o12]\n"
+          "s_waitcnt lgkmcnt(4)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o13], v[244:247], %[p1], %[o13]\n"
+          "s_waitcnt lgkmcnt(2)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o14], v[248:251], %[p1], %[o14]\n"
+          "s_waitcnt lgkmcnt(0)\n"
+          "v_mfma_f32_32x32x16_bf16 %[o15], v[252:255], %[p1], %[o15]\n"
+          : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]), [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]), [o10] "+a"(o[10]), [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]), [o14] "+a"(o[14]), [o15] "+a"(o[15])
+          : [ta] "v"(ta), [p0] "v"(pk[0]), [p1] "v"(pk[1])
+          : "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
       }
     }
   }
 
+  // the accumulators were last written by MFMAs inside asm: cover the MFMA-result to VALU-read
+  // latency before the epilogue reads them
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   // per-head totals: the two lanes of a head hold the sums over their key halves
   const float l_tot = l_sum + __shfl_xor(l_sum, 32);
   const int head = 32 * wave + hl;
