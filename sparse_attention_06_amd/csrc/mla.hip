@@ -92,7 +92,8 @@ static_assert(kNBuf >= 2 && kNBuf <= 4, "wait_gathers covers up to two younger t
 constexpr int kListCap = 2048;                   // resolved entries held in LDS at a time
 constexpr int kListOff = kNBuf * kTileBytes;
 constexpr int kQRopeOff = kListOff + 4 * kListCap; // rope dims of the 128 query heads (16 KB)
-constexpr int kLdsBytes = kQRopeOff + kH * kRopeBytes;
+constexpr int kMaskOff = kQRopeOff + kH * kRopeBytes; // valid-entry mask per tile of the list
+constexpr int kLdsBytes = kMaskOff + 4 * (kListCap / kNK);
 static_assert(kH * kDv * 2 <= kLdsBytes, "output staging");
 static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
 constexpr float kLog2e = 1.4426950408889634f;
@@ -124,56 +125,95 @@ __device__ __forceinline__ int resolve_entry(const AttnArgs& a, int r, int seq, 
   return (int)row;  // caches hold < 2^31 rows
 }
 
-// One wave-wide global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l's bytes
-// land at LDS byte address lds_base + 16 * l; lds_base must be wave-uniform. Issued from inline
-// asm so that the compiler's wait-count pass does not treat these LDS writes as aliasing every
-// later LDS read (it would drain all in-flight tiles before each one); the tile loop waits for
-// them explicitly instead. The instruction writes no VGPR; M0 is saved and restored.
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(gptr)
-      : "memory");
+// A wave-uniform 64-bit value, placed in scalar registers. readfirstlane returns int: each half
+// goes through uint32_t so that the low half is zero-extended, not sign-extended into the high.
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// This wave's share of one tile gather (tile entries tl[0 .. n_in_tile), at most kNK): tile rows
-// 8w..8w+7 as 8 wave-wide latent loads (lane l fetches chunk l, into the row's rotated position)
-// and one rope load (lane l: row 8w + l/8, chunk (l%8) ^ rope_swz(row)). Returns the mask of
-// valid entries (bit e: entry e is a visible position with a valid page); loads nothing when it
-// is 0. Otherwise every lane is active in every load, so each wave has exactly kInstrPerWave
-// loads in flight per tile; rows of invalid entries load the tile's first valid row instead
-// (finite data; their probability is 0). Lanes 0..31 read the tile's entries once and the row ids
-// are taken from them with v_readlane (no LDS round trips between the loads).
-__device__ __forceinline__ uint32_t issue_tile(const uint8_t* __restrict__ kv_base, lds_u8* buf,
-                                               const int* tl, int n_in_tile, int wave, int lane) {
-  // An opaque copy of the lane id: the per-lane offsets below are recomputed per tile (a few
-  // VALU ops) instead of being hoisted out of the tile loop into long-lived registers.
+// This wave's share of one tile gather: latent rows 4i + w (i = 0..7), each one wave-wide
+// 16-byte-per-lane global -> LDS load (global_load_lds_dwordx4) of the row's 1 KB into its rotated
+// line, and the rope chunks of rows 8w..8w+7 (lane l: row 8w + l/8, chunk (l%8) ^ rope_swz(row))
+// in one more load. Returns the tile's valid-entry mask; loads nothing when it is 0. Otherwise
+// every lane is active in every load, so each wave has exactly kInstrPerWave loads in flight per
+// tile. The row ids come from the tile's entries (read from LDS an iteration ahead) through
+// v_readlane. The loads are issued from inline asm so that the compiler's wait-count pass does
+// not treat their LDS writes as aliasing every later LDS read; the tile loop waits for them
+// explicitly. M0 is saved and restored.
+struct TileEntries {
+  int ent;     // entry lane%32 of the tile
+  int my_ent;  // entry 8w + lane/8, whose rope chunk this lane loads
+  int mask;    // valid-entry mask of the tile (same in every lane)
+};
+// The tile's entries after the list pass below: every entry of a tile with a nonzero mask is a
+// row id (invalid ones replaced by a valid row of the same tile).
+__device__ __forceinline__ TileEntries read_entries(const int* list, const int* tmask, int t, int ntiles, int wave, int lane) {
+  // opaque lane id: the addresses are recomputed here (two VALU ops) rather than kept live
+  // across the tile loop, where the register file is full
   asm volatile("" : "+v"(lane));
-  const int ent = (lane < kNK && lane < n_in_tile) ? tl[lane] : -1;
-  const int my_slot = kRowsPerWave * wave + (lane >> 3);
-  const int my_ent = my_slot < n_in_tile ? tl[my_slot] : -1;
-  const uint32_t vmask = (uint32_t)__ballot(ent >= 0);
+  if (t >= ntiles) return TileEntries{0, 0, 0};
+  const int* tl = list + t * kNK;
+  return TileEntries{tl[lane & 31], tl[kRowsPerWave * wave + (lane >> 3)], tmask[t]};
+}
+__device__ __forceinline__ uint32_t issue_tile(const uint8_t* __restrict__ kv_base, lds_u8* buf,
+                                               TileEntries te, int wave, int lane) {
+  // An opaque copy of the lane id: the per-lane values below are recomputed per tile (a few VALU
+  // ops) instead of being hoisted out of the tile loop into long-lived registers.
+  asm volatile("" : "+v"(lane));
+  const uint32_t vmask = (uint32_t)__builtin_amdgcn_readfirstlane(te.mask);
   if (vmask == 0u) return 0u;
-  const int dummy = __builtin_amdgcn_readlane(ent, __ffs(vmask) - 1);
+  // latent row 4i + w: one 64-bit per-lane address (row start + 16 * lane) per load
+  const uint8_t* kvl = kv_base + 16 * lane;
+  uint64_t ad[kRowsPerWave];
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i) {
-    const int row = kRowsPerWave * wave + i;
-    int rid = __builtin_amdgcn_readlane(ent, row);
-    rid = rid < 0 ? dummy : rid;
-    const uint8_t* src = kv_base + (int64_t)rid * kRowBytes + 16 * lane;
-    lds_dma16(src, (uint32_t)(uintptr_t)(buf + row * kLatStride + 16 * lat_rot(row)));
+    const uint32_t rid = (uint32_t)__builtin_amdgcn_readlane(te.ent, 4 * i + wave);
+    ad[i] = (uint64_t)(uintptr_t)(kvl + (uint64_t)rid * kRowBytes);
   }
-  const int my_rid = my_ent < 0 ? dummy : my_ent;
-  const uint8_t* src = kv_base + (int64_t)my_rid * kRowBytes + kLatBytes + 16 * ((lane & 7) ^ rope_swz(my_slot));
-  lds_dma16(src, (uint32_t)(uintptr_t)(buf + kRopeOff + kRowsPerWave * wave * kRopeBytes));
+  // row 4i + w starts 16 * lat_rot(4i + w) = 16 * (4w + i%4) bytes into its line (4i + w) * 1280
+  const uint32_t lat_m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)buf + wave * (kLatStride + 64));
+  const uint32_t rope_m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(buf + kRopeOff + kRowsPerWave * wave * kRopeBytes));
+  const int my_slot = kRowsPerWave * wave + (lane >> 3);
+  const uint64_t rope_src = (uint64_t)(uintptr_t)(kv_base + (int64_t)te.my_ent * kRowBytes + kLatBytes + 16 * ((lane & 7) ^ rope_swz(my_slot)));
+  uint32_t sv;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n"
+      "s_add_u32 m0, %[lm0], 0\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[a0], off\n"
+      "s_add_u32 m0, %[lm0], 5136\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[a1], off\n"
+      "s_add_u32 m0, %[lm0], 10272\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[a2], off\n"
+      "s_add_u32 m0, %[lm0], 15408\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[a3], off\n"
+      "s_add_u32 m0, %[lm0], 20480\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[a4], off\n"
+      "s_add_u32 m0, %[lm0], 25616\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[a5], off\n"
+      "s_add_u32 m0, %[lm0], 30752\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[a6], off\n"
+      "s_add_u32 m0, %[lm0], 35888\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[a7], off\n"
+      "s_mov_b32 m0, %[rm0]\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %[rsrc], off\n"
+      "s_mov_b32 m0, %[sv]\n"
+      : [sv] "=&s"(sv)
+      : [a0] "v"(ad[0]), [a1] "v"(ad[1]), [a2] "v"(ad[2]), [a3] "v"(ad[3]), [a4] "v"(ad[4]), [a5] "v"(ad[5]), [a6] "v"(ad[6]), [a7] "v"(ad[7]), [lm0] "s"(lat_m0), [rm0] "s"(rope_m0), [rsrc] "v"(rope_src)
+      : "memory");
   return vmask;
 }
+static_assert(kLatStride * 4 == 5120, "latent row 4i + w lies 5120*i bytes after row w");
 
 // Wait until this wave's loads of the oldest tile in flight have landed, leaving the loads of
 // `younger` later tiles in flight (each tile is kInstrPerWave loads per wave, issued in order).
@@ -250,24 +290,13 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
   const int e_end = min(n_entries, e_begin + entries_per_split);
   lds_u8* lds = (lds_u8*)smem;
   int* list = (int*)(smem + kListOff);
+  int* tmask = (int*)(smem + kMaskOff);
   const int hl = lane & 31, half = lane >> 5;  // lane's head within the wave, key half
 
   // query heads as B operands: lane holds head 32w + lane%32, dims 16*ks + 8*(lane/32) .. +8 of
   // the latent part in registers; the rope dims of all heads go to LDS (head h keeps chunk c at
-  // c ^ rope_swz(h) of its 128-byte row). The loads are issued here and complete while the
-  // first chunk of the index list is resolved.
+  // c ^ rope_swz(h) of its 128-byte row). Loaded once the first tile gathers are in flight.
   bf16x8 qf[kDv / 16];
-  i32x4 qr[kH * 8 / 256];
-  {
-    const uint16_t* qh = a.q + ((int64_t)r * kH + 32 * wave + hl) * kDqk + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < kDv / 16; ++ks) qf[ks] = *(const bf16x8*)(qh + 16 * ks);
-#pragma unroll
-    for (int j = 0; j < kH * 8 / 256; ++j) {
-      const int i = threadIdx.x + 256 * j, h = i >> 3, c = i & 7;
-      qr[j] = *(const i32x4*)(a.q + ((int64_t)r * kH + h) * kDqk + kDv + 8 * c);
-    }
-  }
   // O^T accumulators: o[mt] = value columns 32mt .. 32mt+31 of head 32w + lane%32
   f32x16 o[kDv / 32];
 #pragma unroll
@@ -300,20 +329,24 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
     const int ce = min(e_end, cb + kListCap);
     __syncthreads();  // the previous chunk is done with the list and the buffers
     for (int e = cb + threadIdx.x; e < ce; e += 256) list[e - cb] = resolve_entry(a, r, seq, t, e);
-    if (cb == e_begin) {
-#pragma unroll
-      for (int j = 0; j < kH * 8 / 256; ++j) {
-        const int i = threadIdx.x + 256 * j, h = i >> 3, c = i & 7;
-        *(__attribute__((address_space(3))) i32x4*)(lds + kQRopeOff + h * kRopeBytes + 16 * (c ^ rope_swz(h))) = qr[j];
-      }
-      // consume the fragments here, so their loads are complete before the tile loop and no
-      // wait for them lands inside it (where it would also drain the in-flight tile gathers)
-#pragma unroll
-      for (int ks = 0; ks < kDv / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
-    }
     __syncthreads();
     const int n_list = ce - cb;
     const int ntiles = (n_list + kNK - 1) / kNK;
+    // Per-tile valid-entry masks; every invalid entry of a tile (and the tail of the last tile)
+    // takes the tile's first valid row id, so a gather loads finite data for it (its probability
+    // is 0). Lanes 0..31 take tile t0, lanes 32..63 tile t0 + 1.
+    for (int t0 = 2 * wave; t0 < ntiles; t0 += 8) {
+      const int tt = t0 + half, e = tt * kNK + hl;
+      const int v = (tt < ntiles && e < n_list) ? list[e] : -1;
+      const uint64_t bal = __ballot(v >= 0);
+      const uint32_t m = half ? (uint32_t)(bal >> 32) : (uint32_t)bal;
+      const int sub = __shfl(v, 32 * half + (m ? __ffs(m) - 1 : 0));
+      if (tt < ntiles) {
+        if (v < 0 && m) list[e] = sub;
+        if (hl == 0) tmask[tt] = (int)m;
+      }
+    }
+    __syncthreads();
     // vm[d] = valid-entry mask of tile it + d (0 past the end); only constant indices, so the
     // masks stay in scalar registers
     uint32_t vm[kNBuf];
@@ -321,7 +354,31 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
     for (int pt = 0; pt < kNBuf; ++pt) {
       vm[pt] = 0u;
       if (pt < kNBuf - 1 && pt < ntiles)
-        vm[pt] = issue_tile(kv_base, lds + pt * kTileBytes, list + pt * kNK, n_list - pt * kNK, wave, lane);
+        vm[pt] = issue_tile(kv_base, lds + pt * kTileBytes, read_entries(list, tmask, pt, ntiles, wave, lane), wave, lane);
+    }
+    // entries of the next tile to gather, read one iteration before they are needed
+    TileEntries nxt = read_entries(list, tmask, kNBuf - 1, ntiles, wave, lane);
+    if (cb == e_begin) {
+      // the query, while the first gathers are in flight
+      const uint16_t* qh = a.q + ((int64_t)r * kH + 32 * wave + hl) * kDqk + 8 * half;
+#pragma unroll
+      for (int ks = 0; ks < kDv / 16; ++ks) qf[ks] = *(const bf16x8*)(qh + 16 * ks);
+      // thread id rebuilt from the lane count (mbcnt) and the wave index, so that nothing has to
+      // stay live from the kernel start for these addresses
+      int lane_now;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_now));
+      const int tid = 64 * wave + lane_now;
+#pragma unroll
+      for (int j = 0; j < kH * 8 / 256; ++j) {
+        const int i = tid + 256 * j, h = i >> 3, c = i & 7;
+        const i32x4 v = *(const i32x4*)(a.q + ((int64_t)r * kH + h) * kDqk + kDv + 8 * c);
+        *(__attribute__((address_space(3))) i32x4*)(lds + kQRopeOff + h * kRopeBytes + 16 * (c ^ rope_swz(h))) = v;
+      }
+      // consume the fragments here, so their loads are complete before the tile loop and no
+      // wait for them lands inside it (where it would also drain the in-flight tile gathers)
+#pragma unroll
+      for (int ks = 0; ks < kDv / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
+      __syncthreads();  // the rope part of the query is in LDS
     }
     int b = 0;  // buffer of tile it (it % kNBuf, kept as a rotating counter)
     for (int it = 0; it < ntiles; ++it) {
@@ -340,7 +397,8 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
       if (it + kNBuf - 1 < ntiles) {
         // tile it + kNBuf - 1 goes to the buffer tile it - 1 used
         const int nt = it + kNBuf - 1, nb = b_cur == 0 ? kNBuf - 1 : b_cur - 1;
-        vm[kNBuf - 1] = issue_tile(kv_base, lds + nb * kTileBytes, list + nt * kNK, n_list - nt * kNK, wave, lane);
+        vm[kNBuf - 1] = issue_tile(kv_base, lds + nb * kTileBytes, nxt, wave, lane);
+        nxt = read_entries(list, tmask, nt + 1, ntiles, wave, lane);
       }
       const uint32_t valid = vm[0];
 #pragma unroll
