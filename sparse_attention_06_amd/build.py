@@ -25,9 +25,14 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# The indexer kernels keep their small MFMA accumulators in VGPRs, next to the VALU epilogue that
+# reads them (the attention kernel needs AGPRs for its output accumulators).
+EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines()
             if "not a recognized feature for this target" not in ln]
