@@ -160,77 +160,90 @@ __device__ __forceinline__ void score_key_tile(const QueryOps<NQ>& o, const KeyT
 
 // ---- decode / MTP key scan: LDS-staged, one DMA ring per wave
 //
-// Each wave scans a contiguous key range of one sequence for all NQ query rows of that sequence
-// (the rows of a sequence share every key read). Keys stream from HBM straight into a wave-private
-// ring of kRing tiles in LDS with global_load_lds (16 keys x 128 B = 2 KB per tile in two
-// wave-wide loads, plus the 16 per-token scales), kRing - 1 tiles ahead of the MFMAs, so enough
-// bytes are in flight to cover HBM latency without holding them in registers; no workgroup
-// barrier is involved. In LDS, key k (0..7) of 1 KB block b keeps its 16-byte chunk c at granule
-// 8k + (c ^ ((k & 6) | b)), so the 16 keys read together by a lane group land on 16 distinct
-// bank groups.
+// Each wave scans a contiguous, page-aligned key range of one sequence for all NQ query rows of
+// that sequence (the rows of a sequence share every key read). One loop iteration is one page of
+// 64 keys, computed as four 16-key sub-tiles. Keys stream from HBM straight into a wave-private
+// ring of eight 16-key slots (two pages) in LDS with global_load_lds: a slot is refilled with the
+// same sub-tile of the page two ahead as soon as its bytes are in registers, so about six slots
+// are in flight while one is computed, and no workgroup barrier is involved. Each page's 64
+// per-token scales ride along in one 4-byte-per-lane load into one of four scale slots.
+//
+// In a slot, key k (0..7) of 1 KB block b keeps its 16-byte chunk c at granule 8k + (c ^ ((k & 6) | b)),
+// so the 16 keys read together by a lane group land on 16 distinct bank groups.
+//
+// The head sums of a page's four sub-tiles are reduced over the four 16-lane groups together (two
+// permlane32 swaps, one permlane16 swap), which leaves lane l with the score of key l of the page:
+// one 256-byte store per query row per page.
 constexpr int kRing = 8;
 constexpr int kTileKeys = 16;
-constexpr int kRingTileBytes = kTileKeys * kDi;         // 2048
-constexpr int kRingScaleBytes = 256;                    // 64 lanes x 4 B (scale of key lane%16)
-constexpr int kWaveRingBytes = kRing * (kRingTileBytes + kRingScaleBytes);
-constexpr int kScanWaves = 4;
 constexpr int kScanPage = 64;                           // page size the scan is built for
-constexpr int kScanLdsBytes = kScanWaves * kWaveRingBytes;  // 73728
+constexpr int kSubTiles = kScanPage / kTileKeys;        // 4
+constexpr int kRingTileBytes = kTileKeys * kDi;         // 2048
+constexpr int kScaleSlots = 4;
+constexpr int kScaleSlotBytes = 4 * kScanPage;          // 256
+constexpr int kWaveRingBytes = kRing * kRingTileBytes + kScaleSlots * kScaleSlotBytes;  // 17408
+constexpr int kScanWaves = 4;
+constexpr int kScanLdsBytes = kScanWaves * kWaveRingBytes;  // 69632
 
 typedef __attribute__((address_space(3))) uint8_t lds8;
 
-// Issue the loads of one tile (16 consecutive keys of one page, starting at physical row row0)
-// into ring slot `slot`: two wave-wide 16-byte-per-lane key loads and one 4-byte-per-lane scale
-// load, always exactly three vector-memory instructions (so the ring's wait counts are exact).
-// row0 < 0 (invalid page) loads key row 0 instead: finite data, and its keys score -inf.
-__device__ __forceinline__ void scan_issue_tile(lds8* ring, int slot, const uint8_t* __restrict__ kbase,
-                                                const float* __restrict__ k_scale, int row0, int lane) {
-  asm volatile("" : "+v"(lane));
-  row0 = row0 < 0 ? 0 : row0;
-  const uint8_t* kb = kbase + (int64_t)row0 * kDi;
-  const int k = lane >> 3, gp = lane & 7;
-  const uint32_t kdst = (uint32_t)(uintptr_t)(ring + slot * kRingTileBytes);
-  const uint32_t sdst = (uint32_t)(uintptr_t)(ring + kRing * kRingTileBytes + slot * kRingScaleBytes);
-  const uint8_t* src0 = kb + k * kDi + 16 * (gp ^ (k & 6));
-  const uint8_t* src1 = kb + (8 + k) * kDi + 16 * (gp ^ ((k & 6) | 1));
-  // without a scale array the scale slot loads key bytes and is never read
-  const void* ssrc = k_scale ? (const void*)(k_scale + row0 + (lane & 15)) : (const void*)(kb + 4 * (lane & 15));
+// Two wave-wide 16-byte-per-lane loads of one 16-key slot (src = first key of the sub-tile);
+// with_scale adds the 4-byte-per-lane load of a page's 64 scales (ssrc = first scale). Exactly
+// 2 (+1) vector-memory instructions, so the ring's wait counts are exact.
+template <bool with_scale>
+__device__ __forceinline__ void scan_dma(uint32_t kdst, uint32_t sdst, uint64_t src, uint64_t ssrc,
+                                         int voff0, int voff1, int soff) {
   uint32_t sv;
-  asm volatile(
-      "s_mov_b32 %[sv], m0\n\t"
-      "s_mov_b32 m0, %[d0]\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %[a0], off\n\t"
-      "s_mov_b32 m0, %[d1]\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %[a1], off\n\t"
-      "s_mov_b32 m0, %[d2]\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %[a2], off\n\t"
-      "s_mov_b32 m0, %[sv]"
-      : [sv] "=&s"(sv)
-      : [d0] "s"(__builtin_amdgcn_readfirstlane(kdst)), [d1] "s"(__builtin_amdgcn_readfirstlane(kdst + 1024)),
-        [d2] "s"(__builtin_amdgcn_readfirstlane(sdst)), [a0] "v"(src0), [a1] "v"(src1), [a2] "v"(ssrc)
-      : "memory");
-}
-
-// Wait until at most 3*d vector-memory instructions of this wave are outstanding (d < kRing - 1).
-__device__ __forceinline__ void scan_wait_tiles(int d) {
-  switch (d) {
-#define W(D) case D: __builtin_amdgcn_s_waitcnt(0x0F70 | ((3 * (D)) & 15) | (((3 * (D)) >> 4) << 14)); break;
-    W(1) W(2) W(3) W(4) W(5) W(6)
-#undef W
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  if (with_scale) {
+    asm volatile(
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_mov_b32 m0, %[d0]\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %[o0], %[src]\n\t"
+        "s_mov_b32 m0, %[d1]\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %[o1], %[src]\n\t"
+        "s_mov_b32 m0, %[d2]\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %[o2], %[ssrc]\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(sv)
+        : [d0] "s"(kdst), [d1] "s"(kdst + 1024), [d2] "s"(sdst), [src] "s"(src), [ssrc] "s"(ssrc),
+          [o0] "v"(voff0), [o1] "v"(voff1), [o2] "v"(soff)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_mov_b32 m0, %[d0]\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %[o0], %[src]\n\t"
+        "s_mov_b32 m0, %[d1]\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %[o1], %[src]\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(sv)
+        : [d0] "s"(kdst), [d1] "s"(kdst + 1024), [src] "s"(src), [o0] "v"(voff0), [o1] "v"(voff1)
+        : "memory");
   }
 }
 
-// Sum over the four 16-lane groups (lanes m, m+16, m+32, m+48), without an LDS round trip.
-__device__ __forceinline__ float sum_lane_groups(float v, int lane) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v += __uint_as_float(lane < 32 ? a[1] : a[0]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v += __uint_as_float(((lane >> 4) & 1) == 0 ? b[1] : b[0]);
-  return v;
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Reduce four per-lane values v[t] (sub-tile t of a page, this lane's 16 heads) over the four
+// 16-lane groups: lane l ends with the 64-head total of sub-tile l/16 at key l%16 = key l of the page.
+__device__ __forceinline__ float reduce_page(float v0, float v1, float v2, float v3) {
+  // halves: lanes < 32 keep sub-tiles 0 and 1, lanes >= 32 keep 2 and 3
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v2), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v1), __float_as_uint(v3), false, false);
+  const float u02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float u13 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  // neighbouring 16-lane groups: even groups keep sub-tile 0 / 2, odd groups 1 / 3
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(u02), __float_as_uint(u13), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 // ReLU on the bit pattern: negative floats (sign bit set) are negative integers, so the integer
@@ -239,117 +252,199 @@ __device__ __forceinline__ float relu_bits(float x) {
   return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
 }
 
+// Vector-memory instructions complete in issue order, so waiting for a slot means allowing only the
+// instructions issued after its loads to be outstanding. Per page the wave issues 2 loads per
+// sub-tile, 1 scale load and NQ score stores; the refill of a page happens two iterations before it
+// is computed. For sub-tile t = 1..3 of the current page the later instructions are the page's
+// remaining sub-tiles, the stores of the two previous iterations, the next page and the refills
+// already issued for the page after it; t = 4 stands for sub-tile 0 of the next page, waited for
+// before this iteration's stores. kTail: 0 = refills run two pages ahead, 1 = the next page is the
+// last one, 2 = this is the last page.
+template <int NQ, int kTail>
+constexpr int scan_wait_count(int t) {
+  if (t == 4) return kTail == 0 ? 16 + NQ : 7 + NQ;
+  return kTail == 0 ? 16 + 2 * NQ : kTail == 1 ? 15 - 2 * t + 2 * NQ : 6 - 2 * t + 2 * NQ;
+}
+
+struct ScanCtx {
+  lds8* ring;            // this wave's ring
+  uint32_t ring_addr;    // its LDS address
+  uint64_t kbase;        // key rows
+  uint64_t sbase;        // per-token scales (key rows when there are none: loaded, never read)
+  int vpage;             // physical page of this wave's page `lane`, or -1
+  int voff0, voff1, soff;
+  int rd0, rd1;          // this lane's LDS read offsets within a slot
+};
+
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// refill sub-tile t of page p (into the slot its page parity and t select)
+template <int t>
+__device__ __forceinline__ void scan_refill(const ScanCtx& c, int p, bool has_scale) {
+  int pid = __builtin_amdgcn_readlane(c.vpage, p);
+  pid = pid < 0 ? 0 : pid;  // a missing page loads page 0: finite bytes whose scores are -inf
+  const uint32_t kdst = c.ring_addr + ((p & 1) * kSubTiles + t) * kRingTileBytes;
+  const uint64_t src = c.kbase + (uint64_t)(uint32_t)pid * (kScanPage * kDi) + t * kRingTileBytes;
+  if (t == 0) {
+    const uint32_t sdst = c.ring_addr + kRing * kRingTileBytes + (p & (kScaleSlots - 1)) * kScaleSlotBytes;
+    const uint64_t ssrc = has_scale ? c.sbase + (uint64_t)(uint32_t)pid * (4 * kScanPage) : c.kbase;
+    scan_dma<true>(__builtin_amdgcn_readfirstlane(kdst), __builtin_amdgcn_readfirstlane(sdst), uniform_u64(src),
+                   uniform_u64(ssrc), c.voff0, c.voff1, c.soff);
+  } else {
+    scan_dma<false>(__builtin_amdgcn_readfirstlane(kdst), 0, uniform_u64(src), 0, c.voff0, c.voff1, 0);
+  }
+}
+
+__device__ __forceinline__ void scan_read(const ScanCtx& c, int p, int t, i32x4& r0, i32x4& r1) {
+  const lds8* tk = c.ring + ((p & 1) * kSubTiles + t) * kRingTileBytes;
+  r0 = *(const __attribute__((address_space(3))) i32x4*)(tk + c.rd0);
+  r1 = *(const __attribute__((address_space(3))) i32x4*)(tk + c.rd1);
+}
+
+// Sub-tile t of page p: its bytes are in raw0/raw1 (read during the previous sub-tile). Leaves
+// v[qi] = this lane's 16-head sum for its key and every query row, and the next sub-tile's bytes
+// in raw0/raw1.
+template <int NQ, int kTail, int t>
+__device__ __forceinline__ void scan_subtile(const ScanCtx& c, const QueryOps<NQ>& o, int p, bool has_scale,
+                                             i32x4& raw0, i32x4& raw1, float (&v)[NQ]) {
+  f16x8 B[4];
+  e4m3x16_to_f16(raw0, B[0], B[1]);
+  e4m3x16_to_f16(raw1, B[2], B[3]);
+  if (kTail == 0) {
+    // the slot's bytes are in registers: refill it with the same sub-tile two pages ahead
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    scan_refill<t>(c, p + 2, has_scale);
+  }
+  // read the next sub-tile (of this page, or sub-tile 0 of the next page)
+  if (t + 1 < kSubTiles) {
+    wait_vm<scan_wait_count<NQ, kTail>(t + 1)>();
+    scan_read(c, p, t + 1, raw0, raw1);
+  } else if (kTail != 2) {
+    wait_vm<scan_wait_count<NQ, kTail>(4)>();
+    scan_read(c, p + 1, 0, raw0, raw1);
+  }
+  // one query row at a time, so its accumulators are free again for the next row; the four
+  // accumulation chains of a row advance together (K step outermost)
+#pragma unroll
+  for (int qi = 0; qi < NQ; ++qi) {
+    f32x4 acc[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(o.A[qi][mt][ks], B[ks],
+                                                          ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mt], 0, 0, 0);
+    float v0 = 0.f, v1 = 0.f;  // two partial sums break the FMA chain
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        v0 = fmaf(o.W[qi][mt][i], relu_bits(acc[mt][i]), v0);
+        v1 = fmaf(o.W[qi][mt][i + 1], relu_bits(acc[mt][i + 1]), v1);
+      }
+    v[qi] = v0 + v1;
+    // pin the row's epilogue here, so its accumulators die before the next MFMAs are issued
+    asm volatile("" : "+v"(v[qi]));
+  }
+  // keep sub-tiles apart in the schedule: interleaving them only raises register pressure
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One page: four sub-tiles, then the page's reduction, scale, mask and stores.
+template <int NQ, int kTail>
+__device__ __forceinline__ void scan_page(const ScanCtx& c, const QueryOps<NQ>& o, int p, int jpage, int jend,
+                                          bool has_scale, float* __restrict__ scores, int64_t ld_scores,
+                                          i32x4& raw0, i32x4& raw1, int lane) {
+  float v0[NQ], v1[NQ], v2[NQ], v3[NQ];
+  scan_subtile<NQ, kTail, 0>(c, o, p, has_scale, raw0, raw1, v0);
+  scan_subtile<NQ, kTail, 1>(c, o, p, has_scale, raw0, raw1, v1);
+  scan_subtile<NQ, kTail, 2>(c, o, p, has_scale, raw0, raw1, v2);
+  scan_subtile<NQ, kTail, 3>(c, o, p, has_scale, raw0, raw1, v3);
+  // lane l now scores key jpage + l
+  const float sc = has_scale ? *(const __attribute__((address_space(3))) float*)(
+                                   c.ring + kRing * kRingTileBytes + (p & (kScaleSlots - 1)) * kScaleSlotBytes + 4 * lane)
+                             : 1.f;
+  const bool page_ok = __builtin_amdgcn_readlane(c.vpage, p) >= 0;
+  const int j = jpage + lane;
+#pragma unroll
+  for (int qi = 0; qi < NQ; ++qi) {
+    const float tot = reduce_page(v0[qi], v1[qi], v2[qi], v3[qi]);
+    // exactly one store instruction per query row per page (lane 0 always has j < jend), so the
+    // wait counts stay exact; positions past the row's q_pos get -inf
+    if (j < jend) scores[o.row[qi] * ld_scores + j] = (j <= o.tpos[qi] && page_ok) ? tot * sc : -INFINITY;
+  }
+}
+
 template <int NQ>
-__global__ void __launch_bounds__(256) indexer_scan_kernel(
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) indexer_scan_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ w, PagedCache kc,
     const float* __restrict__ k_scale, const int32_t* __restrict__ q_pos, int keys_per_wave,
     int max_ctx, float* __restrict__ scores, int64_t ld_scores) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kScanLdsBytes];
   const int seq = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  QueryOps<NQ> o;
-  load_query_ops<NQ>(o, q, w, q_pos, seq * NQ, NQ, lane);
   int tmax = -1;
 #pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) tmax = max(tmax, o.tpos[qi]);
-  // pages of kScanPage keys; a wave's range starts on a page and spans at most 64 pages
+  for (int qi = 0; qi < NQ; ++qi) tmax = max(tmax, q_pos[seq * NQ + qi]);
+  // a wave's range starts on a page and spans at most 64 pages
   const int jbeg = (blockIdx.x * kScanWaves + wave) * keys_per_wave;
   const int jend = min(min(jbeg + keys_per_wave, tmax + 1), max_ctx);  // never past ld_scores
   if (jbeg >= jend) return;
-  const int ntiles = (jend - jbeg + kTileKeys - 1) / kTileKeys;
-  // the physical ids of the range's pages, one per lane, so the tile loop reads no page table
-  // from memory (such a load's wait would drain the ring)
-  int vpage = -1;
+  const int np = (jend - jbeg + kScanPage - 1) / kScanPage;
+  ScanCtx c;
+  // the physical ids of the range's pages, one per lane, so the loop reads no page table from
+  // memory (such a load's wait would drain the ring)
+  c.vpage = -1;
   {
-    const int p = jbeg / kScanPage + lane;
-    if (lane * kScanPage < jend - jbeg && p < kc.ld_pt) vpage = kc.page_table[(int64_t)seq * kc.ld_pt + p];
-    if (vpage >= kc.num_pages) vpage = -1;
+    const int pg = jbeg / kScanPage + lane;
+    if (lane < np && pg < kc.ld_pt) c.vpage = kc.page_table[(int64_t)seq * kc.ld_pt + pg];
+    if (c.vpage >= kc.num_pages) c.vpage = -1;
   }
-  auto tile_row0 = [&](int it) -> int {  // physical row of the tile's first key, or -1
-    const int pid = __builtin_amdgcn_readlane(vpage, (kTileKeys * it) / kScanPage);
-    return pid < 0 ? -1 : pid * kScanPage + (kTileKeys * it) % kScanPage;
-  };
-  // the query operands and page ids are complete before the ring starts, so no compiler wait
-  // for them sits among the ring's loads (it would drain them)
+  QueryOps<NQ> o;
+  load_query_ops<NQ>(o, q, w, q_pos, seq * NQ, NQ, lane);
+  c.ring = (lds8*)smem + wave * kWaveRingBytes;
+  c.ring_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)c.ring);
+  c.kbase = uniform_u64((uint64_t)(uintptr_t)kc.base);
+  const bool has_scale = k_scale != nullptr;
+  c.sbase = uniform_u64((uint64_t)(uintptr_t)(has_scale ? (const void*)k_scale : kc.base));
+  {
+    const int k = lane >> 3, gp = lane & 7;
+    c.voff0 = k * kDi + 16 * (gp ^ (k & 6));
+    c.voff1 = (8 + k) * kDi + 16 * (gp ^ ((k & 6) | 1));
+    c.soff = 4 * lane;
+    const int m = lane & 15, g = lane >> 4;
+    const int kb = m >> 3, kk = m & 7, x = (kk & 6) | kb;
+    c.rd0 = kb * 1024 + 16 * (8 * kk + ((2 * g) ^ x));
+    c.rd1 = kb * 1024 + 16 * (8 * kk + ((2 * g + 1) ^ x));
+  }
+  // the first two pages, then drain everything (query operands included) before the loop
+  scan_refill<0>(c, 0, has_scale); scan_refill<1>(c, 0, has_scale);
+  scan_refill<2>(c, 0, has_scale); scan_refill<3>(c, 0, has_scale);
+  if (np > 1) {
+    scan_refill<0>(c, 1, has_scale); scan_refill<1>(c, 1, has_scale);
+    scan_refill<2>(c, 1, has_scale); scan_refill<3>(c, 1, has_scale);
+  }
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) asm volatile("" ::"v"(o.A[qi][mt][ks]));
-  asm volatile("" ::"v"(vpage));
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  lds8* ring = (lds8*)smem + wave * kWaveRingBytes;
-  const uint8_t* kbase = (const uint8_t*)kc.base;
-  const int m = lane & 15, g = lane >> 4;
-  // this lane's key m within the tile: block b = m/8, key k = m%8; chunks 2g and 2g+1
-  const int kb = m >> 3, kk = m & 7, x = (kk & 6) | kb;
-  const int rd0 = kb * 1024 + 16 * (8 * kk + ((2 * g) ^ x));
-  const int rd1 = kb * 1024 + 16 * (8 * kk + ((2 * g + 1) ^ x));
-#pragma unroll
-  for (int p = 0; p < kRing - 1; ++p)
-    if (p < ntiles) scan_issue_tile(ring, p, kbase, k_scale, tile_row0(p), lane);
-
-  // Wait for tile `it`'s three loads. Vector-memory instructions complete in issue order, so it
-  // is enough that at most the instructions issued after them are outstanding: in steady state
-  // the loads of the kRing - 2 later tiles and the NQ score stores of each of the last kRing - 2
-  // iterations (a tile is waited for one iteration before it is computed). Near the ends of the
-  // range the count ignores the stores (a lower count only waits longer).
-  auto wait_tile = [&](int it) {
-    const int later_tiles = min(kRing - 2, ntiles - 1 - it);
-    if (it >= kRing - 1 && later_tiles == kRing - 2) {
-      constexpr int n = 3 * (kRing - 2) + NQ * (kRing - 2);
-      static_assert(n < 64, "vmcnt range");
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
-    } else {
-      scan_wait_tiles(later_tiles);
-    }
-  };
-  // the raw key bytes and scale of the tile computed next, read from LDS one iteration ahead
-  auto read_tile = [&](int it, i32x4& r0, i32x4& r1, float& sc) {
-    const int slot = it % kRing;
-    const lds8* tk = ring + slot * kRingTileBytes;
-    r0 = *(const __attribute__((address_space(3))) i32x4*)(tk + rd0);
-    r1 = *(const __attribute__((address_space(3))) i32x4*)(tk + rd1);
-    sc = k_scale ? *(const __attribute__((address_space(3))) float*)(ring + kRing * kRingTileBytes + slot * kRingScaleBytes + 4 * m) : 1.f;
-  };
+  wait_vm<0>();
   i32x4 raw0, raw1;
-  float scale;
-  wait_tile(0);
-  read_tile(0, raw0, raw1, scale);
-  for (int it = 0; it < ntiles; ++it) {
-    if (it + kRing - 1 < ntiles)
-      scan_issue_tile(ring, (it + kRing - 1) % kRing, kbase, k_scale, tile_row0(it + kRing - 1), lane);
-    f16x8 B[4];
-    e4m3x16_to_f16(raw0, B[0], B[1]);
-    e4m3x16_to_f16(raw1, B[2], B[3]);
-    const float sc = scale;
-    const int j = jbeg + kTileKeys * it + m;
-    const bool page_ok = tile_row0(it) >= 0;
-    if (it + 1 < ntiles) {
-      wait_tile(it + 1);
-      read_tile(it + 1, raw0, raw1, scale);
-    }
-#pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) {
-      float v = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(o.A[qi][mt][ks], B[ks], acc, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v = fmaf(o.W[qi][mt][i], relu_bits(acc[i]), v);
-      }
-      v = sum_lane_groups(v, lane);
-      // exactly one store instruction per query per tile (lane 0 always has j < jend), so the
-      // wait counts above stay exact; positions past q_pos get -inf
-      if (lane < 16 && j < jend) {
-        const float s = (j <= o.tpos[qi] && page_ok) ? v * sc : -INFINITY;
-        scores[o.row[qi] * ld_scores + j] = s;
-      }
-    }
+  scan_read(c, 0, 0, raw0, raw1);
+  int p = 0;
+  for (; p + 2 < np; ++p)
+    scan_page<NQ, 0>(c, o, p, jbeg + kScanPage * p, jend, has_scale, scores, ld_scores, raw0, raw1, lane);
+  if (p + 1 < np) {
+    scan_page<NQ, 1>(c, o, p, jbeg + kScanPage * p, jend, has_scale, scores, ld_scores, raw0, raw1, lane);
+    ++p;
   }
+  scan_page<NQ, 2>(c, o, p, jbeg + kScanPage * p, jend, has_scale, scores, ld_scores, raw0, raw1, lane);
 }
 
 // Prefill tiles: each wave owns 2 consecutive rows of one sequence and scans their causal
