@@ -69,6 +69,7 @@ enum {
   DSA_PATH_INDEXER_PREFILL_MFMA = 3,  /* Hi=64, Di=128, E4M3, q_per_seq > 2: query x key tiles */
   DSA_PATH_TOPK_COPY = 10,            /* every row no longer than k: all positions kept */
   DSA_PATH_TOPK_RADIX = 11,           /* radix select, one workgroup per row */
+  DSA_PATH_TOPK_RADIX_REG = 12,       /* as 11 for max_ctx <= 16384, the row held in registers */
   DSA_PATH_MLA_GENERIC = 20,          /* any shape: one wave per (row, head), VALU */
   DSA_PATH_MLA_MFMA = 21,             /* H=128, Dqk=576, Dv=512: bf16 MFMA, one pass */
   DSA_PATH_MLA_MFMA_SPLIT = 22        /* as 21, key set split over workgroups + combine */

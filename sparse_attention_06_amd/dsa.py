@@ -18,7 +18,7 @@ DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP
 DSA_E4M3, DSA_F32 = 0, 1
 PATHS = {
     0: "none", 1: "indexer_generic", 2: "indexer_scan_mfma", 3: "indexer_prefill_mfma",
-    10: "topk_copy", 11: "topk_radix", 20: "mla_generic", 21: "mla_mfma", 22: "mla_mfma_split",
+    10: "topk_copy", 11: "topk_radix", 12: "topk_radix_reg", 20: "mla_generic", 21: "mla_mfma", 22: "mla_mfma_split",
 }
 
 EXPORTS = [

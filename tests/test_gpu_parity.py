@@ -90,7 +90,7 @@ def _topk_case(scores, q_pos, k):
     return g, r
 
 
-@pytest.mark.parametrize("n,k", [(5000, 2048), (16384, 2048), (40000, 2048), (300, 32), (100, 1), (2048, 2048)])
+@pytest.mark.parametrize("n,k", [(5000, 2048), (16384, 2048), (40000, 2048), (300, 32), (100, 1), (2048, 2048), (12000, 5000)])
 def test_topk_matches_oracle_exactly(oracle_lib, n, k):
     _say(f"case: topk n={n} k={k}")
     rng = np.random.default_rng(n + k)
@@ -101,16 +101,37 @@ def test_topk_matches_oracle_exactly(oracle_lib, n, k):
     np.testing.assert_array_equal(g, r)
 
 
-def test_topk_ties_and_signed_zeros(oracle_lib):
-    _say("case: topk ties")
+@pytest.mark.parametrize("n", [20000, 16000])
+def test_topk_ties_and_signed_zeros(oracle_lib, n):
+    _say(f"case: topk ties n={n}")
     rng = np.random.default_rng(5)
-    n, k = 20000, 2048
+    k = 2048
     vals = np.array([-1.0, -0.0, 0.0, 0.25, 0.5, 1.0], np.float32)
     sc = rng.choice(vals, size=(4, n)).astype(np.float32)
     sc[1] = 0.0
     sc[1, ::3] = -0.0
     q_pos = np.array([n - 1, n - 1, 5000, 2047], np.int32)
     g, r = _topk_case(sc, q_pos, k)
+    np.testing.assert_array_equal(g, r)
+
+
+def test_topk_register_path_special_rows(oracle_lib):
+    """Rows of at most 16384 positions: the register-resident kernel, including rows whose
+    undecided keys overflow the candidate buffer (all equal), -inf entries, a threshold inside a
+    run of equal scores, and scores packed into a narrow range (long shared key prefixes)."""
+    _say("case: topk register path special rows")
+    rng = np.random.default_rng(11)
+    n, k = 16384, 2048
+    sc = rng.standard_normal((6, n)).astype(np.float32)
+    sc[0] = 3.0                                   # all equal: every key ties with the threshold
+    sc[1, ::2] = -np.inf                          # half the row masked
+    sc[2, : n // 2] = 1.0                         # threshold inside a run of 8192 equal scores
+    sc[2, n // 2:] = rng.uniform(0.0, 0.5, n // 2)
+    sc[3] = (100.0 + rng.uniform(0.0, 1e-3, n)).astype(np.float32)   # narrow range
+    sc[4, 7::13] = np.inf                         # +inf above everything
+    q_pos = np.array([n - 1, n - 1, n - 1, n - 1, n - 1, 9000], np.int32)
+    g, r = _topk_case(sc, q_pos, k)
+    assert dsa.last_path() == "topk_radix_reg"
     np.testing.assert_array_equal(g, r)
 
 
