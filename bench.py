@@ -107,21 +107,79 @@ class DecodeStep:
             self.copies.append(d)
         self.stream = torch.cuda.current_stream()
 
-    def run(self, c, events=None):
-        w, dsa, d = self.w, self.dsa, self.copies[c % len(self.copies)]
+    def call_indexer(self, c, st):
+        w, d = self.w, self.copies[c % len(self.copies)]
+        self.dsa.indexer_scores(d["iq"], d["iw"], d["ik"], d["iks"], d["page_table"], d["q_pos"], w.n_seq,
+                                w.q_per_seq, w.max_ctx, scores=d["scores"], stream=st)
+
+    def call_topk(self, c, st):
+        w, d = self.w, self.copies[c % len(self.copies)]
+        self.dsa.topk(d["scores"], d["q_pos"], w.max_ctx, w.topk, idx=d["idx"], stream=st)
+
+    def call_mla(self, c, st):
+        w, d = self.w, self.copies[c % len(self.copies)]
+        self.dsa.sparse_mla_decode(d["q"], d["kv"], d["page_table"], d["q_pos"], w.n_seq, w.q_per_seq, d["idx"],
+                                   w.Dqk, w.Dv, w.v_col0, w.sm_scale, out=d["out"], ws=d["ws"], stream=st)
+
+    def run(self, c, events=None, stream=None):
+        st = stream if stream is not None else self.stream
+        calls = (self.call_indexer, self.call_topk, self.call_mla)
+        for i, fn in enumerate(calls):
+            if events:
+                events[i].record(st)
+            fn(c, st)
         if events:
-            events[0].record(self.stream)
-        dsa.indexer_scores(d["iq"], d["iw"], d["ik"], d["iks"], d["page_table"], d["q_pos"], w.n_seq, w.q_per_seq,
-                           w.max_ctx, scores=d["scores"], stream=self.stream)
-        if events:
-            events[1].record(self.stream)
-        dsa.topk(d["scores"], d["q_pos"], w.max_ctx, w.topk, idx=d["idx"], stream=self.stream)
-        if events:
-            events[2].record(self.stream)
-        dsa.sparse_mla_decode(d["q"], d["kv"], d["page_table"], d["q_pos"], w.n_seq, w.q_per_seq, d["idx"], w.Dqk,
-                              w.Dv, w.v_col0, w.sm_scale, out=d["out"], ws=d["ws"], stream=self.stream)
-        if events:
-            events[3].record(self.stream)
+            events[3].record(st)
+
+    def capture(self, fns=None):
+        """One HIP graph per input copy holding `fns` (default: the whole step, i.e. the four
+        kernel launches), so replays carry no host-side launch gaps."""
+        torch = self.torch
+        fns = fns or (self.call_indexer, self.call_topk, self.call_mla)
+        graphs = []
+        for c in range(len(self.copies)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                st = torch.cuda.current_stream()
+                for fn in fns:
+                    fn(c, st)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        return graphs
+
+
+def time_replays(torch, graphs, steps):
+    """ms per replay over `steps` replays (alternating graphs) between device-wide syncs."""
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
+
+
+def time_graph_steps(step, steps, warmup):
+    """Time `steps` whole-step graph replays (alternating input copies) between device-wide
+    synchronisations; returns (ms per step, wall seconds). The first replay of every graph is
+    checked against an eager step on the same inputs."""
+    torch = step.torch
+    for i in range(warmup):
+        step.run(i)
+    torch.cuda.synchronize()
+    eager = [(d["idx"].clone(), d["out"].clone()) for d in step.copies]
+    graphs = step.capture()
+    for c, g in enumerate(graphs):
+        g.replay()
+        torch.cuda.synchronize()
+        d = step.copies[c]
+        if not (torch.equal(d["idx"], eager[c][0]) and torch.equal(d["out"], eager[c][1])):
+            raise SystemExit("graph replay differs from the eager step")
+    return time_replays(torch, graphs, steps)
 
 
 def time_steps(step, steps, warmup):
@@ -215,16 +273,23 @@ def run_decode_bench(args):
     log(f"[bench] workload {w.name}: {w.n_seq} requests x {w.q_per_seq} rows, ctx {w.max_ctx}, "
         f"generated in {time.time() - t0:.1f} s")
     step = DecodeStep(w, copies=2)
-    wall, per = time_steps(step, args.steps, args.warmup)
-    ms = per.mean(axis=0)
+    # the step as deployed: graph replays; then an eager pass with events between the three
+    # calls for the per-call times (those include each call's launch gap)
+    ms_step, wall = time_graph_steps(step, args.steps, args.warmup)
+    ms_step = float(ms_step)
+    # per-call times: graphs holding one call each, replayed back to back
+    ms = [time_replays(torch, step.capture((fn,)), args.steps)[0]
+          for fn in (step.call_indexer, step.call_topk, step.call_mla)]
+    _, per = time_steps(step, args.steps, 1)
+    ms.append(float(per.mean(axis=0)[3]))
     ctx = w.q_pos.reshape(w.n_seq, w.q_per_seq).max(axis=1) + 1
     by = decode_step_bytes(w.n_seq, w.q_per_seq, ctx, w.topk)
     fl = decode_step_flops(w.n_seq, w.q_per_seq, ctx, w.topk)
     rows = w.rows
-    ms_step = float(ms[3])
     qps = rows / (ms_step * 1e-3)
     detail = {
-        "ms": {"indexer": float(ms[0]), "topk": float(ms[1]), "sparse_mla": float(ms[2]), "step": ms_step},
+        "ms": {"indexer": float(ms[0]), "topk": float(ms[1]), "sparse_mla": float(ms[2]), "step": ms_step,
+               "step_eager_with_events": float(ms[3])},
         "wall_ms_per_step": wall / args.steps * 1e3,
         "algorithmic_GBps": {"indexer": by["indexer"] / ms[0] / 1e6, "topk": by["topk"] / ms[1] / 1e6,
                              "sparse_mla": by["mla"] / ms[2] / 1e6, "step": by["step"] / ms_step / 1e6},
@@ -238,7 +303,8 @@ def run_decode_bench(args):
     mla_bytes = by["mla"]
     achieved = mla_bytes / (ms[2] * 1e-3) / 1e9
     traffic = measured_traffic("sparse_mla_decode")
-    roof = {"bound": "hbm", "kernel": "mla_mfma_kernel (dsa_sparse_mla_decode)", "achieved": round(achieved, 1),
+    roof = {"bound": "hbm", "kernel": "dsa_sparse_mla_decode (mla_mfma_kernel + mla_combine_kernel)",
+            "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic, "algorithmic_bytes_per_launch": mla_bytes}
     cpu = None
