@@ -118,8 +118,10 @@ class DecodeStep:
 
     def call_mla(self, c, st):
         w, d = self.w, self.copies[c % len(self.copies)]
-        self.dsa.sparse_mla_decode(d["q"], d["kv"], d["page_table"], d["q_pos"], w.n_seq, w.q_per_seq, d["idx"],
-                                   w.Dqk, w.Dv, w.v_col0, w.sm_scale, out=d["out"], ws=d["ws"], stream=st)
+        # decode / MTP rows (at most 2 per request) and prefill blocks have their own entry points
+        fn = self.dsa.sparse_mla_decode if w.q_per_seq <= 2 else self.dsa.sparse_mla_prefill
+        fn(d["q"], d["kv"], d["page_table"], d["q_pos"], w.n_seq, w.q_per_seq, d["idx"], w.Dqk, w.Dv, w.v_col0,
+           w.sm_scale, out=d["out"], ws=d["ws"], stream=st)
 
     def run(self, c, events=None, stream=None):
         st = stream if stream is not None else self.stream
@@ -326,6 +328,54 @@ def run_decode_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def run_prefill_bench(args):
+    """One prefill block (indexer prefill contraction + top-k + sparse MLA prefill) timed like the
+    decode step: graph replays of the whole block, and of each call on its own."""
+    import torch
+
+    import workloads
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    t0 = time.time()
+    w = workloads.MAKERS[args.workload]()
+    log(f"[bench] workload {w.name}: {w.rows} query rows over {w.max_ctx} positions, generated in "
+        f"{time.time() - t0:.1f} s")
+    step = DecodeStep(w, copies=1)
+    ms_step, wall = time_graph_steps(step, args.steps, args.warmup)
+    ms = [time_replays(torch, step.capture((fn,)), args.steps)[0]
+          for fn in (step.call_indexer, step.call_topk, step.call_mla)]
+    ctx = w.q_pos.astype(np.int64) + 1
+    sel = np.minimum(ctx, w.topk)
+    flops = {"indexer": float(np.sum(ctx)) * 2 * w.Hi * w.Di,
+             "mla": float(np.sum(sel)) * 2 * w.H * (w.Dqk + w.Dv)}
+    tflops = {"indexer_f16": flops["indexer"] / ms[0] / 1e9, "sparse_mla_bf16": flops["mla"] / ms[2] / 1e9}
+    dominant = "indexer" if ms[0] >= ms[2] else "mla"
+    achieved = tflops["indexer_f16"] if dominant == "indexer" else tflops["sparse_mla_bf16"]
+    roof = {"bound": "mfma",
+            "kernel": "indexer_prefill_kernel (dsa_indexer_scores)" if dominant == "indexer"
+            else "mla_mfma_kernel (dsa_sparse_mla_prefill)",
+            "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "algorithmic_flops_per_launch": flops[dominant]}
+    line = {
+        "metric": "DSA prefill queries/s (indexer + top-2048 + sparse MLA)", "value": round(w.rows / (ms_step * 1e-3), 1),
+        "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(float(ms_step), 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "query_rows": w.rows, "context": int(w.max_ctx), "topk": w.topk,
+                   "indexer": "64 heads x 128 dims, FP8 E4M3", "mla": "128 heads, 576-wide bf16 latent rows, v 512",
+                   "page_size": w.page_size},
+        "roofline": roof,
+        "cpu_baseline": None,
+        "detail": {"ms": {"indexer": ms[0], "topk": ms[1], "sparse_mla": ms[2], "step": float(ms_step)},
+                   "wall_ms_per_step": wall / args.steps * 1e3, "mfma_TFLOPs": tflops,
+                   "TFLOP": {k: v / 1e12 for k, v in flops.items()},
+                   "topk_rows_per_s": w.rows / (ms[1] * 1e-3)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def run_crossover(args):
     """Dense causal fallback vs sparse prefill (indexer + top-k + sparse attention) for one
     sequence of T queries over a T-token prefix."""
@@ -398,7 +448,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode_mtp_b64_16k",
-                    choices=["decode_mtp_b64_16k", "decode_b16_4k", "decode_b4_128k"])
+                    choices=["decode_mtp_b64_16k", "decode_b16_4k", "decode_b4_128k", "prefill_8k",
+                             "prefill_chunk_128k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--crossover", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -412,6 +463,8 @@ def main():
         run_copy_calibration(args)
     elif args.crossover:
         run_crossover(args)
+    elif args.workload.startswith("prefill"):
+        run_prefill_bench(args)
     else:
         run_decode_bench(args)
 
