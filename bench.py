@@ -104,6 +104,8 @@ class DecodeStep:
             d["out"] = torch.empty(w.rows, w.H, w.Dv, dtype=torch.bfloat16, device="cuda")
             need = dsa.sparse_mla_workspace_size(w.rows, w.H, w.Dv, w.topk)
             d["ws"] = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda") if need else None
+            tneed = dsa.topk_workspace_size(w.rows, w.max_ctx, w.topk)
+            d["tws"] = torch.empty(tneed, dtype=torch.uint8, device="cuda") if tneed else None
             self.copies.append(d)
         self.stream = torch.cuda.current_stream()
 
@@ -114,7 +116,7 @@ class DecodeStep:
 
     def call_topk(self, c, st):
         w, d = self.w, self.copies[c % len(self.copies)]
-        self.dsa.topk(d["scores"], d["q_pos"], w.max_ctx, w.topk, idx=d["idx"], stream=st)
+        self.dsa.topk(d["scores"], d["q_pos"], w.max_ctx, w.topk, idx=d["idx"], ws=d["tws"], stream=st)
 
     def call_mla(self, c, st):
         w, d = self.w, self.copies[c % len(self.copies)]

@@ -70,6 +70,7 @@ enum {
   DSA_PATH_TOPK_COPY = 10,            /* every row no longer than k: all positions kept */
   DSA_PATH_TOPK_RADIX = 11,           /* radix select, one workgroup per row */
   DSA_PATH_TOPK_RADIX_REG = 12,       /* as 11 for max_ctx <= 16384, the row held in registers */
+  DSA_PATH_TOPK_RADIX_STAGED = 13,    /* longer rows: per-chunk candidates, then a merge (workspace) */
   DSA_PATH_MLA_GENERIC = 20,          /* any shape: one wave per (row, head), VALU */
   DSA_PATH_MLA_MFMA = 21,             /* H=128, Dqk=576, Dv=512: bf16 MFMA, one pass */
   DSA_PATH_MLA_MFMA_SPLIT = 22        /* as 21, key set split over workgroups + combine */
@@ -111,8 +112,11 @@ dsa_status_t dsa_indexer_scores(const void* q, const float* w, const void* k_cac
  *          ASCENDING order, then -1 up to slot k-1.
  * Ranking: larger score first; equal scores (by value: -0 == +0) rank the smaller position
  * first, so the result is unique. NaN scores are not supported (their rank is unspecified).
- * Needs no workspace (ws may be NULL; dsa_topk_workspace_size returns 0); the arguments are
- * kept so that future variants can use one without an ABI change.
+ * Workspace: rows longer than 16384 positions (max_ctx > 16384, k <= 4096, and
+ * ceil(max_ctx / 16384) * k <= 16384) are selected in two stages (per-chunk candidates, then a
+ * merge), which needs dsa_topk_workspace_size(rows, max_ctx, k) bytes at ws (device memory owned
+ * by the caller, contents not preserved; 0 for shorter rows). With ws NULL or smaller, the
+ * same result comes from a single-workgroup-per-row kernel (reported as DSA_PATH_TOPK_RADIX).
  * ------------------------------------------------------------------------------------------- */
 size_t dsa_topk_workspace_size(int rows, int max_ctx, int k);
 dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int rows,

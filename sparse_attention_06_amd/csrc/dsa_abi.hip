@@ -153,14 +153,13 @@ dsa_status_t dsa_indexer_scores(const void* q, const float* w, const void* k_cac
 }
 
 size_t dsa_topk_workspace_size(int rows, int max_ctx, int k) {
-  (void)rows; (void)max_ctx; (void)k;
-  return 0;
+  if (rows <= 0 || max_ctx < 1 || k < 1) return 0;
+  return dsa::topk_staged_ws_bytes(rows, max_ctx, k);
 }
 
 dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int rows,
                       int max_ctx, int k, int32_t* idx, int64_t ld_idx, void* ws, size_t ws_bytes,
                       void* stream) {
-  (void)ws; (void)ws_bytes;
   REQUIRE(rows >= 0 && k >= 1 && max_ctx >= 1, "need rows >= 0, k >= 1, max_ctx >= 1");
   if (rows == 0) return ok(DSA_PATH_NONE);  // nothing to do; pointers may be NULL
   REQUIRE(scores && q_pos && idx, "scores, q_pos and idx must be non-NULL");
@@ -168,8 +167,8 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_p
   REQUIRE(ld_idx >= k, "ld_idx (%lld) must be >= k (%d)", (long long)ld_idx, k);
   if (rows == 0) return ok(DSA_PATH_NONE);
   int path = DSA_PATH_NONE;
-  dsa_status_t s = hip_status(dsa::launch_topk(scores, ld_scores, q_pos, rows, max_ctx, k, idx, ld_idx,
-                                               (hipStream_t)stream, &path), "topk launch");
+  dsa_status_t s = hip_status(dsa::launch_topk(scores, ld_scores, q_pos, rows, max_ctx, k, idx, ld_idx, ws,
+                                               ws_bytes, (hipStream_t)stream, &path), "topk launch");
   return s == DSA_OK ? ok(path) : s;
 }
 

@@ -89,8 +89,9 @@ hipError_t launch_indexer_prefill(const uint8_t* q, const float* w, PagedCache k
                                   hipStream_t stream);
 
 hipError_t launch_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int rows,
-                       int max_ctx, int k, int32_t* idx, int64_t ld_idx, hipStream_t stream,
-                       int* path);
+                       int max_ctx, int k, int32_t* idx, int64_t ld_idx, void* ws, size_t ws_bytes,
+                       hipStream_t stream, int* path);
+size_t topk_staged_ws_bytes(int rows, int max_ctx, int k);
 
 struct AttnArgs {
   const uint16_t* q;

@@ -169,16 +169,17 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
-// hist[digit] += 1 for each active key. A lane adds all its keys that share the digit of its
-// first active key with one atomic (the leading digits of real scores repeat a lot, and one
-// atomic per key would serialise on the hot address); its other keys are added one by one.
-__device__ __forceinline__ void hist_add_keys(uint32_t* hist, const uint32_t (&key)[kRegE], int cnt,
+// hist[digit] += 1 for each active key (valid: bit e of vmask). A lane adds all its keys that
+// share the digit of its first active key with one atomic (the leading digits of real scores
+// repeat a lot, and one atomic per key would serialise on the hot address); its other keys are
+// added one by one.
+__device__ __forceinline__ void hist_add_keys(uint32_t* hist, const uint32_t (&key)[kRegE], uint32_t vmask,
                                               uint32_t pmask, uint32_t prefix, int pass) {
   uint32_t d0 = 0, run = 0;
   bool have = false;
 #pragma unroll
   for (int e = 0; e < kRegE; ++e) {
-    const bool act = e < cnt && (key[e] & pmask) == prefix;
+    const bool act = ((vmask >> e) & 1u) && (key[e] & pmask) == prefix;
     const uint32_t d = digit_of(key[e], pass);
     if (act && !have) { d0 = d; have = true; }
     run += (act && d == d0) ? 1u : 0u;
@@ -186,7 +187,7 @@ __device__ __forceinline__ void hist_add_keys(uint32_t* hist, const uint32_t (&k
   if (have) atomicAdd(&hist[d0], run);
 #pragma unroll
   for (int e = 0; e < kRegE; ++e) {
-    const bool act = e < cnt && (key[e] & pmask) == prefix;
+    const bool act = ((vmask >> e) & 1u) && (key[e] & pmask) == prefix;
     const uint32_t d = digit_of(key[e], pass);
     if (act && d != d0) atomicAdd(&hist[d], 1u);
   }
@@ -221,64 +222,39 @@ __device__ __forceinline__ void pick_digit_wave(const uint32_t* hist, uint32_t r
   }
 }
 
-__global__ void __launch_bounds__(kTopkThreads) topk_reg_kernel(const float* __restrict__ scores,
-                                                                int64_t ld_scores,
-                                                                const int32_t* __restrict__ q_pos,
-                                                                int max_ctx, int k,
-                                                                int32_t* __restrict__ idx, int64_t ld_idx) {
-  __shared__ __attribute__((aligned(16))) uint32_t hist[3][kRegBins];  // one histogram per pass
-  __shared__ uint32_t cand_key[kCandCap], cand_pos[kCandCap];
-  __shared__ uint32_t wtot[kTopkWaves][2];
-  __shared__ uint32_t pub[3][3], ncand;
+struct TopkLds {
+  uint32_t hist[3][kRegBins];  // one histogram per pass
+  uint32_t cand_key[kCandCap], cand_pos[kCandCap];
+  uint32_t wtot[kTopkWaves][2];
+  uint32_t pub[3][3];
+  uint32_t ncand;
+};
 
-  const int r = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // this thread's positions: p0 .. p0 + 15. The row is read before q_pos is known (every position
-  // below max_ctx lies inside the row), so the two memory latencies overlap.
-  const float* row = scores + (int64_t)r * ld_scores;
-  const int p0 = kRegE * tid;
-  float f[kRegE];
-  if (p0 + kRegE <= max_ctx && ((uintptr_t)(row + p0) & 15) == 0) {
-#pragma unroll
-    for (int v = 0; v < kRegE / 4; ++v) {
-      const float4 x = *(const float4*)(row + p0 + 4 * v);
-      f[4 * v] = x.x; f[4 * v + 1] = x.y; f[4 * v + 2] = x.z; f[4 * v + 3] = x.w;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < kRegE; ++e) f[e] = p0 + e < max_ctx ? row[p0 + e] : 0.f;
-  }
-  int n = q_pos[r] + 1;
-  n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
-  int32_t* out = idx + (int64_t)r * ld_idx;
-  if (n <= k) {
-    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
-    return;
-  }
-  const int cnt = n - p0 < 0 ? 0 : (n - p0 > kRegE ? kRegE : n - p0);
-  uint32_t key[kRegE];
-#pragma unroll
-  for (int e = 0; e < kRegE; ++e) key[e] = e < cnt ? order_key(f[e]) : 0u;
-  for (int i = tid; i < 3 * kRegBins; i += kTopkThreads) (&hist[0][0])[i] = 0;
-  if (tid == 0) ncand = 0;
+// The key of the k-th largest valid key (tau) and how many keys equal to tau are taken, over the
+// keys the block's threads hold (16 each, valid where vmask has the bit). Needs more than k valid
+// keys. Three passes over 11-, 11- and 10-bit digits; once the keys still undecided fit in LDS
+// they are compacted there and the remaining passes run over them alone.
+__device__ __forceinline__ void reg_select(const uint32_t (&key)[kRegE], uint32_t vmask, uint32_t k, TopkLds& sh, int tid,
+                           int wave, int lane, uint32_t& tau_out, uint32_t& remaining_out) {
+  for (int i = tid; i < 3 * kRegBins; i += kTopkThreads) (&sh.hist[0][0])[i] = 0;
+  if (tid == 0) sh.ncand = 0;
   __syncthreads();
-
-  uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)k;
+  uint32_t prefix = 0, pmask = 0, remaining = k;
   bool compacted = false;
   uint32_t nc = 0;
   for (int pass = 0; pass < 3; ++pass) {
     if (!compacted) {
-      hist_add_keys(hist[pass], key, cnt, pmask, prefix, pass);
+      hist_add_keys(sh.hist[pass], key, vmask, pmask, prefix, pass);
     } else {
       for (int i = tid; i < (int)nc; i += kTopkThreads) {
-        const uint32_t kk = cand_key[i];
-        if ((kk & pmask) == prefix) atomicAdd(&hist[pass][digit_of(kk, pass)], 1u);
+        const uint32_t kk = sh.cand_key[i];
+        if ((kk & pmask) == prefix) atomicAdd(&sh.hist[pass][digit_of(kk, pass)], 1u);
       }
     }
     __syncthreads();
-    if (wave == 0) pick_digit_wave(hist[pass], remaining, pub[pass], lane);
+    if (wave == 0) pick_digit_wave(sh.hist[pass], remaining, sh.pub[pass], lane);
     __syncthreads();
-    const uint32_t digit = pub[pass][0], above = pub[pass][1], count = pub[pass][2];
+    const uint32_t digit = sh.pub[pass][0], above = sh.pub[pass][1], count = sh.pub[pass][2];
     remaining -= above;
     prefix |= digit << (pass == 0 ? 21 : pass == 1 ? 10 : 0);
     pmask = mask_through(pass);
@@ -287,61 +263,209 @@ __global__ void __launch_bounds__(kTopkThreads) topk_reg_kernel(const float* __r
       // one LDS atomic per wave for the wave's slots
       uint32_t mine = 0;
 #pragma unroll
-      for (int e = 0; e < kRegE; ++e) mine += (e < cnt && (key[e] & pmask) == prefix) ? 1u : 0u;
+      for (int e = 0; e < kRegE; ++e) mine += (((vmask >> e) & 1u) && (key[e] & pmask) == prefix) ? 1u : 0u;
       const uint32_t incl = wave_incl_scan(mine);
       const uint32_t wsum = __builtin_amdgcn_readlane(incl, 63);
       uint32_t base = 0;
-      if (lane == 0 && wsum) base = atomicAdd(&ncand, wsum);
+      if (lane == 0 && wsum) base = atomicAdd(&sh.ncand, wsum);
       uint32_t slot = __builtin_amdgcn_readfirstlane(base) + incl - mine;
 #pragma unroll
       for (int e = 0; e < kRegE; ++e) {
-        if (e < cnt && (key[e] & pmask) == prefix) {
-          cand_key[slot] = key[e];
-          cand_pos[slot] = (uint32_t)(p0 + e);
-          ++slot;
-        }
+        if (((vmask >> e) & 1u) && (key[e] & pmask) == prefix) sh.cand_key[slot++] = key[e];
       }
       __syncthreads();
-      nc = ncand;
+      nc = sh.ncand;
       compacted = true;
     }
   }
-  const uint32_t tau = prefix;
+  tau_out = prefix;
+  remaining_out = remaining;
+}
 
-  // ordered output: block-wide exclusive scan of (greater, equal) counts per thread
+// Stage the selected keys in input order: every valid key above tau and the first `remaining`
+// keys equal to tau (every valid key when take_all). Their positions (pos_of(e) for this thread's
+// key e) and, with_keys, their order keys land in sh.cand_pos / sh.cand_key at their output
+// slots; returns how many were selected.
+template <class PosOf>
+__device__ __forceinline__ uint32_t stage_selected(const uint32_t (&key)[kRegE], PosOf pos_of, uint32_t vmask, bool take_all,
+                                   uint32_t tau, uint32_t remaining, bool with_keys, TopkLds& sh, int wave,
+                                   int lane) {
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int e = 0; e < kRegE; ++e) {
-    gt += (e < cnt && key[e] > tau) ? 1u : 0u;
-    eq += (e < cnt && key[e] == tau) ? 1u : 0u;
+    const bool v = (vmask >> e) & 1u;
+    gt += (v && (take_all || key[e] > tau)) ? 1u : 0u;
+    eq += (v && !take_all && key[e] == tau) ? 1u : 0u;
   }
   const uint32_t gi = wave_incl_scan(gt), ei = wave_incl_scan(eq);
-  if (lane == 63) { wtot[wave][0] = gi; wtot[wave][1] = ei; }
+  __syncthreads();  // the selection may still read the candidate buffers and the wave totals
+  if (lane == 63) { sh.wtot[wave][0] = gi; sh.wtot[wave][1] = ei; }
   __syncthreads();
-  uint32_t gb = gi - gt, eb = ei - eq;
-  for (int w = 0; w < wave; ++w) { gb += wtot[w][0]; eb += wtot[w][1]; }
-  // stage the k positions in LDS (the candidate buffer is free now), then store them coalesced
-  uint32_t* staged = cand_pos;
+  uint32_t gb = gi - gt, eb = ei - eq, gall = 0, eall = 0;
+  for (int w = 0; w < kTopkWaves; ++w) {
+    if (w < wave) { gb += sh.wtot[w][0]; eb += sh.wtot[w][1]; }
+    gall += sh.wtot[w][0];
+    eall += sh.wtot[w][1];
+  }
   uint32_t slot = gb + min(eb, remaining), eq_rank = eb;
 #pragma unroll
   for (int e = 0; e < kRegE; ++e) {
-    if (e < cnt) {
-      bool take = key[e] > tau;
-      if (key[e] == tau) { take = eq_rank < remaining; ++eq_rank; }
-      if (take) staged[slot++] = (uint32_t)(p0 + e);
+    if ((vmask >> e) & 1u) {
+      bool take = take_all || key[e] > tau;
+      if (!take_all && key[e] == tau) { take = eq_rank < remaining; ++eq_rank; }
+      if (take) {
+        sh.cand_pos[slot] = pos_of(e);
+        if (with_keys) sh.cand_key[slot] = key[e];
+        ++slot;
+      }
     }
   }
   __syncthreads();
-  for (int i = tid; i < k; i += kTopkThreads) out[i] = (int32_t)staged[i];
+  return gall + min(eall, remaining);
+}
+
+// One selection over up to 16384 keys per block. With kSrcScores the keys are the scores of row
+// blockIdx.y at positions [16384 * blockIdx.x, ...) below the row's length; otherwise they are the
+// candidate slots of row blockIdx.y written by a previous stage (in_chunks chunks of k slots, the
+// first in_cnt of each valid, in ascending position order). With kFinal the block writes the row's
+// index list (positions ascending, -1 padded to k); otherwise this chunk's candidates (at most k
+// order keys with their positions, ascending by position) and their count.
+struct TopkStageArgs {
+  const float* scores;
+  int64_t ld_scores;
+  const int32_t* q_pos;
+  int max_ctx, k;
+  int32_t* idx;
+  int64_t ld_idx;
+  const uint32_t* in_key;
+  const int32_t* in_pos;
+  const int32_t* in_cnt;
+  int in_chunks;
+  uint32_t* out_key;
+  int32_t* out_pos;
+  int32_t* out_cnt;
+  int out_chunks;
+};
+
+template <bool kSrcScores, bool kFinal>
+__global__ void __launch_bounds__(kTopkThreads) topk_stage_kernel(TopkStageArgs a) {
+  __shared__ __attribute__((aligned(16))) TopkLds sh;
+  const int r = blockIdx.y, c = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t key[kRegE], vmask = 0;
+  if (kSrcScores) {
+    // this thread's positions: base .. base + 15. The row is read before q_pos is known (every
+    // position below max_ctx lies inside the row), so the two memory latencies overlap.
+    const float* row = a.scores + (int64_t)r * a.ld_scores;
+    const int base = kRegKeys * c + kRegE * tid;
+    float f[kRegE];
+    if (base + kRegE <= a.max_ctx && ((uintptr_t)(row + base) & 15) == 0) {
+#pragma unroll
+      for (int v = 0; v < kRegE / 4; ++v) {
+        const float4 x = *(const float4*)(row + base + 4 * v);
+        f[4 * v] = x.x; f[4 * v + 1] = x.y; f[4 * v + 2] = x.z; f[4 * v + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kRegE; ++e) f[e] = base + e < a.max_ctx ? row[base + e] : 0.f;
+    }
+    int n = a.q_pos[r] + 1;
+    n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+#pragma unroll
+    for (int e = 0; e < kRegE; ++e) {
+      const bool v = base + e < n;
+      vmask |= (v ? 1u : 0u) << e;
+      key[e] = v ? order_key(f[e]) : 0u;
+    }
+  } else {
+    // candidate slot g = 16 * tid + e of the row: chunk g / k, entry g % k
+    const int64_t rb = (int64_t)r * a.in_chunks * a.k;
+#pragma unroll
+    for (int e = 0; e < kRegE; ++e) {
+      const int g = kRegE * tid + e;
+      const int ch = g / a.k;
+      const bool v = ch < a.in_chunks && g - ch * a.k < a.in_cnt[(int64_t)r * a.in_chunks + ch];
+      vmask |= (v ? 1u : 0u) << e;
+      key[e] = v ? a.in_key[rb + g] : 0u;
+    }
+  }
+  // keys held by the block: the chunk's share of the row, or the sum of the input chunks' counts
+  uint32_t nvalid = 0;
+  if (kSrcScores) {
+    int n = a.q_pos[r] + 1;
+    n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+    const int len = n - kRegKeys * c;
+    nvalid = len < 0 ? 0u : (uint32_t)min(len, kRegKeys);
+  } else {
+    for (int ch = 0; ch < a.in_chunks; ++ch) nvalid += (uint32_t)a.in_cnt[(int64_t)r * a.in_chunks + ch];
+  }
+  const uint32_t k = (uint32_t)a.k;
+  const bool take_all = nvalid <= k;
+  uint32_t tau = 0, remaining = k;
+  if (!take_all) reg_select(key, vmask, k, sh, tid, wave, lane, tau, remaining);
+  // positions: computed for a score row, read back from the input slots for candidates (from an
+  // opaque copy of the base, so that the 16 positions are not kept live since the loads)
+  int obase = kSrcScores ? kRegKeys * c + kRegE * tid : kRegE * tid;
+  asm volatile("" : "+v"(obase));
+  const int64_t rb = (int64_t)r * a.in_chunks * a.k;
+  const uint32_t nsel = stage_selected(
+      key, [&](int e) { return kSrcScores ? (uint32_t)(obase + e) : (uint32_t)a.in_pos[rb + obase + e]; }, vmask,
+      take_all, tau, remaining, !kFinal, sh, wave, lane);
+  if (kFinal) {
+    int32_t* out = a.idx + (int64_t)r * a.ld_idx;
+    for (int i = tid; i < a.k; i += kTopkThreads) out[i] = i < (int)nsel ? (int32_t)sh.cand_pos[i] : -1;
+  } else {
+    const int64_t ob = ((int64_t)r * a.out_chunks + c) * a.k;
+    for (int i = tid; i < (int)nsel; i += kTopkThreads) {
+      a.out_key[ob + i] = sh.cand_key[i];
+      a.out_pos[ob + i] = (int32_t)sh.cand_pos[i];
+    }
+    if (tid == 0) a.out_cnt[(int64_t)r * a.out_chunks + c] = (int32_t)nsel;
+  }
+}
+
+// Long rows: candidates per chunk of kRegKeys positions (at most k each), then one selection over
+// them. The union of the chunks' top-k sets holds the row's top-k under the same order (value,
+// then position), and the candidates stay in ascending position order, so ties still go to the
+// smaller position. Usable while every row's candidates fit one block.
+int topk_chunks(int max_ctx) { return (max_ctx + kRegKeys - 1) / kRegKeys; }
+bool topk_staged_ok(int max_ctx, int k) {
+  return max_ctx > kRegKeys && k <= kCandCap && (int64_t)topk_chunks(max_ctx) * k <= kRegKeys;
+}
+size_t topk_staged_ws_bytes(int rows, int max_ctx, int k) {
+  if (!topk_staged_ok(max_ctx, k)) return 0;
+  const size_t slots = (size_t)rows * topk_chunks(max_ctx) * k;
+  return slots * 8 + (size_t)rows * topk_chunks(max_ctx) * 4 + 256;
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int rows,
-                       int max_ctx, int k, int32_t* idx, int64_t ld_idx, hipStream_t stream,
-                       int* path) {
+                       int max_ctx, int k, int32_t* idx, int64_t ld_idx, void* ws, size_t ws_bytes,
+                       hipStream_t stream, int* path) {
+  TopkStageArgs a{};
+  a.scores = scores; a.ld_scores = ld_scores; a.q_pos = q_pos; a.max_ctx = max_ctx; a.k = k;
+  a.idx = idx; a.ld_idx = ld_idx;
   if (max_ctx <= kRegKeys && k <= kCandCap) {
     *path = (max_ctx <= k) ? DSA_PATH_TOPK_COPY : DSA_PATH_TOPK_RADIX_REG;
-    hipLaunchKernelGGL(topk_reg_kernel, dim3(rows), dim3(kTopkThreads), 0, stream, scores, ld_scores, q_pos,
-                       max_ctx, k, idx, ld_idx);
+    hipLaunchKernelGGL((topk_stage_kernel<true, true>), dim3(1, rows), dim3(kTopkThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  const size_t need = topk_staged_ws_bytes(rows, max_ctx, k);
+  if (need && ws && ws_bytes >= need) {
+    *path = DSA_PATH_TOPK_RADIX_STAGED;
+    const int C = topk_chunks(max_ctx);
+    uint8_t* p = (uint8_t*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
+    const size_t slots = (size_t)rows * C * k;
+    a.out_key = (uint32_t*)p;
+    a.out_pos = (int32_t*)(p + slots * 4);
+    a.out_cnt = (int32_t*)(p + slots * 8);
+    a.out_chunks = C;
+    hipLaunchKernelGGL((topk_stage_kernel<true, false>), dim3(C, rows), dim3(kTopkThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    TopkStageArgs b = a;
+    b.in_key = a.out_key; b.in_pos = a.out_pos; b.in_cnt = a.out_cnt; b.in_chunks = C;
+    b.out_key = nullptr; b.out_pos = nullptr; b.out_cnt = nullptr; b.out_chunks = 0;
+    hipLaunchKernelGGL((topk_stage_kernel<false, true>), dim3(1, rows), dim3(kTopkThreads), 0, stream, b);
     return hipGetLastError();
   }
   const int cap = max_ctx < kTopkLdsCap ? max_ctx : kTopkLdsCap;

@@ -18,7 +18,7 @@ DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP
 DSA_E4M3, DSA_F32 = 0, 1
 PATHS = {
     0: "none", 1: "indexer_generic", 2: "indexer_scan_mfma", 3: "indexer_prefill_mfma",
-    10: "topk_copy", 11: "topk_radix", 12: "topk_radix_reg", 20: "mla_generic", 21: "mla_mfma", 22: "mla_mfma_split",
+    10: "topk_copy", 11: "topk_radix", 12: "topk_radix_reg", 13: "topk_radix_staged", 20: "mla_generic", 21: "mla_mfma", 22: "mla_mfma_split",
 }
 
 EXPORTS = [
@@ -137,16 +137,24 @@ def indexer_scores(q, w, k_cache, k_scale, page_table, q_pos, n_seq, q_per_seq, 
     return scores
 
 
-def topk(scores, q_pos, max_ctx, k, idx=None, stream=None):
-    """Top-k positions per row, ascending, -1 padded: idx [rows, k] int32."""
+def topk_workspace_size(rows, max_ctx, k) -> int:
+    return int(load().dsa_topk_workspace_size(rows, max_ctx, k))
+
+
+def topk(scores, q_pos, max_ctx, k, idx=None, ws=None, stream=None):
+    """Top-k positions per row, ascending, -1 padded: idx [rows, k] int32. `ws` (uint8, at least
+    topk_workspace_size bytes) is allocated here when needed and not given."""
     _need(scores, "scores", torch.float32, 2)
     _need(q_pos, "q_pos", torch.int32, 1)
     rows = scores.shape[0]
     if idx is None:
         idx = torch.empty(rows, k, dtype=torch.int32, device=scores.device)
     _need(idx, "idx", torch.int32, 2)
-    st = load().dsa_topk(_p(scores), scores.shape[1], _p(q_pos), rows, max_ctx, k, _p(idx), idx.shape[1], None, 0,
-                         _stream(stream))
+    need = topk_workspace_size(rows, max_ctx, k) if rows > 0 else 0
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    st = load().dsa_topk(_p(scores), scores.shape[1], _p(q_pos), rows, max_ctx, k, _p(idx), idx.shape[1], _p(ws),
+                         0 if ws is None else ws.numel(), _stream(stream))
     _check("dsa_topk", st)
     return idx
 

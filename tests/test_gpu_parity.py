@@ -135,6 +135,29 @@ def test_topk_register_path_special_rows(oracle_lib):
     np.testing.assert_array_equal(g, r)
 
 
+def test_topk_long_rows_staged_and_without_workspace(oracle_lib):
+    """Rows over 16384 positions: the two-stage selection (chunk candidates, then a merge) with the
+    workspace the binding allocates, and the single-workgroup kernel the ABI falls back to when it
+    gets no workspace; both must equal the oracle."""
+    _say("case: topk long rows, staged and without workspace")
+    rng = np.random.default_rng(21)
+    n, k = 40000, 2048
+    sc = rng.standard_normal((4, n)).astype(np.float32)
+    sc[1, 5000:30000] = 0.75                      # a long run of equal scores across chunks
+    q_pos = np.array([n - 1, n - 1, 2047, 17000], np.int32)
+    g, r = _topk_case(sc, q_pos, k)
+    assert dsa.last_path() == "topk_radix_staged"
+    np.testing.assert_array_equal(g, r)
+    d_s = torch.from_numpy(sc).cuda()
+    d_p = torch.from_numpy(q_pos).cuda()
+    idx = torch.empty(4, k, dtype=torch.int32, device="cuda")
+    st = dsa.load().dsa_topk(dsa._p(d_s), n, dsa._p(d_p), 4, n, k, dsa._p(idx), k, None, 0,
+                             dsa._stream(None))
+    assert st == dsa.DSA_OK
+    assert dsa.last_path() == "topk_radix"
+    np.testing.assert_array_equal(idx.cpu().numpy(), r)
+
+
 def test_topk_empty_and_tiny_rows(oracle_lib):
     _say("case: topk tiny rows")
     sc = np.random.default_rng(6).standard_normal((3, 64)).astype(np.float32)
