@@ -182,7 +182,10 @@ def time_graph_steps(step, steps, warmup):
         torch.cuda.synchronize()
         d = step.copies[c]
         if not (torch.equal(d["idx"], eager[c][0]) and torch.equal(d["out"], eager[c][1])):
-            raise SystemExit("graph replay differs from the eager step")
+            bad_idx = int((d["idx"] != eager[c][0]).sum())
+            bad_out = int((d["out"].view(torch.int16) != eager[c][1].view(torch.int16)).sum())
+            raise SystemExit(f"graph replay differs from the eager step (copy {c}: {bad_idx} index entries, "
+                             f"{bad_out} output elements)")
     return time_replays(torch, graphs, steps)
 
 
@@ -277,15 +280,20 @@ def run_decode_bench(args):
     log(f"[bench] workload {w.name}: {w.n_seq} requests x {w.q_per_seq} rows, ctx {w.max_ctx}, "
         f"generated in {time.time() - t0:.1f} s")
     step = DecodeStep(w, copies=2)
-    # the step as deployed: graph replays; then an eager pass with events between the three
-    # calls for the per-call times (those include each call's launch gap)
-    ms_step, wall = time_graph_steps(step, args.steps, args.warmup)
-    ms_step = float(ms_step)
-    # per-call times: graphs holding one call each, replayed back to back
-    ms = [time_replays(torch, step.capture((fn,)), args.steps)[0]
-          for fn in (step.call_indexer, step.call_topk, step.call_mla)]
-    _, per = time_steps(step, args.steps, 1)
-    ms.append(float(per.mean(axis=0)[3]))
+    if args.no_graph:
+        # eager steps only (for profiler runs that do not follow graph launches)
+        wall, per = time_steps(step, args.steps, args.warmup)
+        ms = [float(x) for x in per.mean(axis=0)]
+        ms_step = ms[3]
+    else:
+        # the step as deployed: graph replays; per-call times from graphs holding one call each,
+        # replayed back to back; and an eager pass with events between the calls
+        ms_step, wall = time_graph_steps(step, args.steps, args.warmup)
+        ms_step = float(ms_step)
+        ms = [time_replays(torch, step.capture((fn,)), args.steps)[0]
+              for fn in (step.call_indexer, step.call_topk, step.call_mla)]
+        _, per = time_steps(step, args.steps, 1)
+        ms.append(float(per.mean(axis=0)[3]))
     ctx = w.q_pos.reshape(w.n_seq, w.q_per_seq).max(axis=1) + 1
     by = decode_step_bytes(w.n_seq, w.q_per_seq, ctx, w.topk)
     fl = decode_step_flops(w.n_seq, w.q_per_seq, ctx, w.topk)
@@ -306,7 +314,9 @@ def run_decode_bench(args):
     log("[bench] " + json.dumps(detail))
     mla_bytes = by["mla"]
     achieved = mla_bytes / (ms[2] * 1e-3) / 1e9
-    traffic = measured_traffic("sparse_mla_decode")
+    # the call's two launches: the attention kernel and the merge of its key splits
+    tr = [measured_traffic(key) for key in ("sparse_mla_decode", "sparse_mla_combine")]
+    traffic = None if None in tr else sum(tr)
     roof = {"bound": "hbm", "kernel": "dsa_sparse_mla_decode (mla_mfma_kernel + mla_combine_kernel)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -453,6 +463,7 @@ def main():
                     choices=["decode_mtp_b64_16k", "decode_b16_4k", "decode_b4_128k", "prefill_8k",
                              "prefill_chunk_128k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager steps (for counter-collection runs)")
     ap.add_argument("--crossover", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()

@@ -789,33 +789,50 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
 }
 
 // Merge the splits of each row from their fp16 partials: out = sum_s w_s N_s / sum_s w_s with
-// w_s = l_s 2^(m_s - M). One thread per (row, head, 8 output columns).
+// w_s = l_s 2^(m_s - M). One thread per (row, head, 8 output columns). The (m, l) pairs of all
+// splits, then the partials of eight splits at a time, are loaded together, so a row split many
+// ways costs a few memory latencies rather than one per split. A split without keys (l = 0) is
+// skipped by selects: whatever its partial holds never enters the sum.
 __global__ void __launch_bounds__(256) mla_combine_kernel(AttnArgs a, int splits, int units, void* __restrict__ ws) {
+  constexpr int kBatch = 8;
   const int r = blockIdx.y;
   const int item = blockIdx.x * 256 + threadIdx.x;  // head * 64 + column group
   if (item >= kH * (kDv / 8)) return;
   const int head = item / (kDv / 8), cg = item % (kDv / 8);
   MlaSplitWs w = mla_split_ws(ws, units);
+  const int64_t u0 = (int64_t)r * splits * kH + head;  // split s2 at u0 + s2 * kH
   float M = -INFINITY;
-  for (int s2 = 0; s2 < splits; ++s2) {
-    const f32x2 ml = w.ml[(int64_t)(r * splits + s2) * kH + head];
-    if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
+  for (int s0 = 0; s0 < splits; s0 += kBatch) {
+    f32x2 ml[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) ml[j] = w.ml[u0 + (int64_t)min(s0 + j, splits - 1) * kH];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (s0 + j < splits && ml[j][1] > 0.f) M = fmaxf(M, ml[j][0]);
   }
   float L = 0.f, acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int s2 = 0; s2 < splits; ++s2) {
-    const int64_t u = (int64_t)(r * splits + s2) * kH + head;
-    const f32x2 ml = w.ml[u];
-    if (!(ml[1] > 0.f)) continue;
-    const float f = ml[1] * exp2f(ml[0] - M);
-    L += f;
-    const i32x4 v = *(const i32x4*)(w.part + u * kDv + 8 * cg);
+  for (int s0 = 0; s0 < splits; s0 += kBatch) {
+    f32x2 ml[kBatch];
+    i32x4 v[kBatch];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const f32x2 x = unpack_f16x2((uint32_t)v[e]);
-      acc[2 * e] = fmaf(f, x[0], acc[2 * e]);
-      acc[2 * e + 1] = fmaf(f, x[1], acc[2 * e + 1]);
+    for (int j = 0; j < kBatch; ++j) {
+      const int64_t u = u0 + (int64_t)min(s0 + j, splits - 1) * kH;
+      ml[j] = w.ml[u];
+      v[j] = *(const i32x4*)(w.part + u * kDv + 8 * cg);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const bool use = s0 + j < splits && ml[j][1] > 0.f;
+      const float f = use ? ml[j][1] * exp2f(ml[j][0] - M) : 0.f;
+      L += f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 x = unpack_f16x2((uint32_t)v[j][e]);
+        acc[2 * e] = use ? fmaf(f, x[0], acc[2 * e]) : acc[2 * e];
+        acc[2 * e + 1] = use ? fmaf(f, x[1], acc[2 * e + 1]) : acc[2 * e + 1];
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
