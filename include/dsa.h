@@ -65,8 +65,8 @@ typedef enum {
 enum {
   DSA_PATH_NONE = 0,
   DSA_PATH_INDEXER_GENERIC = 1,       /* any Hi, Di, dtype: one thread per (row, key), VALU */
-  DSA_PATH_INDEXER_SCAN_MFMA = 2,     /* Hi=64, Di=128, E4M3, q_per_seq <= 2: key scan */
-  DSA_PATH_INDEXER_PREFILL_MFMA = 3,  /* Hi=64, Di=128, E4M3, q_per_seq > 2: query x key tiles */
+  DSA_PATH_INDEXER_SCAN_MFMA = 2,     /* Hi=64, Di=128, E4M3, 64-token pages: key scan, 2 rows/wave */
+  DSA_PATH_INDEXER_PREFILL_MFMA = 3,  /* Hi=64, Di=128, E4M3, other page sizes: query x key tiles */
   DSA_PATH_TOPK_COPY = 10,            /* every row no longer than k: all positions kept */
   DSA_PATH_TOPK_RADIX = 11,           /* radix select, one workgroup per row */
   DSA_PATH_TOPK_RADIX_REG = 12,       /* as 11 for max_ctx <= 16384, the row held in registers */

@@ -137,8 +137,10 @@ dsa_status_t dsa_indexer_scores(const void* q, const float* w, const void* k_cac
   dsa::PagedCache kc{k_cache, page_table, ld_pt, page_size, num_pages};
   hipStream_t st = (hipStream_t)stream;
   if (Hi == 64 && Di == 128 && dtype == DSA_E4M3) {
-    // the scan is built for 64-token pages
-    if (q_per_seq <= 2 && page_size == 64) {
+    // the scan is built for 64-token pages; it takes the rows of a sequence two at a time (one
+    // at a time for an odd count), one block row per unit
+    const int64_t units = (int64_t)n_seq * q_per_seq / dsa::indexer_scan_rows_per_wave(q_per_seq);
+    if (page_size == 64 && units <= 65535) {
       s = hip_status(dsa::launch_indexer_scan((const uint8_t*)q, w, kc, k_scale, q_pos, n_seq, q_per_seq,
                                               max_ctx, scores, ld_scores, st), "indexer_scan launch");
       return s == DSA_OK ? ok(DSA_PATH_INDEXER_SCAN_MFMA) : s;

@@ -80,6 +80,7 @@ hipError_t launch_indexer_generic(const void* q, const float* w, PagedCache kc, 
                                   const int32_t* q_pos, int n_seq, int q_per_seq, int max_ctx, int Hi,
                                   int Di, int is_f32, float* scores, int64_t ld_scores,
                                   hipStream_t stream);
+int indexer_scan_rows_per_wave(int q_per_seq);
 hipError_t launch_indexer_scan(const uint8_t* q, const float* w, PagedCache kc, const float* k_scale,
                                const int32_t* q_pos, int n_seq, int q_per_seq, int max_ctx,
                                float* scores, int64_t ld_scores, hipStream_t stream);

@@ -382,14 +382,17 @@ __device__ __forceinline__ void scan_page(const ScanCtx& c, const QueryOps<NQ>& 
 template <int NQ>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) indexer_scan_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ w, PagedCache kc,
-    const float* __restrict__ k_scale, const int32_t* __restrict__ q_pos, int keys_per_wave,
+    const float* __restrict__ k_scale, const int32_t* __restrict__ q_pos, int q_per_seq, int keys_per_wave,
     int max_ctx, float* __restrict__ scores, int64_t ld_scores) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kScanLdsBytes];
-  const int seq = blockIdx.y;
+  // this block's NQ query rows: unit * NQ .. + NQ - 1, all of one sequence (decode: the request's
+  // rows; prefill: two consecutive rows of the block)
+  const int unit = blockIdx.y;
+  const int seq = unit * NQ / q_per_seq;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int tmax = -1;
 #pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) tmax = max(tmax, q_pos[seq * NQ + qi]);
+  for (int qi = 0; qi < NQ; ++qi) tmax = max(tmax, q_pos[unit * NQ + qi]);
   // a wave's range starts on a page and spans at most 64 pages
   const int jbeg = (blockIdx.x * kScanWaves + wave) * keys_per_wave;
   const int jend = min(min(jbeg + keys_per_wave, tmax + 1), max_ctx);  // never past ld_scores
@@ -405,7 +408,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (c.vpage >= kc.num_pages) c.vpage = -1;
   }
   QueryOps<NQ> o;
-  load_query_ops<NQ>(o, q, w, q_pos, seq * NQ, NQ, lane);
+  load_query_ops<NQ>(o, q, w, q_pos, unit * NQ, NQ, lane);
   c.ring = (lds8*)smem + wave * kWaveRingBytes;
   c.ring_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)c.ring);
   c.kbase = uniform_u64((uint64_t)(uintptr_t)kc.base);
@@ -474,19 +477,24 @@ __global__ void __launch_bounds__(256) indexer_prefill_kernel(
   }
 }
 
+int indexer_scan_rows_per_wave(int q_per_seq) { return q_per_seq % 2 == 0 ? 2 : 1; }
+
 hipError_t launch_indexer_scan(const uint8_t* q, const float* w, PagedCache kc, const float* k_scale,
                                const int32_t* q_pos, int n_seq, int q_per_seq, int max_ctx,
                                float* scores, int64_t ld_scores, hipStream_t stream) {
-  // about 2048 waves (8 per CU) in all, each a whole number of pages (at most 64 of them)
-  const int64_t total = (int64_t)n_seq * max_ctx;
+  // units of NQ query rows of one sequence; about 2048 waves (8 per CU) per launch for a decode
+  // batch, each a whole number of pages (at most 64 of them)
+  const int nq = indexer_scan_rows_per_wave(q_per_seq);
+  const int units = n_seq * q_per_seq / nq;
+  const int64_t total = (int64_t)units * max_ctx;
   int kpw = (int)((total / 2048 + kScanPage - 1) / kScanPage * kScanPage);
   kpw = kpw < kScanPage ? kScanPage : (kpw > 64 * kScanPage ? 64 * kScanPage : kpw);
   const int per_block = kScanWaves * kpw;
-  dim3 grid((max_ctx + per_block - 1) / per_block, n_seq);
-  if (q_per_seq == 1)
-    hipLaunchKernelGGL(indexer_scan_kernel<1>, grid, dim3(64 * kScanWaves), 0, stream, q, w, kc, k_scale, q_pos, kpw, max_ctx, scores, ld_scores);
+  dim3 grid((max_ctx + per_block - 1) / per_block, units);
+  if (nq == 1)
+    hipLaunchKernelGGL(indexer_scan_kernel<1>, grid, dim3(64 * kScanWaves), 0, stream, q, w, kc, k_scale, q_pos, q_per_seq, kpw, max_ctx, scores, ld_scores);
   else
-    hipLaunchKernelGGL(indexer_scan_kernel<2>, grid, dim3(64 * kScanWaves), 0, stream, q, w, kc, k_scale, q_pos, kpw, max_ctx, scores, ld_scores);
+    hipLaunchKernelGGL(indexer_scan_kernel<2>, grid, dim3(64 * kScanWaves), 0, stream, q, w, kc, k_scale, q_pos, q_per_seq, kpw, max_ctx, scores, ld_scores);
   return hipGetLastError();
 }
 

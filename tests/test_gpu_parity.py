@@ -59,11 +59,29 @@ def test_indexer_scan(oracle_lib, qps, q_pos, max_ctx, permute):
 
 @pytest.mark.parametrize("T,offset", [(300, 0), (64, 700), (517, 1531)])
 def test_indexer_prefill(oracle_lib, T, offset):
+    """A prefill block: the key scan takes its rows two at a time (one at a time for odd T)."""
     _say(f"case: indexer prefill T={T} offset={offset}")
     q_pos = np.arange(offset, offset + T, dtype=np.int32)
     w = workloads.make_random(1, T, q_pos, offset + T, H=2, Dqk=16, Dv=8, seed=41 + T, permute_pages=True)
     d = gpu_inputs(w)
     s = _indexer_gpu(w, d)
+    assert dsa.last_path() == "indexer_scan_mfma"
+    check_scores(s, _indexer_ref(w), w.q_pos)
+
+
+@pytest.mark.parametrize("T,offset", [(300, 0), (517, 1531)])
+def test_indexer_prefill_other_page_size(oracle_lib, T, offset):
+    """32-token pages (the same cache split in halves): the query x key tile kernel."""
+    _say(f"case: indexer prefill, 32-token pages, T={T} offset={offset}")
+    q_pos = np.arange(offset, offset + T, dtype=np.int32)
+    w = workloads.make_random(1, T, q_pos, offset + T, H=2, Dqk=16, Dv=8, seed=43 + T, permute_pages=True)
+    d = gpu_inputs(w)
+    P = d["ik"].shape[0]
+    ik32 = d["ik"].reshape(2 * P, 32, d["ik"].shape[2]).contiguous()
+    iks32 = d["iks"].reshape(2 * P, 32).contiguous()
+    pt = d["page_table"].long()
+    pt32 = torch.stack([2 * pt, 2 * pt + 1], dim=2).reshape(pt.shape[0], -1).to(torch.int32).contiguous()
+    s = dsa.indexer_scores(d["iq"], d["iw"], ik32, iks32, pt32, d["q_pos"], 1, T, w.max_ctx).cpu().numpy()
     assert dsa.last_path() == "indexer_prefill_mfma"
     check_scores(s, _indexer_ref(w), w.q_pos)
 
