@@ -325,10 +325,32 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
                     32 * (G & 1) + 8 * (j & 3);
   }
 
+  // The query is loaded first, so that its latency overlaps the index-list resolve (two dependent
+  // loads) below: the latent part as this wave's B operands in registers, the rope part of all
+  // heads into LDS (head h keeps chunk c at c ^ rope_swz(h) of its 128-byte row).
+  {
+    const uint16_t* qh = a.q + ((int64_t)r * kH + 32 * wave + hl) * kDqk + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < kDv / 16; ++ks) qf[ks] = *(const bf16x8*)(qh + 16 * ks);
+    const int tid = 64 * wave + lane;
+#pragma unroll
+    for (int j = 0; j < kH * 8 / 256; ++j) {
+      const int i = tid + 256 * j, h = i >> 3, c = i & 7;
+      const i32x4 v = *(const i32x4*)(a.q + ((int64_t)r * kH + h) * kDqk + kDv + 8 * c);
+      *(__attribute__((address_space(3))) i32x4*)(lds + kQRopeOff + h * kRopeBytes + 16 * (c ^ rope_swz(h))) = v;
+    }
+  }
   for (int cb = e_begin; cb < e_end; cb += kListCap) {
     const int ce = min(e_end, cb + kListCap);
     __syncthreads();  // the previous chunk is done with the list and the buffers
     for (int e = cb + threadIdx.x; e < ce; e += 256) list[e - cb] = resolve_entry(a, r, seq, t, e);
+    if (cb == e_begin) {
+      // consume the query fragments here, before any gather is issued: their wait then covers
+      // the query loads only, and no wait for them lands in the tile loop (where it would also
+      // drain the tile gathers in flight). The barrier below also publishes the rope part in LDS.
+#pragma unroll
+      for (int ks = 0; ks < kDv / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
+    }
     __syncthreads();
     const int n_list = ce - cb;
     const int ntiles = (n_list + kNK - 1) / kNK;
@@ -358,28 +380,6 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
     }
     // entries of the next tile to gather, read one iteration before they are needed
     TileEntries nxt = read_entries(list, tmask, kNBuf - 1, ntiles, wave, lane);
-    if (cb == e_begin) {
-      // the query, while the first gathers are in flight
-      const uint16_t* qh = a.q + ((int64_t)r * kH + 32 * wave + hl) * kDqk + 8 * half;
-#pragma unroll
-      for (int ks = 0; ks < kDv / 16; ++ks) qf[ks] = *(const bf16x8*)(qh + 16 * ks);
-      // thread id rebuilt from the lane count (mbcnt) and the wave index, so that nothing has to
-      // stay live from the kernel start for these addresses
-      int lane_now;
-      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_now));
-      const int tid = 64 * wave + lane_now;
-#pragma unroll
-      for (int j = 0; j < kH * 8 / 256; ++j) {
-        const int i = tid + 256 * j, h = i >> 3, c = i & 7;
-        const i32x4 v = *(const i32x4*)(a.q + ((int64_t)r * kH + h) * kDqk + kDv + 8 * c);
-        *(__attribute__((address_space(3))) i32x4*)(lds + kQRopeOff + h * kRopeBytes + 16 * (c ^ rope_swz(h))) = v;
-      }
-      // consume the fragments here, so their loads are complete before the tile loop and no
-      // wait for them lands inside it (where it would also drain the in-flight tile gathers)
-#pragma unroll
-      for (int ks = 0; ks < kDv / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
-      __syncthreads();  // the rope part of the query is in LDS
-    }
     int b = 0;  // buffer of tile it (it % kNBuf, kept as a rotating counter)
     for (int it = 0; it < ntiles; ++it) {
       int younger = 0;  // later tiles whose gathers are in flight
@@ -789,12 +789,12 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
 }
 
 // Merge the splits of each row from their fp16 partials: out = sum_s w_s N_s / sum_s w_s with
-// w_s = l_s 2^(m_s - M). One thread per (row, head, 8 output columns). The (m, l) pairs of all
-// splits, then the partials of eight splits at a time, are loaded together, so a row split many
-// ways costs a few memory latencies rather than one per split. A split without keys (l = 0) is
-// skipped by selects: whatever its partial holds never enters the sum.
+// w_s = l_s 2^(m_s - M). One thread per (row, head, 8 output columns). The (m, l) pairs, then the
+// partials, of up to kBatch splits at a time are loaded together, so a row split many ways costs a
+// few memory latencies rather than one per split. A split without keys (l = 0) is skipped by
+// selects: whatever its partial holds never enters the sum.
+template <int kBatch>
 __global__ void __launch_bounds__(256) mla_combine_kernel(AttnArgs a, int splits, int units, void* __restrict__ ws) {
-  constexpr int kBatch = 8;
   const int r = blockIdx.y;
   const int item = blockIdx.x * 256 + threadIdx.x;  // head * 64 + column group
   if (item >= kH * (kDv / 8)) return;
@@ -805,7 +805,8 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(AttnArgs a, int splits
   for (int s0 = 0; s0 < splits; s0 += kBatch) {
     f32x2 ml[kBatch];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) ml[j] = w.ml[u0 + (int64_t)min(s0 + j, splits - 1) * kH];
+    for (int j = 0; j < kBatch; ++j)
+      if (s0 + j < splits) ml[j] = w.ml[u0 + (int64_t)(s0 + j) * kH];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j)
       if (s0 + j < splits && ml[j][1] > 0.f) M = fmaxf(M, ml[j][0]);
@@ -818,9 +819,11 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(AttnArgs a, int splits
     i32x4 v[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int64_t u = u0 + (int64_t)min(s0 + j, splits - 1) * kH;
-      ml[j] = w.ml[u];
-      v[j] = *(const i32x4*)(w.part + u * kDv + 8 * cg);
+      if (s0 + j < splits) {  // uniform: the loads of a batch are still issued back to back
+        const int64_t u = u0 + (int64_t)(s0 + j) * kH;
+        ml[j] = w.ml[u];
+        v[j] = *(const i32x4*)(w.part + u * kDv + 8 * cg);
+      }
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
@@ -870,7 +873,11 @@ hipError_t launch_mla_mfma(const AttnArgs& a, int splits, void* ws, hipStream_t 
   hipLaunchKernelGGL(mla_mfma_kernel<kMlaSplitCombine>, dim3(blocks), dim3(256), 0, stream, a, splits, per, units, per_xcd, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((kH * (kDv / 8) + 255) / 256, rows), dim3(256), 0, stream, a, splits, units, ws);
+  const dim3 cgrid((kH * (kDv / 8) + 255) / 256, rows);
+  if (splits <= 2)
+    hipLaunchKernelGGL(mla_combine_kernel<2>, cgrid, dim3(256), 0, stream, a, splits, units, ws);
+  else
+    hipLaunchKernelGGL(mla_combine_kernel<8>, cgrid, dim3(256), 0, stream, a, splits, units, ws);
   return hipGetLastError();
 }
 
