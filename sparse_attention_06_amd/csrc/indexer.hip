@@ -305,12 +305,51 @@ __device__ __forceinline__ void scan_read(const ScanCtx& c, int p, int t, i32x4&
   r1 = *(const __attribute__((address_space(3))) i32x4*)(tk + c.rd1);
 }
 
-// Sub-tile t of page p: its bytes are in raw0/raw1 (read during the previous sub-tile). Leaves
-// v[qi] = this lane's 16-head sum for its key and every query row, and the next sub-tile's bytes
-// in raw0/raw1.
+// One query row's 16 MFMAs over a sub-tile (the four accumulation chains advance together, K step
+// outermost, so consecutive MFMAs never wait on each other).
+__device__ __forceinline__ void row_mfmas(const f16x8 (&A)[4][4], const f16x8 (&B)[4], f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][ks], B[ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mt],
+                                                        0, 0, 0);
+}
+
+// This lane's 16-head sum of w * ReLU(s) from one row's accumulators (two partial sums break the
+// FMA chain).
+__device__ __forceinline__ float head_sum(const float (&W)[4][4], const f32x4 (&acc)[4]) {
+  float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; i += 2) {
+      v0 = fmaf(W[mt][i], relu_bits(acc[mt][i]), v0);
+      v1 = fmaf(W[mt][i + 1], relu_bits(acc[mt][i + 1]), v1);
+    }
+  return v0 + v1;
+}
+
+// Ask the scheduler to alternate one MFMA with two VALU ops, sixteen times: a row's MFMAs then run
+// while the VALU works through another row's head sums, within one wave.
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+  }
+}
+
+// Sub-tile t of page p: its bytes are in raw0/raw1 (read during the previous sub-tile). The rows'
+// MFMAs and head sums are software-pipelined: row 0's MFMAs run alongside the head sum of the
+// last row of the previous sub-tile (its accumulators carried in `carry`), row 1's alongside row
+// 0's head sum; the last row's head sum of this sub-tile is left in `carry` for the next one
+// (for the last sub-tile of a page, the page's epilogue does it). Leaves v[qi][t] (v[NQ-1][t-1])
+// and the next sub-tile's bytes in raw0/raw1.
 template <int NQ, int kTail, int t>
 __device__ __forceinline__ void scan_subtile(const ScanCtx& c, const QueryOps<NQ>& o, int p, bool has_scale,
-                                             i32x4& raw0, i32x4& raw1, float (&v)[NQ]) {
+                                             i32x4& raw0, i32x4& raw1, f32x4 (&carry)[4],
+                                             float (&v)[NQ][kSubTiles]) {
   f16x8 B[4];
   e4m3x16_to_f16(raw0, B[0], B[1]);
   e4m3x16_to_f16(raw1, B[2], B[3]);
@@ -327,31 +366,26 @@ __device__ __forceinline__ void scan_subtile(const ScanCtx& c, const QueryOps<NQ
     wait_vm<scan_wait_count<NQ, kTail>(4)>();
     scan_read(c, p + 1, 0, raw0, raw1);
   }
-  // one query row at a time, so its accumulators are free again for the next row; the four
-  // accumulation chains of a row advance together (K step outermost)
-#pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) {
-    f32x4 acc[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(o.A[qi][mt][ks], B[ks],
-                                                          ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mt], 0, 0, 0);
-    float v0 = 0.f, v1 = 0.f;  // two partial sums break the FMA chain
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        v0 = fmaf(o.W[qi][mt][i], relu_bits(acc[mt][i]), v0);
-        v1 = fmaf(o.W[qi][mt][i + 1], relu_bits(acc[mt][i + 1]), v1);
-      }
-    v[qi] = v0 + v1;
-    // pin the row's epilogue here, so its accumulators die before the next MFMAs are issued
-    asm volatile("" : "+v"(v[qi]));
-  }
-  // keep sub-tiles apart in the schedule: interleaving them only raises register pressure
   __builtin_amdgcn_sched_barrier(0);
+  f32x4 acc0[4];
+  row_mfmas(o.A[0], B, acc0);
+  if (t > 0) v[NQ - 1][t - 1] = head_sum(o.W[NQ - 1], carry);
+  interleave_mfma_valu();
+  if (NQ == 2) {
+    f32x4 acc1[4];
+    row_mfmas(o.A[NQ - 1], B, acc1);
+    v[0][t] = head_sum(o.W[0], acc0);
+    interleave_mfma_valu();
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) carry[mt] = acc1[mt];
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) carry[mt] = acc0[mt];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // pin the head sums here, so that their accumulators die in this sub-tile
+  if (t > 0) asm volatile("" : "+v"(v[NQ - 1][t - 1]));
+  if (NQ == 2) asm volatile("" : "+v"(v[0][t]));
 }
 
 // One page: four sub-tiles, then the page's reduction, scale, mask and stores.
@@ -359,11 +393,13 @@ template <int NQ, int kTail>
 __device__ __forceinline__ void scan_page(const ScanCtx& c, const QueryOps<NQ>& o, int p, int jpage, int jend,
                                           bool has_scale, float* __restrict__ scores, int64_t ld_scores,
                                           i32x4& raw0, i32x4& raw1, int lane) {
-  float v0[NQ], v1[NQ], v2[NQ], v3[NQ];
-  scan_subtile<NQ, kTail, 0>(c, o, p, has_scale, raw0, raw1, v0);
-  scan_subtile<NQ, kTail, 1>(c, o, p, has_scale, raw0, raw1, v1);
-  scan_subtile<NQ, kTail, 2>(c, o, p, has_scale, raw0, raw1, v2);
-  scan_subtile<NQ, kTail, 3>(c, o, p, has_scale, raw0, raw1, v3);
+  float v[NQ][kSubTiles];
+  f32x4 carry[4];
+  scan_subtile<NQ, kTail, 0>(c, o, p, has_scale, raw0, raw1, carry, v);
+  scan_subtile<NQ, kTail, 1>(c, o, p, has_scale, raw0, raw1, carry, v);
+  scan_subtile<NQ, kTail, 2>(c, o, p, has_scale, raw0, raw1, carry, v);
+  scan_subtile<NQ, kTail, 3>(c, o, p, has_scale, raw0, raw1, carry, v);
+  v[NQ - 1][kSubTiles - 1] = head_sum(o.W[NQ - 1], carry);
   // lane l now scores key jpage + l
   const float sc = has_scale ? *(const __attribute__((address_space(3))) float*)(
                                    c.ring + kRing * kRingTileBytes + (p & (kScaleSlots - 1)) * kScaleSlotBytes + 4 * lane)
@@ -372,7 +408,7 @@ __device__ __forceinline__ void scan_page(const ScanCtx& c, const QueryOps<NQ>& 
   const int j = jpage + lane;
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
-    const float tot = reduce_page(v0[qi], v1[qi], v2[qi], v3[qi]);
+    const float tot = reduce_page(v[qi][0], v[qi][1], v[qi][2], v[qi][3]);
     // exactly one store instruction per query row per page (lane 0 always has j < jend), so the
     // wait counts stay exact; positions past the row's q_pos get -inf
     if (j < jend) scores[o.row[qi] * ld_scores + j] = (j <= o.tpos[qi] && page_ok) ? tot * sc : -INFINITY;
