@@ -13,4 +13,5 @@ from .ref import (  # noqa: F401
     topk,
     sparse_mla,
     dense_mla,
+    mha,
 )

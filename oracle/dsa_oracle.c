@@ -244,3 +244,69 @@ int oracle_dense_mla(const uint16_t* q, const uint16_t* kv_cache, const int32_t*
   }
   return 0;
 }
+
+/* ---- expanded multi-head attention (the short-prefill fallback) ----------------------- */
+
+/* [Handbook] "稀疏注意力：NSA 与 DSA", the cost model's expanded pair and the note on short
+ * prefill: the dense fallback runs multi-head attention with per-head keys of 128 + 64 (rope)
+ * dims and 128-dim values, and V3.2 emulates the DSA mask in that mode. For row r (sequence
+ * s = r / q_per_seq, position t = q_pos[r]) and head h, with
+ *   K_hj = [k_nope[s, h, j, 0:Dn] | k_rope[s, j, 0:Dr]]   (the rope part is shared by all heads)
+ *   V_hj = v[s, h, j, 0:Dv]
+ * the set S is {0..t} when idx is NULL, else the positions j in [0, t] listed in idx[r, 0:k]
+ * (as a set: a repeated entry counts once, [DSA-blog] "Sparse Attention", M = 0 on S_t);
+ * positions are taken in ascending order, and the softmax is attend_row's two passes. */
+int oracle_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_rope, const uint16_t* v,
+               int64_t ld_kv, const int32_t* q_pos, int n_seq, int q_per_seq, const int32_t* idx,
+               int64_t ld_idx, int k, int H, int Dn, int Dr, int Dv, double sm_scale, float* out,
+               float* lse, int row_begin, int row_end) {
+  if (bad_common(n_seq, q_per_seq, row_begin, row_end) || k < 0) return 1;
+  if (H < 1 || Dn < 1 || Dr < 0 || Dv < 1 || ld_kv < 1) return 1;
+  const int Dq = Dn + Dr;
+  unsigned char* in_set = (unsigned char*)malloc((size_t)ld_kv);
+  double* logit = (double*)malloc(sizeof(double) * (size_t)ld_kv);
+  double* acc = (double*)malloc(sizeof(double) * (size_t)Dv);
+  if (!in_set || !logit || !acc) { free(in_set); free(logit); free(acc); return 2; }
+  for (int r = row_begin; r < row_end; ++r) {
+    const int s = r / q_per_seq;
+    const int64_t t = q_pos[r];
+    if (t >= ld_kv) { free(in_set); free(logit); free(acc); return 3; }
+    for (int64_t j = 0; j < ld_kv; ++j) in_set[j] = (unsigned char)(idx == NULL && j <= t);
+    if (idx)
+      for (int i = 0; i < k; ++i) {
+        const int64_t j = idx[(int64_t)r * ld_idx + i];
+        if (j >= 0 && j <= t) in_set[j] = 1;
+      }
+    for (int h = 0; h < H; ++h) {
+      const uint16_t* qh = q + ((int64_t)r * H + h) * Dq;
+      double mx = -INFINITY;
+      int64_t n = 0;
+      for (int64_t j = 0; j <= t; ++j) {
+        if (!in_set[j]) continue;
+        const uint16_t* kn = k_nope + (((int64_t)s * H + h) * ld_kv + j) * Dn;
+        const uint16_t* kr = k_rope + ((int64_t)s * ld_kv + j) * Dr;
+        double dot = 0.0;
+        for (int c = 0; c < Dn; ++c) dot += oracle_bf16_to_double(qh[c]) * oracle_bf16_to_double(kn[c]);
+        for (int c = 0; c < Dr; ++c) dot += oracle_bf16_to_double(qh[Dn + c]) * oracle_bf16_to_double(kr[c]);
+        logit[j] = sm_scale * dot;
+        if (logit[j] > mx) mx = logit[j];
+        ++n;
+      }
+      for (int c = 0; c < Dv; ++c) acc[c] = 0.0;
+      double denom = 0.0;
+      for (int64_t j = 0; j <= t; ++j) {
+        if (!in_set[j]) continue;
+        const double p = exp(logit[j] - mx);
+        const uint16_t* vr = v + (((int64_t)s * H + h) * ld_kv + j) * Dv;
+        denom += p;
+        for (int c = 0; c < Dv; ++c) acc[c] += p * oracle_bf16_to_double(vr[c]);
+      }
+      for (int c = 0; c < Dv; ++c) out[((int64_t)r * H + h) * Dv + c] = n > 0 ? (float)(acc[c] / denom) : 0.0f;
+      if (lse) lse[(int64_t)r * H + h] = n > 0 ? (float)(mx + log(denom)) : -INFINITY;
+    }
+  }
+  free(in_set);
+  free(logit);
+  free(acc);
+  return 0;
+}

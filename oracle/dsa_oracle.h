@@ -78,6 +78,19 @@ int oracle_dense_mla(const uint16_t* q, const uint16_t* kv_cache, const int32_t*
                      int q_per_seq, int H, int Dqk, int Dv, int kv_dim, int v_col0,
                      double sm_scale, float* out, float* lse, int row_begin, int row_end);
 
+/* Expanded multi-head attention, the short-prefill fallback ([Handbook] "稀疏注意力：NSA 与
+ * DSA": the expanded pair of the cost model, per head 128 + 64 (rope) query/key dims and 128
+ * value dims, and the masked MHA mode that emulates DSA for short prefill). For row r of
+ * sequence s at position t and head h: K_hj = [k_nope[s,h,j,:] | k_rope[s,j,:]],
+ * V_hj = v[s,h,j,:], S = {0..t} (idx NULL) or the idx[r] entries within [0, t] taken as a set;
+ * out = softmax(sm_scale q K^T over S) V in double, rounded to float; lse natural log.
+ *   q [rows, H, Dn+Dr]; k_nope [n_seq, H, ld_kv, Dn]; k_rope [n_seq, ld_kv, Dr];
+ *   v [n_seq, H, ld_kv, Dv] (all bf16 bits); out [rows, H, Dv]; lse [rows, H] or NULL. */
+int oracle_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_rope, const uint16_t* v,
+               int64_t ld_kv, const int32_t* q_pos, int n_seq, int q_per_seq, const int32_t* idx,
+               int64_t ld_idx, int k, int H, int Dn, int Dr, int Dv, double sm_scale, float* out,
+               float* lse, int row_begin, int row_end);
+
 #ifdef __cplusplus
 }
 #endif

@@ -59,6 +59,9 @@ def _load():
             lib.oracle_dense_mla.restype = i32
             lib.oracle_dense_mla.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, i32, i32, i32, i32,
                                              i32, i32, dbl, vp, vp, i32, i32]
+            lib.oracle_mha.restype = i32
+            lib.oracle_mha.argtypes = [vp, vp, vp, vp, i64, vp, i32, i32, vp, i64, i32, i32, i32, i32, i32,
+                                       dbl, vp, vp, i32, i32]
             _lib = lib
     return _lib
 
@@ -193,6 +196,34 @@ def dense_mla(q, kv_cache, page_table, page_size, q_pos, n_seq, q_per_seq, Dqk, 
         return lib.oracle_dense_mla(_ptr(q), _ptr(kv), _ptr(pt), pt.shape[1], page_size, num_pages,
                                     _ptr(q_pos), n_seq, q_per_seq, H, Dqk, Dv, kv_dim, v_col0,
                                     float(sm_scale), _ptr(out), _ptr(lse), b, e)
+
+    _run_rows(fn, nrows, threads, rows)
+    return out, lse
+
+
+def mha(q, k_nope, k_rope, v, q_pos, n_seq, q_per_seq, idx, sm_scale, threads=1, rows=None, with_lse=True):
+    """Expanded multi-head attention (the short-prefill fallback), dense causal when idx is None,
+    else restricted to the idx entries (as a set). q: uint16 (bf16 bits) [rows, H, Dn+Dr];
+    k_nope [n_seq, H, ld_kv, Dn]; k_rope [n_seq, ld_kv, Dr]; v [n_seq, H, ld_kv, Dv].
+    Returns (out float32 [rows, H, Dv], lse float32 [rows, H])."""
+    lib = _load()
+    q = _c(q, np.uint16)
+    kn = _c(k_nope, np.uint16)
+    kr = _c(k_rope, np.uint16)
+    v = _c(v, np.uint16)
+    q_pos = _c(q_pos, np.int32)
+    idx = None if idx is None else _c(idx, np.int32)
+    nrows, H = q.shape[0], q.shape[1]
+    Dn, Dr, Dv, ld_kv = kn.shape[3], kr.shape[2], v.shape[3], kn.shape[2]
+    if q.shape[2] != Dn + Dr or kr.shape[1] != ld_kv or v.shape[2] != ld_kv or v.shape[1] != H or kn.shape[1] != H:
+        raise ValueError("inconsistent expanded attention shapes")
+    out = np.full((nrows, H, Dv), np.nan, dtype=np.float32)
+    lse = np.full((nrows, H), np.nan, dtype=np.float32) if with_lse else None
+    k = 0 if idx is None else idx.shape[1]
+
+    def fn(b, e):
+        return lib.oracle_mha(_ptr(q), _ptr(kn), _ptr(kr), _ptr(v), ld_kv, _ptr(q_pos), n_seq, q_per_seq,
+                              _ptr(idx), k, k, H, Dn, Dr, Dv, float(sm_scale), _ptr(out), _ptr(lse), b, e)
 
     _run_rows(fn, nrows, threads, rows)
     return out, lse

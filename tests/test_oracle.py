@@ -393,3 +393,123 @@ def test_tiny_workload_end_to_end_invariants(oracle_lib):
         if n > w.topk:
             rest = np.setdiff1d(np.arange(n), sel)
             assert s[r, sel].min() >= s[r, rest].max()
+
+
+# ---------------------------------------------------------------- expanded attention (fallback)
+
+
+def _mha_case(seed=11, n_seq=2, q_per_seq=3, H=4, Dn=16, Dr=8, Dv=12, T=70):
+    rng = np.random.default_rng(seed)
+    rows = n_seq * q_per_seq
+    q = _bf16(rng.standard_normal((rows, H, Dn + Dr)))
+    kn = _bf16(rng.standard_normal((n_seq, H, T, Dn)))
+    kr = _bf16(rng.standard_normal((n_seq, T, Dr)))
+    v = _bf16(rng.standard_normal((n_seq, H, T, Dv)))
+    q_pos = np.concatenate([np.sort(rng.choice(T, q_per_seq, replace=False)) for _ in range(n_seq)]).astype(np.int32)
+    return q, kn, kr, v, q_pos
+
+
+def test_mha_matches_torch_sdpa_per_head_keys(oracle_lib):
+    # per-head keys = [nope | shared rope]: torch's float64 attention with the causal mask, and with
+    # a random position set (the masked MHA mode)
+    q, kn, kr, v, q_pos = _mha_case()
+    n_seq, H, T, Dn = kn.shape
+    rows, Dv, Dr = q.shape[0], v.shape[3], kr.shape[2]
+    qps = rows // n_seq
+    rng = np.random.default_rng(3)
+    idx = np.full((rows, 9), -1, np.int32)
+    for r in range(rows):
+        m = min(9, q_pos[r] + 1)
+        idx[r, :m] = rng.choice(q_pos[r] + 1, m, replace=False)   # unsorted on purpose
+    scale = 0.29
+    for use_idx in (False, True):
+        out, lse = oracle_lib.mha(q, kn, kr, v, q_pos, n_seq, qps, idx if use_idx else None, scale)
+        for r in range(rows):
+            s = r // qps
+            K = torch.cat([_dec_bf16(kn[s]), _dec_bf16(kr[s]).unsqueeze(0).expand(H, T, Dr)], dim=-1)
+            V = _dec_bf16(v[s])
+            mask = torch.arange(T) <= int(q_pos[r])
+            if use_idx:
+                sel = torch.zeros(T, dtype=torch.bool)
+                sel[[j for j in idx[r] if j >= 0]] = True
+                mask &= sel
+            Q = _dec_bf16(q[r]).unsqueeze(1)                              # [H, 1, Dn+Dr]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                Q, K, V, attn_mask=mask.view(1, 1, T).expand(H, 1, T), scale=scale)[:, 0]
+            np.testing.assert_allclose(out[r], ref.numpy(), rtol=1e-6, atol=1e-6)
+            logits = scale * (K @ Q.transpose(1, 2))[:, :, 0]
+            ref_lse = torch.logsumexp(logits.masked_fill(~mask, -math.inf), dim=-1)
+            np.testing.assert_allclose(lse[r], ref_lse.numpy(), rtol=1e-6, atol=1e-6)
+
+
+def test_expanded_equals_absorbed_mla(oracle_lib):
+    # [Handbook] cost model: the expanded pair (per-head k = c W_UK, v = c W_UV) and the absorbed
+    # pair (q W_UK^T against the latent row, output times W_UV) are the same attention. With
+    # W_UK, W_UV made of signed unit columns on distinct latent dims, every product is exact in
+    # bf16, so the absorbed oracle (pinned above) and the expanded one must agree to rounding.
+    rng = np.random.default_rng(21)
+    H, DC, Dn, Dr, Dv, T, rows = 3, 48, 16, 8, 12, 64, 5
+    lat = rng.standard_normal((T, DC))
+    rope = rng.standard_normal((T, Dr))
+    qn = rng.standard_normal((rows, H, Dn))
+    qr = rng.standard_normal((rows, H, Dr))
+    lat, rope, qn, qr = (_dec_bf16(_bf16(x)).numpy() for x in (lat, rope, qn, qr))
+    WUK = np.zeros((H, DC, Dn))
+    WUV = np.zeros((H, DC, Dv))
+    for h in range(H):
+        for d, c in enumerate(rng.choice(DC, Dn, replace=False)):
+            WUK[h, c, d] = rng.choice([-1.0, 1.0])
+        for d, c in enumerate(rng.choice(DC, Dv, replace=False)):
+            WUV[h, c, d] = rng.choice([-1.0, 1.0])
+    q_pos = np.sort(rng.choice(T, rows, replace=False)).astype(np.int32)
+    idx = np.full((rows, 20), -1, np.int32)
+    for r in range(rows):
+        m = min(20, q_pos[r] + 1)
+        idx[r, :m] = np.sort(rng.choice(q_pos[r] + 1, m, replace=False))
+    scale = 1.0 / math.sqrt(Dn + Dr)
+    # expanded operands
+    q_exp = _bf16(np.concatenate([qn, qr], axis=-1))
+    kn = _bf16(np.einsum("jc,hcd->hjd", lat, WUK)[None])
+    kr = _bf16(rope[None])
+    v = _bf16(np.einsum("jc,hcd->hjd", lat, WUV)[None])
+    # absorbed operands: one latent row [c | rope] per position, q_abs = [qn W_UK^T | qr]
+    q_abs = _bf16(np.concatenate([np.einsum("rhd,hcd->rhc", qn, WUK), qr], axis=-1))
+    kv = _bf16(np.concatenate([lat, rope], axis=-1).reshape(1, T, DC + Dr))
+    pt = np.zeros((1, 1), np.int32)
+    for use_idx in (False, True):
+        if use_idx:
+            o_abs, lse_abs = oracle_lib.sparse_mla(q_abs, kv, pt, T, q_pos, 1, rows, idx, DC + Dr, DC, 0, scale)
+        else:
+            o_abs, lse_abs = oracle_lib.dense_mla(q_abs, kv, pt, T, q_pos, 1, rows, DC + Dr, DC, 0, scale)
+        o_exp, lse_exp = oracle_lib.mha(q_exp, kn, kr, v, q_pos, 1, rows, idx if use_idx else None, scale)
+        np.testing.assert_allclose(o_exp, np.einsum("rhc,hcd->rhd", o_abs.astype(np.float64), WUV),
+                                   rtol=1e-6, atol=1e-6)
+        np.testing.assert_allclose(lse_exp, lse_abs, rtol=1e-6, atol=1e-6)
+
+
+def test_mha_full_index_set_equals_dense_bitwise(oracle_lib):
+    q, kn, kr, v, q_pos = _mha_case(seed=13)
+    rows = q.shape[0]
+    n_seq = kn.shape[0]
+    T = kn.shape[2]
+    idx = np.full((rows, T + 3), -1, np.int32)
+    for r in range(rows):
+        idx[r, :q_pos[r] + 1] = np.arange(q_pos[r], -1, -1)      # every visible position, reversed
+        idx[r, q_pos[r] + 1: q_pos[r] + 3] = 0                    # repeats count once
+    dense = oracle_lib.mha(q, kn, kr, v, q_pos, n_seq, rows // n_seq, None, 0.2)
+    full = oracle_lib.mha(q, kn, kr, v, q_pos, n_seq, rows // n_seq, idx, 0.2)
+    assert np.array_equal(dense[0], full[0]) and np.array_equal(dense[1], full[1])
+
+
+def test_mha_single_position_and_empty_set(oracle_lib):
+    q, kn, kr, v, q_pos = _mha_case(seed=17, n_seq=1, q_per_seq=4)
+    rows = q.shape[0]
+    idx = np.full((rows, 3), -1, np.int32)
+    idx[:, 0] = q_pos // 2
+    idx[:, 1] = q_pos + 1                   # invisible: ignored
+    out, lse = oracle_lib.mha(q, kn, kr, v, q_pos, 1, rows, idx, 0.5)
+    for r in range(rows):
+        np.testing.assert_array_equal(out[r], _dec_bf16(v[0, :, q_pos[r] // 2]).numpy().astype(np.float32))
+    idx[:] = -1
+    out, lse = oracle_lib.mha(q, kn, kr, v, q_pos, 1, rows, idx, 0.5)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
