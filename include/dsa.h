@@ -73,7 +73,9 @@ enum {
   DSA_PATH_TOPK_RADIX_STAGED = 13,    /* longer rows: per-chunk candidates, then a merge (workspace) */
   DSA_PATH_MLA_GENERIC = 20,          /* any shape: one wave per (row, head), VALU */
   DSA_PATH_MLA_MFMA = 21,             /* H=128, Dqk=576, Dv=512: bf16 MFMA, one pass */
-  DSA_PATH_MLA_MFMA_SPLIT = 22        /* as 21, key set split over workgroups + combine */
+  DSA_PATH_MLA_MFMA_SPLIT = 22,       /* as 21, key set split over workgroups + combine */
+  DSA_PATH_MHA_MFMA = 30,             /* expanded attention, dense causal: bf16 MFMA */
+  DSA_PATH_MHA_MFMA_MASKED = 31       /* as 30, restricted to the index sets (bitmap in ws) */
 };
 
 const char* dsa_status_string(dsa_status_t status);
@@ -176,6 +178,39 @@ dsa_status_t dsa_dense_mla_prefill(const uint16_t* q, const uint16_t* kv_cache,
                                    int max_ctx, int H, int Dqk, int Dv, int kv_dim, int v_col0,
                                    float sm_scale, uint16_t* out, float* lse, void* ws,
                                    size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * dsa_expanded_mha_prefill -- expanded multi-head attention, the dense fallback for short prefill
+ * ([Handbook] "稀疏注意力：NSA 与 DSA": the cost model's expanded pair, per head a query/key of
+ * 128 + 64 (rope) dims and a 128-dim value, about 3.4x cheaper per (query, key) pair than the
+ * absorbed form; short prefill runs it, and V3.2 emulates DSA in a masked MHA mode). With the
+ * per-head up-projections of the latent row c_j applied beforehand (k_nope = c W_UK, v = c W_UV),
+ * it computes the same attention as the absorbed MLA above, output projected by W_UV.
+ * For row r (sequence s = r / q_per_seq, position t = q_pos[r]) and head h:
+ *     K_hj = [k_nope[s, h, j, :] | k_rope[s, j, :]]      (the rope key is shared by all heads)
+ *     l_j  = sm_scale * q[r, h, :] . K_hj,   j in S
+ *     out[r, h, :] = sum_{j in S} softmax(l)_j v[s, h, j, :];  lse[r, h] = log sum exp(l_j)
+ * with S = {0..t} when idx is NULL (dense causal), else the positions in [0, t] that idx[r, 0..k-1]
+ * lists ([DSA-blog] "Sparse Attention": M = 0 on S_t), as a set (the masked MHA mode: every
+ * pair is computed, then masked). An empty S gives out = 0, lse = -inf.
+ *   q      [rows, H, 192] bf16 bits (128 nope dims, then 64 rope dims), 16-byte aligned
+ *   k_nope [n_seq, H, max_ctx, 128] bf16 bits (head-major per sequence), 16-byte aligned
+ *   k_rope [n_seq, max_ctx, 64] bf16 bits, 16-byte aligned
+ *   v      [n_seq, H, max_ctx, 128] bf16 bits, 16-byte aligned
+ *   q_pos  [rows] int32, each in [0, max_ctx) (larger values see only the first max_ctx positions)
+ *   idx    [rows, ld_idx] int32 or NULL; k entries per row
+ *   out    [rows, H, 128] bf16 bits out (fp32 accumulation, one rounding); lse [rows, H] f32 or NULL
+ *   ws     with idx: at least dsa_expanded_mha_workspace_size(rows, max_ctx, k) bytes, 4-byte
+ *          aligned (one bit per (row, position), rebuilt by every call); else unused
+ * Softmax in fp32 with the probabilities rounded to bf16 for the value product. Shapes other than
+ * (128, 64, 128) or sm_scale <= 0 return DSA_ERR_UNSUPPORTED; max_ctx is limited to 524288.
+ * ------------------------------------------------------------------------------------------- */
+size_t dsa_expanded_mha_workspace_size(int rows, int max_ctx, int k);
+dsa_status_t dsa_expanded_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_rope,
+                                      const uint16_t* v, int max_ctx, const int32_t* q_pos, int n_seq,
+                                      int q_per_seq, const int32_t* idx, int64_t ld_idx, int k, int H,
+                                      int Dn, int Dr, int Dv, float sm_scale, uint16_t* out, float* lse,
+                                      void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -228,4 +228,39 @@ dsa_status_t dsa_dense_mla_prefill(const uint16_t* q, const uint16_t* kv_cache,
   return s == DSA_OK ? ok(DSA_PATH_MLA_MFMA) : s;
 }
 
+size_t dsa_expanded_mha_workspace_size(int rows, int max_ctx, int k) {
+  return k > 0 ? dsa::mha_ws_bytes(rows, max_ctx, true) : 0;
+}
+
+dsa_status_t dsa_expanded_mha_prefill(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_rope,
+                                      const uint16_t* v, int max_ctx, const int32_t* q_pos, int n_seq,
+                                      int q_per_seq, const int32_t* idx, int64_t ld_idx, int k, int H, int Dn,
+                                      int Dr, int Dv, float sm_scale, uint16_t* out, float* lse, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  REQUIRE(n_seq >= 0 && q_per_seq >= 1, "need n_seq >= 0 and q_per_seq >= 1");
+  if (n_seq == 0) return ok(DSA_PATH_NONE);
+  REQUIRE(H >= 1, "H must be >= 1 (got %d)", H);
+  REQUIRE(max_ctx >= 1 && max_ctx <= (1 << 19), "max_ctx must be in [1, 524288] (got %d)", max_ctx);
+  REQUIRE((int64_t)n_seq * q_per_seq < ((int64_t)1 << 31), "too many rows");
+  REQUIRE(q && k_nope && k_rope && v && q_pos && out, "a required pointer is NULL");
+  REQUIRE(!misaligned(q) && !misaligned(k_nope) && !misaligned(k_rope) && !misaligned(v) && !misaligned(out),
+          "q, k_nope, k_rope, v and out must be 16-byte aligned");
+  if (Dn != 128 || Dr != 64 || Dv != 128 || !(sm_scale > 0.f))
+    return fail(DSA_ERR_UNSUPPORTED, "expanded attention runs Dn=128, Dr=64, Dv=128 with sm_scale > 0 "
+                                     "(got %d, %d, %d, %g)", Dn, Dr, Dv, (double)sm_scale);
+  const int rows = n_seq * q_per_seq;
+  if (idx) {
+    REQUIRE(k >= 1 && ld_idx >= k, "need k >= 1 and ld_idx >= k with an index set (got %d, %lld)", k,
+            (long long)ld_idx);
+    const size_t need = dsa::mha_ws_bytes(rows, max_ctx, true);
+    if (!ws || ws_bytes < need)
+      return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    REQUIRE(((uintptr_t)ws & 3u) == 0, "ws must be 4-byte aligned");
+  }
+  dsa_status_t s = hip_status(dsa::launch_mha(q, k_nope, k_rope, v, max_ctx, q_pos, n_seq, q_per_seq, idx, ld_idx, k,
+                                              H, max_ctx, sm_scale, out, lse, ws, (hipStream_t)stream),
+                              "mha launch");
+  return s == DSA_OK ? ok(idx ? DSA_PATH_MHA_MFMA_MASKED : DSA_PATH_MHA_MFMA) : s;
+}
+
 }  // extern "C"

@@ -114,4 +114,11 @@ hipError_t launch_mla_mfma(const AttnArgs& a, int splits, void* ws, hipStream_t 
 size_t mla_mfma_ws_bytes(int rows, int splits);
 int mla_mfma_pick_splits(int rows, int k);
 
+// Expanded multi-head attention (Dn=128, Dr=64, Dv=128). idx NULL: dense causal; else the index
+// sets as a bitmap in ws (mha_ws_bytes).
+size_t mha_ws_bytes(int rows, int max_ctx, bool has_idx);
+hipError_t launch_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_rope, const uint16_t* v,
+                      int64_t ld_kv, const int32_t* q_pos, int n_seq, int q_per_seq, const int32_t* idx,
+                      int64_t ld_idx, int k, int H, int max_ctx, float sm_scale, uint16_t* out, float* lse,
+                      void* ws, hipStream_t stream);
 }  // namespace dsa

@@ -19,6 +19,7 @@ DSA_E4M3, DSA_F32 = 0, 1
 PATHS = {
     0: "none", 1: "indexer_generic", 2: "indexer_scan_mfma", 3: "indexer_prefill_mfma",
     10: "topk_copy", 11: "topk_radix", 12: "topk_radix_reg", 13: "topk_radix_staged", 20: "mla_generic", 21: "mla_mfma", 22: "mla_mfma_split",
+    30: "mha_mfma", 31: "mha_mfma_masked",
 }
 
 EXPORTS = [
@@ -26,6 +27,7 @@ EXPORTS = [
     "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk",
     "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
     "dsa_dense_mla_workspace_size", "dsa_dense_mla_prefill",
+    "dsa_expanded_mha_workspace_size", "dsa_expanded_mha_prefill",
 ]
 
 
@@ -77,6 +79,11 @@ def load():
     lib.dsa_dense_mla_prefill.restype = i32
     lib.dsa_dense_mla_prefill.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                           f32, vp, vp, vp, sz, vp]
+    lib.dsa_expanded_mha_workspace_size.restype = sz
+    lib.dsa_expanded_mha_workspace_size.argtypes = [i32, i32, i32]
+    lib.dsa_expanded_mha_prefill.restype = i32
+    lib.dsa_expanded_mha_prefill.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, i64, i32, i32, i32, i32, i32,
+                                             f32, vp, vp, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -217,4 +224,46 @@ def dense_mla_prefill(q, kv_cache, page_table, q_pos, n_seq, q_per_seq, max_ctx,
                                       kv_cache.shape[2], v_col0, float(sm_scale), _p(out), _p(lse), None, 0,
                                       _stream(stream))
     _check("dsa_dense_mla_prefill", st)
+    return out
+
+
+def expanded_mha_workspace_size(rows, max_ctx, k) -> int:
+    return int(load().dsa_expanded_mha_workspace_size(rows, max_ctx, k))
+
+
+def expanded_mha_prefill(q, k_nope, k_rope, v, q_pos, n_seq, q_per_seq, sm_scale, idx=None, out=None, lse=None,
+                         ws=None, stream=None):
+    """Expanded multi-head attention (the dense fallback for short prefill), dense causal, or over
+    the idx sets when idx is given (the masked MHA mode). q [rows, H, 192] bf16; k_nope
+    [n_seq, H, max_ctx, 128] bf16; k_rope [n_seq, max_ctx, 64] bf16; v [n_seq, H, max_ctx, 128] bf16;
+    q_pos [rows] i32; idx [rows, k] i32 or None. Returns out [rows, H, 128] bf16."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_nope, "k_nope", torch.bfloat16, 4)
+    _need(k_rope, "k_rope", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(q_pos, "q_pos", torch.int32, 1)
+    rows, H, Dq = q.shape
+    max_ctx = k_nope.shape[2]
+    if (k_nope.shape[0] != n_seq or v.shape[0] != n_seq or k_rope.shape[0] != n_seq or k_nope.shape[1] != H
+            or v.shape[1] != H or v.shape[2] != max_ctx or k_rope.shape[1] != max_ctx):
+        raise ValueError("inconsistent expanded attention shapes")
+    if rows != n_seq * q_per_seq or q_pos.numel() != rows:
+        raise ValueError("rows must equal n_seq * q_per_seq")
+    Dn, Dr, Dv = k_nope.shape[3], k_rope.shape[2], v.shape[3]
+    if out is None:
+        out = torch.empty(rows, H, Dv, dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, 3)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2)
+    k, ld_idx = 0, 0
+    if idx is not None:
+        _need(idx, "idx", torch.int32, 2)
+        k, ld_idx = idx.shape[1], idx.shape[1]
+        need = expanded_mha_workspace_size(rows, max_ctx, k)
+        if ws is None and need:
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = load().dsa_expanded_mha_prefill(_p(q), _p(k_nope), _p(k_rope), _p(v), max_ctx, _p(q_pos), n_seq, q_per_seq,
+                                         _p(idx), ld_idx, k, H, Dn, Dr, Dv, float(sm_scale), _p(out), _p(lse),
+                                         _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check("dsa_expanded_mha_prefill", st)
     return out
