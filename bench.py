@@ -389,15 +389,20 @@ def run_prefill_bench(args):
 
 
 def run_crossover(args):
-    """Dense causal fallback vs sparse prefill (indexer + top-k + sparse attention) for one
-    sequence of T queries over a T-token prefix."""
+    """Dense fallbacks vs sparse prefill (indexer + top-k + sparse attention) for one sequence of
+    T queries over a T-token prefix. Two dense fallbacks: the absorbed form (the same attention
+    kernel over every visible position) and the expanded multi-head form (per head 192-dim
+    query/key and 128-dim value), dense causal and in the masked mode over the same index sets.
+    The expanded form also needs its per-head keys and values up-projected from the latent rows
+    (two plain GEMMs, timed here with torch.matmul as `expand_gemm_ms`)."""
     import torch
 
     import workloads
     from sparse_attention_06_amd import dsa
 
+    sizes = [int(x) for x in args.crossover_T.split(",")]
     res = []
-    for T in (1024, 2048, 4096, 8192):
+    for T in sizes:
         w = workloads.make_prefill(T)
         d = {
             "iq": torch.from_numpy(w.iq).cuda(), "iw": torch.from_numpy(w.iw).cuda(),
@@ -406,20 +411,45 @@ def run_crossover(args):
             "kv": torch.from_numpy(w.kv.view(np.int16)).view(torch.bfloat16).cuda(),
             "pt": torch.from_numpy(w.page_table).cuda(), "qp": torch.from_numpy(w.q_pos).cuda(),
         }
+        del w.q, w.kv
         scores = torch.empty(T, T, dtype=torch.float32, device="cuda")
-        idx = torch.empty(T, w.topk, dtype=torch.int32, device="cuda")
+        idx = torch.empty(T, 2048, dtype=torch.int32, device="cuda")
         out = torch.empty(T, 128, 512, dtype=torch.bfloat16, device="cuda")
+        # expanded operands (seeded, N(0,1) rounded to bf16) and the up-projection GEMM operands
+        g = torch.Generator(device="cuda")
+        g.manual_seed(0xD5A0 + T)
+        xq = torch.randn(T, 128, 192, generator=g, device="cuda").to(torch.bfloat16)
+        xkn = torch.randn(1, 128, T, 128, generator=g, device="cuda").to(torch.bfloat16)
+        xkr = torch.randn(1, T, 64, generator=g, device="cuda").to(torch.bfloat16)
+        xv = torch.randn(1, 128, T, 128, generator=g, device="cuda").to(torch.bfloat16)
+        xout = torch.empty(T, 128, 128, dtype=torch.bfloat16, device="cuda")
+        mws = torch.empty(dsa.expanded_mha_workspace_size(T, T, 2048), dtype=torch.uint8, device="cuda")
+        lat = d["kv"].view(-1, 576)[:T, :512]
+        wuk = (torch.randn(512, 128 * 128, generator=g, device="cuda") / 512 ** 0.5).to(torch.bfloat16)
+        kexp = torch.empty(T, 128 * 128, dtype=torch.bfloat16, device="cuda")
+        scale = 1 / 192 ** 0.5
 
         def sparse():
             dsa.indexer_scores(d["iq"], d["iw"], d["ik"], d["iks"], d["pt"], d["qp"], 1, T, T, scores=scores)
-            dsa.topk(scores, d["qp"], T, w.topk, idx=idx)
-            dsa.sparse_mla_prefill(d["q"], d["kv"], d["pt"], d["qp"], 1, T, idx, 576, 512, 0, w.sm_scale, out=out)
+            dsa.topk(scores, d["qp"], T, 2048, idx=idx)
+            dsa.sparse_mla_prefill(d["q"], d["kv"], d["pt"], d["qp"], 1, T, idx, 576, 512, 0, scale, out=out)
 
         def dense():
-            dsa.dense_mla_prefill(d["q"], d["kv"], d["pt"], d["qp"], 1, T, T, 576, 512, 0, w.sm_scale, out=out)
+            dsa.dense_mla_prefill(d["q"], d["kv"], d["pt"], d["qp"], 1, T, T, 576, 512, 0, scale, out=out)
+
+        def expanded():
+            dsa.expanded_mha_prefill(xq, xkn, xkr, xv, d["qp"], 1, T, scale, out=xout)
+
+        def masked():
+            dsa.expanded_mha_prefill(xq, xkn, xkr, xv, d["qp"], 1, T, scale, idx=idx, out=xout, ws=mws)
+
+        def gemm():  # k_nope and v of all heads from the latent rows: two [T,512] x [512,16384]
+            torch.matmul(lat, wuk, out=kexp)
+            torch.matmul(lat, wuk, out=kexp)
 
         row = {"T": T}
-        for name, fn in (("sparse_ms", sparse), ("dense_ms", dense)):
+        for name, fn in (("sparse_ms", sparse), ("dense_absorbed_ms", dense), ("dense_expanded_ms", expanded),
+                         ("masked_expanded_ms", masked), ("expand_gemm_ms", gemm)):
             for _ in range(2):
                 fn()
             torch.cuda.synchronize()
@@ -430,13 +460,17 @@ def run_crossover(args):
             e1.record()
             torch.cuda.synchronize()
             row[name] = e0.elapsed_time(e1) / args.steps
-        row["dense_wins"] = row["dense_ms"] < row["sparse_ms"]
+        pairs = T * (T + 1) / 2
+        row["expanded_TFLOPs"] = pairs * 128 * (2 * 192 + 2 * 128) / (row["dense_expanded_ms"] * 1e-3) / 1e12
+        row["absorbed_wins"] = row["dense_absorbed_ms"] < row["sparse_ms"]
+        row["expanded_wins"] = row["dense_expanded_ms"] + row["expand_gemm_ms"] < row["sparse_ms"]
         log(f"[crossover] {row}")
         res.append(row)
-        del d, scores, idx, out
+        del d, scores, idx, out, xq, xkn, xkr, xv, xout, mws, wuk, kexp
         torch.cuda.empty_cache()
-    cross = next((r["T"] for r in res if not r["dense_wins"]), None)
-    print(json.dumps({"crossover": res, "sparse_wins_from_T": cross}), flush=True)
+    first = lambda key: next((r["T"] for r in res if not r[key]), None)  # noqa: E731
+    print(json.dumps({"crossover": res, "sparse_beats_absorbed_dense_from_T": first("absorbed_wins"),
+                      "sparse_beats_expanded_dense_from_T": first("expanded_wins")}), flush=True)
 
 
 def run_copy_calibration(args):
@@ -465,6 +499,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager steps (for counter-collection runs)")
     ap.add_argument("--crossover", action="store_true")
+    ap.add_argument("--crossover-T", default="1024,2048,4096,8192,16384",
+                    help="prefix lengths of the crossover sweep")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
