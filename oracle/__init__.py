@@ -14,4 +14,8 @@ from .ref import (  # noqa: F401
     sparse_mla,
     dense_mla,
     mha,
+    e4m3_from_float,
+    e4m3_quantize,
+    indexer_cache_write,
+    latent_cache_write,
 )

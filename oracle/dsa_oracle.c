@@ -310,3 +310,86 @@ int oracle_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_rope
   free(acc);
   return 0;
 }
+
+/* ---- upstream: FP8 quantisation and the paged cache writes ---------------------------- */
+
+/* OCP 8-bit floating point, E4M3FN, from a float: round to nearest, ties to even, saturating
+ * to +-448 (the largest finite value; the format has no infinity). Finite input only. Worked
+ * from the format's definition: subnormals are multiples of 2^-9 below 2^-6; a normal value
+ * 2^e * (1 + m/8) has exponent field e + 7 and mantissa field m. */
+uint8_t oracle_e4m3_from_float(float x) {
+  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  double a = fabs((double)x);
+  if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+  if (a < ldexp(1.0, -6)) {
+    /* subnormal range: the code is the count of 2^-9 quanta (8 quanta = the smallest normal,
+     * whose code is also 8) */
+    return (uint8_t)(sign | (uint8_t)rint(a * 512.0));
+  }
+  int e2;
+  frexp(a, &e2);          /* a = f * 2^e2, f in [0.5, 1): the binade is 2^(e2-1) */
+  const int e = e2 - 1;   /* -6 .. 8 */
+  double n = rint(ldexp(a, 3 - e));  /* a / 2^(e-3), in [8, 16] after rounding */
+  int ee = e;
+  if (n >= 16.0) { n = 8.0; ++ee; }
+  const int field = ee + 7;
+  if (field > 15 || (field == 15 && n - 8.0 > 6.0)) return (uint8_t)(sign | 0x7E);
+  return (uint8_t)(sign | (uint8_t)(field << 3) | (uint8_t)(n - 8.0));
+}
+
+/* The indexer query in FP8 without a scale (no query scale is given on the pages; the query
+ * is quantised as is). */
+int oracle_e4m3_quantize(const float* x, int64_t n, uint8_t* out) {
+  if (n < 0) return 1;
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_from_float(x[i]);
+  return 0;
+}
+
+/* The Indexer Key Cache write ([DSA-blog] "Lightning Indexer": each position's indexer key comes
+ * from its own hidden state and is cached; [Handbook] "对推理引擎的新要求": the indexer keys are
+ * paged like the latent cache, IDX_D + 4 bytes per token). Per token: the scale
+ * s = max_c |k_c| / 448 in float, the codes E4M3(k_c / s) with the quotient in float (all zero
+ * when s = 0), written at the token's physical row. Tokens whose position has no valid page are
+ * skipped (nonzero return: the count of skipped tokens is in *skipped). fmt: ORACLE_F32 or
+ * ORACLE_BF16 input rows [n_tok, Di]. */
+int oracle_indexer_cache_write(const void* k, int fmt, int Di, const int32_t* seq, const int32_t* pos,
+                               int n_tok, const int32_t* page_table, int64_t ld_pt, int page_size,
+                               int num_pages, uint8_t* k_cache, float* k_scale, int* skipped) {
+  if (Di < 1 || n_tok < 0 || page_size < 1 || (fmt != ORACLE_F32 && fmt != ORACLE_BF16)) return 1;
+  int skip = 0;
+  float* row = (float*)malloc(sizeof(float) * (size_t)Di);
+  if (!row) return 2;
+  for (int t = 0; t < n_tok; ++t) {
+    const int64_t r = phys_row(page_table, ld_pt, page_size, num_pages, seq[t], pos[t]);
+    if (r < 0) { ++skip; continue; }
+    float mx = 0.0f;
+    for (int c = 0; c < Di; ++c) {
+      row[c] = fmt == ORACLE_F32 ? ((const float*)k)[(int64_t)t * Di + c]
+                                 : (float)oracle_bf16_to_double(((const uint16_t*)k)[(int64_t)t * Di + c]);
+      const float v = fabsf(row[c]);
+      if (v > mx) mx = v;
+    }
+    const float s = mx / 448.0f;
+    for (int c = 0; c < Di; ++c) k_cache[r * Di + c] = s > 0.0f ? oracle_e4m3_from_float(row[c] / s) : 0;
+    k_scale[r] = s;
+  }
+  free(row);
+  if (skipped) *skipped = skip;
+  return 0;
+}
+
+/* The latent cache write: each token's row (kv_dim bf16: the 512 latent dims, then the 64 rope
+ * dims) copied to its physical row; tokens without a valid page are skipped. */
+int oracle_latent_cache_write(const uint16_t* rows, int kv_dim, const int32_t* seq, const int32_t* pos,
+                              int n_tok, const int32_t* page_table, int64_t ld_pt, int page_size,
+                              int num_pages, uint16_t* kv_cache, int* skipped) {
+  if (kv_dim < 1 || n_tok < 0 || page_size < 1) return 1;
+  int skip = 0;
+  for (int t = 0; t < n_tok; ++t) {
+    const int64_t r = phys_row(page_table, ld_pt, page_size, num_pages, seq[t], pos[t]);
+    if (r < 0) { ++skip; continue; }
+    for (int c = 0; c < kv_dim; ++c) kv_cache[r * kv_dim + c] = rows[(int64_t)t * kv_dim + c];
+  }
+  if (skipped) *skipped = skip;
+  return 0;
+}

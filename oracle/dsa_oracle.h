@@ -31,6 +31,7 @@ extern "C" {
 /* Input element formats of the indexer operands. */
 #define ORACLE_E4M3 0 /* OCP FP8 E4M3FN bytes */
 #define ORACLE_F32 1  /* IEEE binary32 */
+#define ORACLE_BF16 2 /* bfloat16 bits (the cache-write inputs only) */
 
 /* Exact decoders (OCP 8-bit floating point spec, E4M3FN; bfloat16 = top half of binary32). */
 double oracle_e4m3_to_double(uint8_t code);
@@ -90,6 +91,24 @@ int oracle_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_rope
                int64_t ld_kv, const int32_t* q_pos, int n_seq, int q_per_seq, const int32_t* idx,
                int64_t ld_idx, int k, int H, int Dn, int Dr, int Dv, double sm_scale, float* out,
                float* lse, int row_begin, int row_end);
+
+/* Upstream of the indexer ([DSA-blog] "Lightning Indexer": keys from each position's hidden
+ * state, cached in their own cache; [Handbook] "对推理引擎的新要求": both caches paged, the indexer
+ * key cache holding FP8 codes plus a float scale per token):
+ *   oracle_e4m3_from_float      float -> E4M3FN, round to nearest even, saturating to +-448
+ *   oracle_e4m3_quantize        elementwise, no scale (the indexer query)
+ *   oracle_indexer_cache_write  per token s = max|k| / 448 (float), codes E4M3(k / s) (float
+ *                               quotient; zero when s = 0), written at the token's physical row
+ *   oracle_latent_cache_write   each token's latent row copied to its physical row
+ * Tokens whose (seq, pos) has no valid page are skipped and counted in *skipped. */
+uint8_t oracle_e4m3_from_float(float x);
+int oracle_e4m3_quantize(const float* x, int64_t n, uint8_t* out);
+int oracle_indexer_cache_write(const void* k, int fmt, int Di, const int32_t* seq, const int32_t* pos,
+                               int n_tok, const int32_t* page_table, int64_t ld_pt, int page_size,
+                               int num_pages, uint8_t* k_cache, float* k_scale, int* skipped);
+int oracle_latent_cache_write(const uint16_t* rows, int kv_dim, const int32_t* seq, const int32_t* pos,
+                              int n_tok, const int32_t* page_table, int64_t ld_pt, int page_size,
+                              int num_pages, uint16_t* kv_cache, int* skipped);
 
 #ifdef __cplusplus
 }

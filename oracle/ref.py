@@ -18,6 +18,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 E4M3 = 0
 F32 = 1
+BF16 = 2
 
 _lib = None
 _lock = threading.Lock()
@@ -59,6 +60,14 @@ def _load():
             lib.oracle_dense_mla.restype = i32
             lib.oracle_dense_mla.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, i32, i32, i32, i32,
                                              i32, i32, dbl, vp, vp, i32, i32]
+            lib.oracle_e4m3_from_float.restype = ctypes.c_uint8
+            lib.oracle_e4m3_from_float.argtypes = [ctypes.c_float]
+            lib.oracle_e4m3_quantize.restype = i32
+            lib.oracle_e4m3_quantize.argtypes = [vp, i64, vp]
+            lib.oracle_indexer_cache_write.restype = i32
+            lib.oracle_indexer_cache_write.argtypes = [vp, i32, i32, vp, vp, i32, vp, i64, i32, i32, vp, vp, vp]
+            lib.oracle_latent_cache_write.restype = i32
+            lib.oracle_latent_cache_write.argtypes = [vp, i32, vp, vp, i32, vp, i64, i32, i32, vp, vp]
             lib.oracle_mha.restype = i32
             lib.oracle_mha.argtypes = [vp, vp, vp, vp, i64, vp, i32, i32, vp, i64, i32, i32, i32, i32, i32,
                                        dbl, vp, vp, i32, i32]
@@ -227,3 +236,46 @@ def mha(q, k_nope, k_rope, v, q_pos, n_seq, q_per_seq, idx, sm_scale, threads=1,
 
     _run_rows(fn, nrows, threads, rows)
     return out, lse
+
+
+def e4m3_from_float(x: float) -> int:
+    return int(_load().oracle_e4m3_from_float(float(x)))
+
+
+def e4m3_quantize(x):
+    """float32 array -> E4M3 codes (uint8), no scale."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    if _load().oracle_e4m3_quantize(_ptr(x), x.size, _ptr(out)) != 0:
+        raise ValueError("oracle call failed")
+    return out
+
+
+def indexer_cache_write(k, seq, pos, page_table, page_size, k_cache, k_scale):
+    """k: float32 [n_tok, Di] or uint16 bf16 bits [n_tok, Di]; writes into k_cache (uint8
+    [P, page, Di]) and k_scale (float32 [P, page]) in place; returns the skipped-token count."""
+    fmt = F32 if k.dtype == np.float32 else BF16
+    k = _c(k, np.float32 if fmt == F32 else np.uint16)
+    seq, pos, pt = _c(seq, np.int32), _c(pos, np.int32), _c(page_table, np.int32)
+    assert k_cache.flags.c_contiguous and k_scale.flags.c_contiguous
+    skipped = ctypes.c_int(0)
+    rc = _load().oracle_indexer_cache_write(_ptr(k), fmt, k.shape[1], _ptr(seq), _ptr(pos), k.shape[0], _ptr(pt),
+                                            pt.shape[1], page_size, k_cache.shape[0], _ptr(k_cache), _ptr(k_scale),
+                                            ctypes.byref(skipped))
+    if rc != 0:
+        raise ValueError(f"oracle call failed with code {rc}")
+    return skipped.value
+
+
+def latent_cache_write(rows, seq, pos, page_table, page_size, kv_cache):
+    """rows: uint16 [n_tok, kv_dim]; writes into kv_cache (uint16 [P, page, kv_dim]) in place."""
+    rows = _c(rows, np.uint16)
+    seq, pos, pt = _c(seq, np.int32), _c(pos, np.int32), _c(page_table, np.int32)
+    assert kv_cache.flags.c_contiguous
+    skipped = ctypes.c_int(0)
+    rc = _load().oracle_latent_cache_write(_ptr(rows), rows.shape[1], _ptr(seq), _ptr(pos), rows.shape[0], _ptr(pt),
+                                           pt.shape[1], page_size, kv_cache.shape[0], _ptr(kv_cache),
+                                           ctypes.byref(skipped))
+    if rc != 0:
+        raise ValueError(f"oracle call failed with code {rc}")
+    return skipped.value

@@ -357,3 +357,31 @@ def test_tiny_workload_end_to_end(oracle_lib):
                                  torch.from_numpy(ref_idx).cuda(), w.Dqk, w.Dv, w.v_col0, w.sm_scale)
     ref, _ = _attn_ref(w, ref_idx)
     check_attn(out.float().cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------ index-set reuse across layers
+
+
+def test_cross_layer_index_reuse(oracle_lib):
+    # [Handbook] "对推理引擎的新要求": some layers reuse the previous layer's top-k instead of running
+    # their own indexer. One index set (indexer + top-k of layer 1, emitted in ascending order) feeds
+    # the attention of layer 1 and of layer 2 (its own queries and latent cache, same pages).
+    _say("case: cross-layer index reuse")
+    q_pos = [4100, 4101, 900, 901]
+    w1 = workloads.make_random(2, 2, q_pos, 4102, seed=71, permute_pages=True)
+    w2 = workloads.make_random(2, 2, q_pos, 4102, seed=72, permute_pages=True)
+    w2.page_table = w1.page_table  # the same token positions: both layers' caches share the page table
+    d1, d2 = gpu_inputs(w1), gpu_inputs(w2)
+    scores = dsa.indexer_scores(d1["iq"], d1["iw"], d1["ik"], d1["iks"], d1["page_table"], d1["q_pos"], w1.n_seq,
+                                w1.q_per_seq, w1.max_ctx)
+    idx = dsa.topk(scores, d1["q_pos"], w1.max_ctx, w1.topk)
+    outs = [dsa.sparse_mla_decode(d["q"], d["kv"], d1["page_table"], d["q_pos"], w.n_seq, w.q_per_seq, idx, w.Dqk,
+                                  w.Dv, w.v_col0, w.sm_scale) for w, d in ((w1, d1), (w2, d2))]
+    torch.cuda.synchronize()
+    ref_s = _indexer_ref(w1)
+    ref_idx = oracle.topk(ref_s, w1.q_pos, w1.topk, threads=8)
+    idx_h = idx.cpu().numpy()
+    check_topk_sets(idx_h, ref_idx, ref_s, w1.q_pos, w1.topk)   # includes: ascending, -1 padded
+    for w, out in ((w1, outs[0]), (w2, outs[1])):
+        ref, _ = _attn_ref(w, idx_h)
+        check_attn(out.float().cpu().numpy(), ref)

@@ -513,3 +513,107 @@ def test_mha_single_position_and_empty_set(oracle_lib):
     idx[:] = -1
     out, lse = oracle_lib.mha(q, kn, kr, v, q_pos, 1, rows, idx, 0.5)
     assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+# ---------------------------------------------------------------- FP8 quantisation, cache writes
+
+
+def _e4m3_values():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    vals = codes.view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    return {c: float(vals[c]) for c in range(256) if not math.isnan(vals[c])}
+
+
+def test_e4m3_encode_round_trips_every_code(oracle_lib):
+    for c, v in _e4m3_values().items():
+        got = oracle_lib.e4m3_from_float(v)
+        if v == 0.0:   # +0 and -0 both decode to zero; the sign bit follows the input's sign
+            assert got == (0x80 if math.copysign(1, v) < 0 else 0x00)
+        else:
+            assert got == c, (hex(c), v, hex(got))
+
+
+def test_e4m3_encode_ties_to_even_and_saturates(oracle_lib):
+    vals = sorted((v, c) for c, v in _e4m3_values().items() if v > 0)
+    for (v0, c0), (v1, c1) in zip(vals, vals[1:]):
+        mid = np.float32((v0 + v1) / 2)           # exactly representable: one more mantissa bit
+        assert float(mid) == (v0 + v1) / 2
+        want = c0 if (c0 & 1) == 0 else c1
+        assert oracle_lib.e4m3_from_float(float(mid)) == want, (v0, v1)
+        assert oracle_lib.e4m3_from_float(-float(mid)) == (want | 0x80)
+        assert oracle_lib.e4m3_from_float(float(np.nextafter(mid, np.float32(0)))) == c0
+        assert oracle_lib.e4m3_from_float(float(np.nextafter(mid, np.float32(1e9)))) == c1
+    for big in (448.0, 448.0001, 463.9, 464.0, 480.0, 1e6, 3.0e38):
+        assert oracle_lib.e4m3_from_float(big) == 0x7E
+        assert oracle_lib.e4m3_from_float(-big) == 0xFE
+
+
+def test_e4m3_quantize_matches_torch_in_range(oracle_lib):
+    rng = np.random.default_rng(31)
+    mag = np.exp2(rng.uniform(-12, 8.8, 200000)).astype(np.float32)
+    x = np.where(rng.random(mag.size) < 0.5, -mag, mag).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    got = oracle_lib.e4m3_quantize(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_indexer_cache_write_matches_torch_quantiser_and_pages(oracle_lib):
+    # the per-token quantiser against an independent torch statement of it (s = max|k|/448 and
+    # k/s in float32, torch's E4M3 rounding), written through a permuted page table; rows of
+    # other positions stay untouched and a token without a valid page is skipped
+    rng = np.random.default_rng(33)
+    n_seq, pages, Di = 2, 3, 128
+    pt = rng.permutation(n_seq * pages + 1)[: n_seq * pages].astype(np.int32).reshape(n_seq, pages)
+    P = n_seq * pages + 1
+    n_tok = 50
+    seq = rng.integers(0, n_seq, n_tok).astype(np.int32)
+    pos = rng.choice(pages * 64, n_tok, replace=False).astype(np.int32)
+    k = (rng.standard_normal((n_tok, Di)) * np.exp2(rng.uniform(-8, 8, (n_tok, 1)))).astype(np.float32)
+    k[3] = 0.0                                        # a zero key: scale 0, codes 0
+    pos_bad = pos.copy()
+    pos_bad[7] = pages * 64 + 5                       # past the page table: skipped
+    cache = np.full((P, 64, Di), 0xAB, np.uint8)
+    scale = np.full((P, 64), -1.0, np.float32)
+    skipped = oracle_lib.indexer_cache_write(k, seq, pos_bad, pt, 64, cache, scale)
+    assert skipped == 1
+    kt = torch.from_numpy(k)
+    s = kt.abs().amax(dim=1) / 448.0
+    ref = torch.where(s[:, None] > 0, kt / torch.where(s > 0, s, torch.ones_like(s))[:, None], torch.zeros_like(kt))
+    ref8 = ref.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    written = set()
+    for t in range(n_tok):
+        if t == 7:
+            continue
+        r = pt[seq[t], pos[t] // 64] * 64 + pos[t] % 64
+        written.add(int(r))
+        np.testing.assert_array_equal(cache.reshape(-1, Di)[r], ref8[t])
+        assert scale.reshape(-1)[r] == s[t].item()
+    for r in range(P * 64):
+        if r not in written:
+            assert (cache.reshape(-1, Di)[r] == 0xAB).all() and scale.reshape(-1)[r] == -1.0
+    # bf16 input: the same as float input of the bf16 values
+    kb = workloads.bf16_bits(kt)
+    c2 = np.zeros_like(cache)
+    s2 = np.zeros_like(scale)
+    oracle_lib.indexer_cache_write(kb, seq, pos, pt, 64, c2, s2)
+    c3 = np.zeros_like(cache)
+    s3 = np.zeros_like(scale)
+    oracle_lib.indexer_cache_write(_dec_bf16(kb).to(torch.float32).numpy(), seq, pos, pt, 64, c3, s3)
+    np.testing.assert_array_equal(c2, c3)
+    np.testing.assert_array_equal(s2, s3)
+
+
+def test_latent_cache_write_places_rows(oracle_lib):
+    rng = np.random.default_rng(35)
+    pt = np.array([[2, 0], [1, 3]], np.int32)
+    rows = rng.integers(0, 65535, (6, 576)).astype(np.uint16)
+    seq = np.array([0, 0, 1, 1, 0, 1], np.int32)
+    pos = np.array([0, 70, 5, 127, 63, 200], np.int32)   # the last: no page -> skipped
+    cache = np.zeros((4, 64, 576), np.uint16)
+    assert oracle_lib.latent_cache_write(rows, seq, pos, pt, 64, cache) == 1
+    flat = cache.reshape(-1, 576)
+    for t in range(5):
+        r = pt[seq[t], pos[t] // 64] * 64 + pos[t] % 64
+        np.testing.assert_array_equal(flat[r], rows[t])
+    assert np.count_nonzero(flat.any(axis=1)) == 5
