@@ -52,9 +52,11 @@ static double elem(const void* base, int64_t i, int fmt) {
   return (double)((const float*)base)[i];
 }
 
-/* Physical row of position p of sequence s in a paged cache; -1 if the page id is invalid. */
+/* Physical row of position p of sequence s in a paged cache; -1 if p lies outside the sequence's
+ * page-table row or the page id is invalid. */
 static int64_t phys_row(const int32_t* page_table, int64_t ld_pt, int page_size, int num_pages,
                         int s, int64_t p) {
+  if (p < 0 || p / page_size >= ld_pt) return -1; /* outside the sequence's page table row */
   int32_t page = page_table[(int64_t)s * ld_pt + p / page_size];
   if (page < 0 || page >= num_pages) return -1;
   return (int64_t)page * page_size + p % page_size;
@@ -349,18 +351,18 @@ int oracle_e4m3_quantize(const float* x, int64_t n, uint8_t* out) {
  * from its own hidden state and is cached; [Handbook] "对推理引擎的新要求": the indexer keys are
  * paged like the latent cache, IDX_D + 4 bytes per token). Per token: the scale
  * s = max_c |k_c| / 448 in float, the codes E4M3(k_c / s) with the quotient in float (all zero
- * when s = 0), written at the token's physical row. Tokens whose position has no valid page are
- * skipped (nonzero return: the count of skipped tokens is in *skipped). fmt: ORACLE_F32 or
+ * when s = 0), written at the token's physical row. Tokens whose sequence is not in [0, n_seq) or
+ * whose position has no valid page are skipped (their count is put in *skipped). fmt: ORACLE_F32 or
  * ORACLE_BF16 input rows [n_tok, Di]. */
 int oracle_indexer_cache_write(const void* k, int fmt, int Di, const int32_t* seq, const int32_t* pos,
-                               int n_tok, const int32_t* page_table, int64_t ld_pt, int page_size,
+                               int n_tok, int n_seq, const int32_t* page_table, int64_t ld_pt, int page_size,
                                int num_pages, uint8_t* k_cache, float* k_scale, int* skipped) {
   if (Di < 1 || n_tok < 0 || page_size < 1 || (fmt != ORACLE_F32 && fmt != ORACLE_BF16)) return 1;
   int skip = 0;
   float* row = (float*)malloc(sizeof(float) * (size_t)Di);
   if (!row) return 2;
   for (int t = 0; t < n_tok; ++t) {
-    const int64_t r = phys_row(page_table, ld_pt, page_size, num_pages, seq[t], pos[t]);
+    const int64_t r = seq[t] >= 0 && seq[t] < n_seq ? phys_row(page_table, ld_pt, page_size, num_pages, seq[t], pos[t]) : -1;
     if (r < 0) { ++skip; continue; }
     float mx = 0.0f;
     for (int c = 0; c < Di; ++c) {
@@ -381,12 +383,12 @@ int oracle_indexer_cache_write(const void* k, int fmt, int Di, const int32_t* se
 /* The latent cache write: each token's row (kv_dim bf16: the 512 latent dims, then the 64 rope
  * dims) copied to its physical row; tokens without a valid page are skipped. */
 int oracle_latent_cache_write(const uint16_t* rows, int kv_dim, const int32_t* seq, const int32_t* pos,
-                              int n_tok, const int32_t* page_table, int64_t ld_pt, int page_size,
+                              int n_tok, int n_seq, const int32_t* page_table, int64_t ld_pt, int page_size,
                               int num_pages, uint16_t* kv_cache, int* skipped) {
   if (kv_dim < 1 || n_tok < 0 || page_size < 1) return 1;
   int skip = 0;
   for (int t = 0; t < n_tok; ++t) {
-    const int64_t r = phys_row(page_table, ld_pt, page_size, num_pages, seq[t], pos[t]);
+    const int64_t r = seq[t] >= 0 && seq[t] < n_seq ? phys_row(page_table, ld_pt, page_size, num_pages, seq[t], pos[t]) : -1;
     if (r < 0) { ++skip; continue; }
     for (int c = 0; c < kv_dim; ++c) kv_cache[r * kv_dim + c] = rows[(int64_t)t * kv_dim + c];
   }

@@ -100,14 +100,15 @@ int oracle_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_rope
  *   oracle_indexer_cache_write  per token s = max|k| / 448 (float), codes E4M3(k / s) (float
  *                               quotient; zero when s = 0), written at the token's physical row
  *   oracle_latent_cache_write   each token's latent row copied to its physical row
- * Tokens whose (seq, pos) has no valid page are skipped and counted in *skipped. */
+ * Tokens whose sequence is not in [0, n_seq) (page_table is [n_seq, ld_pt]) or whose position has
+ * no valid page are skipped and counted in *skipped. */
 uint8_t oracle_e4m3_from_float(float x);
 int oracle_e4m3_quantize(const float* x, int64_t n, uint8_t* out);
 int oracle_indexer_cache_write(const void* k, int fmt, int Di, const int32_t* seq, const int32_t* pos,
-                               int n_tok, const int32_t* page_table, int64_t ld_pt, int page_size,
+                               int n_tok, int n_seq, const int32_t* page_table, int64_t ld_pt, int page_size,
                                int num_pages, uint8_t* k_cache, float* k_scale, int* skipped);
 int oracle_latent_cache_write(const uint16_t* rows, int kv_dim, const int32_t* seq, const int32_t* pos,
-                              int n_tok, const int32_t* page_table, int64_t ld_pt, int page_size,
+                              int n_tok, int n_seq, const int32_t* page_table, int64_t ld_pt, int page_size,
                               int num_pages, uint16_t* kv_cache, int* skipped);
 
 #ifdef __cplusplus

@@ -65,9 +65,9 @@ def _load():
             lib.oracle_e4m3_quantize.restype = i32
             lib.oracle_e4m3_quantize.argtypes = [vp, i64, vp]
             lib.oracle_indexer_cache_write.restype = i32
-            lib.oracle_indexer_cache_write.argtypes = [vp, i32, i32, vp, vp, i32, vp, i64, i32, i32, vp, vp, vp]
+            lib.oracle_indexer_cache_write.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, i64, i32, i32, vp, vp, vp]
             lib.oracle_latent_cache_write.restype = i32
-            lib.oracle_latent_cache_write.argtypes = [vp, i32, vp, vp, i32, vp, i64, i32, i32, vp, vp]
+            lib.oracle_latent_cache_write.argtypes = [vp, i32, vp, vp, i32, i32, vp, i64, i32, i32, vp, vp]
             lib.oracle_mha.restype = i32
             lib.oracle_mha.argtypes = [vp, vp, vp, vp, i64, vp, i32, i32, vp, i64, i32, i32, i32, i32, i32,
                                        dbl, vp, vp, i32, i32]
@@ -259,7 +259,7 @@ def indexer_cache_write(k, seq, pos, page_table, page_size, k_cache, k_scale):
     seq, pos, pt = _c(seq, np.int32), _c(pos, np.int32), _c(page_table, np.int32)
     assert k_cache.flags.c_contiguous and k_scale.flags.c_contiguous
     skipped = ctypes.c_int(0)
-    rc = _load().oracle_indexer_cache_write(_ptr(k), fmt, k.shape[1], _ptr(seq), _ptr(pos), k.shape[0], _ptr(pt),
+    rc = _load().oracle_indexer_cache_write(_ptr(k), fmt, k.shape[1], _ptr(seq), _ptr(pos), k.shape[0], pt.shape[0], _ptr(pt),
                                             pt.shape[1], page_size, k_cache.shape[0], _ptr(k_cache), _ptr(k_scale),
                                             ctypes.byref(skipped))
     if rc != 0:
@@ -273,7 +273,7 @@ def latent_cache_write(rows, seq, pos, page_table, page_size, kv_cache):
     seq, pos, pt = _c(seq, np.int32), _c(pos, np.int32), _c(page_table, np.int32)
     assert kv_cache.flags.c_contiguous
     skipped = ctypes.c_int(0)
-    rc = _load().oracle_latent_cache_write(_ptr(rows), rows.shape[1], _ptr(seq), _ptr(pos), rows.shape[0], _ptr(pt),
+    rc = _load().oracle_latent_cache_write(_ptr(rows), rows.shape[1], _ptr(seq), _ptr(pos), rows.shape[0], pt.shape[0], _ptr(pt),
                                            pt.shape[1], page_size, kv_cache.shape[0], _ptr(kv_cache),
                                            ctypes.byref(skipped))
     if rc != 0:

@@ -607,11 +607,11 @@ def test_indexer_cache_write_matches_torch_quantiser_and_pages(oracle_lib):
 def test_latent_cache_write_places_rows(oracle_lib):
     rng = np.random.default_rng(35)
     pt = np.array([[2, 0], [1, 3]], np.int32)
-    rows = rng.integers(0, 65535, (6, 576)).astype(np.uint16)
-    seq = np.array([0, 0, 1, 1, 0, 1], np.int32)
-    pos = np.array([0, 70, 5, 127, 63, 200], np.int32)   # the last: no page -> skipped
+    rows = rng.integers(0, 65535, (7, 576)).astype(np.uint16)
+    seq = np.array([0, 0, 1, 1, 0, 1, 2], np.int32)
+    pos = np.array([0, 70, 5, 127, 63, 200, 1], np.int32)   # the last two: no page, no sequence
     cache = np.zeros((4, 64, 576), np.uint16)
-    assert oracle_lib.latent_cache_write(rows, seq, pos, pt, 64, cache) == 1
+    assert oracle_lib.latent_cache_write(rows, seq, pos, pt, 64, cache) == 2
     flat = cache.reshape(-1, 576)
     for t in range(5):
         r = pt[seq[t], pos[t] // 64] * 64 + pos[t] % 64
