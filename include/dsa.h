@@ -58,7 +58,8 @@ typedef enum {
 /* Element format of the indexer operands. */
 typedef enum {
   DSA_E4M3 = 0, /* OCP FP8 E4M3FN bytes (gfx950's native FP8) */
-  DSA_F32 = 1   /* IEEE binary32 */
+  DSA_F32 = 1,  /* IEEE binary32 */
+  DSA_BF16 = 2  /* bfloat16 (dsa_indexer_cache_write input only) */
 } dsa_dtype_t;
 
 /* Kernel variants reported by dsa_last_path() (observability only, never a control). */
@@ -75,7 +76,9 @@ enum {
   DSA_PATH_MLA_MFMA = 21,             /* H=128, Dqk=576, Dv=512: bf16 MFMA, one pass */
   DSA_PATH_MLA_MFMA_SPLIT = 22,       /* as 21, key set split over workgroups + combine */
   DSA_PATH_MHA_MFMA = 30,             /* expanded attention, dense causal: bf16 MFMA */
-  DSA_PATH_MHA_MFMA_MASKED = 31       /* as 30, restricted to the index sets (bitmap in ws) */
+  DSA_PATH_MHA_MFMA_MASKED = 31,      /* as 30, restricted to the index sets (bitmap in ws) */
+  DSA_PATH_CACHE_WRITE = 40,          /* quantise / place rows into a paged cache */
+  DSA_PATH_QUANTIZE = 41              /* elementwise E4M3 quantisation */
 };
 
 const char* dsa_status_string(dsa_status_t status);
@@ -211,6 +214,37 @@ dsa_status_t dsa_expanded_mha_prefill(const uint16_t* q, const uint16_t* k_nope,
                                       int q_per_seq, const int32_t* idx, int64_t ld_idx, int k, int H,
                                       int Dn, int Dr, int Dv, float sm_scale, uint16_t* out, float* lse,
                                       void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * The step before the indexer ([DSA-blog] "Lightning Indexer": every position's indexer key is
+ * produced from its own hidden state and cached in an Indexer Key Cache of its own; [Handbook]
+ * "对推理引擎的新要求": both caches are paged, and the cost model stores 128 + 4 bytes per token for
+ * the indexer key, FP8 codes plus a float scale). The projections that produce k, q and w from
+ * the hidden state are plain GEMMs the caller runs; these entry points quantise and place.
+ *
+ * dsa_indexer_cache_write -- for each of n_tok tokens (sequence seq[t] in [0, n_seq), position
+ * pos[t]; device int32 arrays; page_table [n_seq, ld_pt]): s = max_c |k[t, c]| / 448 and codes E4M3(k[t, c] / s), both rounded as float
+ * operations (round to nearest even, saturating to +-448; all codes 0 when s = 0), written to the
+ * token's physical row of k_cache [num_pages, page_size, Di] (E4M3 bytes) and k_scale
+ * [num_pages, page_size] (f32). This is the key format dsa_indexer_scores reads. A token whose
+ * sequence is out of range or whose position has no valid page is not written.
+ *   k  [n_tok, Di] f32 (dtype DSA_F32) or bf16 bits (DSA_BF16); Di = 128; k and k_cache 16-byte
+ *   aligned.
+ * dsa_latent_cache_write -- each token's latent row rows[t, 0:kv_dim] (bf16 bits) copied to its
+ * physical row of kv_cache [num_pages, page_size, kv_dim]; kv_dim a multiple of 8; 16-byte aligned.
+ * dsa_e4m3_quantize -- out[i] = E4M3(x[i]) for i < n (round to nearest even, saturating), the
+ * indexer query's format (the pages give the query no scale).
+ * Errors: DSA_ERR_INVALID_ARG for NULL or misaligned pointers and bad sizes, DSA_ERR_UNSUPPORTED
+ * for Di != 128 or another dtype. Out-of-range seq / pos values are not checked on the host (they
+ * are device data); such tokens are skipped by the kernels.
+ * ------------------------------------------------------------------------------------------- */
+dsa_status_t dsa_indexer_cache_write(const void* k, dsa_dtype_t dtype, int n_tok, int Di, const int32_t* seq,
+                                     const int32_t* pos, int n_seq, const int32_t* page_table, int64_t ld_pt, int page_size,
+                                     int num_pages, uint8_t* k_cache, float* k_scale, void* stream);
+dsa_status_t dsa_latent_cache_write(const uint16_t* rows, int n_tok, int kv_dim, const int32_t* seq,
+                                    const int32_t* pos, int n_seq, const int32_t* page_table, int64_t ld_pt, int page_size,
+                                    int num_pages, uint16_t* kv_cache, void* stream);
+dsa_status_t dsa_e4m3_quantize(const float* x, int64_t n, uint8_t* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libdsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["dsa_abi.hip", "indexer.hip", "topk.hip", "mla.hip", "mha.hip"]
+SOURCES = ["dsa_abi.hip", "indexer.hip", "topk.hip", "mla.hip", "mha.hip", "cache.hip"]
 
 # Packed fp32 arithmetic is disabled for all device code (a target feature, device pass only).
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

@@ -1,0 +1,123 @@
+// cache.hip -- the step before the indexer on gfx950: FP8 quantisation of the indexer keys with a
+// per-token scale and their paged cache write, the latent cache write, and the indexer query's
+// FP8 quantisation.
+//
+// Page references:
+//   [DSA-blog]  "DeepSeek Sparse Attention：从 SWA 到稀疏 Attention 计算" (kevinye.org), section
+//               "Lightning Indexer": each position's indexer key is produced from its own hidden
+//               state and kept in a separate Indexer Key Cache shared by all indexer heads
+//   [Handbook]  "MTP 与稀疏注意力：NSA 与 DSA" (anrans.github.io), section "对推理引擎的新要求": two
+//               paged caches (latent rows and indexer keys); the cost model's IDX_BYTES = 128 + 4
+//               (FP8 codes plus a float scale per token)
+//
+// All three are plain HBM streams (bytes in, bytes out, one pass); one wave handles one token's
+// row, so every load and store is a contiguous, coalesced run.
+#include "dsa_internal.h"
+
+namespace dsa {
+
+// float -> OCP E4M3FN, round to nearest even, saturating to +-448 (finite input). Normal values:
+// round the 23-bit mantissa to 3 bits by adding half an output ulp minus one plus the kept LSB
+// (a carry moves into the exponent); below 2^-6 the value is a count of 2^-9 quanta.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x43E00000u) return sign | 0x7Eu;  // |f| >= 448
+  if (a < 0x3C800000u) {                      // |f| < 2^-6: subnormal codes 0..8 (8 = 2^-6)
+    const float q = __uint_as_float(a) * 512.0f;  // exact
+    return sign | (uint32_t)__builtin_rintf(q);
+  }
+  const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+  const uint32_t e = (r >> 23) - 127u + 7u;  // 1 .. 15
+  const uint32_t code = (e << 3) | ((r >> 20) & 7u);
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+// One wave per token, Di = 128: lane l holds elements 2l, 2l+1.
+template <bool kF32>
+__global__ void __launch_bounds__(256) indexer_cache_write_kernel(const void* __restrict__ k, int n_tok, int n_seq,
+                                                                  const int32_t* __restrict__ seq,
+                                                                  const int32_t* __restrict__ pos, PagedCache kc,
+                                                                  uint8_t* __restrict__ k_cache,
+                                                                  float* __restrict__ k_scale) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= n_tok) return;
+  const int sq = seq[t];
+  const int64_t row = sq >= 0 && sq < n_seq ? phys_row(kc.page_table, kc.ld_pt, kc.page_size, kc.num_pages, sq, pos[t]) : -1;
+  if (row < 0) return;  // no valid page for this (sequence, position): the token is not written
+  float x0, x1;
+  if (kF32) {
+    const float2 v = ((const float2*)k)[(int64_t)t * 64 + lane];
+    x0 = v.x;
+    x1 = v.y;
+  } else {
+    const uint32_t v = ((const uint32_t*)k)[(int64_t)t * 64 + lane];
+    x0 = bf16_to_f32((uint16_t)(v & 0xFFFFu));
+    x1 = bf16_to_f32((uint16_t)(v >> 16));
+  }
+  const float m = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+  const float s = m / 448.0f;
+  uint32_t c = 0;
+  if (s > 0.f) c = e4m3_rne_sat(x0 / s) | (e4m3_rne_sat(x1 / s) << 8);
+  ((uint16_t*)(k_cache + row * 128))[lane] = (uint16_t)c;
+  if (lane == 0) k_scale[row] = s;
+}
+
+// One wave per token: the row's 16-byte chunks over the lanes.
+__global__ void __launch_bounds__(256) latent_cache_write_kernel(const uint16_t* __restrict__ rows, int n_tok,
+                                                                 int n_seq, int chunks, const int32_t* __restrict__ seq,
+                                                                 const int32_t* __restrict__ pos, PagedCache kc,
+                                                                 uint16_t* __restrict__ kv_cache) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= n_tok) return;
+  const int sq = seq[t];
+  const int64_t row = sq >= 0 && sq < n_seq ? phys_row(kc.page_table, kc.ld_pt, kc.page_size, kc.num_pages, sq, pos[t]) : -1;
+  if (row < 0) return;
+  const i32x4* src = (const i32x4*)rows + (int64_t)t * chunks;
+  i32x4* dst = (i32x4*)kv_cache + row * chunks;
+  for (int c = lane; c < chunks; c += 64) dst[c] = src[c];
+}
+
+// Elementwise, four values per thread.
+__global__ void __launch_bounds__(256) e4m3_quantize_kernel(const float* __restrict__ x, int64_t n,
+                                                            uint8_t* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i + 4 <= n) {
+    const float4 v = *(const float4*)(x + i);
+    *(uint32_t*)(out + i) = e4m3_rne_sat(v.x) | (e4m3_rne_sat(v.y) << 8) | (e4m3_rne_sat(v.z) << 16) |
+                            (e4m3_rne_sat(v.w) << 24);
+  } else {
+    for (int64_t j = i; j < n; ++j) out[j] = (uint8_t)e4m3_rne_sat(x[j]);
+  }
+}
+
+hipError_t launch_indexer_cache_write(const void* k, bool f32, int n_tok, int n_seq, const int32_t* seq,
+                                      const int32_t* pos, PagedCache kc, uint8_t* k_cache, float* k_scale,
+                                      hipStream_t stream) {
+  const dim3 grid((n_tok + 3) / 4);
+  if (f32)
+    hipLaunchKernelGGL(indexer_cache_write_kernel<true>, grid, dim3(256), 0, stream, k, n_tok, n_seq, seq, pos, kc,
+                       k_cache, k_scale);
+  else
+    hipLaunchKernelGGL(indexer_cache_write_kernel<false>, grid, dim3(256), 0, stream, k, n_tok, n_seq, seq, pos, kc,
+                       k_cache, k_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_latent_cache_write(const uint16_t* rows, int n_tok, int n_seq, int kv_dim, const int32_t* seq,
+                                     const int32_t* pos, PagedCache kc, uint16_t* kv_cache, hipStream_t stream) {
+  hipLaunchKernelGGL(latent_cache_write_kernel, dim3((n_tok + 3) / 4), dim3(256), 0, stream, rows, n_tok, n_seq,
+                     kv_dim / 8, seq, pos, kc, kv_cache);
+  return hipGetLastError();
+}
+
+hipError_t launch_e4m3_quantize(const float* x, int64_t n, uint8_t* out, hipStream_t stream) {
+  const int64_t threads = (n + 3) / 4;
+  hipLaunchKernelGGL(e4m3_quantize_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, x, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

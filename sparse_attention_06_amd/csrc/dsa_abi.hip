@@ -263,4 +263,55 @@ dsa_status_t dsa_expanded_mha_prefill(const uint16_t* q, const uint16_t* k_nope,
   return s == DSA_OK ? ok(idx ? DSA_PATH_MHA_MFMA_MASKED : DSA_PATH_MHA_MFMA) : s;
 }
 
+dsa_status_t dsa_indexer_cache_write(const void* k, dsa_dtype_t dtype, int n_tok, int Di, const int32_t* seq,
+                                     const int32_t* pos, int n_seq, const int32_t* page_table, int64_t ld_pt, int page_size,
+                                     int num_pages, uint8_t* k_cache, float* k_scale, void* stream) {
+  REQUIRE(n_tok >= 0, "n_tok must be >= 0 (got %d)", n_tok);
+  if (n_tok == 0) return ok(DSA_PATH_NONE);
+  REQUIRE(k && seq && pos && page_table && k_cache && k_scale, "a required pointer is NULL");
+  REQUIRE(!misaligned(k) && !misaligned(k_cache) && ((uintptr_t)k_scale & 3u) == 0,
+          "k and k_cache must be 16-byte aligned, k_scale 4-byte aligned");
+  REQUIRE(n_seq >= 1, "n_seq must be >= 1 (got %d)", n_seq);
+  REQUIRE(page_size >= 1 && num_pages >= 1 && ld_pt >= 1, "bad paging (page_size %d, num_pages %d, ld_pt %lld)",
+          page_size, num_pages, (long long)ld_pt);
+  REQUIRE((int64_t)num_pages * page_size < ((int64_t)1 << 31), "cache larger than 2^31 rows");
+  if (Di != 128 || (dtype != DSA_F32 && dtype != DSA_BF16))
+    return fail(DSA_ERR_UNSUPPORTED, "the indexer cache write takes Di = 128 keys in f32 or bf16 (got Di %d, dtype %d)",
+                Di, (int)dtype);
+  dsa::PagedCache kc{k_cache, page_table, ld_pt, page_size, num_pages};
+  dsa_status_t s = hip_status(dsa::launch_indexer_cache_write(k, dtype == DSA_F32, n_tok, n_seq, seq, pos, kc, k_cache, k_scale,
+                                                               (hipStream_t)stream),
+                              "indexer cache write launch");
+  return s == DSA_OK ? ok(DSA_PATH_CACHE_WRITE) : s;
+}
+
+dsa_status_t dsa_latent_cache_write(const uint16_t* rows, int n_tok, int kv_dim, const int32_t* seq,
+                                    const int32_t* pos, int n_seq, const int32_t* page_table, int64_t ld_pt, int page_size,
+                                    int num_pages, uint16_t* kv_cache, void* stream) {
+  REQUIRE(n_tok >= 0, "n_tok must be >= 0 (got %d)", n_tok);
+  if (n_tok == 0) return ok(DSA_PATH_NONE);
+  REQUIRE(rows && seq && pos && page_table && kv_cache, "a required pointer is NULL");
+  REQUIRE(!misaligned(rows) && !misaligned(kv_cache), "rows and kv_cache must be 16-byte aligned");
+  REQUIRE(kv_dim >= 8 && kv_dim % 8 == 0, "kv_dim must be a positive multiple of 8 (got %d)", kv_dim);
+  REQUIRE(n_seq >= 1, "n_seq must be >= 1 (got %d)", n_seq);
+  REQUIRE(page_size >= 1 && num_pages >= 1 && ld_pt >= 1, "bad paging (page_size %d, num_pages %d, ld_pt %lld)",
+          page_size, num_pages, (long long)ld_pt);
+  REQUIRE((int64_t)num_pages * page_size < ((int64_t)1 << 31), "cache larger than 2^31 rows");
+  dsa::PagedCache kc{kv_cache, page_table, ld_pt, page_size, num_pages};
+  dsa_status_t s = hip_status(dsa::launch_latent_cache_write(rows, n_tok, n_seq, kv_dim, seq, pos, kc, kv_cache,
+                                                              (hipStream_t)stream),
+                              "latent cache write launch");
+  return s == DSA_OK ? ok(DSA_PATH_CACHE_WRITE) : s;
+}
+
+dsa_status_t dsa_e4m3_quantize(const float* x, int64_t n, uint8_t* out, void* stream) {
+  REQUIRE(n >= 0, "n must be >= 0");
+  if (n == 0) return ok(DSA_PATH_NONE);
+  REQUIRE(x && out, "a required pointer is NULL");
+  REQUIRE(!misaligned(x) && ((uintptr_t)out & 3u) == 0, "x must be 16-byte and out 4-byte aligned");
+  REQUIRE(n < ((int64_t)1 << 40), "n too large");
+  dsa_status_t s = hip_status(dsa::launch_e4m3_quantize(x, n, out, (hipStream_t)stream), "e4m3 quantize launch");
+  return s == DSA_OK ? ok(DSA_PATH_QUANTIZE) : s;
+}
+
 }  // extern "C"

@@ -121,4 +121,11 @@ hipError_t launch_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t*
                       int64_t ld_kv, const int32_t* q_pos, int n_seq, int q_per_seq, const int32_t* idx,
                       int64_t ld_idx, int k, int H, int max_ctx, float sm_scale, uint16_t* out, float* lse,
                       void* ws, hipStream_t stream);
+// The step before the indexer: per-token FP8 key quantisation and the paged cache writes.
+hipError_t launch_indexer_cache_write(const void* k, bool f32, int n_tok, int n_seq, const int32_t* seq,
+                                      const int32_t* pos, PagedCache kc, uint8_t* k_cache, float* k_scale,
+                                      hipStream_t stream);
+hipError_t launch_latent_cache_write(const uint16_t* rows, int n_tok, int n_seq, int kv_dim, const int32_t* seq,
+                                     const int32_t* pos, PagedCache kc, uint16_t* kv_cache, hipStream_t stream);
+hipError_t launch_e4m3_quantize(const float* x, int64_t n, uint8_t* out, hipStream_t stream);
 }  // namespace dsa

@@ -15,11 +15,11 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
-DSA_E4M3, DSA_F32 = 0, 1
+DSA_E4M3, DSA_F32, DSA_BF16 = 0, 1, 2
 PATHS = {
     0: "none", 1: "indexer_generic", 2: "indexer_scan_mfma", 3: "indexer_prefill_mfma",
     10: "topk_copy", 11: "topk_radix", 12: "topk_radix_reg", 13: "topk_radix_staged", 20: "mla_generic", 21: "mla_mfma", 22: "mla_mfma_split",
-    30: "mha_mfma", 31: "mha_mfma_masked",
+    30: "mha_mfma", 31: "mha_mfma_masked", 40: "cache_write", 41: "quantize",
 }
 
 EXPORTS = [
@@ -28,6 +28,7 @@ EXPORTS = [
     "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
     "dsa_dense_mla_workspace_size", "dsa_dense_mla_prefill",
     "dsa_expanded_mha_workspace_size", "dsa_expanded_mha_prefill",
+    "dsa_indexer_cache_write", "dsa_latent_cache_write", "dsa_e4m3_quantize",
 ]
 
 
@@ -84,6 +85,12 @@ def load():
     lib.dsa_expanded_mha_prefill.restype = i32
     lib.dsa_expanded_mha_prefill.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, i64, i32, i32, i32, i32, i32,
                                              f32, vp, vp, vp, sz, vp]
+    lib.dsa_indexer_cache_write.restype = i32
+    lib.dsa_indexer_cache_write.argtypes = [vp, i32, i32, i32, vp, vp, i32, vp, i64, i32, i32, vp, vp, vp]
+    lib.dsa_latent_cache_write.restype = i32
+    lib.dsa_latent_cache_write.argtypes = [vp, i32, i32, vp, vp, i32, vp, i64, i32, i32, vp, vp]
+    lib.dsa_e4m3_quantize.restype = i32
+    lib.dsa_e4m3_quantize.argtypes = [vp, i64, vp, vp]
     _lib = lib
     return lib
 
@@ -266,4 +273,52 @@ def expanded_mha_prefill(q, k_nope, k_rope, v, q_pos, n_seq, q_per_seq, sm_scale
                                          _p(idx), ld_idx, k, H, Dn, Dr, Dv, float(sm_scale), _p(out), _p(lse),
                                          _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check("dsa_expanded_mha_prefill", st)
+    return out
+
+
+def indexer_cache_write(k, seq, pos, page_table, k_cache, k_scale, stream=None):
+    """Quantise indexer keys per token (s = max|k|/448, codes E4M3(k/s)) into the paged cache.
+    k [n_tok, 128] float32 or bfloat16; seq, pos [n_tok] int32; page_table [n_seq, ld_pt] int32;
+    k_cache [P, page, 128] uint8 and k_scale [P, page] float32, written in place."""
+    if k.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("k must be float32 or bfloat16")
+    _need(k, "k", k.dtype, 2)
+    for t, n in ((seq, "seq"), (pos, "pos")):
+        _need(t, n, torch.int32, 1)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(k_cache, "k_cache", torch.uint8, 3)
+    _need(k_scale, "k_scale", torch.float32, 2)
+    if seq.numel() != k.shape[0] or pos.numel() != k.shape[0]:
+        raise ValueError("seq and pos need one entry per key row")
+    st = load().dsa_indexer_cache_write(_p(k), DSA_F32 if k.dtype == torch.float32 else DSA_BF16, k.shape[0], k.shape[1],
+                                        _p(seq), _p(pos), page_table.shape[0], _p(page_table), page_table.shape[1],
+                                        k_cache.shape[1], k_cache.shape[0], _p(k_cache), _p(k_scale), _stream(stream))
+    _check("dsa_indexer_cache_write", st)
+
+
+def latent_cache_write(rows, seq, pos, page_table, kv_cache, stream=None):
+    """Place latent rows [n_tok, kv_dim] bf16 into the paged cache [P, page, kv_dim] in place."""
+    _need(rows, "rows", torch.bfloat16, 2)
+    for t, n in ((seq, "seq"), (pos, "pos")):
+        _need(t, n, torch.int32, 1)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(kv_cache, "kv_cache", torch.bfloat16, 3)
+    if kv_cache.shape[2] != rows.shape[1]:
+        raise ValueError("rows and kv_cache widths differ")
+    if seq.numel() != rows.shape[0] or pos.numel() != rows.shape[0]:
+        raise ValueError("seq and pos need one entry per row")
+    st = load().dsa_latent_cache_write(_p(rows), rows.shape[0], rows.shape[1], _p(seq), _p(pos), page_table.shape[0],
+                                       _p(page_table), page_table.shape[1], kv_cache.shape[1], kv_cache.shape[0],
+                                       _p(kv_cache), _stream(stream))
+    _check("dsa_latent_cache_write", st)
+
+
+def e4m3_quantize(x, out=None, stream=None):
+    """float32 tensor -> E4M3 codes (uint8, same shape), no scale."""
+    _need(x, "x", torch.float32)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _need(out, "out", torch.uint8)
+    st = load().dsa_e4m3_quantize(_p(x), x.numel(), _p(out), _stream(stream))
+    _check("dsa_e4m3_quantize", st)
     return out

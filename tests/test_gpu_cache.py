@@ -1,0 +1,128 @@
+"""The step before the indexer on the GPU against the oracle, bit for bit: per-token FP8 key
+quantisation into the paged indexer cache (f32 and bf16 keys), the latent cache write, and the
+indexer query quantisation. Permuted pages, ragged token counts, zero keys, tokens without a valid
+page or sequence (skipped), values at the saturation edge and in the subnormal range. Then the
+written cache feeds dsa_indexer_scores, which must agree with the oracle's scores on it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import check_scores
+from sparse_attention_06_amd import dsa
+
+pytestmark = pytest.mark.gpu
+
+
+def _keys(rng, n, Di=128):
+    k = rng.standard_normal((n, Di)) * np.exp2(rng.uniform(-10, 10, (n, 1)))
+    return k.astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_indexer_cache_write_bit_exact(oracle_lib, dtype):
+    print(f"case: indexer cache write {dtype}", flush=True)
+    rng = np.random.default_rng(41)
+    n_seq, pages, page = 3, 5, 64
+    P = n_seq * pages + 2
+    pt = rng.permutation(P)[: n_seq * pages].astype(np.int32).reshape(n_seq, pages)
+    n_tok = 777
+    seq = rng.integers(0, n_seq, n_tok).astype(np.int32)
+    pos = rng.integers(0, pages * page, n_tok).astype(np.int32)
+    # unique (seq, pos) pairs, so no two tokens race for one row
+    _, first = np.unique(seq.astype(np.int64) * 100000 + pos, return_index=True)
+    keep = np.sort(first)
+    seq, pos = seq[keep], pos[keep]
+    n_tok = len(seq)
+    k = _keys(rng, n_tok)
+    k[0] = 0.0
+    k[1, :5] = [448.0, -448.0, 447.99, 1e-9, -3e-3]
+    k[2] = np.float32(2.0 ** -13)                     # subnormal codes after the scale
+    pos[3] = pages * page + 1                         # no page: skipped
+    seq[4] = n_seq                                    # no such sequence: skipped
+    kin = torch.from_numpy(k)
+    if dtype == "bf16":
+        kin = kin.to(torch.bfloat16)
+        k_host = kin.view(torch.int16).numpy().view(np.uint16)
+    else:
+        k_host = k
+    ref_c = np.full((P, page, 128), 0x5A, np.uint8)
+    ref_s = np.full((P, page), -2.0, np.float32)
+    assert oracle_lib.indexer_cache_write(k_host, seq, pos, pt, page, ref_c, ref_s) == 2
+    gc = torch.full((P, page, 128), 0x5A, dtype=torch.uint8, device="cuda")
+    gs = torch.full((P, page), -2.0, dtype=torch.float32, device="cuda")
+    dsa.indexer_cache_write(kin.cuda(), torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(),
+                            torch.from_numpy(pt).cuda(), gc, gs)
+    torch.cuda.synchronize()
+    assert dsa.last_path() == "cache_write"
+    np.testing.assert_array_equal(gc.cpu().numpy(), ref_c)
+    np.testing.assert_array_equal(gs.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+
+
+def test_latent_cache_write_bit_exact(oracle_lib):
+    print("case: latent cache write", flush=True)
+    rng = np.random.default_rng(43)
+    n_seq, pages, page = 2, 5, 64
+    P = n_seq * pages + 1
+    pt = rng.permutation(P)[: n_seq * pages].astype(np.int32).reshape(n_seq, pages)
+    pos = rng.permutation(pages * page)[:301].astype(np.int32)
+    seq = (np.arange(301) % n_seq).astype(np.int32)
+    pos[7] = -1                                       # skipped
+    rows = rng.integers(0, 65536, (301, 576)).astype(np.uint16)
+    ref = np.zeros((P, page, 576), np.uint16)
+    oracle_lib.latent_cache_write(rows, seq, pos, pt, page, ref)
+    g = torch.zeros(P, page, 576, dtype=torch.bfloat16, device="cuda")
+    dsa.latent_cache_write(torch.from_numpy(rows.view(np.int16)).view(torch.bfloat16).cuda(), torch.from_numpy(seq).cuda(),
+                           torch.from_numpy(pos).cuda(), torch.from_numpy(pt).cuda(), g)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(g.view(torch.int16).cpu().numpy().view(np.uint16), ref)
+
+
+def test_e4m3_quantize_bit_exact(oracle_lib):
+    print("case: e4m3 quantize", flush=True)
+    rng = np.random.default_rng(45)
+    mag = np.exp2(rng.uniform(-14, 10, 100003)).astype(np.float32)
+    x = np.where(rng.random(mag.size) < 0.5, -mag, mag).astype(np.float32)
+    # every code's value and the midpoints between neighbours (ties to even), zeros of both signs
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    fin = np.sort(codes[np.isfinite(codes)])
+    mids = ((fin[1:] + fin[:-1]) / 2).astype(np.float32)
+    x = np.concatenate([x, fin, mids, -mids, np.float32([0.0, -0.0, 448.0, 464.0, 1e30, -1e30])]).astype(np.float32)
+    ref = oracle_lib.e4m3_quantize(x)
+    got = dsa.e4m3_quantize(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), ref)
+
+
+def test_written_cache_feeds_the_indexer(oracle_lib):
+    # keys and queries quantised on the GPU, the cache written on the GPU, then scored: the scores
+    # match the oracle's on the same (GPU-written, oracle-checked) cache
+    print("case: cache write -> indexer", flush=True)
+    rng = np.random.default_rng(47)
+    n_seq, qps, L, page = 2, 2, 1000, 64
+    pages = (L + page - 1) // page
+    P = n_seq * pages
+    pt = rng.permutation(P).astype(np.int32).reshape(n_seq, pages)
+    seq = np.repeat(np.arange(n_seq), L).astype(np.int32)
+    pos = np.tile(np.arange(L), n_seq).astype(np.int32)
+    k = _keys(rng, n_seq * L)
+    gc = torch.zeros(P, page, 128, dtype=torch.uint8, device="cuda")
+    gs = torch.zeros(P, page, dtype=torch.float32, device="cuda")
+    dsa.indexer_cache_write(torch.from_numpy(k).cuda(), torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(),
+                            torch.from_numpy(pt).cuda(), gc, gs)
+    q = rng.standard_normal((n_seq * qps, 64, 128)).astype(np.float32)
+    q8 = dsa.e4m3_quantize(torch.from_numpy(q).cuda())
+    w = (rng.standard_normal((n_seq * qps, 64)) / 8).astype(np.float32)
+    q_pos = np.array([L - 2, L - 1, L - 2, L - 1], np.int32)
+    scores = dsa.indexer_scores(q8, torch.from_numpy(w).cuda(), gc, gs, torch.from_numpy(pt).cuda(),
+                                torch.from_numpy(q_pos).cuda(), n_seq, qps, L)
+    torch.cuda.synchronize()
+    ref_c = np.zeros((P, page, 128), np.uint8)
+    ref_s = np.zeros((P, page), np.float32)
+    oracle_lib.indexer_cache_write(k, seq, pos, pt, page, ref_c, ref_s)
+    np.testing.assert_array_equal(gc.cpu().numpy(), ref_c)
+    np.testing.assert_array_equal(q8.cpu().numpy(), oracle_lib.e4m3_quantize(q))
+    ref = oracle_lib.indexer_scores(q8.cpu().numpy(), w, ref_c, ref_s, pt, page, q_pos, n_seq, qps, oracle_lib.E4M3, L,
+                                    threads=8)
+    check_scores(scores.cpu().numpy(), ref, q_pos)
