@@ -473,6 +473,51 @@ def run_crossover(args):
                       "sparse_beats_expanded_dense_from_T": first("expanded_wins")}), flush=True)
 
 
+def run_cache_bench(args):
+    """The step before the indexer at prefill scale: 131072 tokens of one sequence written into
+    both paged caches (indexer keys quantised from f32, latent rows copied) and the indexer
+    queries of a 4096-row block quantised; HBM GB/s of each against the peak."""
+    import torch
+
+    from sparse_attention_06_amd import dsa
+
+    n, page = 131072, 64
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0xD5A0 + 7)
+    pages = n // page
+    pt = torch.randperm(pages, generator=g, device="cuda").to(torch.int32).view(1, pages)
+    seq = torch.zeros(n, dtype=torch.int32, device="cuda")
+    pos = torch.arange(n, dtype=torch.int32, device="cuda")
+    k = torch.randn(n, 128, generator=g, device="cuda")
+    rows = torch.randn(n, 576, generator=g, device="cuda").to(torch.bfloat16)
+    kc = torch.empty(pages, page, 128, dtype=torch.uint8, device="cuda")
+    ks = torch.empty(pages, page, dtype=torch.float32, device="cuda")
+    kv = torch.empty(pages, page, 576, dtype=torch.bfloat16, device="cuda")
+    q = torch.randn(4096, 64, 128, generator=g, device="cuda")
+    q8 = torch.empty(4096, 64, 128, dtype=torch.uint8, device="cuda")
+    calls = {
+        "indexer_cache_write": (lambda: dsa.indexer_cache_write(k, seq, pos, pt, kc, ks), n * (128 * 4 + 8 + 128 + 4)),
+        "latent_cache_write": (lambda: dsa.latent_cache_write(rows, seq, pos, pt, kv), n * (2 * 1152 + 8)),
+        "e4m3_quantize": (lambda: dsa.e4m3_quantize(q, out=q8), q.numel() * 5),
+    }
+    res = {}
+    for name, (fn, nbytes) in calls.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        res[name] = {"us": ms * 1e3, "MB": nbytes / 1e6, "GBps": nbytes / (ms * 1e-3) / 1e9,
+                     "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log(f"[cache] {name}: {res[name]}")
+    print(json.dumps({"cache_write": res, "tokens": n, "query_rows": 4096}), flush=True)
+
+
 def run_copy_calibration(args):
     """A plain device copy of known size (1 GiB read + 1 GiB written per launch): the reference
     for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -502,6 +547,7 @@ def main():
     ap.add_argument("--crossover-T", default="1024,2048,4096,8192,16384",
                     help="prefix lengths of the crossover sweep")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--cache-write", action="store_true", help="time the cache writes and query quantisation")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -510,6 +556,8 @@ def main():
         raise SystemExit(2)
     if args.copy_calibration:
         run_copy_calibration(args)
+    elif args.cache_write:
+        run_cache_bench(args)
     elif args.crossover:
         run_crossover(args)
     elif args.workload.startswith("prefill"):
