@@ -116,15 +116,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ int lat_rot(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 __device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
 
-// Physical row of entry e of row r (sparse: position idx[r, e]; dense: position e), or -1 when
-// the position is not visible or its page id is invalid.
-__device__ __forceinline__ int resolve_entry(const AttnArgs& a, int r, int seq, int t, int e) {
-  const int j = a.idx ? a.idx[(int64_t)r * a.ld_idx + e] : e;
-  if (j < 0 || j > t) return -1;
-  const int64_t row = phys_row(a.kv.page_table, a.kv.ld_pt, a.kv.page_size, a.kv.num_pages, seq, j);
-  return (int)row;  // caches hold < 2^31 rows
-}
-
 // A wave-uniform 64-bit value, placed in scalar registers. readfirstlane returns int: each half
 // goes through uint32_t so that the low half is zero-extended, not sign-extended into the high.
 __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
@@ -343,7 +334,29 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
   for (int cb = e_begin; cb < e_end; cb += kListCap) {
     const int ce = min(e_end, cb + kListCap);
     __syncthreads();  // the previous chunk is done with the list and the buffers
-    for (int e = cb + threadIdx.x; e < ce; e += 256) list[e - cb] = resolve_entry(a, r, seq, t, e);
+    // eight entries per thread at a time: all their index loads, then all their page-table
+    // loads, so the resolve costs two memory latencies rather than two per entry
+    for (int e0 = cb + threadIdx.x; e0 < ce; e0 += 8 * 256) {
+      int jj[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + 256 * u;
+        jj[u] = e < ce ? (a.idx ? a.idx[(int64_t)r * a.ld_idx + e] : e) : -1;
+      }
+      int pg[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = jj[u];
+        const bool vis = j >= 0 && j <= t && j / a.kv.page_size < a.kv.ld_pt;
+        pg[u] = vis ? a.kv.page_table[(int64_t)seq * a.kv.ld_pt + j / a.kv.page_size] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + 256 * u;
+        if (e < ce)
+          list[e - cb] = (pg[u] >= 0 && pg[u] < a.kv.num_pages) ? pg[u] * a.kv.page_size + jj[u] % a.kv.page_size : -1;
+      }
+    }
     if (cb == e_begin) {
       // consume the query fragments here, before any gather is issued: their wait then covers
       // the query loads only, and no wait for them lands in the tile loop (where it would also
