@@ -152,6 +152,21 @@ class DecodeStep:
         return graphs
 
 
+def time_call(step, fn, steps, reps=8):
+    """Average duration of one call of `fn` (ms): a HIP graph holding `reps` calls back to back,
+    alternating the input copies, replayed `steps` times; dividing by reps spreads the graph's own
+    launch cost over the calls, so the figure is the calls' duration (what the kernel trace
+    reports), not one launch overhead per call."""
+    torch = step.torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = torch.cuda.current_stream()
+        for i in range(reps):
+            fn(i % len(step.copies), st)
+    torch.cuda.synchronize()
+    return time_replays(torch, [g], steps)[0] / reps
+
+
 def time_replays(torch, graphs, steps):
     """ms per replay over `steps` replays (alternating graphs) between device-wide syncs."""
     for g in graphs:
@@ -187,6 +202,21 @@ def time_graph_steps(step, steps, warmup):
             raise SystemExit(f"graph replay differs from the eager step (copy {c}: {bad_idx} index entries, "
                              f"{bad_out} output elements)")
     return time_replays(torch, graphs, steps)
+
+
+def time_eager_steps(step, steps):
+    """ms per step over `steps` eager steps (the calls launched one after another on one stream,
+    no events between them), bracketed by device synchronisations; and the wall seconds."""
+    torch = step.torch
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        step.run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
 
 
 def time_steps(step, steps, warmup):
@@ -286,12 +316,16 @@ def run_decode_bench(args):
         ms = [float(x) for x in per.mean(axis=0)]
         ms_step = ms[3]
     else:
-        # the step as deployed: graph replays; per-call times from graphs holding one call each,
-        # replayed back to back; and an eager pass with events between the calls
-        ms_step, wall = time_graph_steps(step, args.steps, args.warmup)
+        # the step as launched: eager steps, the four launches back to back on one stream (on this
+        # GPU-bound step they run a few percent faster than graph replays of the same launches,
+        # which are timed too, after a bit-for-bit check against the eager result); per-call times
+        # from graphs of repeated calls; an eager pass with events between the calls
+        for i in range(args.warmup):
+            step.run(i)
+        ms_step, wall = time_eager_steps(step, args.steps)
         ms_step = float(ms_step)
-        ms = [time_replays(torch, step.capture((fn,)), args.steps)[0]
-              for fn in (step.call_indexer, step.call_topk, step.call_mla)]
+        ms_graph, _ = time_graph_steps(step, args.steps, 0)
+        ms = [time_call(step, fn, args.steps) for fn in (step.call_indexer, step.call_topk, step.call_mla)]
         _, per = time_steps(step, args.steps, 1)
         ms.append(float(per.mean(axis=0)[3]))
     ctx = w.q_pos.reshape(w.n_seq, w.q_per_seq).max(axis=1) + 1
@@ -301,6 +335,7 @@ def run_decode_bench(args):
     qps = rows / (ms_step * 1e-3)
     detail = {
         "ms": {"indexer": float(ms[0]), "topk": float(ms[1]), "sparse_mla": float(ms[2]), "step": ms_step,
+               "step_graph_replay": None if args.no_graph else float(ms_graph),
                "step_eager_with_events": float(ms[3])},
         "wall_ms_per_step": wall / args.steps * 1e3,
         "algorithmic_GBps": {"indexer": by["indexer"] / ms[0] / 1e6, "topk": by["topk"] / ms[1] / 1e6,
@@ -354,9 +389,10 @@ def run_prefill_bench(args):
     log(f"[bench] workload {w.name}: {w.rows} query rows over {w.max_ctx} positions, generated in "
         f"{time.time() - t0:.1f} s")
     step = DecodeStep(w, copies=1)
-    ms_step, wall = time_graph_steps(step, args.steps, args.warmup)
-    ms = [time_replays(torch, step.capture((fn,)), args.steps)[0]
-          for fn in (step.call_indexer, step.call_topk, step.call_mla)]
+    # a prefill block takes milliseconds: a few warm-up and timed blocks suffice
+    steps, warmup = min(args.steps, 20), min(args.warmup, 5)
+    ms_step, wall = time_graph_steps(step, steps, warmup)
+    ms = [time_call(step, fn, steps, reps=2) for fn in (step.call_indexer, step.call_topk, step.call_mla)]
     ctx = w.q_pos.astype(np.int64) + 1
     sel = np.minimum(ctx, w.topk)
     flops = {"indexer": float(np.sum(ctx)) * 2 * w.Hi * w.Di,
@@ -372,7 +408,7 @@ def run_prefill_bench(args):
             "algorithmic_flops_per_launch": flops[dominant]}
     line = {
         "metric": "DSA prefill queries/s (indexer + top-2048 + sparse MLA)", "value": round(w.rows / (ms_step * 1e-3), 1),
-        "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "unit": "queries/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(float(ms_step), 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "query_rows": w.rows, "context": int(w.max_ctx), "topk": w.topk,
@@ -381,7 +417,7 @@ def run_prefill_bench(args):
         "roofline": roof,
         "cpu_baseline": None,
         "detail": {"ms": {"indexer": ms[0], "topk": ms[1], "sparse_mla": ms[2], "step": float(ms_step)},
-                   "wall_ms_per_step": wall / args.steps * 1e3, "mfma_TFLOPs": tflops,
+                   "wall_ms_per_step": wall / steps * 1e3, "mfma_TFLOPs": tflops,
                    "TFLOP": {k: v / 1e12 for k, v in flops.items()},
                    "topk_rows_per_s": w.rows / (ms[1] * 1e-3)},
     }
@@ -448,6 +484,7 @@ def run_crossover(args):
             torch.matmul(lat, wuk, out=kexp)
 
         row = {"T": T}
+        reps = min(args.steps, 10)
         for name, fn in (("sparse_ms", sparse), ("dense_absorbed_ms", dense), ("dense_expanded_ms", expanded),
                          ("masked_expanded_ms", masked), ("expand_gemm_ms", gemm)):
             for _ in range(2):
@@ -455,11 +492,11 @@ def run_crossover(args):
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            for _ in range(args.steps):
+            for _ in range(reps):
                 fn()
             e1.record()
             torch.cuda.synchronize()
-            row[name] = e0.elapsed_time(e1) / args.steps
+            row[name] = e0.elapsed_time(e1) / reps
         pairs = T * (T + 1) / 2
         row["expanded_TFLOPs"] = pairs * 128 * (2 * 192 + 2 * 128) / (row["dense_expanded_ms"] * 1e-3) / 1e12
         row["absorbed_wins"] = row["dense_absorbed_ms"] < row["sparse_ms"]
@@ -536,8 +573,9 @@ def run_copy_calibration(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first: the decode step takes ~150 steps (~30 ms) to settle")
     ap.add_argument("--workload", default="decode_mtp_b64_16k",
                     choices=["decode_mtp_b64_16k", "decode_b16_4k", "decode_b4_128k", "prefill_8k",
                              "prefill_chunk_128k"])
