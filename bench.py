@@ -80,9 +80,11 @@ def decode_step_flops(n_seq, q_per_seq, ctx_per_seq, k, H=128, Dqk=576, Dv=512, 
 
 # ------------------------------------------------------------------ GPU step
 class DecodeStep:
-    """Device buffers for `copies` independent copies of a decode workload and the three calls."""
+    """Device buffers for `copies` independent copies of a decode workload and its calls: the
+    indexer, the top-k and the sparse attention, or (fused) the indexer and top-k as one call
+    sharing the first radix pass, then the attention."""
 
-    def __init__(self, w, copies=2):
+    def __init__(self, w, copies=2, fused=False):
         import torch
         from sparse_attention_06_amd import dsa
 
@@ -106,8 +108,20 @@ class DecodeStep:
             d["ws"] = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda") if need else None
             tneed = dsa.topk_workspace_size(w.rows, w.max_ctx, w.topk)
             d["tws"] = torch.empty(tneed, dtype=torch.uint8, device="cuda") if tneed else None
+            # the fused call's workspace starts zeroed and every call leaves it so
+            fneed = dsa.indexer_topk_workspace_size(w.rows, w.max_ctx, w.topk)
+            d["fws"] = torch.zeros(fneed, dtype=torch.uint8, device="cuda")
             self.copies.append(d)
         self.stream = torch.cuda.current_stream()
+        self.fused = fused
+        self.calls = ((self.call_indexer_topk, self.call_mla) if fused else
+                      (self.call_indexer, self.call_topk, self.call_mla))
+
+    def call_indexer_topk(self, c, st):
+        w, d = self.w, self.copies[c % len(self.copies)]
+        self.dsa.indexer_topk(d["iq"], d["iw"], d["ik"], d["iks"], d["page_table"], d["q_pos"], w.n_seq,
+                              w.q_per_seq, w.max_ctx, w.topk, scores=d["scores"], idx=d["idx"], ws=d["fws"],
+                              stream=st)
 
     def call_indexer(self, c, st):
         w, d = self.w, self.copies[c % len(self.copies)]
@@ -126,9 +140,18 @@ class DecodeStep:
            w.sm_scale, out=d["out"], ws=d["ws"], stream=st)
 
     def run(self, c, events=None, stream=None):
+        """One step; with `events` (4), events[0..3] bracket indexer | top-k | attention (fused:
+        events[1] and [2] both sit between the fused call and the attention)."""
         st = stream if stream is not None else self.stream
-        calls = (self.call_indexer, self.call_topk, self.call_mla)
-        for i, fn in enumerate(calls):
+        if events and self.fused:
+            events[0].record(st)
+            self.call_indexer_topk(c, st)
+            events[1].record(st)
+            events[2].record(st)
+            self.call_mla(c, st)
+            events[3].record(st)
+            return
+        for i, fn in enumerate(self.calls):
             if events:
                 events[i].record(st)
             fn(c, st)
@@ -139,7 +162,7 @@ class DecodeStep:
         """One HIP graph per input copy holding `fns` (default: the whole step, i.e. the four
         kernel launches), so replays carry no host-side launch gaps."""
         torch = self.torch
-        fns = fns or (self.call_indexer, self.call_topk, self.call_mla)
+        fns = fns or self.calls
         graphs = []
         for c in range(len(self.copies)):
             g = torch.cuda.CUDAGraph()
@@ -309,7 +332,7 @@ def run_decode_bench(args):
     w = workloads.MAKERS[args.workload]()
     log(f"[bench] workload {w.name}: {w.n_seq} requests x {w.q_per_seq} rows, ctx {w.max_ctx}, "
         f"generated in {time.time() - t0:.1f} s")
-    step = DecodeStep(w, copies=2)
+    step = DecodeStep(w, copies=2, fused=not args.separate_indexer_topk)
     if args.no_graph:
         # eager steps only (for profiler runs that do not follow graph launches)
         wall, per = time_steps(step, args.steps, args.warmup)
@@ -326,6 +349,7 @@ def run_decode_bench(args):
         ms_step = float(ms_step)
         ms_graph, _ = time_graph_steps(step, args.steps, 0)
         ms = [time_call(step, fn, args.steps) for fn in (step.call_indexer, step.call_topk, step.call_mla)]
+        ms_fused = time_call(step, step.call_indexer_topk, args.steps)
         _, per = time_steps(step, args.steps, 1)
         ms.append(float(per.mean(axis=0)[3]))
     ctx = w.q_pos.reshape(w.n_seq, w.q_per_seq).max(axis=1) + 1
@@ -336,7 +360,9 @@ def run_decode_bench(args):
     detail = {
         "ms": {"indexer": float(ms[0]), "topk": float(ms[1]), "sparse_mla": float(ms[2]), "step": ms_step,
                "step_graph_replay": None if args.no_graph else float(ms_graph),
-               "step_eager_with_events": float(ms[3])},
+               "step_eager_with_events": float(ms[3]),
+               "indexer_topk_fused": None if args.no_graph else float(ms_fused)},
+        "step_calls": "indexer_topk (fused) + sparse_mla" if step.fused else "indexer + topk + sparse_mla",
         "wall_ms_per_step": wall / args.steps * 1e3,
         "algorithmic_GBps": {"indexer": by["indexer"] / ms[0] / 1e6, "topk": by["topk"] / ms[1] / 1e6,
                              "sparse_mla": by["mla"] / ms[2] / 1e6, "step": by["step"] / ms_step / 1e6},
@@ -346,6 +372,16 @@ def run_decode_bench(args):
         "mfma_TFLOPs": {"indexer_f16": fl["indexer"] / ms[0] / 1e9, "sparse_mla_bf16": fl["mla"] / ms[2] / 1e9},
         "requests_per_s": w.n_seq / (ms_step * 1e-3),
     }
+    if w.q_per_seq == 2:
+        # KV rows the two MTP rows of a request read: each row's own set, and their union (what a
+        # gather shared by the two rows would read)
+        idx = step.copies[0]["idx"].cpu().numpy().reshape(w.n_seq, 2, w.topk)
+        own = sum(int((idx[s_] >= 0).sum()) for s_ in range(w.n_seq))
+        union = sum(np.union1d(idx[s_, 0][idx[s_, 0] >= 0], idx[s_, 1][idx[s_, 1] >= 0]).size
+                    for s_ in range(w.n_seq))
+        row_bytes = 2 * 576
+        detail["mtp_kv_rows"] = {"per_row_sets": own, "union_of_request_sets": union,
+                                 "per_row_MB": own * row_bytes / 1e6, "union_MB": union * row_bytes / 1e6}
     log("[bench] " + json.dumps(detail))
     mla_bytes = by["mla"]
     achieved = mla_bytes / (ms[2] * 1e-3) / 1e9
@@ -580,6 +616,8 @@ def main():
                     choices=["decode_mtp_b64_16k", "decode_b16_4k", "decode_b4_128k", "prefill_8k",
                              "prefill_chunk_128k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-indexer-topk", action="store_true",
+                    help="decode step as three calls (indexer, top-k, attention) instead of the fused indexer+top-k")
     ap.add_argument("--no-graph", action="store_true", help="time eager steps (for counter-collection runs)")
     ap.add_argument("--crossover", action="store_true")
     ap.add_argument("--crossover-T", default="1024,2048,4096,8192,16384",

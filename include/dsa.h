@@ -68,6 +68,8 @@ enum {
   DSA_PATH_INDEXER_GENERIC = 1,       /* any Hi, Di, dtype: one thread per (row, key), VALU */
   DSA_PATH_INDEXER_SCAN_MFMA = 2,     /* Hi=64, Di=128, E4M3, 64-token pages: key scan, 2 rows/wave */
   DSA_PATH_INDEXER_PREFILL_MFMA = 3,  /* Hi=64, Di=128, E4M3, other page sizes: query x key tiles */
+  DSA_PATH_INDEXER_TOPK_FUSED = 4,    /* dsa_indexer_topk: scan counting the first radix digit, then
+                                         the register top-k starting from those counts */
   DSA_PATH_TOPK_COPY = 10,            /* every row no longer than k: all positions kept */
   DSA_PATH_TOPK_RADIX = 11,           /* radix select, one workgroup per row */
   DSA_PATH_TOPK_RADIX_REG = 12,       /* as 11 for max_ctx <= 16384, the row held in registers */
@@ -127,6 +129,31 @@ size_t dsa_topk_workspace_size(int rows, int max_ctx, int k);
 dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int rows,
                       int max_ctx, int k, int32_t* idx, int64_t ld_idx, void* ws,
                       size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * dsa_indexer_topk -- dsa_indexer_scores followed by dsa_topk in one call, with the top-k's first
+ * radix pass done while the scores are produced ([DSA-blog] "Lightning Indexer": the index
+ * scores exist only to feed TopK; [Handbook] "对推理引擎的新要求": the indexer and the top-k are
+ * the new kernels the method asks of an engine). The scan counts, per row, its valid scores by
+ * the first digit (the top 11 bits of the order key the top-k ranks by) in LDS, adds the counts
+ * into a per-row histogram in the workspace, and the top-k starts from those counts instead of
+ * its own first pass over the row.
+ *   Arguments as dsa_indexer_scores (scores is still written in full: the caller may keep it)
+ *   and dsa_topk (k, idx, ld_idx); the results equal those of the two calls bit for bit.
+ *   ws  dsa_indexer_topk_workspace_size(rows, max_ctx, k) bytes of device memory, owned by the
+ *       caller and reused across calls: it must be ZERO-FILLED before its first use, and every
+ *       call that returns DSA_OK leaves its histogram part zero again (after a failed call,
+ *       zero it again). Calls sharing one workspace must not overlap in time.
+ * The shared histogram is used for the MFMA scan shapes (Hi=64, Di=128, E4M3, 64-token pages)
+ * with max_ctx <= 16384 and k <= 4096 (DSA_PATH_INDEXER_TOPK_FUSED). Other shapes run the two
+ * calls one after the other (the path is then the top-k's).
+ * ------------------------------------------------------------------------------------------- */
+size_t dsa_indexer_topk_workspace_size(int rows, int max_ctx, int k);
+dsa_status_t dsa_indexer_topk(const void* q, const float* w, const void* k_cache, const float* k_scale,
+                              const int32_t* page_table, int64_t ld_pt, int page_size, int num_pages,
+                              const int32_t* q_pos, int n_seq, int q_per_seq, int max_ctx, int Hi, int Di,
+                              dsa_dtype_t dtype, float* scores, int64_t ld_scores, int k, int32_t* idx,
+                              int64_t ld_idx, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * dsa_sparse_mla_decode / dsa_sparse_mla_prefill -- attention over the selected rows only

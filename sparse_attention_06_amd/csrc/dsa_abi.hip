@@ -142,7 +142,7 @@ dsa_status_t dsa_indexer_scores(const void* q, const float* w, const void* k_cac
     const int64_t units = (int64_t)n_seq * q_per_seq / dsa::indexer_scan_rows_per_wave(q_per_seq);
     if (page_size == 64 && units <= 65535) {
       s = hip_status(dsa::launch_indexer_scan((const uint8_t*)q, w, kc, k_scale, q_pos, n_seq, q_per_seq,
-                                              max_ctx, scores, ld_scores, st), "indexer_scan launch");
+                                              max_ctx, scores, ld_scores, nullptr, st), "indexer_scan launch");
       return s == DSA_OK ? ok(DSA_PATH_INDEXER_SCAN_MFMA) : s;
     }
     s = hip_status(dsa::launch_indexer_prefill((const uint8_t*)q, w, kc, k_scale, q_pos, n_seq, q_per_seq,
@@ -170,8 +170,56 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_p
   if (rows == 0) return ok(DSA_PATH_NONE);
   int path = DSA_PATH_NONE;
   dsa_status_t s = hip_status(dsa::launch_topk(scores, ld_scores, q_pos, rows, max_ctx, k, idx, ld_idx, ws,
-                                               ws_bytes, (hipStream_t)stream, &path), "topk launch");
+                                               ws_bytes, nullptr, (hipStream_t)stream, &path), "topk launch");
   return s == DSA_OK ? ok(path) : s;
+}
+
+size_t dsa_indexer_topk_workspace_size(int rows, int max_ctx, int k) {
+  if (rows <= 0 || max_ctx < 1 || k < 1) return 0;
+  return 256 + (size_t)rows * dsa::kTopkDigit0Bins * 4 + dsa::topk_staged_ws_bytes(rows, max_ctx, k);
+}
+
+dsa_status_t dsa_indexer_topk(const void* q, const float* w, const void* k_cache, const float* k_scale,
+                              const int32_t* page_table, int64_t ld_pt, int page_size, int num_pages,
+                              const int32_t* q_pos, int n_seq, int q_per_seq, int max_ctx, int Hi, int Di,
+                              dsa_dtype_t dtype, float* scores, int64_t ld_scores, int k, int32_t* idx,
+                              int64_t ld_idx, void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(n_seq >= 0 && q_per_seq >= 1 && k >= 1 && max_ctx >= 1,
+          "need n_seq >= 0, q_per_seq >= 1, k >= 1 and max_ctx >= 1");
+  if (n_seq == 0) return ok(DSA_PATH_NONE);  // nothing to do; pointers may be NULL
+  REQUIRE(idx && ld_idx >= k, "idx must be non-NULL with ld_idx >= k");
+  REQUIRE((int64_t)n_seq * q_per_seq < ((int64_t)1 << 31), "too many rows");
+  const int rows = n_seq * q_per_seq;
+  const size_t need = dsa_indexer_topk_workspace_size(rows, max_ctx, k);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws ? ws_bytes : (size_t)0);
+  uint32_t* hist0 = (uint32_t*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
+  uint8_t* topk_ws = (uint8_t*)(hist0 + (size_t)rows * dsa::kTopkDigit0Bins);
+  const size_t topk_ws_bytes = (size_t)((uint8_t*)ws + ws_bytes - topk_ws);
+  const bool fused = Hi == 64 && Di == 128 && dtype == DSA_E4M3 && page_size == 64 &&
+                     (int64_t)rows / dsa::indexer_scan_rows_per_wave(q_per_seq) <= 65535 &&
+                     max_ctx <= dsa::topk_reg_max_ctx() && k <= dsa::topk_reg_max_k();
+  if (!fused) {
+    // the same two steps without the shared histogram
+    dsa_status_t s = dsa_indexer_scores(q, w, k_cache, k_scale, page_table, ld_pt, page_size, num_pages, q_pos,
+                                        n_seq, q_per_seq, max_ctx, Hi, Di, dtype, scores, ld_scores, stream);
+    if (s != DSA_OK) return s;
+    return dsa_topk(scores, ld_scores, q_pos, rows, max_ctx, k, idx, ld_idx, topk_ws, topk_ws_bytes, stream);
+  }
+  REQUIRE(q && w && k_cache && q_pos && scores, "q, w, k_cache, q_pos and scores must be non-NULL");
+  REQUIRE(!misaligned(q) && !misaligned(k_cache), "q and k_cache must be 16-byte aligned");
+  dsa_status_t s = check_paging(page_table, ld_pt, page_size, num_pages, max_ctx);
+  if (s != DSA_OK) return s;
+  REQUIRE(ld_scores >= max_ctx, "ld_scores (%lld) must be >= max_ctx (%d)", (long long)ld_scores, max_ctx);
+  dsa::PagedCache kc{k_cache, page_table, ld_pt, page_size, num_pages};
+  hipStream_t st = (hipStream_t)stream;
+  s = hip_status(dsa::launch_indexer_scan((const uint8_t*)q, w, kc, k_scale, q_pos, n_seq, q_per_seq, max_ctx,
+                                          scores, ld_scores, hist0, st), "indexer_scan launch");
+  if (s != DSA_OK) return s;
+  int path = DSA_PATH_NONE;
+  s = hip_status(dsa::launch_topk(scores, ld_scores, q_pos, rows, max_ctx, k, idx, ld_idx, nullptr, 0, hist0, st,
+                                  &path), "topk launch");
+  return s == DSA_OK ? ok(DSA_PATH_INDEXER_TOPK_FUSED) : s;
 }
 
 size_t dsa_sparse_mla_workspace_size(int rows, int H, int Dv, int k) {

@@ -186,6 +186,7 @@ constexpr int kScanWaves = 4;
 constexpr int kScanLdsBytes = kScanWaves * kWaveRingBytes;  // 69632
 
 typedef __attribute__((address_space(3))) uint8_t lds8;
+typedef __attribute__((address_space(3))) uint32_t lds32;
 
 // Two wave-wide 16-byte-per-lane loads of one 16-key slot (src = first key of the sub-tile);
 // with_scale adds the 4-byte-per-lane load of a page's 64 scales (ssrc = first scale). Exactly
@@ -389,10 +390,10 @@ __device__ __forceinline__ void scan_subtile(const ScanCtx& c, const QueryOps<NQ
 }
 
 // One page: four sub-tiles, then the page's reduction, scale, mask and stores.
-template <int NQ, int kTail>
+template <int NQ, bool kHist, int kTail>
 __device__ __forceinline__ void scan_page(const ScanCtx& c, const QueryOps<NQ>& o, int p, int jpage, int jend,
                                           bool has_scale, float* __restrict__ scores, int64_t ld_scores,
-                                          i32x4& raw0, i32x4& raw1, int lane) {
+                                          i32x4& raw0, i32x4& raw1, lds32* hist, int lane) {
   float v[NQ][kSubTiles];
   f32x4 carry[4];
   scan_subtile<NQ, kTail, 0>(c, o, p, has_scale, raw0, raw1, carry, v);
@@ -411,28 +412,23 @@ __device__ __forceinline__ void scan_page(const ScanCtx& c, const QueryOps<NQ>& 
     const float tot = reduce_page(v[qi][0], v[qi][1], v[qi][2], v[qi][3]);
     // exactly one store instruction per query row per page (lane 0 always has j < jend), so the
     // wait counts stay exact; positions past the row's q_pos get -inf
-    if (j < jend) scores[o.row[qi] * ld_scores + j] = (j <= o.tpos[qi] && page_ok) ? tot * sc : -INFINITY;
+    const float val = (j <= o.tpos[qi] && page_ok) ? tot * sc : -INFINITY;
+    if (j < jend) scores[o.row[qi] * ld_scores + j] = val;
+    if (kHist && j < jend && j <= o.tpos[qi]) {
+      // the row's first-digit histogram, two 16-bit counts per word
+      const uint32_t d = order_key(val) >> 21;
+      __hip_atomic_fetch_add(hist + qi * (kTopkDigit0Bins / 2) + (d >> 1), 1u << ((d & 1u) << 4), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
   }
 }
 
-template <int NQ>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) indexer_scan_kernel(
-    const uint8_t* __restrict__ q, const float* __restrict__ w, PagedCache kc,
-    const float* __restrict__ k_scale, const int32_t* __restrict__ q_pos, int q_per_seq, int keys_per_wave,
-    int max_ctx, float* __restrict__ scores, int64_t ld_scores) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kScanLdsBytes];
-  // this block's NQ query rows: unit * NQ .. + NQ - 1, all of one sequence (decode: the request's
-  // rows; prefill: two consecutive rows of the block)
-  const int unit = blockIdx.y;
-  const int seq = unit * NQ / q_per_seq;
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int tmax = -1;
-#pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) tmax = max(tmax, q_pos[unit * NQ + qi]);
-  // a wave's range starts on a page and spans at most 64 pages
-  const int jbeg = (blockIdx.x * kScanWaves + wave) * keys_per_wave;
-  const int jend = min(min(jbeg + keys_per_wave, tmax + 1), max_ctx);  // never past ld_scores
-  if (jbeg >= jend) return;
+// One wave's key range [jbeg, jend) of a unit's rows.
+template <int NQ, bool kHist>
+__device__ __forceinline__ void scan_range(const uint8_t* __restrict__ q, const float* __restrict__ w, PagedCache kc,
+                                           const float* __restrict__ k_scale, const int32_t* __restrict__ q_pos,
+                                           int unit, int seq, int jbeg, int jend, float* __restrict__ scores,
+                                           int64_t ld_scores, lds32* hist, uint8_t* smem, int lane, int wave) {
   const int np = (jend - jbeg + kScanPage - 1) / kScanPage;
   ScanCtx c;
   // the physical ids of the range's pages, one per lane, so the loop reads no page table from
@@ -478,12 +474,55 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   scan_read(c, 0, 0, raw0, raw1);
   int p = 0;
   for (; p + 2 < np; ++p)
-    scan_page<NQ, 0>(c, o, p, jbeg + kScanPage * p, jend, has_scale, scores, ld_scores, raw0, raw1, lane);
+    scan_page<NQ, kHist, 0>(c, o, p, jbeg + kScanPage * p, jend, has_scale, scores, ld_scores, raw0, raw1, hist, lane);
   if (p + 1 < np) {
-    scan_page<NQ, 1>(c, o, p, jbeg + kScanPage * p, jend, has_scale, scores, ld_scores, raw0, raw1, lane);
+    scan_page<NQ, kHist, 1>(c, o, p, jbeg + kScanPage * p, jend, has_scale, scores, ld_scores, raw0, raw1, hist, lane);
     ++p;
   }
-  scan_page<NQ, 2>(c, o, p, jbeg + kScanPage * p, jend, has_scale, scores, ld_scores, raw0, raw1, lane);
+  scan_page<NQ, kHist, 2>(c, o, p, jbeg + kScanPage * p, jend, has_scale, scores, ld_scores, raw0, raw1, hist, lane);
+}
+
+
+// Adds the workgroup's histogram counts into the rows' global histograms (non-zero bins only).
+template <int NQ>
+__device__ __forceinline__ void flush_hist(lds32* hist, uint32_t* __restrict__ hist0, int unit) {
+  __syncthreads();
+  for (int i = threadIdx.x; i < NQ * kTopkDigit0Bins / 2; i += 64 * kScanWaves) {
+    const uint32_t v = hist[i];
+    if (v == 0u) continue;
+    const int qi = i / (kTopkDigit0Bins / 2), b = 2 * (i % (kTopkDigit0Bins / 2));
+    uint32_t* g = hist0 + (int64_t)(unit * NQ + qi) * kTopkDigit0Bins + b;
+    if (v & 0xFFFFu) __hip_atomic_fetch_add(g, v & 0xFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v >> 16) __hip_atomic_fetch_add(g + 1, v >> 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int NQ, bool kHist>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) indexer_scan_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ w, PagedCache kc,
+    const float* __restrict__ k_scale, const int32_t* __restrict__ q_pos, int q_per_seq, int keys_per_wave,
+    int max_ctx, float* __restrict__ scores, int64_t ld_scores, uint32_t* __restrict__ hist0) {
+  // with kHist, the rows' first-digit histograms (2 x 16 bits per word) follow the rings
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kScanLdsBytes + (kHist ? NQ * kTopkDigit0Bins * 2 : 0)];
+  lds32* hist = (lds32*)((lds8*)smem + kScanLdsBytes);
+  if (kHist) {
+    for (int i = threadIdx.x; i < NQ * kTopkDigit0Bins / 8; i += 64 * kScanWaves)
+      *(__attribute__((address_space(3))) i32x4*)(hist + 4 * i) = i32x4{0, 0, 0, 0};
+    __syncthreads();
+  }
+  // this block's NQ query rows: unit * NQ .. + NQ - 1, all of one sequence (decode: the request's
+  // rows; prefill: two consecutive rows of the block)
+  const int unit = blockIdx.y;
+  const int seq = unit * NQ / q_per_seq;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int tmax = -1;
+#pragma unroll
+  for (int qi = 0; qi < NQ; ++qi) tmax = max(tmax, q_pos[unit * NQ + qi]);
+  // a wave's range starts on a page and spans at most 64 pages
+  const int jbeg = (blockIdx.x * kScanWaves + wave) * keys_per_wave;
+  const int jend = min(min(jbeg + keys_per_wave, tmax + 1), max_ctx);  // never past ld_scores
+  if (jbeg < jend) scan_range<NQ, kHist>(q, w, kc, k_scale, q_pos, unit, seq, jbeg, jend, scores, ld_scores, hist, smem, lane, wave);
+  if (kHist) flush_hist<NQ>(hist, hist0, unit);
 }
 
 // Prefill tiles: each wave owns 2 consecutive rows of one sequence and scans their causal
@@ -517,7 +556,7 @@ int indexer_scan_rows_per_wave(int q_per_seq) { return q_per_seq % 2 == 0 ? 2 : 
 
 hipError_t launch_indexer_scan(const uint8_t* q, const float* w, PagedCache kc, const float* k_scale,
                                const int32_t* q_pos, int n_seq, int q_per_seq, int max_ctx,
-                               float* scores, int64_t ld_scores, hipStream_t stream) {
+                               float* scores, int64_t ld_scores, uint32_t* hist0, hipStream_t stream) {
   // units of NQ query rows of one sequence; about 2048 waves (8 per CU) per launch for a decode
   // batch, each a whole number of pages (at most 64 of them)
   const int nq = indexer_scan_rows_per_wave(q_per_seq);
@@ -527,10 +566,15 @@ hipError_t launch_indexer_scan(const uint8_t* q, const float* w, PagedCache kc, 
   kpw = kpw < kScanPage ? kScanPage : (kpw > 64 * kScanPage ? 64 * kScanPage : kpw);
   const int per_block = kScanWaves * kpw;
   dim3 grid((max_ctx + per_block - 1) / per_block, units);
-  if (nq == 1)
-    hipLaunchKernelGGL(indexer_scan_kernel<1>, grid, dim3(64 * kScanWaves), 0, stream, q, w, kc, k_scale, q_pos, q_per_seq, kpw, max_ctx, scores, ld_scores);
+  const dim3 block(64 * kScanWaves);
+  if (nq == 1 && !hist0)
+    hipLaunchKernelGGL((indexer_scan_kernel<1, false>), grid, block, 0, stream, q, w, kc, k_scale, q_pos, q_per_seq, kpw, max_ctx, scores, ld_scores, hist0);
+  else if (nq == 1)
+    hipLaunchKernelGGL((indexer_scan_kernel<1, true>), grid, block, 0, stream, q, w, kc, k_scale, q_pos, q_per_seq, kpw, max_ctx, scores, ld_scores, hist0);
+  else if (!hist0)
+    hipLaunchKernelGGL((indexer_scan_kernel<2, false>), grid, block, 0, stream, q, w, kc, k_scale, q_pos, q_per_seq, kpw, max_ctx, scores, ld_scores, hist0);
   else
-    hipLaunchKernelGGL(indexer_scan_kernel<2>, grid, dim3(64 * kScanWaves), 0, stream, q, w, kc, k_scale, q_pos, q_per_seq, kpw, max_ctx, scores, ld_scores);
+    hipLaunchKernelGGL((indexer_scan_kernel<2, true>), grid, block, 0, stream, q, w, kc, k_scale, q_pos, q_per_seq, kpw, max_ctx, scores, ld_scores, hist0);
   return hipGetLastError();
 }
 

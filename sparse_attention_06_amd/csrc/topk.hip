@@ -34,12 +34,6 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kTopkLdsCap = 32768;  // positions staged in LDS (128 KB)
 
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;  // -0 ranks with +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (lane == 0) ? 0ull : (~0ull >> (64 - lane)); }
 
 __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restrict__ scores,
@@ -150,12 +144,11 @@ constexpr int kRegBins = 2048;                    // 11-bit digits: passes over 
 constexpr int kCandCap = 4096;                    // undecided keys compacted into LDS (also
                                                   // holds the k output positions, so k <= kCandCap)
 
-__device__ __forceinline__ uint32_t digit_of(uint32_t key, int pass) {
-  return pass == 0 ? key >> 21 : pass == 1 ? (key >> 10) & 2047u : key & 1023u;
-}
-__device__ __forceinline__ uint32_t mask_through(int pass) {  // key bits decided after `pass`
-  return pass == 0 ? 0xFFE00000u : pass == 1 ? 0xFFFFFC00u : 0xFFFFFFFFu;
-}
+// A pass's digit: `width` (at most 11) key bits from bit `shift` up.
+struct Digit {
+  uint32_t shift, mask;
+  __device__ __forceinline__ uint32_t of(uint32_t key) const { return (key >> shift) & mask; }
+};
 
 // Inclusive prefix sum over the 64 lanes of a wave: shifts within rows of 16 lanes, then the row
 // broadcasts carry row totals forward (DPP, no LDS round trip).
@@ -174,13 +167,13 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 // repeat a lot, and one atomic per key would serialise on the hot address); its other keys are
 // added one by one.
 __device__ __forceinline__ void hist_add_keys(uint32_t* hist, const uint32_t (&key)[kRegE], uint32_t vmask,
-                                              uint32_t pmask, uint32_t prefix, int pass) {
+                                              uint32_t pmask, uint32_t prefix, Digit dg) {
   uint32_t d0 = 0, run = 0;
   bool have = false;
 #pragma unroll
   for (int e = 0; e < kRegE; ++e) {
     const bool act = ((vmask >> e) & 1u) && (key[e] & pmask) == prefix;
-    const uint32_t d = digit_of(key[e], pass);
+    const uint32_t d = dg.of(key[e]);
     if (act && !have) { d0 = d; have = true; }
     run += (act && d == d0) ? 1u : 0u;
   }
@@ -188,7 +181,7 @@ __device__ __forceinline__ void hist_add_keys(uint32_t* hist, const uint32_t (&k
 #pragma unroll
   for (int e = 0; e < kRegE; ++e) {
     const bool act = ((vmask >> e) & 1u) && (key[e] & pmask) == prefix;
-    const uint32_t d = digit_of(key[e], pass);
+    const uint32_t d = dg.of(key[e]);
     if (act && d != d0) atomicAdd(&hist[d], 1u);
   }
 }
@@ -230,25 +223,48 @@ struct TopkLds {
   uint32_t ncand;
 };
 
+// Zero the histograms and the candidate count; the caller does this before its keys arrive and
+// reg_select's first barrier publishes it. With hist0 (the row's first-digit histogram, counted
+// by the producer of the scores) the first histogram is taken from there instead, and hist0 is
+// zeroed for the producer's next use.
+__device__ __forceinline__ void reg_select_init(TopkLds& sh, int tid, uint32_t* hist0) {
+  static_assert(kRegBins == kTopkDigit0Bins, "first digit: key bits 31..21");
+  const int given = hist0 ? kRegBins / 4 : 0;
+  for (int i = tid; i < 3 * kRegBins / 4; i += kTopkThreads) {
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (i < given) {
+      v = ((const uint4*)hist0)[i];
+      ((uint4*)hist0)[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    ((uint4*)&sh.hist[0][0])[i] = v;
+  }
+  if (tid == 0) sh.ncand = 0;
+}
+
 // The key of the k-th largest valid key (tau) and how many keys equal to tau are taken, over the
 // keys the block's threads hold (16 each, valid where vmask has the bit). Needs more than k valid
-// keys. Three passes over 11-, 11- and 10-bit digits; once the keys still undecided fit in LDS
-// they are compacted there and the remaining passes run over them alone.
-__device__ __forceinline__ void reg_select(const uint32_t (&key)[kRegE], uint32_t vmask, uint32_t k, TopkLds& sh, int tid,
-                           int wave, int lane, uint32_t& tau_out, uint32_t& remaining_out) {
-  for (int i = tid; i < 3 * kRegBins; i += kTopkThreads) (&sh.hist[0][0])[i] = 0;
-  if (tid == 0) sh.ncand = 0;
-  __syncthreads();
-  uint32_t prefix = 0, pmask = 0, remaining = k;
+// keys and reg_select_init since the keys' arrival. Three passes over 11-, 11- and 10-bit digits;
+// once the keys still undecided fit in LDS they are compacted there and the remaining passes run
+// over them alone.
+__device__ __forceinline__ void reg_select(const uint32_t (&key)[kRegE], uint32_t vmask, uint32_t k, bool hist0_given,
+                           TopkLds& sh, int tid, int wave, int lane, uint32_t& tau_out, uint32_t& remaining_out) {
+  __syncthreads();  // publishes reg_select_init
+  const int npass = 3;
+  uint32_t pmask = 0u;
+  uint32_t prefix = 0u, remaining = k;
   bool compacted = false;
   uint32_t nc = 0;
-  for (int pass = 0; pass < 3; ++pass) {
-    if (!compacted) {
-      hist_add_keys(sh.hist[pass], key, vmask, pmask, prefix, pass);
+  for (int pass = 0; pass < npass; ++pass) {
+    const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+    const Digit dg{(uint32_t)shift, pass == 2 ? 1023u : 2047u};
+    if (pass == 0 && hist0_given) {
+      // counted already
+    } else if (!compacted) {
+      hist_add_keys(sh.hist[pass], key, vmask, pmask, prefix, dg);
     } else {
       for (int i = tid; i < (int)nc; i += kTopkThreads) {
         const uint32_t kk = sh.cand_key[i];
-        if ((kk & pmask) == prefix) atomicAdd(&sh.hist[pass][digit_of(kk, pass)], 1u);
+        if ((kk & pmask) == prefix) atomicAdd(&sh.hist[pass][dg.of(kk)], 1u);
       }
     }
     __syncthreads();
@@ -256,9 +272,9 @@ __device__ __forceinline__ void reg_select(const uint32_t (&key)[kRegE], uint32_
     __syncthreads();
     const uint32_t digit = sh.pub[pass][0], above = sh.pub[pass][1], count = sh.pub[pass][2];
     remaining -= above;
-    prefix |= digit << (pass == 0 ? 21 : pass == 1 ? 10 : 0);
-    pmask = mask_through(pass);
-    if (!compacted && pass < 2 && count <= (uint32_t)kCandCap) {
+    prefix |= digit << shift;
+    pmask = shift == 0 ? 0xFFFFFFFFu : ~((1u << shift) - 1u);
+    if (!compacted && pass + 1 < npass && count <= (uint32_t)kCandCap) {
       // only keys sharing the decided top bits with the k-th largest are undecided: compact them,
       // one LDS atomic per wave for the wave's slots
       uint32_t mine = 0;
@@ -345,6 +361,7 @@ struct TopkStageArgs {
   int32_t* out_pos;
   int32_t* out_cnt;
   int out_chunks;
+  uint32_t* hist0;  // score rows of one chunk only: per row, the first-digit histogram (or null)
 };
 
 template <bool kSrcScores, bool kFinal>
@@ -353,6 +370,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_stage_kernel(TopkStageArgs 
   const int r = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t key[kRegE], vmask = 0;
+  uint32_t* const hist0 = kSrcScores && a.hist0 ? a.hist0 + (int64_t)r * kRegBins : nullptr;
+  reg_select_init(sh, tid, hist0);
   if (kSrcScores) {
     // this thread's positions: base .. base + 15. The row is read before q_pos is known (every
     // position below max_ctx lies inside the row), so the two memory latencies overlap.
@@ -378,16 +397,37 @@ __global__ void __launch_bounds__(kTopkThreads) topk_stage_kernel(TopkStageArgs 
       key[e] = v ? order_key(f[e]) : 0u;
     }
   } else {
-    // candidate slot g = 16 * tid + e of the row: chunk g / k, entry g % k
+    // candidate slot g = 16 * tid + e of the row: chunk g / k, entry g % k. Every slot below
+    // in_chunks * k lies in the workspace, so the keys and counts are loaded without waiting on
+    // each other (a slot past its chunk's count holds stale data and is masked off).
     const int64_t rb = (int64_t)r * a.in_chunks * a.k;
+    const int total = a.in_chunks * a.k, g0 = kRegE * tid;
+    const int32_t* cnt = a.in_cnt + (int64_t)r * a.in_chunks;
+    if (g0 + kRegE <= total && ((uintptr_t)(a.in_key + rb + g0) & 15) == 0) {
 #pragma unroll
-    for (int e = 0; e < kRegE; ++e) {
-      const int g = kRegE * tid + e;
-      const int ch = g / a.k;
-      const bool v = ch < a.in_chunks && g - ch * a.k < a.in_cnt[(int64_t)r * a.in_chunks + ch];
-      vmask |= (v ? 1u : 0u) << e;
-      key[e] = v ? a.in_key[rb + g] : 0u;
+      for (int v = 0; v < kRegE / 4; ++v) {
+        const uint4 x = *(const uint4*)(a.in_key + rb + g0 + 4 * v);
+        key[4 * v] = x.x; key[4 * v + 1] = x.y; key[4 * v + 2] = x.z; key[4 * v + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kRegE; ++e) key[e] = g0 + e < total ? a.in_key[rb + g0 + e] : 0u;
     }
+    const int ch0 = g0 / a.k, ch1 = (g0 + kRegE - 1) / a.k;
+    if (ch0 == ch1) {  // the thread's slots share one chunk (always when k is a multiple of 16)
+      const int n0 = ch0 < a.in_chunks ? cnt[ch0] : 0, e_end = ch0 * a.k + n0 - g0;
+#pragma unroll
+      for (int e = 0; e < kRegE; ++e) vmask |= (e < e_end ? 1u : 0u) << e;
+    } else {
+#pragma unroll
+      for (int e = 0; e < kRegE; ++e) {
+        const int g = g0 + e, ch = g / a.k;
+        const bool v = ch < a.in_chunks && g - ch * a.k < cnt[ch];
+        vmask |= (v ? 1u : 0u) << e;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kRegE; ++e) key[e] = ((vmask >> e) & 1u) ? key[e] : 0u;
   }
   // keys held by the block: the chunk's share of the row, or the sum of the input chunks' counts
   uint32_t nvalid = 0;
@@ -397,28 +437,42 @@ __global__ void __launch_bounds__(kTopkThreads) topk_stage_kernel(TopkStageArgs 
     const int len = n - kRegKeys * c;
     nvalid = len < 0 ? 0u : (uint32_t)min(len, kRegKeys);
   } else {
-    for (int ch = 0; ch < a.in_chunks; ++ch) nvalid += (uint32_t)a.in_cnt[(int64_t)r * a.in_chunks + ch];
+    // lanes load the counts side by side (a loop of dependent loads would serialise them)
+    uint32_t part = 0;
+    for (int ch = lane; ch < a.in_chunks; ch += kWave) part += (uint32_t)a.in_cnt[(int64_t)r * a.in_chunks + ch];
+    nvalid = __builtin_amdgcn_readlane(wave_incl_scan(part), 63);
   }
   const uint32_t k = (uint32_t)a.k;
   const bool take_all = nvalid <= k;
   uint32_t tau = 0, remaining = k;
-  if (!take_all) reg_select(key, vmask, k, sh, tid, wave, lane, tau, remaining);
-  // positions: computed for a score row, read back from the input slots for candidates (from an
-  // opaque copy of the base, so that the 16 positions are not kept live since the loads)
+  if (!take_all) reg_select(key, vmask, k, hist0 != nullptr, sh, tid, wave, lane, tau, remaining);
+  // staged per selected key: its position for a score row, its input slot for candidates (the
+  // slot's position is read when the result is written, by every thread at once)
   int obase = kSrcScores ? kRegKeys * c + kRegE * tid : kRegE * tid;
-  asm volatile("" : "+v"(obase));
+  asm volatile("" : "+v"(obase));  // opaque: the 16 values are formed when they are stored
   const int64_t rb = (int64_t)r * a.in_chunks * a.k;
-  const uint32_t nsel = stage_selected(
-      key, [&](int e) { return kSrcScores ? (uint32_t)(obase + e) : (uint32_t)a.in_pos[rb + obase + e]; }, vmask,
-      take_all, tau, remaining, !kFinal, sh, wave, lane);
+  const uint32_t nsel = stage_selected(key, [&](int e) { return (uint32_t)(obase + e); }, vmask, take_all, tau,
+                                       remaining, !kFinal, sh, wave, lane);
+  auto pos_at = [&](int i) { return kSrcScores ? (int32_t)sh.cand_pos[i] : a.in_pos[rb + sh.cand_pos[i]]; };
   if (kFinal) {
+    // all of a thread's (at most kCandCap / kTopkThreads) reads are issued before its stores
     int32_t* out = a.idx + (int64_t)r * a.ld_idx;
-    for (int i = tid; i < a.k; i += kTopkThreads) out[i] = i < (int)nsel ? (int32_t)sh.cand_pos[i] : -1;
+    int32_t v[kCandCap / kTopkThreads];
+#pragma unroll
+    for (int j = 0; j < kCandCap / kTopkThreads; ++j) {
+      const int i = tid + j * kTopkThreads;
+      v[j] = i < (int)nsel ? pos_at(i) : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kCandCap / kTopkThreads; ++j) {
+      const int i = tid + j * kTopkThreads;
+      if (i < a.k) out[i] = v[j];
+    }
   } else {
     const int64_t ob = ((int64_t)r * a.out_chunks + c) * a.k;
     for (int i = tid; i < (int)nsel; i += kTopkThreads) {
       a.out_key[ob + i] = sh.cand_key[i];
-      a.out_pos[ob + i] = (int32_t)sh.cand_pos[i];
+      a.out_pos[ob + i] = pos_at(i);
     }
     if (tid == 0) a.out_cnt[(int64_t)r * a.out_chunks + c] = (int32_t)nsel;
   }
@@ -428,6 +482,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_stage_kernel(TopkStageArgs 
 // them. The union of the chunks' top-k sets holds the row's top-k under the same order (value,
 // then position), and the candidates stay in ascending position order, so ties still go to the
 // smaller position. Usable while every row's candidates fit one block.
+int topk_reg_max_ctx() { return kRegKeys; }
+int topk_reg_max_k() { return kCandCap; }
 int topk_chunks(int max_ctx) { return (max_ctx + kRegKeys - 1) / kRegKeys; }
 bool topk_staged_ok(int max_ctx, int k) {
   return max_ctx > kRegKeys && k <= kCandCap && (int64_t)topk_chunks(max_ctx) * k <= kRegKeys;
@@ -440,11 +496,12 @@ size_t topk_staged_ws_bytes(int rows, int max_ctx, int k) {
 
 hipError_t launch_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int rows,
                        int max_ctx, int k, int32_t* idx, int64_t ld_idx, void* ws, size_t ws_bytes,
-                       hipStream_t stream, int* path) {
+                       uint32_t* hist0, hipStream_t stream, int* path) {
   TopkStageArgs a{};
   a.scores = scores; a.ld_scores = ld_scores; a.q_pos = q_pos; a.max_ctx = max_ctx; a.k = k;
   a.idx = idx; a.ld_idx = ld_idx;
   if (max_ctx <= kRegKeys && k <= kCandCap) {
+    a.hist0 = hist0;
     *path = (max_ctx <= k) ? DSA_PATH_TOPK_COPY : DSA_PATH_TOPK_RADIX_REG;
     hipLaunchKernelGGL((topk_stage_kernel<true, true>), dim3(1, rows), dim3(kTopkThreads), 0, stream, a);
     return hipGetLastError();

@@ -17,7 +17,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so"
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
 DSA_E4M3, DSA_F32, DSA_BF16 = 0, 1, 2
 PATHS = {
-    0: "none", 1: "indexer_generic", 2: "indexer_scan_mfma", 3: "indexer_prefill_mfma",
+    0: "none", 1: "indexer_generic", 2: "indexer_scan_mfma", 3: "indexer_prefill_mfma", 4: "indexer_topk_fused",
     10: "topk_copy", 11: "topk_radix", 12: "topk_radix_reg", 13: "topk_radix_staged", 20: "mla_generic", 21: "mla_mfma", 22: "mla_mfma_split",
     30: "mha_mfma", 31: "mha_mfma_masked", 40: "cache_write", 41: "quantize",
 }
@@ -25,6 +25,7 @@ PATHS = {
 EXPORTS = [
     "dsa_status_string", "dsa_last_error", "dsa_last_path",
     "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk",
+    "dsa_indexer_topk_workspace_size", "dsa_indexer_topk",
     "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
     "dsa_dense_mla_workspace_size", "dsa_dense_mla_prefill",
     "dsa_expanded_mha_workspace_size", "dsa_expanded_mha_prefill",
@@ -68,6 +69,11 @@ def load():
     lib.dsa_topk_workspace_size.argtypes = [i32, i32, i32]
     lib.dsa_topk.restype = i32
     lib.dsa_topk.argtypes = [vp, i64, vp, i32, i32, i32, vp, i64, vp, sz, vp]
+    lib.dsa_indexer_topk_workspace_size.restype = sz
+    lib.dsa_indexer_topk_workspace_size.argtypes = [i32, i32, i32]
+    lib.dsa_indexer_topk.restype = i32
+    lib.dsa_indexer_topk.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, vp, i32, i32, i32, i32, i32, i32,
+                                     vp, i64, i32, vp, i64, vp, sz, vp]
     lib.dsa_sparse_mla_workspace_size.restype = sz
     lib.dsa_sparse_mla_workspace_size.argtypes = [i32, i32, i32, i32]
     attn = [vp, vp, vp, i64, i32, i32, vp, i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, sz, vp]
@@ -171,6 +177,43 @@ def topk(scores, q_pos, max_ctx, k, idx=None, ws=None, stream=None):
                          0 if ws is None else ws.numel(), _stream(stream))
     _check("dsa_topk", st)
     return idx
+
+
+def indexer_topk_workspace_size(rows, max_ctx, k) -> int:
+    return int(load().dsa_indexer_topk_workspace_size(rows, max_ctx, k))
+
+
+def indexer_topk(q, w, k_cache, k_scale, page_table, q_pos, n_seq, q_per_seq, max_ctx, k, scores=None, idx=None,
+                 ws=None, stream=None):
+    """indexer_scores then topk in one call (the top-k's first radix pass counted during the scan).
+    `ws` (uint8, at least indexer_topk_workspace_size bytes) must be zero-filled before its first
+    use and is left so by every successful call; a zeroed one is allocated here when not given.
+    Returns (scores, idx)."""
+    dtype = DSA_E4M3 if q.dtype == torch.uint8 else DSA_F32
+    _need(q, "q", q.dtype, 3)
+    _need(k_cache, "k_cache", q.dtype, 3)
+    _need(w, "w", torch.float32, 2)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(q_pos, "q_pos", torch.int32, 1)
+    if k_scale is not None:
+        _need(k_scale, "k_scale", torch.float32)
+    rows, Hi, Di = q.shape
+    if rows != n_seq * q_per_seq or q_pos.numel() != rows:
+        raise ValueError("rows must equal n_seq * q_per_seq")
+    if scores is None:
+        scores = torch.empty(rows, max_ctx, dtype=torch.float32, device=q.device)
+    _need(scores, "scores", torch.float32, 2)
+    if idx is None:
+        idx = torch.empty(rows, k, dtype=torch.int32, device=q.device)
+    _need(idx, "idx", torch.int32, 2)
+    if ws is None and rows > 0:
+        ws = torch.zeros(indexer_topk_workspace_size(rows, max_ctx, k), dtype=torch.uint8, device=q.device)
+    st = load().dsa_indexer_topk(_p(q), _p(w), _p(k_cache), _p(k_scale), _p(page_table), page_table.shape[1],
+                                 k_cache.shape[1], k_cache.shape[0], _p(q_pos), n_seq, q_per_seq, max_ctx, Hi, Di,
+                                 dtype, _p(scores), scores.shape[1], k, _p(idx), idx.shape[1], _p(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream))
+    _check("dsa_indexer_topk", st)
+    return scores, idx
 
 
 def sparse_mla_workspace_size(rows, H, Dv, k) -> int:

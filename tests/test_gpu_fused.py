@@ -1,0 +1,113 @@
+"""The fused indexer -> top-k call (dsa_indexer_topk) on the GPU.
+
+The scan counts each row's valid scores by the top-k's first radix digit and the top-k starts
+from those counts. Checks: the scores against the oracle (as for dsa_indexer_scores); the index
+sets against the oracle's top-k of the oracle's scores (sets equal outside the tie band, as for
+the separate calls); and the index lists bit for bit against dsa_topk on the same scores, whose
+own parity with the oracle is exact. Repeated calls on one workspace (the histogram is left
+zero by each call), rows of both unit widths (two MTP rows per scan unit, or one), rows no
+longer than k, rows whose scores all tie (zero head weights) or are all <= 0 with signed zeros
+(negative head weights), and the full-size decode batches.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import check_scores, check_topk_sets, gpu_inputs
+from sparse_attention_06_amd import dsa
+
+pytestmark = pytest.mark.gpu
+
+
+def _fused(w, d, ws, k=None):
+    return dsa.indexer_topk(d["iq"], d["iw"], d["ik"], d["iks"], d["page_table"], d["q_pos"], w.n_seq, w.q_per_seq,
+                            w.max_ctx, k or w.topk, ws=ws)
+
+
+def _hist_part_zero(ws, rows):
+    base = (-ws.data_ptr()) % 256
+    return bool((ws[base: base + rows * 2048 * 4] == 0).all())
+
+
+@pytest.mark.parametrize("qps,q_pos,max_ctx", [
+    (2, [4999, 4998, 3000, 3001, 100, 2047], 5000),
+    (1, [4095, 0, 2048, 3333, 64], 4096),
+    (2, [16383, 16383, 9000, 9001], 16384),
+])
+def test_fused_indexer_topk_matches_oracle(oracle_lib, qps, q_pos, max_ctx):
+    print(f"case: fused indexer+topk qps={qps} q_pos={q_pos}", flush=True)
+    n_seq = len(q_pos) // qps
+    w = workloads.make_random(n_seq, qps, q_pos, max_ctx, H=2, Dqk=16, Dv=8, seed=57 + qps, permute_pages=True,
+                              extra_pages=3)
+    if qps == 2:
+        w.iw[2:4] = 0.0                     # one unit: every score 0, all keys tie
+        if w.rows > 4:
+            w.iw[4] = -np.abs(w.iw[4])      # scores <= 0: -0 and +0 rank equal
+    d = gpu_inputs(w)
+    rows = w.rows
+    ws = torch.zeros(dsa.indexer_topk_workspace_size(rows, max_ctx, w.topk), dtype=torch.uint8, device="cuda")
+    results = []
+    for _ in range(3):                      # the workspace is reused: each call re-zeroes its histogram
+        s, idx = _fused(w, d, ws)
+        torch.cuda.synchronize()
+        assert dsa.last_path() == "indexer_topk_fused"
+        assert _hist_part_zero(ws, rows)
+        results.append((s.cpu().numpy(), idx.cpu().numpy()))
+    for s_i, idx_i in results[1:]:
+        for r in range(rows):               # entries past q_pos[r] are unspecified
+            n = int(w.q_pos[r]) + 1
+            np.testing.assert_array_equal(s_i[r, :n].view(np.uint32), results[0][0][r, :n].view(np.uint32))
+        np.testing.assert_array_equal(idx_i, results[0][1])
+    s_gpu, idx_gpu = results[0]
+    ref_s = oracle.indexer_scores(w.iq, w.iw, w.ik, w.iks, w.page_table, w.page_size, w.q_pos, w.n_seq,
+                                  w.q_per_seq, w.fmt, w.max_ctx, threads=8)
+    check_scores(s_gpu, ref_s, w.q_pos)
+    check_topk_sets(idx_gpu, oracle.topk(ref_s, w.q_pos, w.topk, threads=8), ref_s, w.q_pos, w.topk)
+    sep = dsa.topk(torch.from_numpy(s_gpu).cuda(), d["q_pos"], max_ctx, w.topk).cpu().numpy()
+    np.testing.assert_array_equal(idx_gpu, sep)
+    if qps == 2:
+        # all-tie unit: the k smallest positions; non-positive row: equal to the separate top-k
+        for r in (2, 3):
+            n = int(w.q_pos[r]) + 1
+            np.testing.assert_array_equal(idx_gpu[r, :min(n, w.topk)], np.arange(min(n, w.topk)))
+
+
+@pytest.mark.parametrize("name", ["decode_mtp_b64_16k", "decode_b16_4k", "decode_b4_128k"])
+def test_fused_full_size_equals_separate_calls(oracle_lib, name):
+    """Full-size decode batches: index lists bit for bit equal to the separate calls; 128K rows
+    take the separate calls inside the fused entry point (staged top-k)."""
+    print(f"case: fused full size {name}", flush=True)
+    w = getattr(workloads, "make_" + name)()
+    d = gpu_inputs(w)
+    ws = torch.zeros(dsa.indexer_topk_workspace_size(w.rows, w.max_ctx, w.topk), dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        s, idx = _fused(w, d, ws)
+    torch.cuda.synchronize()
+    assert dsa.last_path() == ("indexer_topk_fused" if w.max_ctx <= 16384 else "topk_radix_staged")
+    assert _hist_part_zero(ws, w.rows)
+    s_sep = dsa.indexer_scores(d["iq"], d["iw"], d["ik"], d["iks"], d["page_table"], d["q_pos"], w.n_seq,
+                               w.q_per_seq, w.max_ctx)
+    idx_sep = dsa.topk(s_sep, d["q_pos"], w.max_ctx, w.topk)
+    torch.cuda.synchronize()
+    s_h, s_sep_h = s.cpu().numpy().view(np.uint32), s_sep.cpu().numpy().view(np.uint32)
+    for r in range(w.rows):                 # entries past q_pos[r] are unspecified
+        n = int(w.q_pos[r]) + 1
+        np.testing.assert_array_equal(s_h[r, :n], s_sep_h[r, :n])
+    assert torch.equal(idx, idx_sep)
+    # sampled rows against the oracle
+    rows = sorted({0, w.rows - 1, w.rows // 2})
+    ref_s = oracle.indexer_scores(w.iq, w.iw, w.ik, w.iks, w.page_table, w.page_size, w.q_pos, w.n_seq,
+                                  w.q_per_seq, w.fmt, w.max_ctx, threads=8, rows=rows)
+    check_scores(s.cpu().numpy(), ref_s, w.q_pos, rows=rows)
+    ref_idx = oracle.topk(ref_s[rows], w.q_pos[rows], w.topk, threads=8)
+    check_topk_sets(idx.cpu().numpy()[rows], ref_idx, ref_s[rows], w.q_pos[rows], w.topk)
+
+
+def test_fused_rejects_small_workspace():
+    w = workloads.make_random(1, 2, [300, 301], 320, H=2, Dqk=16, Dv=8, seed=3)
+    d = gpu_inputs(w)
+    need = dsa.indexer_topk_workspace_size(w.rows, w.max_ctx, w.topk)
+    with pytest.raises(dsa.DSAError, match="WORKSPACE"):
+        _fused(w, d, torch.zeros(need - 1, dtype=torch.uint8, device="cuda"))

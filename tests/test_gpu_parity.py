@@ -176,6 +176,21 @@ def test_topk_long_rows_staged_and_without_workspace(oracle_lib):
     np.testing.assert_array_equal(idx.cpu().numpy(), r)
 
 
+@pytest.mark.parametrize("n,k", [(40000, 1001), (50000, 2047), (70000, 16)])
+def test_topk_staged_ragged_k(oracle_lib, n, k):
+    """The two-stage selection with k not a multiple of 16: a thread's candidate slots straddle two
+    chunks, and rows start at offsets that are not 16-byte aligned; rows that end inside the first
+    and second chunks leave chunks with fewer than k (or no) candidates."""
+    _say(f"case: topk staged n={n} k={k}")
+    rng = np.random.default_rng(n ^ k)
+    sc = rng.standard_normal((5, n)).astype(np.float32)
+    sc[2, ::7] = 0.5                              # ties across chunk boundaries
+    q_pos = np.array([n - 1, n - 2, n - 1, 16383 + k // 2, 20000], np.int32)
+    g, r = _topk_case(sc, q_pos, k)
+    assert dsa.last_path() == "topk_radix_staged"
+    np.testing.assert_array_equal(g, r)
+
+
 def test_topk_empty_and_tiny_rows(oracle_lib):
     _say("case: topk tiny rows")
     sc = np.random.default_rng(6).standard_normal((3, 64)).astype(np.float32)
