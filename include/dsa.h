@@ -144,9 +144,10 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_p
  *       caller and reused across calls: it must be ZERO-FILLED before its first use, and every
  *       call that returns DSA_OK leaves its histogram part zero again (after a failed call,
  *       zero it again). Calls sharing one workspace must not overlap in time.
- * The shared histogram is used for the MFMA scan shapes (Hi=64, Di=128, E4M3, 64-token pages)
- * with max_ctx <= 16384 and k <= 4096 (DSA_PATH_INDEXER_TOPK_FUSED). Other shapes run the two
- * calls one after the other (the path is then the top-k's).
+ * The shared counts are used for the MFMA scan shapes (Hi=64, Di=128, E4M3, 64-token pages) with
+ * max_ctx <= 16384 and k <= 4096, or rows the two-stage top-k takes (counts per 16384-position
+ * chunk) (DSA_PATH_INDEXER_TOPK_FUSED). Other shapes run the two calls one after the other (the
+ * path is then the top-k's).
  * ------------------------------------------------------------------------------------------- */
 size_t dsa_indexer_topk_workspace_size(int rows, int max_ctx, int k);
 dsa_status_t dsa_indexer_topk(const void* q, const float* w, const void* k_cache, const float* k_scale,

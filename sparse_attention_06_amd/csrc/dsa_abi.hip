@@ -176,7 +176,8 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_p
 
 size_t dsa_indexer_topk_workspace_size(int rows, int max_ctx, int k) {
   if (rows <= 0 || max_ctx < 1 || k < 1) return 0;
-  return 256 + (size_t)rows * dsa::kTopkDigit0Bins * 4 + dsa::topk_staged_ws_bytes(rows, max_ctx, k);
+  return 256 + (size_t)rows * dsa::topk_chunks(max_ctx) * dsa::kTopkDigit0Bins * 4 +
+         dsa::topk_staged_ws_bytes(rows, max_ctx, k);
 }
 
 dsa_status_t dsa_indexer_topk(const void* q, const float* w, const void* k_cache, const float* k_scale,
@@ -194,11 +195,12 @@ dsa_status_t dsa_indexer_topk(const void* q, const float* w, const void* k_cache
   if (!ws || ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws ? ws_bytes : (size_t)0);
   uint32_t* hist0 = (uint32_t*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
-  uint8_t* topk_ws = (uint8_t*)(hist0 + (size_t)rows * dsa::kTopkDigit0Bins);
+  uint8_t* topk_ws = (uint8_t*)(hist0 + (size_t)rows * dsa::topk_chunks(max_ctx) * dsa::kTopkDigit0Bins);
   const size_t topk_ws_bytes = (size_t)((uint8_t*)ws + ws_bytes - topk_ws);
   const bool fused = Hi == 64 && Di == 128 && dtype == DSA_E4M3 && page_size == 64 &&
                      (int64_t)rows / dsa::indexer_scan_rows_per_wave(q_per_seq) <= 65535 &&
-                     max_ctx <= dsa::topk_reg_max_ctx() && k <= dsa::topk_reg_max_k();
+                     (max_ctx <= dsa::topk_reg_max_ctx() ? k <= dsa::topk_reg_max_k()
+                                                        : dsa::topk_staged_ok(max_ctx, k));
   if (!fused) {
     // the same two steps without the shared histogram
     dsa_status_t s = dsa_indexer_scores(q, w, k_cache, k_scale, page_table, ld_pt, page_size, num_pages, q_pos,
@@ -217,8 +219,8 @@ dsa_status_t dsa_indexer_topk(const void* q, const float* w, const void* k_cache
                                           scores, ld_scores, hist0, st), "indexer_scan launch");
   if (s != DSA_OK) return s;
   int path = DSA_PATH_NONE;
-  s = hip_status(dsa::launch_topk(scores, ld_scores, q_pos, rows, max_ctx, k, idx, ld_idx, nullptr, 0, hist0, st,
-                                  &path), "topk launch");
+  s = hip_status(dsa::launch_topk(scores, ld_scores, q_pos, rows, max_ctx, k, idx, ld_idx, topk_ws, topk_ws_bytes,
+                                  hist0, st, &path), "topk launch");
   return s == DSA_OK ? ok(DSA_PATH_INDEXER_TOPK_FUSED) : s;
 }
 

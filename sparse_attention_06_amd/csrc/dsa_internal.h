@@ -76,6 +76,7 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 constexpr int kTopkDigit0Bins = 2048;  // first radix digit: key bits 31..21
+constexpr int kTopkChunkKeys = 16384;  // positions per top-k chunk (a row's first-digit counts are per chunk)
 
 struct PagedCache {
   const void* base;
@@ -90,8 +91,9 @@ hipError_t launch_indexer_generic(const void* q, const float* w, PagedCache kc, 
                                   int Di, int is_f32, float* scores, int64_t ld_scores,
                                   hipStream_t stream);
 int indexer_scan_rows_per_wave(int q_per_seq);
-// hist0 (optional, zero on entry): per row, a kTopkDigit0Bins-bin count of the scores at
-// positions 0..q_pos[r] by their key's first digit, added with device-scope atomics
+// hist0 (optional, zero on entry): per row and kTopkChunkKeys-position chunk (row-major), a
+// kTopkDigit0Bins-bin count of the scores at positions 0..q_pos[r] by their key's first digit,
+// added with device-scope atomics
 hipError_t launch_indexer_scan(const uint8_t* q, const float* w, PagedCache kc, const float* k_scale,
                                const int32_t* q_pos, int n_seq, int q_per_seq, int max_ctx,
                                float* scores, int64_t ld_scores, uint32_t* hist0, hipStream_t stream);
@@ -100,14 +102,16 @@ hipError_t launch_indexer_prefill(const uint8_t* q, const float* w, PagedCache k
                                   int q_per_seq, int max_ctx, float* scores, int64_t ld_scores,
                                   hipStream_t stream);
 
-// hist0 (optional, rows of at most topk_reg_max_ctx() positions and k <= topk_reg_max_k()):
-// per row, the first-digit histogram of the row's valid scores, as launch_indexer_scan counts
-// it; read in place of the first radix pass and left zeroed
+// hist0 (optional; rows of at most topk_reg_max_ctx() positions with k <= topk_reg_max_k(), or
+// the two-stage path): per row and chunk, the first-digit histogram of the valid scores, as
+// launch_indexer_scan counts it; read in place of the first radix pass and left zeroed
 hipError_t launch_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int rows,
                        int max_ctx, int k, int32_t* idx, int64_t ld_idx, void* ws, size_t ws_bytes,
                        uint32_t* hist0, hipStream_t stream, int* path);
 int topk_reg_max_ctx();
 int topk_reg_max_k();
+int topk_chunks(int max_ctx);
+bool topk_staged_ok(int max_ctx, int k);
 size_t topk_staged_ws_bytes(int rows, int max_ctx, int k);
 
 struct AttnArgs {

@@ -485,13 +485,13 @@ __device__ __forceinline__ void scan_range(const uint8_t* __restrict__ q, const 
 
 // Adds the workgroup's histogram counts into the rows' global histograms (non-zero bins only).
 template <int NQ>
-__device__ __forceinline__ void flush_hist(lds32* hist, uint32_t* __restrict__ hist0, int unit) {
+__device__ __forceinline__ void flush_hist(lds32* hist, uint32_t* __restrict__ hist0, int unit, int chunks, int chunk) {
   __syncthreads();
   for (int i = threadIdx.x; i < NQ * kTopkDigit0Bins / 2; i += 64 * kScanWaves) {
     const uint32_t v = hist[i];
     if (v == 0u) continue;
     const int qi = i / (kTopkDigit0Bins / 2), b = 2 * (i % (kTopkDigit0Bins / 2));
-    uint32_t* g = hist0 + (int64_t)(unit * NQ + qi) * kTopkDigit0Bins + b;
+    uint32_t* g = hist0 + ((int64_t)(unit * NQ + qi) * chunks + chunk) * kTopkDigit0Bins + b;
     if (v & 0xFFFFu) __hip_atomic_fetch_add(g, v & 0xFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (v >> 16) __hip_atomic_fetch_add(g + 1, v >> 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -522,7 +522,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int jbeg = (blockIdx.x * kScanWaves + wave) * keys_per_wave;
   const int jend = min(min(jbeg + keys_per_wave, tmax + 1), max_ctx);  // never past ld_scores
   if (jbeg < jend) scan_range<NQ, kHist>(q, w, kc, k_scale, q_pos, unit, seq, jbeg, jend, scores, ld_scores, hist, smem, lane, wave);
-  if (kHist) flush_hist<NQ>(hist, hist0, unit);
+  // a workgroup's keys lie in one top-k chunk (its range is a power of two of at most a chunk)
+  if (kHist) flush_hist<NQ>(hist, hist0, unit, (max_ctx + kTopkChunkKeys - 1) / kTopkChunkKeys,
+                         blockIdx.x * kScanWaves * keys_per_wave / kTopkChunkKeys);
 }
 
 // Prefill tiles: each wave owns 2 consecutive rows of one sequence and scans their causal
@@ -552,6 +554,8 @@ __global__ void __launch_bounds__(256) indexer_prefill_kernel(
   }
 }
 
+static_assert(kTopkChunkKeys % (kScanWaves * 64 * kScanPage) == 0, "a workgroup range never straddles a chunk");
+
 int indexer_scan_rows_per_wave(int q_per_seq) { return q_per_seq % 2 == 0 ? 2 : 1; }
 
 hipError_t launch_indexer_scan(const uint8_t* q, const float* w, PagedCache kc, const float* k_scale,
@@ -564,6 +568,13 @@ hipError_t launch_indexer_scan(const uint8_t* q, const float* w, PagedCache kc, 
   const int64_t total = (int64_t)units * max_ctx;
   int kpw = (int)((total / 2048 + kScanPage - 1) / kScanPage * kScanPage);
   kpw = kpw < kScanPage ? kScanPage : (kpw > 64 * kScanPage ? 64 * kScanPage : kpw);
+  if (hist0) {
+    // counted per top-k chunk: a workgroup's range (4 kpw) must not straddle one, so kpw is a
+    // power of two (64 .. 4096 keys) and 4 kpw divides the chunk
+    int p2 = kScanPage;
+    while (p2 < kpw) p2 *= 2;
+    kpw = p2;
+  }
   const int per_block = kScanWaves * kpw;
   dim3 grid((max_ctx + per_block - 1) / per_block, units);
   const dim3 block(64 * kScanWaves);

@@ -361,7 +361,7 @@ struct TopkStageArgs {
   int32_t* out_pos;
   int32_t* out_cnt;
   int out_chunks;
-  uint32_t* hist0;  // score rows of one chunk only: per row, the first-digit histogram (or null)
+  uint32_t* hist0;  // score rows: per row and chunk, the first-digit histogram (or null)
 };
 
 template <bool kSrcScores, bool kFinal>
@@ -370,7 +370,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_stage_kernel(TopkStageArgs 
   const int r = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t key[kRegE], vmask = 0;
-  uint32_t* const hist0 = kSrcScores && a.hist0 ? a.hist0 + (int64_t)r * kRegBins : nullptr;
+  uint32_t* const hist0 = kSrcScores && a.hist0 ? a.hist0 + ((int64_t)r * gridDim.x + c) * kRegBins : nullptr;
   reg_select_init(sh, tid, hist0);
   if (kSrcScores) {
     // this thread's positions: base .. base + 15. The row is read before q_pos is known (every
@@ -482,6 +482,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_stage_kernel(TopkStageArgs 
 // them. The union of the chunks' top-k sets holds the row's top-k under the same order (value,
 // then position), and the candidates stay in ascending position order, so ties still go to the
 // smaller position. Usable while every row's candidates fit one block.
+static_assert(kRegKeys == kTopkChunkKeys, "chunks of the first-digit counts");
 int topk_reg_max_ctx() { return kRegKeys; }
 int topk_reg_max_k() { return kCandCap; }
 int topk_chunks(int max_ctx) { return (max_ctx + kRegKeys - 1) / kRegKeys; }
@@ -516,12 +517,14 @@ hipError_t launch_topk(const float* scores, int64_t ld_scores, const int32_t* q_
     a.out_pos = (int32_t*)(p + slots * 4);
     a.out_cnt = (int32_t*)(p + slots * 8);
     a.out_chunks = C;
+    a.hist0 = hist0;
     hipLaunchKernelGGL((topk_stage_kernel<true, false>), dim3(C, rows), dim3(kTopkThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     TopkStageArgs b = a;
     b.in_key = a.out_key; b.in_pos = a.out_pos; b.in_cnt = a.out_cnt; b.in_chunks = C;
     b.out_key = nullptr; b.out_pos = nullptr; b.out_cnt = nullptr; b.out_chunks = 0;
+    b.hist0 = nullptr;
     hipLaunchKernelGGL((topk_stage_kernel<false, true>), dim3(1, rows), dim3(kTopkThreads), 0, stream, b);
     return hipGetLastError();
   }

@@ -26,15 +26,16 @@ def _fused(w, d, ws, k=None):
                             w.max_ctx, k or w.topk, ws=ws)
 
 
-def _hist_part_zero(ws, rows):
+def _hist_part_zero(ws, hists):
     base = (-ws.data_ptr()) % 256
-    return bool((ws[base: base + rows * 2048 * 4] == 0).all())
+    return bool((ws[base: base + hists * 2048 * 4] == 0).all())
 
 
 @pytest.mark.parametrize("qps,q_pos,max_ctx", [
     (2, [4999, 4998, 3000, 3001, 100, 2047], 5000),
     (1, [4095, 0, 2048, 3333, 64], 4096),
     (2, [16383, 16383, 9000, 9001], 16384),
+    (1, [40000, 16384, 16383, 30000, 2047], 40001),   # rows over one chunk: two-stage top-k
 ])
 def test_fused_indexer_topk_matches_oracle(oracle_lib, qps, q_pos, max_ctx):
     print(f"case: fused indexer+topk qps={qps} q_pos={q_pos}", flush=True)
@@ -53,7 +54,7 @@ def test_fused_indexer_topk_matches_oracle(oracle_lib, qps, q_pos, max_ctx):
         s, idx = _fused(w, d, ws)
         torch.cuda.synchronize()
         assert dsa.last_path() == "indexer_topk_fused"
-        assert _hist_part_zero(ws, rows)
+        assert _hist_part_zero(ws, rows * ((max_ctx + 16383) // 16384))
         results.append((s.cpu().numpy(), idx.cpu().numpy()))
     for s_i, idx_i in results[1:]:
         for r in range(rows):               # entries past q_pos[r] are unspecified
@@ -76,8 +77,8 @@ def test_fused_indexer_topk_matches_oracle(oracle_lib, qps, q_pos, max_ctx):
 
 @pytest.mark.parametrize("name", ["decode_mtp_b64_16k", "decode_b16_4k", "decode_b4_128k"])
 def test_fused_full_size_equals_separate_calls(oracle_lib, name):
-    """Full-size decode batches: index lists bit for bit equal to the separate calls; 128K rows
-    take the separate calls inside the fused entry point (staged top-k)."""
+    """Full-size decode batches: index lists bit for bit equal to the separate calls (128K rows: the
+    counts are per 16384-position chunk and the two-stage top-k's chunk stage starts from them)."""
     print(f"case: fused full size {name}", flush=True)
     w = getattr(workloads, "make_" + name)()
     d = gpu_inputs(w)
@@ -85,8 +86,8 @@ def test_fused_full_size_equals_separate_calls(oracle_lib, name):
     for _ in range(2):
         s, idx = _fused(w, d, ws)
     torch.cuda.synchronize()
-    assert dsa.last_path() == ("indexer_topk_fused" if w.max_ctx <= 16384 else "topk_radix_staged")
-    assert _hist_part_zero(ws, w.rows)
+    assert dsa.last_path() == "indexer_topk_fused"
+    assert _hist_part_zero(ws, w.rows * ((w.max_ctx + 16383) // 16384))
     s_sep = dsa.indexer_scores(d["iq"], d["iw"], d["ik"], d["iks"], d["page_table"], d["q_pos"], w.n_seq,
                                w.q_per_seq, w.max_ctx)
     idx_sep = dsa.topk(s_sep, d["q_pos"], w.max_ctx, w.topk)
