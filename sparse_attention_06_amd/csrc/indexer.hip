@@ -555,6 +555,7 @@ __global__ void __launch_bounds__(256) indexer_prefill_kernel(
 }
 
 static_assert(kTopkChunkKeys % (kScanWaves * 64 * kScanPage) == 0, "a workgroup range never straddles a chunk");
+static_assert(kScanWaves * 64 * kScanPage < 65536, "a workgroup's count per bin fits the 16-bit LDS counters");
 
 int indexer_scan_rows_per_wave(int q_per_seq) { return q_per_seq % 2 == 0 ? 2 : 1; }
 
