@@ -242,6 +242,30 @@ def time_eager_steps(step, steps):
     return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
 
 
+def time_eager_same_copy(step, steps):
+    """ms per eager step when every step reads the same input copy (caches warm: what the last
+    step left in L2 and the 256 MB MALL is there for the next)."""
+    torch = step.torch
+    for _ in range(20):
+        step.run(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step.run(0)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def input_copies(w):
+    """Input copies to rotate so that a step's inputs were last touched more than the MALL's
+    256 MB of other traffic ago (at least 2)."""
+    per_copy = (w.ik.nbytes + (w.iks.nbytes if w.iks is not None else 0) + w.kv.nbytes + w.q.nbytes +
+                w.iq.nbytes + w.iw.nbytes)
+    return max(2, -(-384 * 2**20 // max(per_copy, 1)))
+
+
 def time_steps(step, steps, warmup):
     torch = step.torch
     for i in range(warmup):
@@ -332,7 +356,8 @@ def run_decode_bench(args):
     w = workloads.MAKERS[args.workload]()
     log(f"[bench] workload {w.name}: {w.n_seq} requests x {w.q_per_seq} rows, ctx {w.max_ctx}, "
         f"generated in {time.time() - t0:.1f} s")
-    step = DecodeStep(w, copies=2, fused=not args.separate_indexer_topk)
+    copies = input_copies(w)
+    step = DecodeStep(w, copies=copies, fused=not args.separate_indexer_topk)
     if args.no_graph:
         # eager steps only (for profiler runs that do not follow graph launches)
         wall, per = time_steps(step, args.steps, args.warmup)
@@ -348,6 +373,7 @@ def run_decode_bench(args):
         ms_step, wall = time_eager_steps(step, args.steps)
         ms_step = float(ms_step)
         ms_graph, _ = time_graph_steps(step, args.steps, 0)
+        ms_warm = time_eager_same_copy(step, args.steps)
         ms = [time_call(step, fn, args.steps) for fn in (step.call_indexer, step.call_topk, step.call_mla)]
         ms_fused = time_call(step, step.call_indexer_topk, args.steps)
         _, per = time_steps(step, args.steps, 1)
@@ -361,7 +387,9 @@ def run_decode_bench(args):
         "ms": {"indexer": float(ms[0]), "topk": float(ms[1]), "sparse_mla": float(ms[2]), "step": ms_step,
                "step_graph_replay": None if args.no_graph else float(ms_graph),
                "step_eager_with_events": float(ms[3]),
-               "indexer_topk_fused": None if args.no_graph else float(ms_fused)},
+               "indexer_topk_fused": None if args.no_graph else float(ms_fused),
+               "step_warm_same_inputs": None if args.no_graph else float(ms_warm)},
+        "input_copies": copies,
         "step_calls": "indexer_topk (fused) + sparse_mla" if step.fused else "indexer + topk + sparse_mla",
         "wall_ms_per_step": wall / args.steps * 1e3,
         "algorithmic_GBps": {"indexer": by["indexer"] / ms[0] / 1e6, "topk": by["topk"] / ms[1] / 1e6,
