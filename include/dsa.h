@@ -146,7 +146,7 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_p
  *       zero it again). Calls sharing one workspace must not overlap in time.
  * The shared counts are used for the MFMA scan shapes (Hi=64, Di=128, E4M3, 64-token pages) with
  * max_ctx <= 16384 and k <= 4096, or rows the two-stage top-k takes (counts per 16384-position
- * chunk) (DSA_PATH_INDEXER_TOPK_FUSED). Other shapes run the two calls one after the other (the
+ * chunk; the chunk stage also counts the merge's candidates) (DSA_PATH_INDEXER_TOPK_FUSED). Other shapes run the two calls one after the other (the
  * path is then the top-k's).
  * ------------------------------------------------------------------------------------------- */
 size_t dsa_indexer_topk_workspace_size(int rows, int max_ctx, int k);

@@ -176,7 +176,10 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_p
 
 size_t dsa_indexer_topk_workspace_size(int rows, int max_ctx, int k) {
   if (rows <= 0 || max_ctx < 1 || k < 1) return 0;
-  return 256 + (size_t)rows * dsa::topk_chunks(max_ctx) * dsa::kTopkDigit0Bins * 4 +
+  // per-chunk counts, then (rows over one chunk) the merge's candidate counts, then the two-stage
+  // top-k's own workspace
+  const int C = dsa::topk_chunks(max_ctx);
+  return 256 + (size_t)rows * (C + (C > 1 ? 1 : 0)) * dsa::kTopkDigit0Bins * 4 +
          dsa::topk_staged_ws_bytes(rows, max_ctx, k);
 }
 
@@ -195,7 +198,8 @@ dsa_status_t dsa_indexer_topk(const void* q, const float* w, const void* k_cache
   if (!ws || ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws ? ws_bytes : (size_t)0);
   uint32_t* hist0 = (uint32_t*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
-  uint8_t* topk_ws = (uint8_t*)(hist0 + (size_t)rows * dsa::topk_chunks(max_ctx) * dsa::kTopkDigit0Bins);
+  const int nchunks = dsa::topk_chunks(max_ctx);
+  uint8_t* topk_ws = (uint8_t*)(hist0 + (size_t)rows * (nchunks + (nchunks > 1 ? 1 : 0)) * dsa::kTopkDigit0Bins);
   const size_t topk_ws_bytes = (size_t)((uint8_t*)ws + ws_bytes - topk_ws);
   const bool fused = Hi == 64 && Di == 128 && dtype == DSA_E4M3 && page_size == 64 &&
                      (int64_t)rows / dsa::indexer_scan_rows_per_wave(q_per_seq) <= 65535 &&

@@ -362,6 +362,8 @@ struct TopkStageArgs {
   int32_t* out_cnt;
   int out_chunks;
   uint32_t* hist0;  // score rows: per row and chunk, the first-digit histogram (or null)
+  uint32_t* mhist;  // per row, the first-digit histogram of the merge's candidates (or null): the
+                    // chunk stage adds its selection's counts, the merge starts from them
 };
 
 template <bool kSrcScores, bool kFinal>
@@ -370,7 +372,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_stage_kernel(TopkStageArgs 
   const int r = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t key[kRegE], vmask = 0;
-  uint32_t* const hist0 = kSrcScores && a.hist0 ? a.hist0 + ((int64_t)r * gridDim.x + c) * kRegBins : nullptr;
+  uint32_t* const hist0 = kSrcScores ? (a.hist0 ? a.hist0 + ((int64_t)r * gridDim.x + c) * kRegBins : nullptr)
+                                     : (a.mhist ? a.mhist + (int64_t)r * kRegBins : nullptr);
   reg_select_init(sh, tid, hist0);
   if (kSrcScores) {
     // this thread's positions: base .. base + 15. The row is read before q_pos is known (every
@@ -446,6 +449,17 @@ __global__ void __launch_bounds__(kTopkThreads) topk_stage_kernel(TopkStageArgs 
   const bool take_all = nvalid <= k;
   uint32_t tau = 0, remaining = k;
   if (!take_all) reg_select(key, vmask, k, hist0 != nullptr, sh, tid, wave, lane, tau, remaining);
+  if (kSrcScores && !kFinal && hist0 && a.mhist) {
+    // this chunk's selection by first digit, from its full counts (still in the first LDS
+    // histogram): every bin above the k-th key's, and k - (keys above) from its bin; all of
+    // them when the chunk keeps every key
+    const uint32_t d0 = sh.pub[0][0], above0 = sh.pub[0][1];
+    uint32_t* mh = a.mhist + (int64_t)r * kRegBins;
+    for (int b = tid; b < kRegBins; b += kTopkThreads) {
+      const uint32_t n = take_all || (uint32_t)b > d0 ? sh.hist[0][b] : ((uint32_t)b == d0 ? k - above0 : 0u);
+      if (n) __hip_atomic_fetch_add(mh + b, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   // staged per selected key: its position for a score row, its input slot for candidates (the
   // slot's position is read when the result is written, by every thread at once)
   int obase = kSrcScores ? kRegKeys * c + kRegE * tid : kRegE * tid;
@@ -518,6 +532,8 @@ hipError_t launch_topk(const float* scores, int64_t ld_scores, const int32_t* q_
     a.out_cnt = (int32_t*)(p + slots * 8);
     a.out_chunks = C;
     a.hist0 = hist0;
+    // with the chunks' counts given, the merge's candidate counts follow the chunks' histograms
+    a.mhist = hist0 ? hist0 + (size_t)rows * C * kRegBins : nullptr;
     hipLaunchKernelGGL((topk_stage_kernel<true, false>), dim3(C, rows), dim3(kTopkThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

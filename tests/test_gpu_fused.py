@@ -26,6 +26,12 @@ def _fused(w, d, ws, k=None):
                             w.max_ctx, k or w.topk, ws=ws)
 
 
+def _nh(max_ctx):
+    # histograms per row in the workspace: one per 16384-position chunk, plus the merge's
+    c = (max_ctx + 16383) // 16384
+    return c + (1 if c > 1 else 0)
+
+
 def _hist_part_zero(ws, hists):
     base = (-ws.data_ptr()) % 256
     return bool((ws[base: base + hists * 2048 * 4] == 0).all())
@@ -54,7 +60,7 @@ def test_fused_indexer_topk_matches_oracle(oracle_lib, qps, q_pos, max_ctx):
         s, idx = _fused(w, d, ws)
         torch.cuda.synchronize()
         assert dsa.last_path() == "indexer_topk_fused"
-        assert _hist_part_zero(ws, rows * ((max_ctx + 16383) // 16384))
+        assert _hist_part_zero(ws, rows * _nh(max_ctx))
         results.append((s.cpu().numpy(), idx.cpu().numpy()))
     for s_i, idx_i in results[1:]:
         for r in range(rows):               # entries past q_pos[r] are unspecified
@@ -87,7 +93,7 @@ def test_fused_full_size_equals_separate_calls(oracle_lib, name):
         s, idx = _fused(w, d, ws)
     torch.cuda.synchronize()
     assert dsa.last_path() == "indexer_topk_fused"
-    assert _hist_part_zero(ws, w.rows * ((w.max_ctx + 16383) // 16384))
+    assert _hist_part_zero(ws, w.rows * _nh(w.max_ctx))
     s_sep = dsa.indexer_scores(d["iq"], d["iw"], d["ik"], d["iks"], d["page_table"], d["q_pos"], w.n_seq,
                                w.q_per_seq, w.max_ctx)
     idx_sep = dsa.topk(s_sep, d["q_pos"], w.max_ctx, w.topk)
