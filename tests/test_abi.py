@@ -69,6 +69,24 @@ def test_topk_rejects_bad_k(lib):
     assert lib.dsa_topk_workspace_size(128, 16384, 2048) == 0
 
 
+def test_fused_indexer_topk_workspace_and_arguments(lib):
+    """The fused call sizes its workspace from the rows' chunks (per-chunk counts, the merge's counts
+    for rows over one chunk, then the two-stage top-k's own workspace) and rejects a missing or
+    small workspace and bad k before any launch."""
+    size = lib.dsa_indexer_topk_workspace_size
+    one = size(128, 16384, 2048)
+    assert one == 256 + 128 * 2048 * 4                       # one chunk: counts only
+    long_rows = size(4, 131072, 2048)
+    assert long_rows == 256 + 4 * (8 + 1) * 2048 * 4 + lib.dsa_topk_workspace_size(4, 131072, 2048)
+    assert size(0, 16384, 2048) == 0
+    fake = ctypes.c_void_p(0x1000)
+    args = (fake, fake, fake, fake, fake, 256, 64, 256, fake, 64, 2, 16384, 64, 128, 0, fake, 16384)
+    assert lib.dsa_indexer_topk(*args, 2048, fake, 2048, NULL, 0, NULL) == dsa.DSA_ERR_WORKSPACE
+    assert lib.dsa_indexer_topk(*args, 2048, fake, 2048, fake, one - 1, NULL) == dsa.DSA_ERR_WORKSPACE
+    assert lib.dsa_indexer_topk(*args, 0, fake, 2048, fake, one, NULL) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_indexer_topk(*args, 2048, fake, 1024, fake, one, NULL) == dsa.DSA_ERR_INVALID_ARG
+
+
 def test_attention_rejects_unsupported_and_inconsistent(lib):
     fake = ctypes.c_void_p(0x1000)
     # v_col0 + Dv beyond the row
