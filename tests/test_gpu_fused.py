@@ -42,6 +42,7 @@ def _hist_part_zero(ws, hists):
     (1, [4095, 0, 2048, 3333, 64], 4096),
     (2, [16383, 16383, 9000, 9001], 16384),
     (1, [40000, 16384, 16383, 30000, 2047], 40001),   # rows over one chunk: two-stage top-k
+    (3, [2999, 3000, 3001, 100, 2500, 2600], 3002),  # three rows per sequence: one row per scan unit
 ])
 def test_fused_indexer_topk_matches_oracle(oracle_lib, qps, q_pos, max_ctx):
     print(f"case: fused indexer+topk qps={qps} q_pos={q_pos}", flush=True)
