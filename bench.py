@@ -39,25 +39,39 @@ def log(*a):
 
 
 # ------------------------------------------------------------------ analytic model
-def handbook_cost_table(Ls=(4096, 32768, 131072)):
-    """Per-layer, per-query cost model of the MTP/sparse-attention handbook page (its printed
-    table): MLA 279K FLOPs and indexer 16K FLOPs per (query, key) pair, 1152-byte latent rows,
-    132-byte indexer keys, k = min(L, 2048)."""
-    H, DC, ROPE = 128, 512, 64
-    pair_mla = 2 * H * (DC + ROPE) + 2 * H * DC
-    pair_expand = 2 * H * (128 + ROPE) + 2 * H * 128
-    pair_idx = 2 * 64 * 128
-    kv_bytes, idx_bytes = (DC + ROPE) * 2, 128 + 4
-    rows = []
-    for L in Ls:
-        k = min(L, 2048)
-        rows.append({
-            "L": L,
-            "decode_gflops": (L * pair_mla / 1e9, (L * pair_idx + k * pair_mla) / 1e9),
-            "decode_mib": (L * kv_bytes / 2 ** 20, (L * idx_bytes + k * kv_bytes) / 2 ** 20),
-            "prefill_tflops": (L * L / 2 * pair_expand / 1e12, (L * L / 2 * pair_idx + L * k * pair_mla) / 1e12),
-        })
-    return {"pair_mla": pair_mla, "pair_idx": pair_idx, "cache_ratio": idx_bytes / kv_bytes, "rows": rows}
+# Unit costs of the method's shapes: the [Handbook] "稀疏注意力：NSA 与 DSA" dims (absorbed MLA: 128
+# heads over one 512 + 64 latent row per position, value = its first 512 columns; the indexer: 64
+# heads of 128 dims, FP8 keys with a float scale; the expanded form: per head 128 + 64 qk dims and
+# 128 value dims).
+def attention_pair_flops(H=128, Dqk=576, Dv=512):
+    """FLOPs of one (query, position) pair: a Dqk-long logit and a Dv-wide value update per head."""
+    return 2 * H * Dqk + 2 * H * Dv
+
+
+def indexer_pair_flops(Hi=64, Di=128):
+    """FLOPs of one (query, key) index score: one Di-long dot per indexer head (the ReLU and the
+    head-weighted sum are not counted)."""
+    return 2 * Hi * Di
+
+
+def per_layer_cost(L, k=2048):
+    """One layer, one sequence of context L, dense MLA against DSA (index set of min(L, k)):
+      decode_flops   one query: every position attended, against every key scored plus the
+                     selected positions attended
+      decode_bytes   the cache rows that query reads: every latent row, against every indexer key
+                     plus the selected latent rows
+      prefill_flops  L causal queries: dense runs the expanded form over L^2 / 2 pairs (the count the
+                     page's table uses), DSA scores the same pairs and attends L * min(L, k) pairs
+                     in the absorbed form
+    Each entry is a (dense, dsa) pair."""
+    sel = min(L, k)
+    pairs = L * L / 2
+    mla, idx = attention_pair_flops(), indexer_pair_flops()
+    return {
+        "decode_flops": (L * mla, L * idx + sel * mla),
+        "decode_bytes": (L * KV_ROW_BYTES, L * IDX_KEY_BYTES + sel * KV_ROW_BYTES),
+        "prefill_flops": (pairs * attention_pair_flops(128, 128 + 64, 128), pairs * idx + L * sel * mla),
+    }
 
 
 def decode_step_bytes(n_seq, q_per_seq, ctx_per_seq, k, H=128, Dqk=576, Dv=512, Hi=64, Di=128):
@@ -75,7 +89,8 @@ def decode_step_bytes(n_seq, q_per_seq, ctx_per_seq, k, H=128, Dqk=576, Dv=512, 
 
 def decode_step_flops(n_seq, q_per_seq, ctx_per_seq, k, H=128, Dqk=576, Dv=512, Hi=64, Di=128):
     rows_ctx = int(np.sum(np.repeat(ctx_per_seq, q_per_seq)))
-    return {"indexer": rows_ctx * 2 * Hi * Di, "mla": n_seq * q_per_seq * k * (2 * H * Dqk + 2 * H * Dv)}
+    return {"indexer": rows_ctx * indexer_pair_flops(Hi, Di),
+            "mla": n_seq * q_per_seq * k * attention_pair_flops(H, Dqk, Dv)}
 
 
 # ------------------------------------------------------------------ GPU step
@@ -284,18 +299,30 @@ def time_steps(step, steps, warmup):
 
 
 # ------------------------------------------------------------------ CPU baseline (the oracle)
-def cpu_baseline(w, max_seconds=30.0):
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where it is not readable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, max_threads=16):
     """The oracle as it stands, on the host cores, over a bounded sample of the same workload:
-    whole requests (both query rows), indexer + top-k + attention, one request per thread."""
+    whole requests (all their query rows), indexer + top-k + attention, one request per thread.
+    Threads: the cores this process may run on, at most max_threads (the per-GPU CPU share of the
+    boxes this runs on); also timed on one thread with one request."""
     import oracle
 
-    cores = min(os.cpu_count() or 1, 16)
     try:
-        cores = min(cores, len(os.sched_getaffinity(0)))
+        visible = len(os.sched_getaffinity(0))
     except AttributeError:
-        pass
-    n_req = max(1, cores)
-    reqs = list(range(min(n_req, w.n_seq)))
+        visible = os.cpu_count() or 1
+    threads = max(1, min(visible, max_threads))
     qps = w.q_per_seq
 
     def one_request(s):
@@ -306,18 +333,23 @@ def cpu_baseline(w, max_seconds=30.0):
         oracle.sparse_mla(w.q, w.kv, w.page_table, w.page_size, w.q_pos, w.n_seq, qps, idx, w.Dqk, w.Dv, w.v_col0,
                           w.sm_scale, rows=rows)
 
-    t0 = time.perf_counter()
-    ths = [threading.Thread(target=one_request, args=(s,)) for s in reqs]
-    for t in ths:
-        t.start()
-    for t in ths:
-        t.join()
-    dt = time.perf_counter() - t0
-    q = len(reqs) * qps
-    return {"value": q / dt, "unit": "queries/s", "cores": len(reqs), "kind": "oracle",
+    def timed(reqs):
+        t0 = time.perf_counter()
+        ths = [threading.Thread(target=one_request, args=(s,)) for s in reqs]
+        for t in ths:
+            t.start()
+        for t in ths:
+            t.join()
+        return time.perf_counter() - t0
+
+    reqs = list(range(min(threads, w.n_seq)))
+    dt = timed(reqs)
+    dt1 = timed([w.n_seq - 1])
+    return {"value": len(reqs) * qps / dt, "unit": "queries/s", "cores": len(reqs), "kind": "oracle",
             "sample": f"{len(reqs)} requests x {qps} query rows of the benchmark workload (indexer over "
                       f"{int(w.q_pos[0]) + 1}+ positions, top-{w.topk}, 128-head attention), one request per "
-                      f"thread, {dt:.1f} s wall"}
+                      f"thread, {dt:.1f} s wall; then 1 request on 1 thread, {dt1:.1f} s",
+            "cpu_model": cpu_model(), "cores_visible": visible, "value_1core": qps / dt1}
 
 
 # ------------------------------------------------------------------ roofline / traffic
@@ -360,7 +392,7 @@ def run_decode_bench(args):
     step = DecodeStep(w, copies=copies, fused=not args.separate_indexer_topk)
     if args.no_graph:
         # eager steps only (for profiler runs that do not follow graph launches)
-        wall, per = time_steps(step, args.steps, args.warmup)
+        wall, per = time_steps(step, args.steps, args.settle + args.warmup)
         ms = [float(x) for x in per.mean(axis=0)]
         ms_step = ms[3]
     else:
@@ -368,7 +400,7 @@ def run_decode_bench(args):
         # GPU-bound step they run a few percent faster than graph replays of the same launches,
         # which are timed too, after a bit-for-bit check against the eager result); per-call times
         # from graphs of repeated calls; an eager pass with events between the calls
-        for i in range(args.warmup):
+        for i in range(args.settle + args.warmup):
             step.run(i)
         ms_step, wall = time_eager_steps(step, args.steps)
         ms_step = float(ms_step)
@@ -426,7 +458,7 @@ def run_decode_bench(args):
         cpu = cpu_baseline(w)
     line = {
         "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "settle_steps": args.settle, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "requests": w.n_seq, "query_rows_per_request": w.q_per_seq,
                    "context": int(w.max_ctx), "topk": w.topk, "indexer": "64 heads x 128 dims, FP8 E4M3",
@@ -488,6 +520,71 @@ def run_prefill_bench(args):
     print(json.dumps(line), flush=True)
 
 
+class CrossoverCase:
+    """The crossover sweep's inputs and calls for one sequence of T queries over a T-token prefix:
+    the sparse path (indexer + top-k + sparse attention), the absorbed dense fallback, the expanded
+    multi-head fallback (dense causal, and masked to the sparse path's index sets) and the two
+    up-projection GEMMs the expanded form needs. With keep_host, the workload's host arrays stay in
+    `w` (for checks against the oracle); otherwise the large ones are dropped after the upload."""
+
+    def __init__(self, T, keep_host=False):
+        import torch
+
+        import workloads
+        from sparse_attention_06_amd import dsa
+
+        self.T, self.dsa, self.torch = T, dsa, torch
+        w = workloads.make_prefill(T)
+        self.d = d = {
+            "iq": torch.from_numpy(w.iq).cuda(), "iw": torch.from_numpy(w.iw).cuda(),
+            "ik": torch.from_numpy(w.ik).cuda(), "iks": torch.from_numpy(w.iks).cuda(),
+            "q": torch.from_numpy(w.q.view(np.int16)).view(torch.bfloat16).cuda(),
+            "kv": torch.from_numpy(w.kv.view(np.int16)).view(torch.bfloat16).cuda(),
+            "pt": torch.from_numpy(w.page_table).cuda(), "qp": torch.from_numpy(w.q_pos).cuda(),
+        }
+        if not keep_host:
+            del w.q, w.kv
+        self.w = w
+        self.scores = torch.empty(T, T, dtype=torch.float32, device="cuda")
+        self.idx = torch.empty(T, 2048, dtype=torch.int32, device="cuda")
+        self.out = torch.empty(T, 128, 512, dtype=torch.bfloat16, device="cuda")
+        # expanded operands (seeded, N(0,1) rounded to bf16) and the up-projection GEMM operands
+        g = torch.Generator(device="cuda")
+        g.manual_seed(0xD5A0 + T)
+        self.xq = torch.randn(T, 128, 192, generator=g, device="cuda").to(torch.bfloat16)
+        self.xkn = torch.randn(1, 128, T, 128, generator=g, device="cuda").to(torch.bfloat16)
+        self.xkr = torch.randn(1, T, 64, generator=g, device="cuda").to(torch.bfloat16)
+        self.xv = torch.randn(1, 128, T, 128, generator=g, device="cuda").to(torch.bfloat16)
+        self.xout = torch.empty(T, 128, 128, dtype=torch.bfloat16, device="cuda")
+        self.mws = torch.empty(dsa.expanded_mha_workspace_size(T, T, 2048), dtype=torch.uint8, device="cuda")
+        self.lat = d["kv"].view(-1, 576)[:T, :512]
+        self.wuk = (torch.randn(512, 128 * 128, generator=g, device="cuda") / 512 ** 0.5).to(torch.bfloat16)
+        self.kexp = torch.empty(T, 128 * 128, dtype=torch.bfloat16, device="cuda")
+        self.scale = 1 / 192 ** 0.5
+
+    def sparse(self):
+        d, T, dsa = self.d, self.T, self.dsa
+        dsa.indexer_scores(d["iq"], d["iw"], d["ik"], d["iks"], d["pt"], d["qp"], 1, T, T, scores=self.scores)
+        dsa.topk(self.scores, d["qp"], T, 2048, idx=self.idx)
+        dsa.sparse_mla_prefill(d["q"], d["kv"], d["pt"], d["qp"], 1, T, self.idx, 576, 512, 0, self.scale, out=self.out)
+
+    def dense(self):
+        d, T = self.d, self.T
+        self.dsa.dense_mla_prefill(d["q"], d["kv"], d["pt"], d["qp"], 1, T, T, 576, 512, 0, self.scale, out=self.out)
+
+    def expanded(self):
+        self.dsa.expanded_mha_prefill(self.xq, self.xkn, self.xkr, self.xv, self.d["qp"], 1, self.T, self.scale,
+                                      out=self.xout)
+
+    def masked(self):
+        self.dsa.expanded_mha_prefill(self.xq, self.xkn, self.xkr, self.xv, self.d["qp"], 1, self.T, self.scale,
+                                      idx=self.idx, out=self.xout, ws=self.mws)
+
+    def gemm(self):  # k_nope and v of all heads from the latent rows: two [T,512] x [512,16384]
+        self.torch.matmul(self.lat, self.wuk, out=self.kexp)
+        self.torch.matmul(self.lat, self.wuk, out=self.kexp)
+
+
 def run_crossover(args):
     """Dense fallbacks vs sparse prefill (indexer + top-k + sparse attention) for one sequence of
     T queries over a T-token prefix. Two dense fallbacks: the absorbed form (the same attention
@@ -497,60 +594,14 @@ def run_crossover(args):
     (two plain GEMMs, timed here with torch.matmul as `expand_gemm_ms`)."""
     import torch
 
-    import workloads
-    from sparse_attention_06_amd import dsa
-
     sizes = [int(x) for x in args.crossover_T.split(",")]
     res = []
     for T in sizes:
-        w = workloads.make_prefill(T)
-        d = {
-            "iq": torch.from_numpy(w.iq).cuda(), "iw": torch.from_numpy(w.iw).cuda(),
-            "ik": torch.from_numpy(w.ik).cuda(), "iks": torch.from_numpy(w.iks).cuda(),
-            "q": torch.from_numpy(w.q.view(np.int16)).view(torch.bfloat16).cuda(),
-            "kv": torch.from_numpy(w.kv.view(np.int16)).view(torch.bfloat16).cuda(),
-            "pt": torch.from_numpy(w.page_table).cuda(), "qp": torch.from_numpy(w.q_pos).cuda(),
-        }
-        del w.q, w.kv
-        scores = torch.empty(T, T, dtype=torch.float32, device="cuda")
-        idx = torch.empty(T, 2048, dtype=torch.int32, device="cuda")
-        out = torch.empty(T, 128, 512, dtype=torch.bfloat16, device="cuda")
-        # expanded operands (seeded, N(0,1) rounded to bf16) and the up-projection GEMM operands
-        g = torch.Generator(device="cuda")
-        g.manual_seed(0xD5A0 + T)
-        xq = torch.randn(T, 128, 192, generator=g, device="cuda").to(torch.bfloat16)
-        xkn = torch.randn(1, 128, T, 128, generator=g, device="cuda").to(torch.bfloat16)
-        xkr = torch.randn(1, T, 64, generator=g, device="cuda").to(torch.bfloat16)
-        xv = torch.randn(1, 128, T, 128, generator=g, device="cuda").to(torch.bfloat16)
-        xout = torch.empty(T, 128, 128, dtype=torch.bfloat16, device="cuda")
-        mws = torch.empty(dsa.expanded_mha_workspace_size(T, T, 2048), dtype=torch.uint8, device="cuda")
-        lat = d["kv"].view(-1, 576)[:T, :512]
-        wuk = (torch.randn(512, 128 * 128, generator=g, device="cuda") / 512 ** 0.5).to(torch.bfloat16)
-        kexp = torch.empty(T, 128 * 128, dtype=torch.bfloat16, device="cuda")
-        scale = 1 / 192 ** 0.5
-
-        def sparse():
-            dsa.indexer_scores(d["iq"], d["iw"], d["ik"], d["iks"], d["pt"], d["qp"], 1, T, T, scores=scores)
-            dsa.topk(scores, d["qp"], T, 2048, idx=idx)
-            dsa.sparse_mla_prefill(d["q"], d["kv"], d["pt"], d["qp"], 1, T, idx, 576, 512, 0, scale, out=out)
-
-        def dense():
-            dsa.dense_mla_prefill(d["q"], d["kv"], d["pt"], d["qp"], 1, T, T, 576, 512, 0, scale, out=out)
-
-        def expanded():
-            dsa.expanded_mha_prefill(xq, xkn, xkr, xv, d["qp"], 1, T, scale, out=xout)
-
-        def masked():
-            dsa.expanded_mha_prefill(xq, xkn, xkr, xv, d["qp"], 1, T, scale, idx=idx, out=xout, ws=mws)
-
-        def gemm():  # k_nope and v of all heads from the latent rows: two [T,512] x [512,16384]
-            torch.matmul(lat, wuk, out=kexp)
-            torch.matmul(lat, wuk, out=kexp)
-
+        c = CrossoverCase(T)
         row = {"T": T}
         reps = min(args.steps, 10)
-        for name, fn in (("sparse_ms", sparse), ("dense_absorbed_ms", dense), ("dense_expanded_ms", expanded),
-                         ("masked_expanded_ms", masked), ("expand_gemm_ms", gemm)):
+        for name, fn in (("sparse_ms", c.sparse), ("dense_absorbed_ms", c.dense), ("dense_expanded_ms", c.expanded),
+                         ("masked_expanded_ms", c.masked), ("expand_gemm_ms", c.gemm)):
             for _ in range(2):
                 fn()
             torch.cuda.synchronize()
@@ -567,7 +618,7 @@ def run_crossover(args):
         row["expanded_wins"] = row["dense_expanded_ms"] + row["expand_gemm_ms"] < row["sparse_ms"]
         log(f"[crossover] {row}")
         res.append(row)
-        del d, scores, idx, out, xq, xkn, xkr, xv, xout, mws, wuk, kexp
+        del c
         torch.cuda.empty_cache()
     first = lambda key: next((r["T"] for r in res if not r[key]), None)  # noqa: E731
     print(json.dumps({"crossover": res, "sparse_beats_absorbed_dense_from_T": first("absorbed_wins"),
@@ -638,8 +689,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed steps first: the decode step takes ~150 steps (~30 ms) to settle")
+    ap.add_argument("--warmup", type=int, default=10, help="untimed warmup steps before the timed ones")
+    ap.add_argument("--settle", type=int, default=300,
+                    help="further untimed steps run before the warmup, whatever --warmup is: the decode step "
+                         "takes ~150 steps (~30 ms) to reach its steady speed (reported as settle_steps)")
     ap.add_argument("--workload", default="decode_mtp_b64_16k",
                     choices=["decode_mtp_b64_16k", "decode_b16_4k", "decode_b4_128k", "prefill_8k",
                              "prefill_chunk_128k"])

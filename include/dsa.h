@@ -161,8 +161,9 @@ dsa_status_t dsa_indexer_topk(const void* q, const float* w, const void* k_cache
  * ([DSA-blog] "Sparse Attention": softmax(QK^T/sqrt(d_h) + M^DSA)V with M = 0 on S_t and -inf
  * elsewhere, computed by reading only the indexed rows; [Handbook] absorbed MLA: one latent row
  * of 512+64 bf16 per position is the key of all 128 heads, its first 512 columns the value).
- * For row r and head h, with S = the entries of idx[r, 0..k-1] lying in [0, q_pos[r]] (so the
- * -1 padding and any invisible position are skipped):
+ * For row r and head h, with S = the SET of positions that idx[r, 0..k-1] lists within
+ * [0, q_pos[r]] (the -1 padding and any invisible position are skipped, and a position listed
+ * several times is in S once: [DSA-blog] "Sparse Attention", M_tj = 0 exactly when j is in S_t):
  *     l_j    = sm_scale * q[r, h, 0:Dqk] . kv[j, 0:Dqk]
  *     out[r, h, :] = sum_{j in S} softmax(l)_j * kv[j, v_col0 : v_col0 + Dv]
  *     lse[r, h]    = log sum_{j in S} exp(l_j)         (natural log; -inf for an empty S)
@@ -176,6 +177,9 @@ dsa_status_t dsa_indexer_topk(const void* q, const float* w, const void* k_cache
  *   ws       device workspace of at least dsa_sparse_mla_workspace_size(...) bytes (may be
  *            NULL when that size is 0); its contents on entry do not matter
  * Softmax runs in fp32 with the probabilities rounded to bf16 for the value product.
+ * List order: any. A row whose visible entries run strictly ascending from entry 0 (what
+ * dsa_topk writes) cannot repeat a position and is attended directly; any other row is first
+ * checked for repeats (a bitmap of the row's positions in LDS), which costs extra time.
  * Tuned shape: H=128, Dqk=576, Dv=512, kv_dim=576, v_col0=0 (bf16 MFMA). Other shapes with
  * Dqk <= 1024 and Dv <= 512 run a generic VALU kernel (reported by dsa_last_path()).
  * The decode entry point may split each row's index set over several workgroups and merge

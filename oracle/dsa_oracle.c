@@ -208,13 +208,22 @@ int oracle_sparse_mla(const uint16_t* q, const uint16_t* kv_cache, const int32_t
   for (int r = row_begin; r < row_end; ++r) {
     int s = r / q_per_seq;
     int64_t t = q_pos[r], n_set = 0;
+    /* S_t is a set ([DSA-blog] "Sparse Attention": the mask is 0 exactly on S_t): mark every
+     * listed visible position once, then visit the marked positions in ascending order */
+    unsigned char* in_set = (unsigned char*)calloc((size_t)(t >= 0 ? t + 1 : 1), 1);
+    if (!in_set) { free(set); return 2; }
     for (int i = 0; i < k; ++i) {
       int64_t j = idx[(int64_t)r * ld_idx + i];
       if (j < 0 || j > t) continue; /* not a visible position, so not in S_t */
+      in_set[j] = 1;
+    }
+    for (int64_t j = 0; j <= t; ++j) {
+      if (!in_set[j]) continue;
       int64_t row = phys_row(page_table, ld_pt, page_size, num_pages, s, j);
-      if (row < 0) { free(set); return 3; }
+      if (row < 0) { free(in_set); free(set); return 3; }
       set[n_set++] = row;
     }
+    free(in_set);
     int rc = attend_row(q + (int64_t)r * H * Dqk, kv_cache, set, n_set, H, Dqk, Dv, kv_dim, v_col0,
                         sm_scale, out + (int64_t)r * H * Dv, lse ? lse + (int64_t)r * H : NULL);
     if (rc) { free(set); return rc; }

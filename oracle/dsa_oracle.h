@@ -62,8 +62,10 @@ int oracle_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, in
  *   for head h:  l_j = sm_scale * q[r,h,:Dqk] . row_j[0:Dqk]          for j in S
  *                o[r,h,:] = sum_j softmax(l)_j * row_j[v_col0 : v_col0+Dv]
  *                lse[r,h] = log sum_j exp(l_j)
- * S = the entries of idx[r * ld_idx + 0 .. k-1] that lie in [0, q_pos[r]], in the order
- * given (entries outside that range, e.g. the -1 padding, are not visible and are skipped).
+ * S = the set of positions that idx[r * ld_idx + 0 .. k-1] lists within [0, q_pos[r]]: a
+ * position listed several times is in S once ([DSA-blog] "Sparse Attention": M_tj = 0 exactly
+ * when j is in S_t, so S_t is a set), and S is visited in ascending position order. Entries
+ * outside that range (e.g. the -1 padding) are not visible and are skipped.
  * An empty S gives o = 0 and lse = -inf. q: bf16 [rows, H, Dqk]; kv_cache: bf16
  * [num_pages*page_size, kv_dim]; out: float [rows, H, Dv]; lse: float [rows, H] or NULL. */
 int oracle_sparse_mla(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,

@@ -26,6 +26,23 @@
 
 namespace dsa {
 
+// ------------------------------------------------------------------ index sets
+
+// S_t is a set ([DSA-blog] "Sparse Attention": M_tj = 0 exactly when j is in S_t), so a position
+// listed more than once is attended once. A list whose visible entries (0 <= j <= t) run strictly
+// ascending from entry 0 -- what the top-k writes -- cannot repeat one, and needs no filtering.
+// This checks entries e = e0, e0 + stride, ... below e_end (e0 >= 1) against that form: true if
+// one of them is visible while the entry before it is not visible or not smaller.
+__device__ __forceinline__ bool list_needs_dedupe(const int* irow, int t, int e0, int e_end, int stride) {
+  bool bad = false;
+  for (int e = e0; e < e_end; e += stride) {
+    const int c = irow[e], p = irow[e - 1];
+    const bool vc = c >= 0 && c <= t, vp = p >= 0 && p <= t;
+    bad |= vc && !(vp && p < c);
+  }
+  return bad;
+}
+
 // ------------------------------------------------------------------ generic (any shape)
 
 // One wave per (row, head); lanes stride the feature dims. Online softmax in fp32.
@@ -45,9 +62,19 @@ __global__ void __launch_bounds__(256) mla_generic_kernel(AttnArgs a) {
   float m = -INFINITY, l = 0.f;
   const int n = a.idx ? a.k : min(t + 1, a.k);  // dense: a.k = max_ctx
   const uint16_t* kv = (const uint16_t*)a.kv.base;
+  // S_t is a set: a position the list repeats counts once. A list whose visible entries run
+  // strictly ascending from entry 0 (the top-k's output) holds no repeat; any other list has each
+  // entry checked against the entries before it.
+  const int* irow = a.idx ? a.idx + (int64_t)r * a.ld_idx : nullptr;
+  const bool dedupe = irow && __any(list_needs_dedupe(irow, t, 1 + lane, n, 64));
   for (int e = 0; e < n; ++e) {
-    const int j = a.idx ? a.idx[(int64_t)r * a.ld_idx + e] : e;
+    const int j = irow ? irow[e] : e;
     if (j < 0 || j > t) continue;
+    if (dedupe) {
+      bool seen = false;
+      for (int e2 = lane; e2 < e; e2 += 64) seen |= irow[e2] == j;
+      if (__any(seen)) continue;
+    }
     const int64_t row = phys_row(a.kv.page_table, a.kv.ld_pt, a.kv.page_size, a.kv.num_pages, seq, j);
     if (row < 0) continue;
     const uint16_t* kr = kv + row * a.kv_dim;
@@ -93,7 +120,12 @@ constexpr int kListCap = 2048;                   // resolved entries held in LDS
 constexpr int kListOff = kNBuf * kTileBytes;
 constexpr int kQRopeOff = kListOff + 4 * kListCap; // rope dims of the 128 query heads (16 KB)
 constexpr int kMaskOff = kQRopeOff + kH * kRopeBytes; // valid-entry mask per tile of the list
-constexpr int kLdsBytes = kMaskOff + 4 * (kListCap / kNK);
+constexpr int kFlagOff = kMaskOff + 4 * (kListCap / kNK);  // one flag per wave
+constexpr int kLdsBytes = kFlagOff + 16;
+// Positions per pass of the repeat filter: a bitmap of 128 KB in the tile buffers, which are idle
+// while a list chunk is resolved.
+constexpr int kDedupWindow = 1 << 20;
+static_assert(kDedupWindow / 8 <= kNBuf * kTileBytes, "repeat filter bitmap in the tile buffers");
 static_assert(kH * kDv * 2 <= kLdsBytes, "output staging");
 static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
 constexpr float kLog2e = 1.4426950408889634f;
@@ -217,6 +249,59 @@ __device__ __forceinline__ void wait_gathers(int younger) {
   else __builtin_amdgcn_s_waitcnt(kBase);
 }
 
+// list_needs_dedupe over this workgroup's entries [e0, e_end) (e0 >= 1), eight per thread at a
+// time with all their loads issued together; true in every thread if any entry fails. flags:
+// four ints of LDS.
+__device__ __forceinline__ bool block_needs_dedupe(const int* irow, int t, int e0, int e_end, int* flags, int wave,
+                                                   int lane) {
+  bool bad = false;
+  for (int b0 = e0 + (int)threadIdx.x; b0 < e_end; b0 += 8 * 256) {
+    int c[8], p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = b0 + 256 * u;
+      c[u] = e < e_end ? irow[e] : -1;
+      p[u] = e < e_end ? irow[e - 1] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool vc = c[u] >= 0 && c[u] <= t, vp = p[u] >= 0 && p[u] <= t;
+      bad |= vc && !(vp && p[u] < c[u]);
+    }
+  }
+  const bool any = __any(bad);
+  if (lane == 0) flags[wave] = any ? 1 : 0;
+  __syncthreads();
+  return (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
+}
+
+// The repeat filter: list[e - cb] = -1 for every entry e of [cb, ce) whose position an entry
+// listed before it (anywhere in the row, so across splits too) also holds. One window of
+// kDedupWindow positions at a time, as a bitmap in LDS (bm, idle tile buffers): the row's entries
+// before cb set their bits, then each entry of the chunk that resolved to a row test-and-sets its
+// own; of several equal entries the first atomic keeps its entry. Threads own the same entries as
+// in the resolve (e = cb + threadIdx.x + 256 m).
+__device__ void drop_repeats(const int* irow, int t, int cb, int ce, int* list, uint32_t* bm) {
+  for (int64_t w0 = 0; w0 <= t; w0 += kDedupWindow) {
+    const int nb = (int)min((int64_t)kDedupWindow, (int64_t)t + 1 - w0);
+    for (int i = threadIdx.x; i < (nb + 31) >> 5; i += 256) bm[i] = 0u;
+    __syncthreads();
+    for (int e = threadIdx.x; e < cb; e += 256) {
+      const int64_t j = (int64_t)irow[e] - w0;
+      if (j >= 0 && j < nb) atomicOr(&bm[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+    for (int e = cb + threadIdx.x; e < ce; e += 256) {
+      const int64_t j = (int64_t)irow[e] - w0;
+      if (j >= 0 && j < nb && list[e - cb] >= 0) {
+        const uint32_t bit = 1u << (j & 31);
+        if (atomicOr(&bm[j >> 5], bit) & bit) list[e - cb] = -1;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // Workspace of the split path: fp16 partial outputs [unit][head][column] and (reference, sum)
 // per (unit, head), each part 256-byte aligned.
 struct MlaSplitWs {
@@ -331,6 +416,10 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
       *(__attribute__((address_space(3))) i32x4*)(lds + kQRopeOff + h * kRopeBytes + 16 * (c ^ rope_swz(h))) = v;
     }
   }
+  // S_t is a set: only lists that are not a strictly ascending run of visible entries from entry 0
+  // up to this split's end can repeat a position into this split; those go through the filter.
+  const int* irow = a.idx ? a.idx + (int64_t)r * a.ld_idx : nullptr;
+  const bool dedupe = irow && block_needs_dedupe(irow, t, 1, e_end, (int*)(smem + kFlagOff), wave, lane);
   for (int cb = e_begin; cb < e_end; cb += kListCap) {
     const int ce = min(e_end, cb + kListCap);
     __syncthreads();  // the previous chunk is done with the list and the buffers
@@ -357,6 +446,7 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
           list[e - cb] = (pg[u] >= 0 && pg[u] < a.kv.num_pages) ? pg[u] * a.kv.page_size + jj[u] % a.kv.page_size : -1;
       }
     }
+    if (dedupe) drop_repeats(irow, t, cb, ce, list, (uint32_t*)smem);
     if (cb == e_begin) {
       // consume the query fragments here, before any gather is issued: their wait then covers
       // the query loads only, and no wait for them lands in the tile loop (where it would also

@@ -453,6 +453,9 @@ __global__ void __launch_bounds__(kTopkThreads) topk_stage_kernel(TopkStageArgs 
     // this chunk's selection by first digit, from its full counts (still in the first LDS
     // histogram): every bin above the k-th key's, and k - (keys above) from its bin; all of
     // them when the chunk keeps every key
+    // A chunk that keeps every key skipped reg_select and its barriers: publish the histogram
+    // reg_select_init wrote (each thread wrote other bins than it reads here) before reading it.
+    if (take_all) __syncthreads();  // block-uniform
     const uint32_t d0 = sh.pub[0][0], above0 = sh.pub[0][1];
     uint32_t* mh = a.mhist + (int64_t)r * kRegBins;
     for (int b = tid; b < kRegBins; b += kTopkThreads) {

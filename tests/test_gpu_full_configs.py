@@ -82,3 +82,37 @@ def test_full_size_workload(oracle_lib, name, nsample):
     ref_o, _ = oracle.sparse_mla(sub["q"], w.kv, sub["pt"], w.page_size, sub["q_pos"], ns, 1, ref_idx, w.Dqk, w.Dv,
                                  w.v_col0, w.sm_scale, threads=THREADS)
     check_attn(d["out"].index_select(0, rows_t).float().cpu().numpy(), ref_o)
+
+
+@pytest.mark.parametrize("T", [1024, 2048])
+def test_crossover_dense_fallbacks(oracle_lib, T):
+    """The prefill blocks the crossover sweep runs against the dense fallbacks (T = 1024 and 2048,
+    both no longer than k = 2048, so dense causal attention is exact DSA: [Handbook] k = min(L,
+    2048)), through the calls the sweep times (bench.CrossoverCase). Sampled rows of the absorbed
+    dense fallback against the oracle's dense attention and its sparse attention over the full
+    set; sampled rows of the expanded multi-head fallback against the oracle's expanded attention."""
+    print(f"case: crossover dense fallbacks T={T}", flush=True)
+    c = bench.CrossoverCase(T, keep_host=True)
+    w = c.w
+    c.dense()
+    c.expanded()
+    torch.cuda.synchronize()
+    rows = _sample_rows(w, 16, seed=0xD5A0 + T)
+    rows_t = torch.from_numpy(rows).cuda()
+    got = c.out.index_select(0, rows_t).float().cpu().numpy()
+    sub = _subset(w, rows)
+    ns = len(rows)
+    ref_d, _ = oracle.dense_mla(sub["q"], w.kv, sub["pt"], w.page_size, sub["q_pos"], ns, 1, w.Dqk, w.Dv, w.v_col0,
+                                w.sm_scale, threads=THREADS)
+    check_attn(got, ref_d)
+    full = np.full((ns, w.topk), -1, np.int32)
+    for i, t in enumerate(sub["q_pos"]):
+        full[i, : t + 1] = np.arange(t + 1)
+    ref_s, _ = oracle.sparse_mla(sub["q"], w.kv, sub["pt"], w.page_size, sub["q_pos"], ns, 1, full, w.Dqk, w.Dv,
+                                 w.v_col0, w.sm_scale, threads=THREADS)
+    np.testing.assert_array_equal(ref_s, ref_d)   # exact inside the oracle when k >= t + 1
+    # expanded fallback: the sampled rows' queries against the whole sequence's keys and values
+    bits = lambda x: x.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+    ref_x, _ = oracle.mha(bits(c.xq.index_select(0, rows_t)), bits(c.xkn), bits(c.xkr), bits(c.xv), sub["q_pos"], 1,
+                          ns, None, c.scale, threads=THREADS)
+    check_attn(c.xout.index_select(0, rows_t).float().cpu().numpy(), ref_x)

@@ -113,6 +113,36 @@ def test_fused_full_size_equals_separate_calls(oracle_lib, name):
     check_topk_sets(idx.cpu().numpy()[rows], ref_idx, ref_s[rows], w.q_pos[rows], w.topk)
 
 
+def test_fused_ragged_long_rows_equal_separate_calls(oracle_lib):
+    """The 128K-context decode size with ragged lengths (16385, 20000, 70000, 131072): most rows
+    end in a short 16384-position chunk or have empty ones, whose chunk stage keeps every key and
+    adds all its counts to the merge's histogram. Index lists bit for bit equal to the separate
+    calls and to the oracle's top-k of the same scores (exact), on one workspace used twice."""
+    print("case: fused ragged long rows", flush=True)
+    q_pos = [16384, 19999, 69999, 131071]
+    w = workloads.make_random(4, 1, q_pos, 131072, H=2, Dqk=16, Dv=8, seed=93, permute_pages=True, extra_pages=5)
+    d = gpu_inputs(w)
+    ws = torch.zeros(dsa.indexer_topk_workspace_size(w.rows, w.max_ctx, w.topk), dtype=torch.uint8, device="cuda")
+    runs = []
+    for _ in range(2):
+        s, idx = _fused(w, d, ws)
+        torch.cuda.synchronize()
+        assert dsa.last_path() == "indexer_topk_fused"
+        assert _hist_part_zero(ws, w.rows * _nh(w.max_ctx))
+        runs.append(idx.cpu().numpy())
+    np.testing.assert_array_equal(runs[0], runs[1])
+    s_sep = dsa.indexer_scores(d["iq"], d["iw"], d["ik"], d["iks"], d["page_table"], d["q_pos"], w.n_seq,
+                               w.q_per_seq, w.max_ctx)
+    idx_sep = dsa.topk(s_sep, d["q_pos"], w.max_ctx, w.topk)
+    torch.cuda.synchronize()
+    s_h = s.cpu().numpy()
+    for r in range(w.rows):
+        n = int(w.q_pos[r]) + 1
+        np.testing.assert_array_equal(s_h[r, :n].view(np.uint32), s_sep.cpu().numpy()[r, :n].view(np.uint32))
+    np.testing.assert_array_equal(runs[0], idx_sep.cpu().numpy())
+    np.testing.assert_array_equal(runs[0], oracle.topk(s_h, w.q_pos, w.topk, threads=8))
+
+
 def test_fused_rejects_small_workspace():
     w = workloads.make_random(1, 2, [300, 301], 320, H=2, Dqk=16, Dv=8, seed=3)
     d = gpu_inputs(w)

@@ -246,6 +246,76 @@ def test_sparse_mla_tuned(oracle_lib, entry, q_pos, qps, k):
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=1e-4)
 
 
+def _lists_with_repeats(q_pos, k, seed):
+    """Index lists that are sets only after removing repeats ([DSA-blog] "Sparse Attention": S_t
+    is a set), one kind per row: shuffled with repeats spread over the whole list (so over the
+    decode entry point's splits), sorted with adjacent repeats, every visible position listed many
+    times, and (control) a strictly ascending run that needs no filtering. All with holes and
+    invisible entries mixed in."""
+    rng = np.random.default_rng(seed)
+    idx = np.full((len(q_pos), k), -1, np.int32)
+    for r, t in enumerate(q_pos):
+        kind = r % 4
+        if kind == 0:
+            sel = rng.choice(t + 1, min(t + 1, k // 2), replace=False)
+            lst = np.concatenate([sel, rng.choice(sel, k - sel.size - 8), [-1] * 4, [t + 1, t + 9, -3, t + 2]])
+            rng.shuffle(lst)
+        elif kind == 1:
+            sel = np.sort(rng.choice(t + 1, min(t + 1, k // 2), replace=False))
+            lst = np.sort(np.concatenate([sel, rng.choice(sel, min(k - sel.size, sel.size // 3))]))
+        elif kind == 2:
+            lst = np.concatenate([rng.permutation(t + 1) for _ in range(max(1, k // (t + 1)))])[:k]
+        else:
+            lst = np.sort(rng.choice(t + 1, min(t + 1, k - 1), replace=False))
+        idx[r, : lst.size] = lst[:k]
+    return idx
+
+
+@pytest.mark.parametrize("entry", ["decode", "prefill"])
+def test_sparse_mla_repeated_entries_count_once(oracle_lib, entry):
+    """A repeated position is attended once, whatever the list order: against the oracle (which
+    takes the list as a set), and equal to the same call on the deduplicated ascending lists."""
+    _say(f"case: sparse mla {entry} with repeated entries")
+    q_pos = [3000, 2500, 129, 40, 2047, 2046, 700, 1500]
+    k = 2048
+    w = workloads.make_random(len(q_pos), 1, q_pos, max(q_pos) + 1, seed=53, permute_pages=True, extra_pages=2)
+    d = gpu_inputs(w)
+    idx = _lists_with_repeats(w.q_pos, k, seed=17)
+    dedup = np.full_like(idx, -1)
+    for r, t in enumerate(w.q_pos):
+        u = np.unique(idx[r][(idx[r] >= 0) & (idx[r] <= t)])
+        dedup[r, : u.size] = u
+    assert any(len(np.unique(x[x >= 0])) < int((x >= 0).sum()) for x in idx)
+    fn = dsa.sparse_mla_decode if entry == "decode" else dsa.sparse_mla_prefill
+    args = (w.Dqk, w.Dv, w.v_col0, w.sm_scale)
+    lse = torch.empty(w.rows, w.H, dtype=torch.float32, device="cuda")
+    out = fn(d["q"], d["kv"], d["page_table"], d["q_pos"], w.n_seq, 1, torch.from_numpy(idx).cuda(), *args, lse=lse)
+    assert dsa.last_path().startswith("mla_mfma")
+    ref, ref_lse = _attn_ref(w, idx)
+    check_attn(out.float().cpu().numpy(), ref)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=1e-4)
+    ref2, _ = _attn_ref(w, dedup)
+    np.testing.assert_array_equal(ref, ref2)
+    out2 = fn(d["q"], d["kv"], d["page_table"], d["q_pos"], w.n_seq, 1, torch.from_numpy(dedup).cuda(), *args)
+    check_attn(out2.float().cpu().numpy(), ref)
+    # the control rows (a strictly ascending run) take the same path either way: bit-identical
+    same = [r for r in range(w.rows) if r % 4 == 3]
+    assert torch.equal(out[same].view(torch.int16), out2[same].view(torch.int16))
+
+
+def test_sparse_mla_generic_repeated_entries(oracle_lib):
+    """The generic kernel (tiny one-head shape) takes the lists as sets too."""
+    _say("case: sparse mla tiny (generic) with repeated entries")
+    w = workloads.make_tiny()
+    d = gpu_inputs(w)
+    idx = _lists_with_repeats(w.q_pos, w.topk, seed=19)
+    out = dsa.sparse_mla_prefill(d["q"], d["kv"], d["page_table"], d["q_pos"], 1, w.rows, torch.from_numpy(idx).cuda(),
+                                 w.Dqk, w.Dv, w.v_col0, w.sm_scale)
+    assert dsa.last_path() == "mla_generic"
+    ref, _ = _attn_ref(w, idx)
+    check_attn(out.float().cpu().numpy(), ref)
+
+
 def test_sparse_mla_generic_tiny(oracle_lib):
     _say("case: sparse mla tiny (generic)")
     w = workloads.make_tiny()

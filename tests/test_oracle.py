@@ -367,6 +367,39 @@ def test_sparse_ignores_padding_and_invisible_entries(oracle_lib):
     np.testing.assert_array_equal(l1, l2)
 
 
+def test_sparse_repeated_and_shuffled_entries_are_a_set(oracle_lib):
+    """S_t is a set ([DSA-blog] "Sparse Attention": the mask is 0 exactly on S_t): a list that
+    repeats positions, in any order and with holes, gives the masked softmax of its distinct
+    positions -- torch's float64 SDPA under the boolean mask -- and equals the deduplicated
+    ascending list bit for bit. Counting a repeat twice would weight that row double."""
+    q, kv, pt, q_pos = _attn_case(seed=15)
+    rows, H, Dqk = q.shape
+    Dv, v0, T, k = 8, 8, 128, 16
+    rng = np.random.default_rng(16)
+    rep = np.full((rows, k), -1, np.int32)
+    ded = np.full((rows, k), -1, np.int32)
+    mask = torch.zeros(rows, T, dtype=torch.bool)
+    for r in range(rows):
+        m = min(5, q_pos[r] + 1)
+        sel = np.sort(rng.choice(q_pos[r] + 1, m, replace=False))
+        lst = np.concatenate([sel, sel[: max(1, m // 2)], sel[:1], [-1, q_pos[r] + 3]])
+        rng.shuffle(lst)
+        rep[r, : len(lst)] = lst
+        ded[r, :m] = sel
+        mask[r, torch.from_numpy(sel).long()] = True
+    assert any(len(set(x[x >= 0].tolist())) < int((x >= 0).sum()) for x in rep)
+    o1, l1 = oracle_lib.sparse_mla(q, kv, pt, 64, q_pos, 1, rows, rep, Dqk, Dv, v0, 0.41)
+    o2, l2 = oracle_lib.sparse_mla(q, kv, pt, 64, q_pos, 1, rows, ded, Dqk, Dv, v0, 0.41)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    allrows = _dec_bf16(_rows_of(kv, pt, T))
+    K, V = allrows[:, :Dqk], allrows[:, v0: v0 + Dv]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        _dec_bf16(q).transpose(0, 1), K.expand(H, T, Dqk), V.expand(H, T, Dv),
+        attn_mask=mask.unsqueeze(0).expand(H, rows, T), scale=0.41).transpose(0, 1)
+    np.testing.assert_allclose(o1, ref.numpy(), rtol=1e-6, atol=1e-6)
+
+
 def test_sparse_empty_set(oracle_lib):
     q, kv, pt, q_pos = _attn_case(seed=14)
     rows, H, Dqk = q.shape
