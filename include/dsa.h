@@ -201,6 +201,24 @@ dsa_status_t dsa_sparse_mla_prefill(const uint16_t* q, const uint16_t* kv_cache,
                                     float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * dsa_sparse_mla_decode_noalloc -- dsa_sparse_mla_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without ws / ws_bytes, the same kernels and the same results
+ * bit for bit. Its split-merge workspace is a 65 MiB array the library holds on each device it
+ * runs on (from the first call on that device until the process ends), which covers every shape
+ * the decode entry point splits (at most 510 (row, split) units of 128 x 512 fp16 partials plus
+ * their (max, sum) pairs); a call needing more returns DSA_ERR_WORKSPACE. It allocates nothing.
+ * The stream must belong to the calling thread's current device. All calls on one device share
+ * that array: calls that overlap in time on one device (different streams, or host threads)
+ * race and give undefined results; calls ordered on one stream are safe.
+ * ------------------------------------------------------------------------------------------- */
+dsa_status_t dsa_sparse_mla_decode_noalloc(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
+                                           int64_t ld_pt, int page_size, int num_pages, const int32_t* q_pos,
+                                           int n_seq, int q_per_seq, const int32_t* idx, int64_t ld_idx, int k, int H,
+                                           int Dqk, int Dv, int kv_dim, int v_col0, float sm_scale, uint16_t* out,
+                                           float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * dsa_dense_mla_prefill -- dense causal attention: the computation above with S = {0..q_pos[r]}
  * ([DSA-blog] "SWA" section, the causal set C_t). It equals DSA exactly when q_pos[r] + 1 <= k
  * for every row ([Handbook]: short prefill falls back to dense). Arguments as above, without

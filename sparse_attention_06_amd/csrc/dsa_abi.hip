@@ -1,9 +1,20 @@
 // dsa_abi.hip -- the extern "C" entry points of libdsa.so: host-side argument checks, kernel
 // choice and launch. No allocation, no synchronisation: every call only enqueues on `stream`.
+#include <limits.h>
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "dsa_internal.h"
+
+// Scratch memory of dsa_sparse_mla_decode_noalloc: the split-merge workspace of the decode
+// attention, held by the library itself. A decode call splits rows * splits < 512 units (the
+// split count doubles only while rows * splits < 256), each needing one fp16 partial row block and
+// one (max, sum) block, so 510 units always fit. Every GPU the library runs on holds its own copy
+// until the process ends.
+constexpr size_t kNoallocScratchBytes = 65u << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -98,6 +109,28 @@ dsa_status_t run_sparse(bool decode, const uint16_t* q, const uint16_t* kv_cache
   if (need > 0 && misaligned(ws)) return fail(DSA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
   s = hip_status(dsa::launch_mla_mfma(a, splits, ws, st), "mla_mfma launch");
   return s == DSA_OK ? ok(splits > 1 ? DSA_PATH_MLA_MFMA_SPLIT : DSA_PATH_MLA_MFMA) : s;
+}
+
+// Device address of `scratch` on the calling thread's current device, looked up once per device
+// with that device current (in host code the array's name is only a stand-in, never an address).
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+dsa_status_t scratch_on_current_device(void** ptr) {
+  int dev = -1;
+  dsa_status_t s = hip_status(hipGetDevice(&dev), "hipGetDevice");
+  if (s != DSA_OK) return s;
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&] { slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch)); });
+  if (slot.err != hipSuccess) return hip_status(slot.err, "hipGetSymbolAddress(scratch)");
+  *ptr = slot.ptr;
+  return DSA_OK;
 }
 
 }  // namespace
@@ -241,6 +274,27 @@ dsa_status_t dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* kv_cache,
                                    float* lse, void* ws, size_t ws_bytes, void* stream) {
   return run_sparse(true, q, kv_cache, page_table, ld_pt, page_size, num_pages, q_pos, n_seq, q_per_seq,
                     idx, ld_idx, k, H, Dqk, Dv, kv_dim, v_col0, sm_scale, out, lse, ws, ws_bytes, stream);
+}
+
+dsa_status_t dsa_sparse_mla_decode_noalloc(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
+                                           int64_t ld_pt, int page_size, int num_pages, const int32_t* q_pos,
+                                           int n_seq, int q_per_seq, const int32_t* idx, int64_t ld_idx, int k, int H,
+                                           int Dqk, int Dv, int kv_dim, int v_col0, float sm_scale, uint16_t* out,
+                                           float* lse, void* stream) {
+  const int64_t rows64 = (int64_t)n_seq * q_per_seq;
+  const int rows = (n_seq < 0 || q_per_seq < 1 || rows64 > INT_MAX) ? -1 : (int)rows64;
+  const size_t need = dsa_sparse_mla_workspace_size(rows, H, Dv, k);
+  if (need > kNoallocScratchBytes)
+    return fail(DSA_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the no-allocation entry point holds %zu",
+                need, kNoallocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    dsa_status_t s = scratch_on_current_device(&ws);
+    if (s != DSA_OK) return s;
+  }
+  return run_sparse(true, q, kv_cache, page_table, ld_pt, page_size, num_pages, q_pos, n_seq, q_per_seq, idx, ld_idx,
+                    k, H, Dqk, Dv, kv_dim, v_col0, sm_scale, out, lse, ws, need > 0 ? kNoallocScratchBytes : 0,
+                    stream);
 }
 
 dsa_status_t dsa_sparse_mla_prefill(const uint16_t* q, const uint16_t* kv_cache,

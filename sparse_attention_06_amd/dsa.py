@@ -27,6 +27,7 @@ EXPORTS = [
     "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk",
     "dsa_indexer_topk_workspace_size", "dsa_indexer_topk",
     "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
+    "dsa_sparse_mla_decode_noalloc",
     "dsa_dense_mla_workspace_size", "dsa_dense_mla_prefill",
     "dsa_expanded_mha_workspace_size", "dsa_expanded_mha_prefill",
     "dsa_indexer_cache_write", "dsa_latent_cache_write", "dsa_e4m3_quantize",
@@ -81,6 +82,8 @@ def load():
     lib.dsa_sparse_mla_decode.argtypes = attn
     lib.dsa_sparse_mla_prefill.restype = i32
     lib.dsa_sparse_mla_prefill.argtypes = attn
+    lib.dsa_sparse_mla_decode_noalloc.restype = i32
+    lib.dsa_sparse_mla_decode_noalloc.argtypes = attn[:-3] + [vp]
     lib.dsa_dense_mla_workspace_size.restype = sz
     lib.dsa_dense_mla_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.dsa_dense_mla_prefill.restype = i32
@@ -263,6 +266,23 @@ def sparse_mla_decode(*args, **kw):
 
 def sparse_mla_prefill(*args, **kw):
     return _sparse("dsa_sparse_mla_prefill", *args, **kw)
+
+
+def sparse_mla_decode_noalloc(q, kv_cache, page_table, q_pos, n_seq, q_per_seq, idx, Dqk, Dv, v_col0, sm_scale,
+                              out, lse=None, stream=None):
+    """dsa_sparse_mla_decode without a workspace argument: the library's own device scratch is
+    used, and nothing is allocated here either (out, and lse if wanted, are the caller's)."""
+    if out is None:
+        raise ValueError("sparse_mla_decode_noalloc needs the caller's out tensor")
+    _attn_common(q, kv_cache, page_table, q_pos, out, lse, Dv)
+    _need(idx, "idx", torch.int32, 2)
+    rows, H, _ = q.shape
+    st = load().dsa_sparse_mla_decode_noalloc(
+        _p(q), _p(kv_cache), _p(page_table), page_table.shape[1], kv_cache.shape[1], kv_cache.shape[0], _p(q_pos),
+        n_seq, q_per_seq, _p(idx), idx.shape[1], idx.shape[1], H, Dqk, Dv, kv_cache.shape[2], v_col0,
+        float(sm_scale), _p(out), _p(lse), _stream(stream))
+    _check("dsa_sparse_mla_decode_noalloc", st)
+    return out
 
 
 def dense_mla_prefill(q, kv_cache, page_table, q_pos, n_seq, q_per_seq, max_ctx, Dqk, Dv, v_col0, sm_scale,
