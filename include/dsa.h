@@ -17,12 +17,19 @@
  *   owns all memory. The library never allocates, frees or synchronises: each call validates
  *   its host-side arguments, then only enqueues kernels on `stream` and returns. Arrays must
  *   stay valid until that work completes. Calls on different streams are independent.
- * Rows: a call processes rows = n_seq * q_per_seq query rows; row r belongs to sequence
- *   s = r / q_per_seq and sits at 0-based position q_pos[r] (device int32 [rows]). It sees
- *   positions j in [0, q_pos[r]], itself included ([DSA-blog] "Lightning Indexer": j <= t; the
- *   worked example selects the query's own position 8). Decode uses q_per_seq = 1, MTP
- *   verification q_per_seq = 2 (both rows of a request share one scan of its keys), a prefill
- *   chunk n_seq = 1 and q_per_seq = chunk length.
+ * Rows: a call processes `rows` query rows. Row r sits at 0-based position q_pos[r] (device
+ *   int32 [rows]) of its sequence and sees positions j in [0, q_pos[r]], itself included
+ *   ([DSA-blog] "Lightning Indexer": j <= t; the worked example selects the query's own position
+ *   8). Its sequence (the page-table row of its caches) is given in one of two ways:
+ *     q_seq == NULL   rows = n_seq * q_per_seq, and row r belongs to sequence r / q_per_seq:
+ *                     decode uses q_per_seq = 1, MTP verification q_per_seq = 2 (both rows of a
+ *                     request share one scan of its keys), a prefill chunk n_seq = 1 and
+ *                     q_per_seq = chunk length;
+ *     q_seq != NULL   device int32 [rows]: row r belongs to sequence q_seq[r], in [0, n_seq);
+ *                     q_per_seq must be 1. Any mix of rows fits (a decode batch beside a prefill
+ *                     chunk, requests with different numbers of rows); the indexer then scans
+ *                     each row's keys on its own. A row whose q_seq is outside [0, n_seq) has no
+ *                     page-table row: no access is made for it and its results are unspecified.
  * Paging: both caches are paged. Position p of sequence s is physical row
  *   page_table[s * ld_pt + p / page_size] * page_size + p % page_size
  *   of a cache holding num_pages * page_size rows. page_table is device int32 [n_seq, ld_pt].
@@ -106,9 +113,9 @@ int dsa_last_path(void);
  * ------------------------------------------------------------------------------------------- */
 dsa_status_t dsa_indexer_scores(const void* q, const float* w, const void* k_cache,
                                 const float* k_scale, const int32_t* page_table, int64_t ld_pt,
-                                int page_size, int num_pages, const int32_t* q_pos, int n_seq,
-                                int q_per_seq, int max_ctx, int Hi, int Di, dsa_dtype_t dtype,
-                                float* scores, int64_t ld_scores, void* stream);
+                                int page_size, int num_pages, const int32_t* q_seq, const int32_t* q_pos,
+                                int rows, int n_seq, int q_per_seq, int max_ctx, int Hi, int Di,
+                                dsa_dtype_t dtype, float* scores, int64_t ld_scores, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * dsa_topk -- S_t = TopK_{j <= t}(I_tj, k) ([DSA-blog] "Lightning Indexer", the TopK equation);
@@ -152,9 +159,9 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_p
 size_t dsa_indexer_topk_workspace_size(int rows, int max_ctx, int k);
 dsa_status_t dsa_indexer_topk(const void* q, const float* w, const void* k_cache, const float* k_scale,
                               const int32_t* page_table, int64_t ld_pt, int page_size, int num_pages,
-                              const int32_t* q_pos, int n_seq, int q_per_seq, int max_ctx, int Hi, int Di,
-                              dsa_dtype_t dtype, float* scores, int64_t ld_scores, int k, int32_t* idx,
-                              int64_t ld_idx, void* ws, size_t ws_bytes, void* stream);
+                              const int32_t* q_seq, const int32_t* q_pos, int rows, int n_seq, int q_per_seq,
+                              int max_ctx, int Hi, int Di, dsa_dtype_t dtype, float* scores, int64_t ld_scores, int k,
+                              int32_t* idx, int64_t ld_idx, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * dsa_sparse_mla_decode / dsa_sparse_mla_prefill -- attention over the selected rows only
@@ -187,18 +194,18 @@ dsa_status_t dsa_indexer_topk(const void* q, const float* w, const void* k_cache
  * fp32 (max, sum) pair per head; the prefill entry point does one pass per row.
  * ------------------------------------------------------------------------------------------- */
 size_t dsa_sparse_mla_workspace_size(int rows, int H, int Dv, int k);
-dsa_status_t dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* kv_cache,
-                                   const int32_t* page_table, int64_t ld_pt, int page_size,
-                                   int num_pages, const int32_t* q_pos, int n_seq, int q_per_seq,
-                                   const int32_t* idx, int64_t ld_idx, int k, int H, int Dqk,
-                                   int Dv, int kv_dim, int v_col0, float sm_scale, uint16_t* out,
-                                   float* lse, void* ws, size_t ws_bytes, void* stream);
-dsa_status_t dsa_sparse_mla_prefill(const uint16_t* q, const uint16_t* kv_cache,
-                                    const int32_t* page_table, int64_t ld_pt, int page_size,
-                                    int num_pages, const int32_t* q_pos, int n_seq, int q_per_seq,
-                                    const int32_t* idx, int64_t ld_idx, int k, int H, int Dqk,
-                                    int Dv, int kv_dim, int v_col0, float sm_scale, uint16_t* out,
-                                    float* lse, void* ws, size_t ws_bytes, void* stream);
+dsa_status_t dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
+                                   int64_t ld_pt, int page_size, int num_pages, const int32_t* q_seq,
+                                   const int32_t* q_pos, int rows, int n_seq, int q_per_seq, const int32_t* idx,
+                                   int64_t ld_idx, int k, int H, int Dqk, int Dv, int kv_dim, int v_col0,
+                                   float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                   void* stream);
+dsa_status_t dsa_sparse_mla_prefill(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
+                                    int64_t ld_pt, int page_size, int num_pages, const int32_t* q_seq,
+                                    const int32_t* q_pos, int rows, int n_seq, int q_per_seq, const int32_t* idx,
+                                    int64_t ld_idx, int k, int H, int Dqk, int Dv, int kv_dim, int v_col0,
+                                    float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                    void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * dsa_sparse_mla_decode_noalloc -- dsa_sparse_mla_decode for callers that cannot allocate
@@ -213,10 +220,11 @@ dsa_status_t dsa_sparse_mla_prefill(const uint16_t* q, const uint16_t* kv_cache,
  * race and give undefined results; calls ordered on one stream are safe.
  * ------------------------------------------------------------------------------------------- */
 dsa_status_t dsa_sparse_mla_decode_noalloc(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
-                                           int64_t ld_pt, int page_size, int num_pages, const int32_t* q_pos,
-                                           int n_seq, int q_per_seq, const int32_t* idx, int64_t ld_idx, int k, int H,
-                                           int Dqk, int Dv, int kv_dim, int v_col0, float sm_scale, uint16_t* out,
-                                           float* lse, void* stream);
+                                           int64_t ld_pt, int page_size, int num_pages, const int32_t* q_seq,
+                                           const int32_t* q_pos, int rows, int n_seq, int q_per_seq,
+                                           const int32_t* idx, int64_t ld_idx, int k, int H, int Dqk, int Dv,
+                                           int kv_dim, int v_col0, float sm_scale, uint16_t* out, float* lse,
+                                           void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * dsa_dense_mla_prefill -- dense causal attention: the computation above with S = {0..q_pos[r]}
@@ -225,12 +233,11 @@ dsa_status_t dsa_sparse_mla_decode_noalloc(const uint16_t* q, const uint16_t* kv
  * idx; max_ctx (> every q_pos) sizes the key loop. Workspace: dsa_dense_mla_workspace_size.
  * ------------------------------------------------------------------------------------------- */
 size_t dsa_dense_mla_workspace_size(int rows, int H, int Dv, int max_ctx);
-dsa_status_t dsa_dense_mla_prefill(const uint16_t* q, const uint16_t* kv_cache,
-                                   const int32_t* page_table, int64_t ld_pt, int page_size,
-                                   int num_pages, const int32_t* q_pos, int n_seq, int q_per_seq,
-                                   int max_ctx, int H, int Dqk, int Dv, int kv_dim, int v_col0,
-                                   float sm_scale, uint16_t* out, float* lse, void* ws,
-                                   size_t ws_bytes, void* stream);
+dsa_status_t dsa_dense_mla_prefill(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
+                                   int64_t ld_pt, int page_size, int num_pages, const int32_t* q_seq,
+                                   const int32_t* q_pos, int rows, int n_seq, int q_per_seq, int max_ctx, int H,
+                                   int Dqk, int Dv, int kv_dim, int v_col0, float sm_scale, uint16_t* out, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * dsa_expanded_mha_prefill -- expanded multi-head attention, the dense fallback for short prefill
@@ -239,6 +246,8 @@ dsa_status_t dsa_dense_mla_prefill(const uint16_t* q, const uint16_t* kv_cache,
  * absorbed form; short prefill runs it, and V3.2 emulates DSA in a masked MHA mode). With the
  * per-head up-projections of the latent row c_j applied beforehand (k_nope = c W_UK, v = c W_UV),
  * it computes the same attention as the absorbed MLA above, output projected by W_UV.
+ * Rows take the uniform layout only (rows = n_seq * q_per_seq, no q_seq): a workgroup shares one
+ * sequence's key and value tiles among up to 256 consecutive rows of that sequence.
  * For row r (sequence s = r / q_per_seq, position t = q_pos[r]) and head h:
  *     K_hj = [k_nope[s, h, j, :] | k_rope[s, j, :]]      (the rope key is shared by all heads)
  *     l_j  = sm_scale * q[r, h, :] . K_hj,   j in S

@@ -62,10 +62,19 @@ static int64_t phys_row(const int32_t* page_table, int64_t ld_pt, int page_size,
   return (int64_t)page * page_size + p % page_size;
 }
 
-static int bad_common(int n_seq, int q_per_seq, int row_begin, int row_end) {
-  if (n_seq < 0 || q_per_seq < 1) return 1;
-  if (row_begin < 0 || row_end > n_seq * q_per_seq || row_begin > row_end) return 1;
+/* The query-row descriptor: `rows` rows; row r belongs to sequence q_seq[r] when q_seq is given
+ * (then q_per_seq must be 1), else to sequence r / q_per_seq with rows = n_seq * q_per_seq. */
+static int bad_common(const int32_t* q_seq, int rows, int n_seq, int q_per_seq, int row_begin, int row_end) {
+  if (rows < 0 || n_seq < 0 || q_per_seq < 1) return 1;
+  if (q_seq ? q_per_seq != 1 : (int64_t)n_seq * q_per_seq != rows) return 1;
+  if (row_begin < 0 || row_end > rows || row_begin > row_end) return 1;
   return 0;
+}
+
+/* Sequence of row r, or -1 when its id lies outside [0, n_seq). */
+static int seq_of(const int32_t* q_seq, int q_per_seq, int n_seq, int r) {
+  int s = q_seq ? q_seq[r] : r / q_per_seq;
+  return (s >= 0 && s < n_seq) ? s : -1;
 }
 
 /* ---- Lightning Indexer ------------------------------------------------------------ */
@@ -76,15 +85,16 @@ static int bad_common(int n_seq, int q_per_seq, int row_begin, int row_end) {
  * dot product exactly as written here. */
 int oracle_indexer_scores(const void* q, const float* w, const void* k_cache, const float* k_scale,
                           const int32_t* page_table, int64_t ld_pt, int page_size, int num_pages,
-                          const int32_t* q_pos, int n_seq, int q_per_seq, int Hi, int Di, int fmt,
-                          float* scores, int64_t ld_scores, int row_begin, int row_end) {
-  if (bad_common(n_seq, q_per_seq, row_begin, row_end)) return 1;
+                          const int32_t* q_seq, const int32_t* q_pos, int rows, int n_seq, int q_per_seq,
+                          int Hi, int Di, int fmt, float* scores, int64_t ld_scores, int row_begin, int row_end) {
+  if (bad_common(q_seq, rows, n_seq, q_per_seq, row_begin, row_end)) return 1;
   if (Hi < 1 || Di < 1 || page_size < 1 || (fmt != ORACLE_E4M3 && fmt != ORACLE_F32)) return 1;
   double* key = (double*)malloc(sizeof(double) * (size_t)Di);
   if (!key) return 2;
   for (int r = row_begin; r < row_end; ++r) {
-    int s = r / q_per_seq;
+    int s = seq_of(q_seq, q_per_seq, n_seq, r);
     int64_t t = q_pos[r];
+    if (s < 0) { free(key); return 3; }
     for (int64_t j = 0; j <= t; ++j) {
       int64_t row = phys_row(page_table, ld_pt, page_size, num_pages, s, j);
       if (row < 0) { free(key); return 3; }
@@ -197,17 +207,18 @@ static int bad_attn(int H, int Dqk, int Dv, int kv_dim, int v_col0, int page_siz
 }
 
 int oracle_sparse_mla(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
-                      int64_t ld_pt, int page_size, int num_pages, const int32_t* q_pos, int n_seq,
-                      int q_per_seq, const int32_t* idx, int64_t ld_idx, int k, int H, int Dqk,
-                      int Dv, int kv_dim, int v_col0, double sm_scale, float* out, float* lse,
+                      int64_t ld_pt, int page_size, int num_pages, const int32_t* q_seq, const int32_t* q_pos,
+                      int rows, int n_seq, int q_per_seq, const int32_t* idx, int64_t ld_idx, int k, int H,
+                      int Dqk, int Dv, int kv_dim, int v_col0, double sm_scale, float* out, float* lse,
                       int row_begin, int row_end) {
-  if (bad_common(n_seq, q_per_seq, row_begin, row_end) || k < 0) return 1;
+  if (bad_common(q_seq, rows, n_seq, q_per_seq, row_begin, row_end) || k < 0) return 1;
   if (bad_attn(H, Dqk, Dv, kv_dim, v_col0, page_size)) return 1;
   int64_t* set = (int64_t*)malloc(sizeof(int64_t) * (size_t)(k > 0 ? k : 1));
   if (!set) return 2;
   for (int r = row_begin; r < row_end; ++r) {
-    int s = r / q_per_seq;
+    int s = seq_of(q_seq, q_per_seq, n_seq, r);
     int64_t t = q_pos[r], n_set = 0;
+    if (s < 0) { free(set); return 3; }
     /* S_t is a set ([DSA-blog] "Sparse Attention": the mask is 0 exactly on S_t): mark every
      * listed visible position once, then visit the marked positions in ascending order */
     unsigned char* in_set = (unsigned char*)calloc((size_t)(t >= 0 ? t + 1 : 1), 1);
@@ -233,13 +244,14 @@ int oracle_sparse_mla(const uint16_t* q, const uint16_t* kv_cache, const int32_t
 }
 
 int oracle_dense_mla(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
-                     int64_t ld_pt, int page_size, int num_pages, const int32_t* q_pos, int n_seq,
-                     int q_per_seq, int H, int Dqk, int Dv, int kv_dim, int v_col0,
+                     int64_t ld_pt, int page_size, int num_pages, const int32_t* q_seq, const int32_t* q_pos,
+                     int rows, int n_seq, int q_per_seq, int H, int Dqk, int Dv, int kv_dim, int v_col0,
                      double sm_scale, float* out, float* lse, int row_begin, int row_end) {
-  if (bad_common(n_seq, q_per_seq, row_begin, row_end)) return 1;
+  if (bad_common(q_seq, rows, n_seq, q_per_seq, row_begin, row_end)) return 1;
   if (bad_attn(H, Dqk, Dv, kv_dim, v_col0, page_size)) return 1;
   for (int r = row_begin; r < row_end; ++r) {
-    int s = r / q_per_seq;
+    int s = seq_of(q_seq, q_per_seq, n_seq, r);
+    if (s < 0) return 3;
     int64_t n_set = (int64_t)q_pos[r] + 1;
     if (n_set < 0) n_set = 0;
     int64_t* set = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_set > 0 ? n_set : 1));
@@ -271,7 +283,7 @@ int oracle_mha(const uint16_t* q, const uint16_t* k_nope, const uint16_t* k_rope
                int64_t ld_kv, const int32_t* q_pos, int n_seq, int q_per_seq, const int32_t* idx,
                int64_t ld_idx, int k, int H, int Dn, int Dr, int Dv, double sm_scale, float* out,
                float* lse, int row_begin, int row_end) {
-  if (bad_common(n_seq, q_per_seq, row_begin, row_end) || k < 0) return 1;
+  if (bad_common(NULL, n_seq * q_per_seq, n_seq, q_per_seq, row_begin, row_end) || k < 0) return 1;
   if (H < 1 || Dn < 1 || Dr < 0 || Dv < 1 || ld_kv < 1) return 1;
   const int Dq = Dn + Dr;
   unsigned char* in_set = (unsigned char*)malloc((size_t)ld_kv);

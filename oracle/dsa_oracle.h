@@ -13,8 +13,9 @@
  *   - Positions are 0-based; a query row at position t sees keys j in [0, t]
  *     ([DSA-blog] section "Lightning Indexer", notation j <= t; the worked example
  *     includes the query's own position).
- *   - Rows: rows = n_seq * q_per_seq; row r belongs to sequence r / q_per_seq and sits
- *     at position q_pos[r].
+ *   - Rows: `rows` query rows; row r sits at position q_pos[r] of sequence q_seq[r] when the
+ *     per-row array q_seq is given (q_per_seq must then be 1), else of sequence r / q_per_seq
+ *     with rows = n_seq * q_per_seq. A sequence id outside [0, n_seq) is an error (code 3).
  *   - Paged caches: position p of sequence s lives in physical row
  *       page_table[s * ld_pt + p / page_size] * page_size + p % page_size.
  *   - Every function processes rows [row_begin, row_end) only, so callers may split
@@ -46,8 +47,8 @@ double oracle_bf16_to_double(uint16_t bits);
  * scores[r * ld_scores + j] is written for j <= q_pos[r] only. */
 int oracle_indexer_scores(const void* q, const float* w, const void* k_cache, const float* k_scale,
                           const int32_t* page_table, int64_t ld_pt, int page_size, int num_pages,
-                          const int32_t* q_pos, int n_seq, int q_per_seq, int Hi, int Di, int fmt,
-                          float* scores, int64_t ld_scores, int row_begin, int row_end);
+                          const int32_t* q_seq, const int32_t* q_pos, int rows, int n_seq, int q_per_seq,
+                          int Hi, int Di, int fmt, float* scores, int64_t ld_scores, int row_begin, int row_end);
 
 /* Top-k ([DSA-blog] "Lightning Indexer", S_t = TopK_{j<=t}(I_tj, k)): for row r the
  * m = min(k, q_pos[r] + 1) positions with the largest score; equal scores are ordered by
@@ -69,16 +70,16 @@ int oracle_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, in
  * An empty S gives o = 0 and lse = -inf. q: bf16 [rows, H, Dqk]; kv_cache: bf16
  * [num_pages*page_size, kv_dim]; out: float [rows, H, Dv]; lse: float [rows, H] or NULL. */
 int oracle_sparse_mla(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
-                      int64_t ld_pt, int page_size, int num_pages, const int32_t* q_pos, int n_seq,
-                      int q_per_seq, const int32_t* idx, int64_t ld_idx, int k, int H, int Dqk,
-                      int Dv, int kv_dim, int v_col0, double sm_scale, float* out, float* lse,
+                      int64_t ld_pt, int page_size, int num_pages, const int32_t* q_seq, const int32_t* q_pos,
+                      int rows, int n_seq, int q_per_seq, const int32_t* idx, int64_t ld_idx, int k, int H,
+                      int Dqk, int Dv, int kv_dim, int v_col0, double sm_scale, float* out, float* lse,
                       int row_begin, int row_end);
 
 /* Dense causal attention: the same computation with S = {0, 1, ..., q_pos[r]} visited in
  * ascending order ([DSA-blog] "SWA" section, the causal set C_t). */
 int oracle_dense_mla(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
-                     int64_t ld_pt, int page_size, int num_pages, const int32_t* q_pos, int n_seq,
-                     int q_per_seq, int H, int Dqk, int Dv, int kv_dim, int v_col0,
+                     int64_t ld_pt, int page_size, int num_pages, const int32_t* q_seq, const int32_t* q_pos,
+                     int rows, int n_seq, int q_per_seq, int H, int Dqk, int Dv, int kv_dim, int v_col0,
                      double sm_scale, float* out, float* lse, int row_begin, int row_end);
 
 /* Expanded multi-head attention, the short-prefill fallback ([Handbook] "稀疏注意力：NSA 与

@@ -50,16 +50,16 @@ def _load():
             lib.oracle_bf16_to_double.restype = dbl
             lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
             lib.oracle_indexer_scores.restype = i32
-            lib.oracle_indexer_scores.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, vp, i32, i32, i32,
-                                                  i32, i32, vp, i64, i32, i32]
+            lib.oracle_indexer_scores.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, i32,
+                                                  i32, i32, i32, vp, i64, i32, i32]
             lib.oracle_topk.restype = i32
             lib.oracle_topk.argtypes = [vp, i64, vp, i32, i32, vp, i64, i32, i32]
             lib.oracle_sparse_mla.restype = i32
-            lib.oracle_sparse_mla.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, i32, vp, i64, i32, i32,
-                                              i32, i32, i32, i32, dbl, vp, vp, i32, i32]
+            lib.oracle_sparse_mla.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, i32, vp, i64, i32,
+                                              i32, i32, i32, i32, i32, dbl, vp, vp, i32, i32]
             lib.oracle_dense_mla.restype = i32
-            lib.oracle_dense_mla.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, i32, i32, i32, i32,
-                                             i32, i32, dbl, vp, vp, i32, i32]
+            lib.oracle_dense_mla.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, i32, i32, i32,
+                                             i32, i32, i32, dbl, vp, vp, i32, i32]
             lib.oracle_e4m3_from_float.restype = ctypes.c_uint8
             lib.oracle_e4m3_from_float.argtypes = [ctypes.c_float]
             lib.oracle_e4m3_quantize.restype = i32
@@ -121,10 +121,20 @@ def _c(a, dtype):
     return a
 
 
+def _seq(q_seq, nrows):
+    """The per-row sequence ids as a C array (None: rows in groups of q_per_seq per sequence)."""
+    if q_seq is None:
+        return None
+    q_seq = _c(q_seq, np.int32)
+    assert q_seq.shape == (nrows,)
+    return q_seq
+
+
 def indexer_scores(q, w, k_cache, k_scale, page_table, page_size, q_pos, n_seq, q_per_seq, fmt,
-                   ld_scores, scores=None, threads=1, rows=None):
-    """Scores [n_seq*q_per_seq, ld_scores] float32; entries j > q_pos[r] are left as given
-    (NaN in a fresh array). `rows` optionally restricts the computed rows."""
+                   ld_scores, scores=None, threads=1, rows=None, q_seq=None):
+    """Scores [rows, ld_scores] float32 (rows = q.shape[0]); entries j > q_pos[r] are left as given
+    (NaN in a fresh array). `rows` optionally restricts the computed rows. q_seq: per-row
+    sequence ids (q_per_seq must then be 1), or None for n_seq * q_per_seq rows in groups."""
     lib = _load()
     qdt = np.uint8 if fmt == E4M3 else np.float32
     q = _c(q, qdt)
@@ -133,7 +143,8 @@ def indexer_scores(q, w, k_cache, k_scale, page_table, page_size, q_pos, n_seq, 
     pt = _c(page_table, np.int32)
     q_pos = _c(q_pos, np.int32)
     ks = None if k_scale is None else _c(k_scale, np.float32)
-    nrows = n_seq * q_per_seq
+    nrows = q.shape[0]
+    qs = _seq(q_seq, nrows)
     Hi, Di = q.shape[-2], q.shape[-1]
     num_pages = k_cache.shape[0]
     if scores is None:
@@ -141,8 +152,8 @@ def indexer_scores(q, w, k_cache, k_scale, page_table, page_size, q_pos, n_seq, 
 
     def fn(b, e):
         return lib.oracle_indexer_scores(_ptr(q), _ptr(w), _ptr(k_cache), _ptr(ks), _ptr(pt), pt.shape[1],
-                                         page_size, num_pages, _ptr(q_pos), n_seq, q_per_seq, Hi, Di, fmt,
-                                         _ptr(scores), ld_scores, b, e)
+                                         page_size, num_pages, _ptr(qs), _ptr(q_pos), nrows, n_seq, q_per_seq, Hi,
+                                         Di, fmt, _ptr(scores), ld_scores, b, e)
 
     _run_rows(fn, nrows, threads, rows)
     return scores
@@ -164,7 +175,7 @@ def topk(scores, q_pos, k, threads=1, rows=None, idx=None):
 
 
 def sparse_mla(q, kv_cache, page_table, page_size, q_pos, n_seq, q_per_seq, idx, Dqk, Dv, v_col0,
-               sm_scale, threads=1, rows=None, with_lse=True):
+               sm_scale, threads=1, rows=None, with_lse=True, q_seq=None):
     """q: uint16 (bf16 bits) [rows, H, Dqk]; kv_cache: uint16 [P, page, kv_dim];
     returns (out float32 [rows, H, Dv], lse float32 [rows, H])."""
     lib = _load()
@@ -174,6 +185,7 @@ def sparse_mla(q, kv_cache, page_table, page_size, q_pos, n_seq, q_per_seq, idx,
     q_pos = _c(q_pos, np.int32)
     idx = _c(idx, np.int32)
     nrows, H = q.shape[0], q.shape[1]
+    qs = _seq(q_seq, nrows)
     kv_dim = kv.shape[-1]
     num_pages = kv.shape[0]
     out = np.full((nrows, H, Dv), np.nan, dtype=np.float32)
@@ -181,7 +193,8 @@ def sparse_mla(q, kv_cache, page_table, page_size, q_pos, n_seq, q_per_seq, idx,
 
     def fn(b, e):
         return lib.oracle_sparse_mla(_ptr(q), _ptr(kv), _ptr(pt), pt.shape[1], page_size, num_pages,
-                                     _ptr(q_pos), n_seq, q_per_seq, _ptr(idx), idx.shape[1], idx.shape[1],
+                                     _ptr(qs), _ptr(q_pos), nrows, n_seq, q_per_seq, _ptr(idx), idx.shape[1],
+                                     idx.shape[1],
                                      H, Dqk, Dv, kv_dim, v_col0, float(sm_scale), _ptr(out), _ptr(lse), b, e)
 
     _run_rows(fn, nrows, threads, rows)
@@ -189,13 +202,14 @@ def sparse_mla(q, kv_cache, page_table, page_size, q_pos, n_seq, q_per_seq, idx,
 
 
 def dense_mla(q, kv_cache, page_table, page_size, q_pos, n_seq, q_per_seq, Dqk, Dv, v_col0, sm_scale,
-              threads=1, rows=None, with_lse=True):
+              threads=1, rows=None, with_lse=True, q_seq=None):
     lib = _load()
     q = _c(q, np.uint16)
     kv = _c(kv_cache, np.uint16)
     pt = _c(page_table, np.int32)
     q_pos = _c(q_pos, np.int32)
     nrows, H = q.shape[0], q.shape[1]
+    qs = _seq(q_seq, nrows)
     kv_dim = kv.shape[-1]
     num_pages = kv.shape[0]
     out = np.full((nrows, H, Dv), np.nan, dtype=np.float32)
@@ -203,7 +217,7 @@ def dense_mla(q, kv_cache, page_table, page_size, q_pos, n_seq, q_per_seq, Dqk, 
 
     def fn(b, e):
         return lib.oracle_dense_mla(_ptr(q), _ptr(kv), _ptr(pt), pt.shape[1], page_size, num_pages,
-                                    _ptr(q_pos), n_seq, q_per_seq, H, Dqk, Dv, kv_dim, v_col0,
+                                    _ptr(qs), _ptr(q_pos), nrows, n_seq, q_per_seq, H, Dqk, Dv, kv_dim, v_col0,
                                     float(sm_scale), _ptr(out), _ptr(lse), b, e)
 
     _run_rows(fn, nrows, threads, rows)

@@ -58,19 +58,35 @@ dsa_status_t check_paging(const int32_t* page_table, int64_t ld_pt, int page_siz
   return DSA_OK;
 }
 
+// The query-row descriptor of the indexer and attention calls: `rows` rows, either in groups of
+// q_per_seq consecutive rows per sequence (q_seq NULL; rows == n_seq * q_per_seq), or row r of
+// sequence q_seq[r] (device array; q_per_seq must then be 1).
+dsa_status_t check_rows(const int32_t* q_seq, int rows, int n_seq, int q_per_seq, dsa::RowSeq* rs) {
+  REQUIRE(rows >= 0 && n_seq >= 0 && q_per_seq >= 1, "need rows >= 0, n_seq >= 0 and q_per_seq >= 1 (got %d, %d, %d)",
+          rows, n_seq, q_per_seq);
+  if (q_seq)
+    REQUIRE(q_per_seq == 1, "with per-row sequence ids (q_seq) q_per_seq must be 1 (got %d)", q_per_seq);
+  else
+    REQUIRE((int64_t)n_seq * q_per_seq == rows, "without q_seq, rows (%d) must equal n_seq * q_per_seq (%d * %d)",
+            rows, n_seq, q_per_seq);
+  REQUIRE(rows == 0 || n_seq >= 1, "%d rows but no sequence", rows);
+  *rs = dsa::RowSeq{q_seq, q_per_seq, n_seq};
+  return DSA_OK;
+}
+
 // The MFMA kernels take the absorbed-MLA shape with a positive softmax scale (they track the
 // running maximum on the unscaled scores).
 bool mla_tuned(int H, int Dqk, int Dv, int kv_dim, int v_col0, float sm_scale = 1.f) {
   return H == 128 && Dqk == 576 && Dv == 512 && kv_dim == 576 && v_col0 == 0 && sm_scale > 0.f;
 }
 
-dsa_status_t check_attn(const uint16_t* q, const uint16_t* kv_cache, const int32_t* q_pos,
-                        int n_seq, int q_per_seq, int H, int Dqk, int Dv, int kv_dim, int v_col0,
-                        uint16_t* out) {
-  REQUIRE(n_seq >= 0 && q_per_seq >= 1, "need n_seq >= 0 and q_per_seq >= 1");
-  if (n_seq == 0) return DSA_OK;  // nothing to do; the caller returns before any launch
+dsa_status_t check_attn(const uint16_t* q, const uint16_t* kv_cache, const int32_t* q_seq, const int32_t* q_pos,
+                        int rows, int n_seq, int q_per_seq, int H, int Dqk, int Dv, int kv_dim, int v_col0,
+                        uint16_t* out, dsa::RowSeq* rs) {
+  dsa_status_t s = check_rows(q_seq, rows, n_seq, q_per_seq, rs);
+  if (s != DSA_OK) return s;
+  if (rows == 0) return DSA_OK;  // nothing to do; the caller returns before any launch
   REQUIRE(q && kv_cache && q_pos && out, "q, kv_cache, q_pos and out must be non-NULL");
-  REQUIRE((int64_t)n_seq * q_per_seq < ((int64_t)1 << 31), "too many rows");
   REQUIRE(H >= 1 && Dqk >= 1 && Dv >= 1, "H, Dqk and Dv must be >= 1");
   REQUIRE(kv_dim >= Dqk && v_col0 >= 0 && v_col0 + Dv <= kv_dim,
           "need Dqk <= kv_dim and v_col0 + Dv <= kv_dim");
@@ -83,19 +99,19 @@ dsa_status_t check_attn(const uint16_t* q, const uint16_t* kv_cache, const int32
 
 dsa_status_t run_sparse(bool decode, const uint16_t* q, const uint16_t* kv_cache,
                         const int32_t* page_table, int64_t ld_pt, int page_size, int num_pages,
-                        const int32_t* q_pos, int n_seq, int q_per_seq, const int32_t* idx,
-                        int64_t ld_idx, int k, int H, int Dqk, int Dv, int kv_dim, int v_col0,
-                        float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                        const int32_t* q_seq, const int32_t* q_pos, int rows, int n_seq, int q_per_seq,
+                        const int32_t* idx, int64_t ld_idx, int k, int H, int Dqk, int Dv, int kv_dim,
+                        int v_col0, float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
                         void* stream) {
-  dsa_status_t s = check_attn(q, kv_cache, q_pos, n_seq, q_per_seq, H, Dqk, Dv, kv_dim, v_col0, out);
+  dsa::RowSeq rs;
+  dsa_status_t s = check_attn(q, kv_cache, q_seq, q_pos, rows, n_seq, q_per_seq, H, Dqk, Dv, kv_dim, v_col0, out, &rs);
   if (s != DSA_OK) return s;
   REQUIRE(k >= 1 && ld_idx >= k, "need k >= 1 and ld_idx >= k");
-  const int rows = n_seq * q_per_seq;
   if (rows == 0) return ok(DSA_PATH_NONE);
   REQUIRE(idx != nullptr, "idx is NULL");
   s = check_paging(page_table, ld_pt, page_size, num_pages, 1);
   if (s != DSA_OK) return s;
-  dsa::AttnArgs a{q, {kv_cache, page_table, ld_pt, page_size, num_pages}, q_pos, n_seq, q_per_seq,
+  dsa::AttnArgs a{q, {kv_cache, page_table, ld_pt, page_size, num_pages}, rs, q_pos, rows,
                   idx, ld_idx, k, H, Dqk, Dv, kv_dim, v_col0, sm_scale, out, lse};
   hipStream_t st = (hipStream_t)stream;
   if (!mla_tuned(H, Dqk, Dv, kv_dim, v_col0, sm_scale)) {
@@ -153,37 +169,37 @@ int dsa_last_path(void) { return g_path; }
 
 dsa_status_t dsa_indexer_scores(const void* q, const float* w, const void* k_cache,
                                 const float* k_scale, const int32_t* page_table, int64_t ld_pt,
-                                int page_size, int num_pages, const int32_t* q_pos, int n_seq,
-                                int q_per_seq, int max_ctx, int Hi, int Di, dsa_dtype_t dtype,
-                                float* scores, int64_t ld_scores, void* stream) {
-  REQUIRE(n_seq >= 0 && q_per_seq >= 1, "need n_seq >= 0 and q_per_seq >= 1");
-  if (n_seq == 0) return ok(DSA_PATH_NONE);  // nothing to do; pointers may be NULL
+                                int page_size, int num_pages, const int32_t* q_seq, const int32_t* q_pos,
+                                int rows, int n_seq, int q_per_seq, int max_ctx, int Hi, int Di,
+                                dsa_dtype_t dtype, float* scores, int64_t ld_scores, void* stream) {
+  dsa::RowSeq rs;
+  dsa_status_t s = check_rows(q_seq, rows, n_seq, q_per_seq, &rs);
+  if (s != DSA_OK) return s;
+  if (rows == 0) return ok(DSA_PATH_NONE);  // nothing to do; pointers may be NULL
   REQUIRE(q && w && k_cache && q_pos && scores, "q, w, k_cache, q_pos and scores must be non-NULL");
-  REQUIRE((int64_t)n_seq * q_per_seq < ((int64_t)1 << 31), "too many rows");
   REQUIRE(Hi >= 1 && Di >= 1, "Hi and Di must be >= 1");
   REQUIRE(dtype == DSA_E4M3 || dtype == DSA_F32, "dtype must be DSA_E4M3 or DSA_F32");
   REQUIRE(!misaligned(q) && !misaligned(k_cache), "q and k_cache must be 16-byte aligned");
-  dsa_status_t s = check_paging(page_table, ld_pt, page_size, num_pages, max_ctx);
+  s = check_paging(page_table, ld_pt, page_size, num_pages, max_ctx);
   if (s != DSA_OK) return s;
   REQUIRE(ld_scores >= max_ctx, "ld_scores (%lld) must be >= max_ctx (%d)", (long long)ld_scores, max_ctx);
-  if (n_seq == 0) return ok(DSA_PATH_NONE);
   dsa::PagedCache kc{k_cache, page_table, ld_pt, page_size, num_pages};
   hipStream_t st = (hipStream_t)stream;
   if (Hi == 64 && Di == 128 && dtype == DSA_E4M3) {
     // the scan is built for 64-token pages; it takes the rows of a sequence two at a time (one
-    // at a time for an odd count), one block row per unit
-    const int64_t units = (int64_t)n_seq * q_per_seq / dsa::indexer_scan_rows_per_wave(q_per_seq);
+    // at a time for an odd count or per-row sequence ids), one block row per unit
+    const int64_t units = rows / dsa::indexer_scan_rows_per_wave(rs);
     if (page_size == 64 && units <= 65535) {
-      s = hip_status(dsa::launch_indexer_scan((const uint8_t*)q, w, kc, k_scale, q_pos, n_seq, q_per_seq,
-                                              max_ctx, scores, ld_scores, nullptr, st), "indexer_scan launch");
+      s = hip_status(dsa::launch_indexer_scan((const uint8_t*)q, w, kc, k_scale, rs, q_pos, rows, max_ctx, scores,
+                                              ld_scores, nullptr, st), "indexer_scan launch");
       return s == DSA_OK ? ok(DSA_PATH_INDEXER_SCAN_MFMA) : s;
     }
-    s = hip_status(dsa::launch_indexer_prefill((const uint8_t*)q, w, kc, k_scale, q_pos, n_seq, q_per_seq,
-                                               max_ctx, scores, ld_scores, st), "indexer_prefill launch");
+    s = hip_status(dsa::launch_indexer_prefill((const uint8_t*)q, w, kc, k_scale, rs, q_pos, rows, max_ctx, scores,
+                                               ld_scores, st), "indexer_prefill launch");
     return s == DSA_OK ? ok(DSA_PATH_INDEXER_PREFILL_MFMA) : s;
   }
-  s = hip_status(dsa::launch_indexer_generic(q, w, kc, k_scale, q_pos, n_seq, q_per_seq, max_ctx, Hi, Di,
-                                             dtype == DSA_F32, scores, ld_scores, st), "indexer_generic launch");
+  s = hip_status(dsa::launch_indexer_generic(q, w, kc, k_scale, rs, q_pos, rows, max_ctx, Hi, Di, dtype == DSA_F32,
+                                             scores, ld_scores, st), "indexer_generic launch");
   return s == DSA_OK ? ok(DSA_PATH_INDEXER_GENERIC) : s;
 }
 
@@ -218,15 +234,15 @@ size_t dsa_indexer_topk_workspace_size(int rows, int max_ctx, int k) {
 
 dsa_status_t dsa_indexer_topk(const void* q, const float* w, const void* k_cache, const float* k_scale,
                               const int32_t* page_table, int64_t ld_pt, int page_size, int num_pages,
-                              const int32_t* q_pos, int n_seq, int q_per_seq, int max_ctx, int Hi, int Di,
-                              dsa_dtype_t dtype, float* scores, int64_t ld_scores, int k, int32_t* idx,
-                              int64_t ld_idx, void* ws, size_t ws_bytes, void* stream) {
-  REQUIRE(n_seq >= 0 && q_per_seq >= 1 && k >= 1 && max_ctx >= 1,
-          "need n_seq >= 0, q_per_seq >= 1, k >= 1 and max_ctx >= 1");
-  if (n_seq == 0) return ok(DSA_PATH_NONE);  // nothing to do; pointers may be NULL
+                              const int32_t* q_seq, const int32_t* q_pos, int rows, int n_seq, int q_per_seq,
+                              int max_ctx, int Hi, int Di, dsa_dtype_t dtype, float* scores, int64_t ld_scores, int k,
+                              int32_t* idx, int64_t ld_idx, void* ws, size_t ws_bytes, void* stream) {
+  dsa::RowSeq rs;
+  dsa_status_t s = check_rows(q_seq, rows, n_seq, q_per_seq, &rs);
+  if (s != DSA_OK) return s;
+  REQUIRE(k >= 1 && max_ctx >= 1, "need k >= 1 and max_ctx >= 1");
+  if (rows == 0) return ok(DSA_PATH_NONE);  // nothing to do; pointers may be NULL
   REQUIRE(idx && ld_idx >= k, "idx must be non-NULL with ld_idx >= k");
-  REQUIRE((int64_t)n_seq * q_per_seq < ((int64_t)1 << 31), "too many rows");
-  const int rows = n_seq * q_per_seq;
   const size_t need = dsa_indexer_topk_workspace_size(rows, max_ctx, k);
   if (!ws || ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws ? ws_bytes : (size_t)0);
@@ -235,25 +251,25 @@ dsa_status_t dsa_indexer_topk(const void* q, const float* w, const void* k_cache
   uint8_t* topk_ws = (uint8_t*)(hist0 + (size_t)rows * (nchunks + (nchunks > 1 ? 1 : 0)) * dsa::kTopkDigit0Bins);
   const size_t topk_ws_bytes = (size_t)((uint8_t*)ws + ws_bytes - topk_ws);
   const bool fused = Hi == 64 && Di == 128 && dtype == DSA_E4M3 && page_size == 64 &&
-                     (int64_t)rows / dsa::indexer_scan_rows_per_wave(q_per_seq) <= 65535 &&
+                     (int64_t)rows / dsa::indexer_scan_rows_per_wave(rs) <= 65535 &&
                      (max_ctx <= dsa::topk_reg_max_ctx() ? k <= dsa::topk_reg_max_k()
                                                         : dsa::topk_staged_ok(max_ctx, k));
   if (!fused) {
     // the same two steps without the shared histogram
-    dsa_status_t s = dsa_indexer_scores(q, w, k_cache, k_scale, page_table, ld_pt, page_size, num_pages, q_pos,
-                                        n_seq, q_per_seq, max_ctx, Hi, Di, dtype, scores, ld_scores, stream);
+    s = dsa_indexer_scores(q, w, k_cache, k_scale, page_table, ld_pt, page_size, num_pages, q_seq, q_pos, rows, n_seq,
+                           q_per_seq, max_ctx, Hi, Di, dtype, scores, ld_scores, stream);
     if (s != DSA_OK) return s;
     return dsa_topk(scores, ld_scores, q_pos, rows, max_ctx, k, idx, ld_idx, topk_ws, topk_ws_bytes, stream);
   }
   REQUIRE(q && w && k_cache && q_pos && scores, "q, w, k_cache, q_pos and scores must be non-NULL");
   REQUIRE(!misaligned(q) && !misaligned(k_cache), "q and k_cache must be 16-byte aligned");
-  dsa_status_t s = check_paging(page_table, ld_pt, page_size, num_pages, max_ctx);
+  s = check_paging(page_table, ld_pt, page_size, num_pages, max_ctx);
   if (s != DSA_OK) return s;
   REQUIRE(ld_scores >= max_ctx, "ld_scores (%lld) must be >= max_ctx (%d)", (long long)ld_scores, max_ctx);
   dsa::PagedCache kc{k_cache, page_table, ld_pt, page_size, num_pages};
   hipStream_t st = (hipStream_t)stream;
-  s = hip_status(dsa::launch_indexer_scan((const uint8_t*)q, w, kc, k_scale, q_pos, n_seq, q_per_seq, max_ctx,
-                                          scores, ld_scores, hist0, st), "indexer_scan launch");
+  s = hip_status(dsa::launch_indexer_scan((const uint8_t*)q, w, kc, k_scale, rs, q_pos, rows, max_ctx, scores,
+                                          ld_scores, hist0, st), "indexer_scan launch");
   if (s != DSA_OK) return s;
   int path = DSA_PATH_NONE;
   s = hip_status(dsa::launch_topk(scores, ld_scores, q_pos, rows, max_ctx, k, idx, ld_idx, topk_ws, topk_ws_bytes,
@@ -266,23 +282,22 @@ size_t dsa_sparse_mla_workspace_size(int rows, int H, int Dv, int k) {
   return dsa::mla_mfma_ws_bytes(rows, dsa::mla_mfma_pick_splits(rows, k));
 }
 
-dsa_status_t dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* kv_cache,
-                                   const int32_t* page_table, int64_t ld_pt, int page_size,
-                                   int num_pages, const int32_t* q_pos, int n_seq, int q_per_seq,
-                                   const int32_t* idx, int64_t ld_idx, int k, int H, int Dqk,
-                                   int Dv, int kv_dim, int v_col0, float sm_scale, uint16_t* out,
-                                   float* lse, void* ws, size_t ws_bytes, void* stream) {
-  return run_sparse(true, q, kv_cache, page_table, ld_pt, page_size, num_pages, q_pos, n_seq, q_per_seq,
+dsa_status_t dsa_sparse_mla_decode(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
+                                   int64_t ld_pt, int page_size, int num_pages, const int32_t* q_seq,
+                                   const int32_t* q_pos, int rows, int n_seq, int q_per_seq, const int32_t* idx,
+                                   int64_t ld_idx, int k, int H, int Dqk, int Dv, int kv_dim, int v_col0,
+                                   float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  return run_sparse(true, q, kv_cache, page_table, ld_pt, page_size, num_pages, q_seq, q_pos, rows, n_seq, q_per_seq,
                     idx, ld_idx, k, H, Dqk, Dv, kv_dim, v_col0, sm_scale, out, lse, ws, ws_bytes, stream);
 }
 
 dsa_status_t dsa_sparse_mla_decode_noalloc(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
-                                           int64_t ld_pt, int page_size, int num_pages, const int32_t* q_pos,
-                                           int n_seq, int q_per_seq, const int32_t* idx, int64_t ld_idx, int k, int H,
-                                           int Dqk, int Dv, int kv_dim, int v_col0, float sm_scale, uint16_t* out,
-                                           float* lse, void* stream) {
-  const int64_t rows64 = (int64_t)n_seq * q_per_seq;
-  const int rows = (n_seq < 0 || q_per_seq < 1 || rows64 > INT_MAX) ? -1 : (int)rows64;
+                                           int64_t ld_pt, int page_size, int num_pages, const int32_t* q_seq,
+                                           const int32_t* q_pos, int rows, int n_seq, int q_per_seq,
+                                           const int32_t* idx, int64_t ld_idx, int k, int H, int Dqk, int Dv,
+                                           int kv_dim, int v_col0, float sm_scale, uint16_t* out, float* lse,
+                                           void* stream) {
   const size_t need = dsa_sparse_mla_workspace_size(rows, H, Dv, k);
   if (need > kNoallocScratchBytes)
     return fail(DSA_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the no-allocation entry point holds %zu",
@@ -292,18 +307,18 @@ dsa_status_t dsa_sparse_mla_decode_noalloc(const uint16_t* q, const uint16_t* kv
     dsa_status_t s = scratch_on_current_device(&ws);
     if (s != DSA_OK) return s;
   }
-  return run_sparse(true, q, kv_cache, page_table, ld_pt, page_size, num_pages, q_pos, n_seq, q_per_seq, idx, ld_idx,
-                    k, H, Dqk, Dv, kv_dim, v_col0, sm_scale, out, lse, ws, need > 0 ? kNoallocScratchBytes : 0,
-                    stream);
+  return run_sparse(true, q, kv_cache, page_table, ld_pt, page_size, num_pages, q_seq, q_pos, rows, n_seq, q_per_seq,
+                    idx, ld_idx, k, H, Dqk, Dv, kv_dim, v_col0, sm_scale, out, lse, ws,
+                    need > 0 ? kNoallocScratchBytes : 0, stream);
 }
 
-dsa_status_t dsa_sparse_mla_prefill(const uint16_t* q, const uint16_t* kv_cache,
-                                    const int32_t* page_table, int64_t ld_pt, int page_size,
-                                    int num_pages, const int32_t* q_pos, int n_seq, int q_per_seq,
-                                    const int32_t* idx, int64_t ld_idx, int k, int H, int Dqk,
-                                    int Dv, int kv_dim, int v_col0, float sm_scale, uint16_t* out,
-                                    float* lse, void* ws, size_t ws_bytes, void* stream) {
-  return run_sparse(false, q, kv_cache, page_table, ld_pt, page_size, num_pages, q_pos, n_seq, q_per_seq,
+dsa_status_t dsa_sparse_mla_prefill(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
+                                    int64_t ld_pt, int page_size, int num_pages, const int32_t* q_seq,
+                                    const int32_t* q_pos, int rows, int n_seq, int q_per_seq, const int32_t* idx,
+                                    int64_t ld_idx, int k, int H, int Dqk, int Dv, int kv_dim, int v_col0,
+                                    float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  return run_sparse(false, q, kv_cache, page_table, ld_pt, page_size, num_pages, q_seq, q_pos, rows, n_seq, q_per_seq,
                     idx, ld_idx, k, H, Dqk, Dv, kv_dim, v_col0, sm_scale, out, lse, ws, ws_bytes, stream);
 }
 
@@ -312,20 +327,19 @@ size_t dsa_dense_mla_workspace_size(int rows, int H, int Dv, int max_ctx) {
   return 0;
 }
 
-dsa_status_t dsa_dense_mla_prefill(const uint16_t* q, const uint16_t* kv_cache,
-                                   const int32_t* page_table, int64_t ld_pt, int page_size,
-                                   int num_pages, const int32_t* q_pos, int n_seq, int q_per_seq,
-                                   int max_ctx, int H, int Dqk, int Dv, int kv_dim, int v_col0,
-                                   float sm_scale, uint16_t* out, float* lse, void* ws,
-                                   size_t ws_bytes, void* stream) {
+dsa_status_t dsa_dense_mla_prefill(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
+                                   int64_t ld_pt, int page_size, int num_pages, const int32_t* q_seq,
+                                   const int32_t* q_pos, int rows, int n_seq, int q_per_seq, int max_ctx, int H,
+                                   int Dqk, int Dv, int kv_dim, int v_col0, float sm_scale, uint16_t* out, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream) {
   (void)ws; (void)ws_bytes;
-  dsa_status_t s = check_attn(q, kv_cache, q_pos, n_seq, q_per_seq, H, Dqk, Dv, kv_dim, v_col0, out);
+  dsa::RowSeq rs;
+  dsa_status_t s = check_attn(q, kv_cache, q_seq, q_pos, rows, n_seq, q_per_seq, H, Dqk, Dv, kv_dim, v_col0, out, &rs);
   if (s != DSA_OK) return s;
-  const int rows = n_seq * q_per_seq;
   if (rows == 0) return ok(DSA_PATH_NONE);
   s = check_paging(page_table, ld_pt, page_size, num_pages, max_ctx);
   if (s != DSA_OK) return s;
-  dsa::AttnArgs a{q, {kv_cache, page_table, ld_pt, page_size, num_pages}, q_pos, n_seq, q_per_seq,
+  dsa::AttnArgs a{q, {kv_cache, page_table, ld_pt, page_size, num_pages}, rs, q_pos, rows,
                   nullptr, 0, max_ctx, H, Dqk, Dv, kv_dim, v_col0, sm_scale, out, lse};
   hipStream_t st = (hipStream_t)stream;
   if (!mla_tuned(H, Dqk, Dv, kv_dim, v_col0, sm_scale)) {

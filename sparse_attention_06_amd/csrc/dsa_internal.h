@@ -57,11 +57,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Physical row of position p of sequence s, or -1 if p lies outside the page table's
+// Which sequence (page-table row) a query row belongs to: with q_seq NULL the rows come in
+// groups of q_per_seq consecutive rows per sequence, otherwise row r belongs to sequence q_seq[r].
+// A sequence id outside [0, n_seq) has no page-table row: -1, whose positions resolve to no
+// physical row.
+struct RowSeq {
+  const int32_t* q_seq;
+  int q_per_seq, n_seq;
+  __device__ __forceinline__ int of(int r) const {
+    const int s = q_seq ? q_seq[r] : r / q_per_seq;
+    return (s >= 0 && s < n_seq) ? s : -1;
+  }
+};
+
+// Physical row of position p of sequence s, or -1 if s is -1, p lies outside the page table's
 // [0, ld_pt * page_size) or the page id outside [0, num_pages).
 __device__ __forceinline__ int64_t phys_row(const int32_t* __restrict__ page_table, int64_t ld_pt,
                                             int page_size, int num_pages, int s, int p) {
-  if (p < 0 || p / page_size >= ld_pt) return -1;
+  if (s < 0 || p < 0 || p / page_size >= ld_pt) return -1;
   int32_t page = page_table[(int64_t)s * ld_pt + p / page_size];
   if (page < 0 || page >= num_pages) return -1;
   return (int64_t)page * page_size + p % page_size;
@@ -87,20 +100,20 @@ struct PagedCache {
 };
 
 hipError_t launch_indexer_generic(const void* q, const float* w, PagedCache kc, const float* k_scale,
-                                  const int32_t* q_pos, int n_seq, int q_per_seq, int max_ctx, int Hi,
+                                  RowSeq rs, const int32_t* q_pos, int rows, int max_ctx, int Hi,
                                   int Di, int is_f32, float* scores, int64_t ld_scores,
                                   hipStream_t stream);
-int indexer_scan_rows_per_wave(int q_per_seq);
+// query rows per scan unit: 2 when the uniform layout pairs rows of one sequence, else 1
+int indexer_scan_rows_per_wave(RowSeq rs);
 // hist0 (optional, zero on entry): per row and kTopkChunkKeys-position chunk (row-major), a
 // kTopkDigit0Bins-bin count of the scores at positions 0..q_pos[r] by their key's first digit,
 // added with device-scope atomics
 hipError_t launch_indexer_scan(const uint8_t* q, const float* w, PagedCache kc, const float* k_scale,
-                               const int32_t* q_pos, int n_seq, int q_per_seq, int max_ctx,
+                               RowSeq rs, const int32_t* q_pos, int rows, int max_ctx,
                                float* scores, int64_t ld_scores, uint32_t* hist0, hipStream_t stream);
 hipError_t launch_indexer_prefill(const uint8_t* q, const float* w, PagedCache kc,
-                                  const float* k_scale, const int32_t* q_pos, int n_seq,
-                                  int q_per_seq, int max_ctx, float* scores, int64_t ld_scores,
-                                  hipStream_t stream);
+                                  const float* k_scale, RowSeq rs, const int32_t* q_pos, int rows,
+                                  int max_ctx, float* scores, int64_t ld_scores, hipStream_t stream);
 
 // hist0 (optional; rows of at most topk_reg_max_ctx() positions with k <= topk_reg_max_k(), or
 // the two-stage path): per row and chunk, the first-digit histogram of the valid scores, as
@@ -117,8 +130,9 @@ size_t topk_staged_ws_bytes(int rows, int max_ctx, int k);
 struct AttnArgs {
   const uint16_t* q;
   PagedCache kv;
+  RowSeq rs;
   const int32_t* q_pos;
-  int n_seq, q_per_seq;
+  int rows;
   const int32_t* idx;  // NULL => dense causal set {0..q_pos}
   int64_t ld_idx;
   int k;               // entries per idx row (dense: max_ctx)

@@ -35,7 +35,7 @@ __device__ __forceinline__ float load_elem(const void* base, int64_t i, int is_f
 
 __global__ void __launch_bounds__(256) indexer_generic_kernel(
     const void* __restrict__ q, const float* __restrict__ w, PagedCache kc,
-    const float* __restrict__ k_scale, const int32_t* __restrict__ q_pos, int q_per_seq,
+    const float* __restrict__ k_scale, RowSeq rs, const int32_t* __restrict__ q_pos,
     int max_ctx, int Hi, int Di, int is_f32, float* __restrict__ scores, int64_t ld_scores) {
   const int r = blockIdx.y;
   const int j = blockIdx.x * 256 + threadIdx.x;
@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(256) indexer_generic_kernel(
   const int t = q_pos[r];
   float* out = scores + (int64_t)r * ld_scores + j;
   if (j > t) { *out = -INFINITY; return; }
-  const int64_t row = phys_row(kc.page_table, kc.ld_pt, kc.page_size, kc.num_pages, r / q_per_seq, j);
+  const int64_t row = phys_row(kc.page_table, kc.ld_pt, kc.page_size, kc.num_pages, rs.of(r), j);
   if (row < 0) { *out = -INFINITY; return; }
   float acc = 0.f;
   for (int h = 0; h < Hi; ++h) {
@@ -56,13 +56,12 @@ __global__ void __launch_bounds__(256) indexer_generic_kernel(
 }
 
 hipError_t launch_indexer_generic(const void* q, const float* w, PagedCache kc, const float* k_scale,
-                                  const int32_t* q_pos, int n_seq, int q_per_seq, int max_ctx, int Hi,
+                                  RowSeq rs, const int32_t* q_pos, int rows, int max_ctx, int Hi,
                                   int Di, int is_f32, float* scores, int64_t ld_scores,
                                   hipStream_t stream) {
-  const int rows = n_seq * q_per_seq;
   dim3 grid((max_ctx + 255) / 256, rows);
-  hipLaunchKernelGGL(indexer_generic_kernel, grid, dim3(256), 0, stream, q, w, kc, k_scale, q_pos,
-                     q_per_seq, max_ctx, Hi, Di, is_f32, scores, ld_scores);
+  hipLaunchKernelGGL(indexer_generic_kernel, grid, dim3(256), 0, stream, q, w, kc, k_scale, rs, q_pos,
+                     max_ctx, Hi, Di, is_f32, scores, ld_scores);
   return hipGetLastError();
 }
 
@@ -436,7 +435,7 @@ __device__ __forceinline__ void scan_range(const uint8_t* __restrict__ q, const 
   c.vpage = -1;
   {
     const int pg = jbeg / kScanPage + lane;
-    if (lane < np && pg < kc.ld_pt) c.vpage = kc.page_table[(int64_t)seq * kc.ld_pt + pg];
+    if (seq >= 0 && lane < np && pg < kc.ld_pt) c.vpage = kc.page_table[(int64_t)seq * kc.ld_pt + pg];
     if (c.vpage >= kc.num_pages) c.vpage = -1;
   }
   QueryOps<NQ> o;
@@ -500,7 +499,7 @@ __device__ __forceinline__ void flush_hist(lds32* hist, uint32_t* __restrict__ h
 template <int NQ, bool kHist>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) indexer_scan_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ w, PagedCache kc,
-    const float* __restrict__ k_scale, const int32_t* __restrict__ q_pos, int q_per_seq, int keys_per_wave,
+    const float* __restrict__ k_scale, RowSeq rs, const int32_t* __restrict__ q_pos, int keys_per_wave,
     int max_ctx, float* __restrict__ scores, int64_t ld_scores, uint32_t* __restrict__ hist0) {
   // with kHist, the rows' first-digit histograms (2 x 16 bits per word) follow the rings
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kScanLdsBytes + (kHist ? NQ * kTopkDigit0Bins * 2 : 0)];
@@ -511,9 +510,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     __syncthreads();
   }
   // this block's NQ query rows: unit * NQ .. + NQ - 1, all of one sequence (decode: the request's
-  // rows; prefill: two consecutive rows of the block)
+  // rows; prefill: two consecutive rows of the block; one row per unit with per-row sequence ids)
   const int unit = blockIdx.y;
-  const int seq = unit * NQ / q_per_seq;
+  const int seq = rs.of(unit * NQ);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int tmax = -1;
 #pragma unroll
@@ -527,45 +526,48 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
                          blockIdx.x * kScanWaves * keys_per_wave / kTopkChunkKeys);
 }
 
-// Prefill tiles: each wave owns 2 consecutive rows of one sequence and scans their causal
-// prefix; the 4 waves of a block walk the same keys in step, so key reads hit the caches.
+// Prefill tiles: each wave owns 2 consecutive rows and scans their causal prefix, the two
+// together when they belong to one sequence, else one after the other; the 4 waves of a block walk
+// the same keys in step, so key reads hit the caches.
 __global__ void __launch_bounds__(256) indexer_prefill_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ w, PagedCache kc,
-    const float* __restrict__ k_scale, const int32_t* __restrict__ q_pos, int q_per_seq,
+    const float* __restrict__ k_scale, RowSeq rs, const int32_t* __restrict__ q_pos,
     int rows, int max_ctx, float* __restrict__ scores, int64_t ld_scores) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // heavy blocks first: in a causal chunk the last rows have the longest prefixes
   const int block = gridDim.x - 1 - blockIdx.x;
   const int row0 = block * 8 + 2 * wave;
-  if (row0 >= rows) return;
-  const int seq = row0 / q_per_seq;
-  const int nvalid = (row0 + 1 < rows && (row0 + 1) / q_per_seq == seq) ? 2 : 1;
-  QueryOps<2> o;
-  load_query_ops<2>(o, q, w, q_pos, row0, nvalid, lane);
-  const int jend = min(max(o.tpos[0], o.tpos[1]) + 1, max_ctx);  // never past ld_scores
-  if (jend <= 0) return;
-  KeyTile cur, nxt;
-  int jb = 0;
-  fetch_key_tile(cur, kc, k_scale, seq, jb, jend, lane);
-  for (; jb < jend; jb += 16) {
-    if (jb + 16 < jend) fetch_key_tile(nxt, kc, k_scale, seq, jb + 16, jend, lane);
-    score_key_tile<2>(o, cur, scores, ld_scores, jend, lane);
-    cur = nxt;
+  const int row_end = min(row0 + 2, rows);
+  for (int r = row0; r < row_end;) {
+    const int seq = rs.of(r);
+    const int nvalid = (r + 1 < row_end && rs.of(r + 1) == seq) ? 2 : 1;
+    QueryOps<2> o;
+    load_query_ops<2>(o, q, w, q_pos, r, nvalid, lane);
+    const int jend = min(max(o.tpos[0], o.tpos[1]) + 1, max_ctx);  // never past ld_scores
+    KeyTile cur, nxt;
+    int jb = 0;
+    if (jend > 0) fetch_key_tile(cur, kc, k_scale, seq, jb, jend, lane);
+    for (; jb < jend; jb += 16) {
+      if (jb + 16 < jend) fetch_key_tile(nxt, kc, k_scale, seq, jb + 16, jend, lane);
+      score_key_tile<2>(o, cur, scores, ld_scores, jend, lane);
+      cur = nxt;
+    }
+    r += nvalid;
   }
 }
 
 static_assert(kTopkChunkKeys % (kScanWaves * 64 * kScanPage) == 0, "a workgroup range never straddles a chunk");
 static_assert(kScanWaves * 64 * kScanPage < 65536, "a workgroup's count per bin fits the 16-bit LDS counters");
 
-int indexer_scan_rows_per_wave(int q_per_seq) { return q_per_seq % 2 == 0 ? 2 : 1; }
+int indexer_scan_rows_per_wave(RowSeq rs) { return (!rs.q_seq && rs.q_per_seq % 2 == 0) ? 2 : 1; }
 
 hipError_t launch_indexer_scan(const uint8_t* q, const float* w, PagedCache kc, const float* k_scale,
-                               const int32_t* q_pos, int n_seq, int q_per_seq, int max_ctx,
+                               RowSeq rs, const int32_t* q_pos, int rows, int max_ctx,
                                float* scores, int64_t ld_scores, uint32_t* hist0, hipStream_t stream) {
   // units of NQ query rows of one sequence; about 2048 waves (8 per CU) per launch for a decode
   // batch, each a whole number of pages (at most 64 of them)
-  const int nq = indexer_scan_rows_per_wave(q_per_seq);
-  const int units = n_seq * q_per_seq / nq;
+  const int nq = indexer_scan_rows_per_wave(rs);
+  const int units = rows / nq;
   const int64_t total = (int64_t)units * max_ctx;
   int kpw = (int)((total / 2048 + kScanPage - 1) / kScanPage * kScanPage);
   kpw = kpw < kScanPage ? kScanPage : (kpw > 64 * kScanPage ? 64 * kScanPage : kpw);
@@ -580,23 +582,21 @@ hipError_t launch_indexer_scan(const uint8_t* q, const float* w, PagedCache kc, 
   dim3 grid((max_ctx + per_block - 1) / per_block, units);
   const dim3 block(64 * kScanWaves);
   if (nq == 1 && !hist0)
-    hipLaunchKernelGGL((indexer_scan_kernel<1, false>), grid, block, 0, stream, q, w, kc, k_scale, q_pos, q_per_seq, kpw, max_ctx, scores, ld_scores, hist0);
+    hipLaunchKernelGGL((indexer_scan_kernel<1, false>), grid, block, 0, stream, q, w, kc, k_scale, rs, q_pos, kpw, max_ctx, scores, ld_scores, hist0);
   else if (nq == 1)
-    hipLaunchKernelGGL((indexer_scan_kernel<1, true>), grid, block, 0, stream, q, w, kc, k_scale, q_pos, q_per_seq, kpw, max_ctx, scores, ld_scores, hist0);
+    hipLaunchKernelGGL((indexer_scan_kernel<1, true>), grid, block, 0, stream, q, w, kc, k_scale, rs, q_pos, kpw, max_ctx, scores, ld_scores, hist0);
   else if (!hist0)
-    hipLaunchKernelGGL((indexer_scan_kernel<2, false>), grid, block, 0, stream, q, w, kc, k_scale, q_pos, q_per_seq, kpw, max_ctx, scores, ld_scores, hist0);
+    hipLaunchKernelGGL((indexer_scan_kernel<2, false>), grid, block, 0, stream, q, w, kc, k_scale, rs, q_pos, kpw, max_ctx, scores, ld_scores, hist0);
   else
-    hipLaunchKernelGGL((indexer_scan_kernel<2, true>), grid, block, 0, stream, q, w, kc, k_scale, q_pos, q_per_seq, kpw, max_ctx, scores, ld_scores, hist0);
+    hipLaunchKernelGGL((indexer_scan_kernel<2, true>), grid, block, 0, stream, q, w, kc, k_scale, rs, q_pos, kpw, max_ctx, scores, ld_scores, hist0);
   return hipGetLastError();
 }
 
 hipError_t launch_indexer_prefill(const uint8_t* q, const float* w, PagedCache kc,
-                                  const float* k_scale, const int32_t* q_pos, int n_seq,
-                                  int q_per_seq, int max_ctx, float* scores, int64_t ld_scores,
-                                  hipStream_t stream) {
-  const int rows = n_seq * q_per_seq;
+                                  const float* k_scale, RowSeq rs, const int32_t* q_pos, int rows,
+                                  int max_ctx, float* scores, int64_t ld_scores, hipStream_t stream) {
   dim3 grid((rows + 7) / 8);
-  hipLaunchKernelGGL(indexer_prefill_kernel, grid, dim3(256), 0, stream, q, w, kc, k_scale, q_pos, q_per_seq, rows, max_ctx, scores, ld_scores);
+  hipLaunchKernelGGL(indexer_prefill_kernel, grid, dim3(256), 0, stream, q, w, kc, k_scale, rs, q_pos, rows, max_ctx, scores, ld_scores);
   return hipGetLastError();
 }
 

@@ -49,10 +49,9 @@ __device__ __forceinline__ bool list_needs_dedupe(const int* irow, int t, int e0
 __global__ void __launch_bounds__(256) mla_generic_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int rows = a.n_seq * a.q_per_seq;
-  if (gw >= rows * a.H) return;
+  if (gw >= a.rows * a.H) return;
   const int r = gw / a.H, h = gw % a.H;
-  const int t = a.q_pos[r], seq = r / a.q_per_seq;
+  const int t = a.q_pos[r], seq = a.rs.of(r);
   const uint16_t* qh = a.q + ((int64_t)r * a.H + h) * a.Dqk;
   float qv[16], o[8];
 #pragma unroll
@@ -97,7 +96,7 @@ __global__ void __launch_bounds__(256) mla_generic_kernel(AttnArgs a) {
 }
 
 hipError_t launch_mla_generic(const AttnArgs& a, hipStream_t stream) {
-  const int waves = a.n_seq * a.q_per_seq * a.H;
+  const int waves = a.rows * a.H;
   hipLaunchKernelGGL(mla_generic_kernel, dim3((waves + 3) / 4), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -359,7 +358,7 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
   const int unit = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (unit >= units) return;
   const int r = unit / splits, sp = unit % splits;
-  const int seq = r / a.q_per_seq;
+  const int seq = a.rs.of(r);  // -1: no page-table row, every entry resolves to no row
   const int t = a.q_pos[r];
   const int n_entries = a.idx ? a.k : max(0, min(t + 1, a.k));  // dense: a.k = max_ctx
   const int e_begin = sp * entries_per_split;
@@ -436,7 +435,7 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int j = jj[u];
-        const bool vis = j >= 0 && j <= t && j / a.kv.page_size < a.kv.ld_pt;
+        const bool vis = seq >= 0 && j >= 0 && j <= t && j / a.kv.page_size < a.kv.ld_pt;
         pg[u] = vis ? a.kv.page_table[(int64_t)seq * a.kv.ld_pt + j / a.kv.page_size] : -1;
       }
 #pragma unroll
@@ -963,7 +962,7 @@ int mla_mfma_pick_splits(int rows, int k) {
 }
 
 hipError_t launch_mla_mfma(const AttnArgs& a, int splits, void* ws, hipStream_t stream) {
-  const int rows = a.n_seq * a.q_per_seq;
+  const int rows = a.rows;
   const int units = rows * (splits > 1 ? splits : 1);
   const int per_xcd = (units + 7) / 8;
   const int blocks = 8 * per_xcd;

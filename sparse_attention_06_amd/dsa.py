@@ -64,7 +64,7 @@ def load():
     lib.dsa_last_path.restype = i32
     lib.dsa_last_path.argtypes = []
     lib.dsa_indexer_scores.restype = i32
-    lib.dsa_indexer_scores.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, vp, i32, i32, i32, i32, i32, i32,
+    lib.dsa_indexer_scores.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                        vp, i64, vp]
     lib.dsa_topk_workspace_size.restype = sz
     lib.dsa_topk_workspace_size.argtypes = [i32, i32, i32]
@@ -73,11 +73,12 @@ def load():
     lib.dsa_indexer_topk_workspace_size.restype = sz
     lib.dsa_indexer_topk_workspace_size.argtypes = [i32, i32, i32]
     lib.dsa_indexer_topk.restype = i32
-    lib.dsa_indexer_topk.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, vp, i32, i32, i32, i32, i32, i32,
+    lib.dsa_indexer_topk.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                      vp, i64, i32, vp, i64, vp, sz, vp]
     lib.dsa_sparse_mla_workspace_size.restype = sz
     lib.dsa_sparse_mla_workspace_size.argtypes = [i32, i32, i32, i32]
-    attn = [vp, vp, vp, i64, i32, i32, vp, i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, sz, vp]
+    attn = [vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp,
+            sz, vp]
     lib.dsa_sparse_mla_decode.restype = i32
     lib.dsa_sparse_mla_decode.argtypes = attn
     lib.dsa_sparse_mla_prefill.restype = i32
@@ -87,8 +88,8 @@ def load():
     lib.dsa_dense_mla_workspace_size.restype = sz
     lib.dsa_dense_mla_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.dsa_dense_mla_prefill.restype = i32
-    lib.dsa_dense_mla_prefill.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, i32, i32, i32, i32, i32, i32, i32,
-                                          f32, vp, vp, vp, sz, vp]
+    lib.dsa_dense_mla_prefill.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                          i32, f32, vp, vp, vp, sz, vp]
     lib.dsa_expanded_mha_workspace_size.restype = sz
     lib.dsa_expanded_mha_workspace_size.argtypes = [i32, i32, i32]
     lib.dsa_expanded_mha_prefill.restype = i32
@@ -134,8 +135,23 @@ def _need(t, name, dtype, dim=None):
         raise ValueError(f"{name} must have {dim} dims (got {t.dim()})")
 
 
+def _check_rows(rows, q_pos, n_seq, q_per_seq, q_seq):
+    """The query-row descriptor: rows = n_seq * q_per_seq in groups per sequence (q_seq None), or
+    row r of sequence q_seq[r] (q_per_seq must then be 1)."""
+    _need(q_pos, "q_pos", torch.int32, 1)
+    if q_pos.numel() != rows:
+        raise ValueError(f"q_pos has {q_pos.numel()} entries for {rows} rows")
+    if q_seq is None:
+        if rows != n_seq * q_per_seq:
+            raise ValueError("rows must equal n_seq * q_per_seq (or pass q_seq)")
+    else:
+        _need(q_seq, "q_seq", torch.int32, 1)
+        if q_seq.numel() != rows or q_per_seq != 1:
+            raise ValueError("q_seq needs one entry per row and q_per_seq = 1")
+
+
 def indexer_scores(q, w, k_cache, k_scale, page_table, q_pos, n_seq, q_per_seq, max_ctx, scores=None,
-                   stream=None):
+                   stream=None, q_seq=None):
     """q [rows, Hi, Di] uint8 (E4M3 bytes) or float32; w [rows, Hi] f32; k_cache [P, page, Di];
     k_scale [P, page] f32 or None; page_table [n_seq, ld_pt] i32; q_pos [rows] i32.
     Returns scores [rows, max_ctx] f32 (entries j > q_pos[r] are -inf or unspecified)."""
@@ -144,18 +160,16 @@ def indexer_scores(q, w, k_cache, k_scale, page_table, q_pos, n_seq, q_per_seq, 
     _need(k_cache, "k_cache", q.dtype, 3)
     _need(w, "w", torch.float32, 2)
     _need(page_table, "page_table", torch.int32, 2)
-    _need(q_pos, "q_pos", torch.int32, 1)
     if k_scale is not None:
         _need(k_scale, "k_scale", torch.float32)
     rows, Hi, Di = q.shape
-    if rows != n_seq * q_per_seq or q_pos.numel() != rows:
-        raise ValueError("rows must equal n_seq * q_per_seq")
+    _check_rows(rows, q_pos, n_seq, q_per_seq, q_seq)
     if scores is None:
         scores = torch.empty(rows, max_ctx, dtype=torch.float32, device=q.device)
     _need(scores, "scores", torch.float32, 2)
     st = load().dsa_indexer_scores(_p(q), _p(w), _p(k_cache), _p(k_scale), _p(page_table), page_table.shape[1],
-                                   k_cache.shape[1], k_cache.shape[0], _p(q_pos), n_seq, q_per_seq, max_ctx, Hi, Di,
-                                   dtype, _p(scores), scores.shape[1], _stream(stream))
+                                   k_cache.shape[1], k_cache.shape[0], _p(q_seq), _p(q_pos), rows, n_seq, q_per_seq,
+                                   max_ctx, Hi, Di, dtype, _p(scores), scores.shape[1], _stream(stream))
     _check("dsa_indexer_scores", st)
     return scores
 
@@ -187,7 +201,7 @@ def indexer_topk_workspace_size(rows, max_ctx, k) -> int:
 
 
 def indexer_topk(q, w, k_cache, k_scale, page_table, q_pos, n_seq, q_per_seq, max_ctx, k, scores=None, idx=None,
-                 ws=None, stream=None):
+                 ws=None, stream=None, q_seq=None):
     """indexer_scores then topk in one call (the top-k's first radix pass counted during the scan).
     `ws` (uint8, at least indexer_topk_workspace_size bytes) must be zero-filled before its first
     use and is left so by every successful call; a zeroed one is allocated here when not given.
@@ -197,12 +211,10 @@ def indexer_topk(q, w, k_cache, k_scale, page_table, q_pos, n_seq, q_per_seq, ma
     _need(k_cache, "k_cache", q.dtype, 3)
     _need(w, "w", torch.float32, 2)
     _need(page_table, "page_table", torch.int32, 2)
-    _need(q_pos, "q_pos", torch.int32, 1)
     if k_scale is not None:
         _need(k_scale, "k_scale", torch.float32)
     rows, Hi, Di = q.shape
-    if rows != n_seq * q_per_seq or q_pos.numel() != rows:
-        raise ValueError("rows must equal n_seq * q_per_seq")
+    _check_rows(rows, q_pos, n_seq, q_per_seq, q_seq)
     if scores is None:
         scores = torch.empty(rows, max_ctx, dtype=torch.float32, device=q.device)
     _need(scores, "scores", torch.float32, 2)
@@ -212,8 +224,8 @@ def indexer_topk(q, w, k_cache, k_scale, page_table, q_pos, n_seq, q_per_seq, ma
     if ws is None and rows > 0:
         ws = torch.zeros(indexer_topk_workspace_size(rows, max_ctx, k), dtype=torch.uint8, device=q.device)
     st = load().dsa_indexer_topk(_p(q), _p(w), _p(k_cache), _p(k_scale), _p(page_table), page_table.shape[1],
-                                 k_cache.shape[1], k_cache.shape[0], _p(q_pos), n_seq, q_per_seq, max_ctx, Hi, Di,
-                                 dtype, _p(scores), scores.shape[1], k, _p(idx), idx.shape[1], _p(ws),
+                                 k_cache.shape[1], k_cache.shape[0], _p(q_seq), _p(q_pos), rows, n_seq, q_per_seq,
+                                 max_ctx, Hi, Di, dtype, _p(scores), scores.shape[1], k, _p(idx), idx.shape[1], _p(ws),
                                  0 if ws is None else ws.numel(), _stream(stream))
     _check("dsa_indexer_topk", st)
     return scores, idx
@@ -242,10 +254,11 @@ def _attn_common(q, kv_cache, page_table, q_pos, out, lse, Dv):
 
 
 def _sparse(fn_name, q, kv_cache, page_table, q_pos, n_seq, q_per_seq, idx, Dqk, Dv, v_col0, sm_scale,
-            out=None, lse=None, ws=None, stream=None):
+            out=None, lse=None, ws=None, stream=None, q_seq=None):
     out = _attn_common(q, kv_cache, page_table, q_pos, out, lse, Dv)
     _need(idx, "idx", torch.int32, 2)
     rows, H, _ = q.shape
+    _check_rows(rows, q_pos, n_seq, q_per_seq, q_seq)
     k = idx.shape[1]
     lib = load()
     need = lib.dsa_sparse_mla_workspace_size(rows, H, Dv, k) if fn_name == "dsa_sparse_mla_decode" else 0
@@ -253,7 +266,7 @@ def _sparse(fn_name, q, kv_cache, page_table, q_pos, n_seq, q_per_seq, idx, Dqk,
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     fn = getattr(lib, fn_name)
     st = fn(_p(q), _p(kv_cache), _p(page_table), page_table.shape[1], kv_cache.shape[1], kv_cache.shape[0],
-            _p(q_pos), n_seq, q_per_seq, _p(idx), idx.shape[1], k, H, Dqk, Dv, kv_cache.shape[2], v_col0,
+            _p(q_seq), _p(q_pos), rows, n_seq, q_per_seq, _p(idx), idx.shape[1], k, H, Dqk, Dv, kv_cache.shape[2], v_col0,
             float(sm_scale), _p(out), _p(lse), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
             _stream(stream))
     _check(fn_name, st)
@@ -269,7 +282,7 @@ def sparse_mla_prefill(*args, **kw):
 
 
 def sparse_mla_decode_noalloc(q, kv_cache, page_table, q_pos, n_seq, q_per_seq, idx, Dqk, Dv, v_col0, sm_scale,
-                              out, lse=None, stream=None):
+                              out, lse=None, stream=None, q_seq=None):
     """dsa_sparse_mla_decode without a workspace argument: the library's own device scratch is
     used, and nothing is allocated here either (out, and lse if wanted, are the caller's)."""
     if out is None:
@@ -277,20 +290,23 @@ def sparse_mla_decode_noalloc(q, kv_cache, page_table, q_pos, n_seq, q_per_seq, 
     _attn_common(q, kv_cache, page_table, q_pos, out, lse, Dv)
     _need(idx, "idx", torch.int32, 2)
     rows, H, _ = q.shape
+    _check_rows(rows, q_pos, n_seq, q_per_seq, q_seq)
     st = load().dsa_sparse_mla_decode_noalloc(
-        _p(q), _p(kv_cache), _p(page_table), page_table.shape[1], kv_cache.shape[1], kv_cache.shape[0], _p(q_pos),
-        n_seq, q_per_seq, _p(idx), idx.shape[1], idx.shape[1], H, Dqk, Dv, kv_cache.shape[2], v_col0,
+        _p(q), _p(kv_cache), _p(page_table), page_table.shape[1], kv_cache.shape[1], kv_cache.shape[0], _p(q_seq),
+        _p(q_pos), rows, n_seq, q_per_seq, _p(idx), idx.shape[1], idx.shape[1], H, Dqk, Dv, kv_cache.shape[2], v_col0,
         float(sm_scale), _p(out), _p(lse), _stream(stream))
     _check("dsa_sparse_mla_decode_noalloc", st)
     return out
 
 
 def dense_mla_prefill(q, kv_cache, page_table, q_pos, n_seq, q_per_seq, max_ctx, Dqk, Dv, v_col0, sm_scale,
-                      out=None, lse=None, stream=None):
+                      out=None, lse=None, stream=None, q_seq=None):
     out = _attn_common(q, kv_cache, page_table, q_pos, out, lse, Dv)
     rows, H, _ = q.shape
+    _check_rows(rows, q_pos, n_seq, q_per_seq, q_seq)
     st = load().dsa_dense_mla_prefill(_p(q), _p(kv_cache), _p(page_table), page_table.shape[1], kv_cache.shape[1],
-                                      kv_cache.shape[0], _p(q_pos), n_seq, q_per_seq, max_ctx, H, Dqk, Dv,
+                                      kv_cache.shape[0], _p(q_seq), _p(q_pos), rows, n_seq, q_per_seq, max_ctx, H,
+                                      Dqk, Dv,
                                       kv_cache.shape[2], v_col0, float(sm_scale), _p(out), _p(lse), None, 0,
                                       _stream(stream))
     _check("dsa_dense_mla_prefill", st)

@@ -25,40 +25,48 @@ int main(void) {
   void* f = (void*)(uintptr_t)0x1000;  /* never dereferenced: validation fails first */
   void* mis = (void*)(uintptr_t)0x1004;
   const int32_t* fi = (const int32_t*)f;
-  EXPECT(dsa_indexer_scores(NULL, NULL, NULL, NULL, NULL, 1, 64, 1, NULL, 1, 1, 64, 64, 128, DSA_E4M3, NULL, 64, NULL),
+  EXPECT(dsa_indexer_scores(NULL, NULL, NULL, NULL, NULL, 1, 64, 1, NULL, NULL, 1, 1, 1, 64, 64, 128, DSA_E4M3, NULL,
+                            64, NULL),
          DSA_ERR_INVALID_ARG);
-  EXPECT(dsa_indexer_scores(mis, f, f, NULL, fi, 2, 64, 1, fi, 1, 1, 128, 64, 128, DSA_E4M3, f, 128, NULL),
+  EXPECT(dsa_indexer_scores(mis, f, f, NULL, fi, 2, 64, 1, NULL, fi, 1, 1, 1, 128, 64, 128, DSA_E4M3, f, 128, NULL),
          DSA_ERR_INVALID_ARG);
-  EXPECT(dsa_indexer_scores(f, f, f, NULL, fi, 1, 64, 1, fi, 1, 1, INT_MAX, 64, 128, DSA_E4M3, f, INT_MAX, NULL),
+  EXPECT(dsa_indexer_scores(f, f, f, NULL, fi, 1, 64, 1, NULL, fi, 1, 1, 1, INT_MAX, 64, 128, DSA_E4M3, f, INT_MAX,
+                            NULL),
          DSA_ERR_INVALID_ARG);
-  EXPECT(dsa_indexer_scores(f, f, f, NULL, fi, 1, 0, 1, fi, 1, 1, 64, 64, 128, DSA_E4M3, f, 64, NULL),
+  EXPECT(dsa_indexer_scores(f, f, f, NULL, fi, 1, 0, 1, NULL, fi, 1, 1, 1, 64, 64, 128, DSA_E4M3, f, 64, NULL),
          DSA_ERR_INVALID_ARG);
-  EXPECT(dsa_indexer_scores(f, f, f, NULL, fi, 1, 64, 1, fi, INT_MAX, INT_MAX, 64, 64, 128, DSA_E4M3, f, 64, NULL),
-         DSA_ERR_INVALID_ARG);
-  EXPECT(dsa_indexer_scores(f, f, f, NULL, fi, 1, 64, 1, fi, 0, 1, 64, 64, 128, DSA_E4M3, f, 64, NULL), DSA_OK);
+  EXPECT(dsa_indexer_scores(f, f, f, NULL, fi, 1, 64, 1, NULL, fi, INT_MAX, INT_MAX, INT_MAX, 64, 64, 128, DSA_E4M3,
+                            f, 64, NULL),
+         DSA_ERR_INVALID_ARG);                                   /* rows != n_seq * q_per_seq */
+  EXPECT(dsa_indexer_scores(f, f, f, NULL, fi, 1, 64, 1, fi, fi, 3, 2, 2, 64, 64, 128, DSA_E4M3, f, 64, NULL),
+         DSA_ERR_INVALID_ARG);                                   /* q_seq with q_per_seq != 1 */
+  EXPECT(dsa_indexer_scores(f, f, f, NULL, fi, 1, 64, 1, fi, fi, 3, 0, 1, 64, 64, 128, DSA_E4M3, f, 64, NULL),
+         DSA_ERR_INVALID_ARG);                                   /* rows without any sequence */
+  EXPECT(dsa_indexer_scores(f, f, f, NULL, fi, 1, 64, 1, NULL, fi, 0, 0, 1, 64, 64, 128, DSA_E4M3, f, 64, NULL),
+         DSA_OK);
   EXPECT(dsa_topk(f, 64, fi, 4, 64, 0, f, 64, NULL, 0, NULL), DSA_ERR_INVALID_ARG);
   EXPECT(dsa_topk(f, 64, fi, 4, 64, 32, f, 16, NULL, 0, NULL), DSA_ERR_INVALID_ARG);
   EXPECT(dsa_topk(f, 32, fi, 4, 64, 32, f, 64, NULL, 0, NULL), DSA_ERR_INVALID_ARG);
   EXPECT(dsa_topk(f, 64, fi, 0, 64, 32, f, 64, NULL, 0, NULL), DSA_OK);
-  EXPECT(dsa_indexer_topk(f, f, f, f, fi, 256, 64, 256, fi, 64, 2, 16384, 64, 128, DSA_E4M3, f, 16384, 2048, f, 2048,
-                          NULL, 0, NULL),
+  EXPECT(dsa_indexer_topk(f, f, f, f, fi, 256, 64, 256, NULL, fi, 128, 64, 2, 16384, 64, 128, DSA_E4M3, f, 16384,
+                          2048, f, 2048, NULL, 0, NULL),
          DSA_ERR_WORKSPACE);
-  EXPECT(dsa_indexer_topk(f, f, f, f, fi, 256, 64, 256, fi, 64, 2, 16384, 64, 128, DSA_E4M3, f, 16384, 0, f, 2048,
-                          f, 1 << 30, NULL),
+  EXPECT(dsa_indexer_topk(f, f, f, f, fi, 256, 64, 256, NULL, fi, 128, 64, 2, 16384, 64, 128, DSA_E4M3, f, 16384, 0,
+                          f, 2048, f, 1 << 30, NULL),
          DSA_ERR_INVALID_ARG);
-  EXPECT(dsa_sparse_mla_decode(f, f, fi, 1, 64, 1, fi, 1, 1, fi, 8, 8, 128, 576, 512, 576, 65, 0.1f, f, NULL, NULL,
+  EXPECT(dsa_sparse_mla_decode(f, f, fi, 1, 64, 1, NULL, fi, 1, 1, 1, fi, 8, 8, 128, 576, 512, 576, 65, 0.1f, f, NULL, NULL,
                                0, NULL),
          DSA_ERR_INVALID_ARG);
-  EXPECT(dsa_sparse_mla_decode(f, f, fi, 1, 64, 1, fi, 1, 1, fi, 8, 8, 4, 2048, 64, 2048, 0, 0.1f, f, NULL, NULL, 0,
+  EXPECT(dsa_sparse_mla_decode(f, f, fi, 1, 64, 1, NULL, fi, 1, 1, 1, fi, 8, 8, 4, 2048, 64, 2048, 0, 0.1f, f, NULL, NULL, 0,
                                NULL),
          DSA_ERR_UNSUPPORTED);
-  EXPECT(dsa_sparse_mla_decode(f, f, fi, 64, 64, 64, fi, 4, 1, fi, 2048, 2048, 128, 576, 512, 576, 0, 0.1f, f, NULL,
+  EXPECT(dsa_sparse_mla_decode(f, f, fi, 64, 64, 64, NULL, fi, 4, 4, 1, fi, 2048, 2048, 128, 576, 512, 576, 0, 0.1f, f, NULL,
                                NULL, 0, NULL),
          DSA_ERR_WORKSPACE);
-  EXPECT(dsa_sparse_mla_prefill(mis, f, fi, 1, 64, 1, fi, 1, 1, fi, 8, 8, 128, 576, 512, 576, 0, 0.1f, f, NULL, NULL,
+  EXPECT(dsa_sparse_mla_prefill(mis, f, fi, 1, 64, 1, NULL, fi, 1, 1, 1, fi, 8, 8, 128, 576, 512, 576, 0, 0.1f, f, NULL, NULL,
                                 0, NULL),
          DSA_ERR_INVALID_ARG);
-  EXPECT(dsa_dense_mla_prefill(f, f, fi, 1, 64, 1, fi, 1, 4, 0, 128, 576, 512, 576, 0, 0.1f, f, NULL, NULL, 0, NULL),
+  EXPECT(dsa_dense_mla_prefill(f, f, fi, 1, 64, 1, NULL, fi, 4, 1, 4, 0, 128, 576, 512, 576, 0, 0.1f, f, NULL, NULL, 0, NULL),
          DSA_ERR_INVALID_ARG);
   EXPECT(dsa_expanded_mha_prefill(f, f, f, f, 1 << 20, fi, 1, 1, NULL, 0, 0, 128, 128, 64, 128, 0.1f, f, NULL, NULL,
                                   0, NULL),

@@ -50,10 +50,13 @@ int main(void) {
   for (int i = 0; i < ROWS * HI; ++i) w[i] = uniform();
   float* scores = xmalloc(sizeof(float) * ROWS * max_ctx);
   for (int i = 0; i < ROWS * max_ctx; ++i) scores[i] = -INFINITY;
-  CHECK(oracle_indexer_scores(q8, w, k8, ks, pt, LDPT, PAGE, NPAGES, q_pos, NSEQ, QPS, HI, DI, ORACLE_E4M3, scores,
-                              max_ctx, 0, ROWS));
-  CHECK(oracle_indexer_scores(qf, w, kf, NULL, pt, LDPT, PAGE, NPAGES, q_pos, NSEQ, QPS, HI, DI, ORACLE_F32, scores,
-                              max_ctx, 1, ROWS - 1));
+  int32_t* q_seq = xmalloc(sizeof(int32_t) * ROWS);            /* a ragged mix: 1 row, then 5 rows */
+  const int32_t qs[ROWS] = {1, 0, 0, 0, 0, 0};
+  memcpy(q_seq, qs, sizeof qs);
+  CHECK(oracle_indexer_scores(q8, w, k8, ks, pt, LDPT, PAGE, NPAGES, NULL, q_pos, ROWS, NSEQ, QPS, HI, DI, ORACLE_E4M3,
+                              scores, max_ctx, 0, ROWS));
+  CHECK(oracle_indexer_scores(qf, w, kf, NULL, pt, LDPT, PAGE, NPAGES, q_seq, q_pos, ROWS, NSEQ, 1, HI, DI, ORACLE_F32,
+                              scores, max_ctx, 1, ROWS - 1));
 
   /* top-k: k above and below the prefix lengths, k = 1, ties */
   int32_t* idx = xmalloc(sizeof(int32_t) * ROWS * K);
@@ -73,12 +76,14 @@ int main(void) {
   for (int e = 0; e < K; ++e) idx[5 * K + e] = -1;
   float* out = xmalloc(sizeof(float) * ROWS * H * DV);
   float* lse = xmalloc(sizeof(float) * ROWS * H);
-  CHECK(oracle_sparse_mla(q, kv, pt, LDPT, PAGE, NPAGES, q_pos, NSEQ, QPS, idx, K, K, H, DQK, DV, KVD, V0, 0.3, out,
-                          lse, 0, ROWS));
-  CHECK(oracle_sparse_mla(q, kv, pt, LDPT, PAGE, NPAGES, q_pos, NSEQ, QPS, idx, K, K, H, DQK, DV, KVD, V0, 0.3, out,
-                          NULL, 2, 4));
-  CHECK(oracle_dense_mla(q, kv, pt, LDPT, PAGE, NPAGES, q_pos, NSEQ, QPS, H, DQK, DV, KVD, V0, 0.3, out, lse, 0,
-                         ROWS));
+  CHECK(oracle_sparse_mla(q, kv, pt, LDPT, PAGE, NPAGES, NULL, q_pos, ROWS, NSEQ, QPS, idx, K, K, H, DQK, DV, KVD, V0,
+                          0.3, out, lse, 0, ROWS));
+  CHECK(oracle_sparse_mla(q, kv, pt, LDPT, PAGE, NPAGES, q_seq, q_pos, ROWS, NSEQ, 1, idx, K, K, H, DQK, DV, KVD, V0,
+                          0.3, out, NULL, 2, 4));
+  CHECK(oracle_dense_mla(q, kv, pt, LDPT, PAGE, NPAGES, NULL, q_pos, ROWS, NSEQ, QPS, H, DQK, DV, KVD, V0, 0.3, out,
+                         lse, 0, ROWS));
+  CHECK(oracle_dense_mla(q, kv, pt, LDPT, PAGE, NPAGES, q_seq, q_pos, ROWS, NSEQ, 1, H, DQK, DV, KVD, V0, 0.3, out,
+                         lse, 0, ROWS));
 
   /* expanded attention, dense and masked */
   enum { DN = 16, DR = 8, DVX = 8 };
@@ -119,7 +124,7 @@ int main(void) {
   (void)oracle_e4m3_to_double(0x7F);
   (void)oracle_bf16_to_double(0xFFFF);
 
-  free(pt); free(q_pos); free(q8); free(qf); free(k8); free(kf); free(ks); free(w); free(scores); free(idx);
+  free(pt); free(q_pos); free(q_seq); free(q8); free(qf); free(k8); free(kf); free(ks); free(w); free(scores); free(idx);
   free(idx1); free(q); free(kv); free(out); free(lse); free(xq); free(xkn); free(xkr); free(xv); free(xo);
   free(src); free(codes); free(seq); free(pos); free(kc); free(ksc); free(lat);
   printf("oracle driver: ok\n");

@@ -47,18 +47,18 @@ NULL = None
 
 
 def test_indexer_rejects_null_and_bad_dims(lib):
-    st = lib.dsa_indexer_scores(NULL, NULL, NULL, NULL, NULL, 1, 64, 1, NULL, 1, 1, 64, 64, 128, 0, NULL, 64, NULL)
+    st = lib.dsa_indexer_scores(NULL, NULL, NULL, NULL, NULL, 1, 64, 1, NULL, NULL, 1, 1, 1, 64, 64, 128, 0, NULL, 64, NULL)
     assert st == dsa.DSA_ERR_INVALID_ARG
     assert b"non-NULL" in lib.dsa_last_error()
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
-    st = lib.dsa_indexer_scores(fake, fake, fake, NULL, fake, 1, 64, 1, fake, 1, 1, 64, 64, 128, 7, fake, 64, NULL)
+    st = lib.dsa_indexer_scores(fake, fake, fake, NULL, fake, 1, 64, 1, NULL, fake, 1, 1, 1, 64, 64, 128, 7, fake, 64, NULL)
     assert st == dsa.DSA_ERR_INVALID_ARG and b"dtype" in lib.dsa_last_error()
-    st = lib.dsa_indexer_scores(fake, fake, fake, NULL, fake, 1, 64, 1, fake, 1, 1, 128, 64, 128, 0, fake, 64, NULL)
+    st = lib.dsa_indexer_scores(fake, fake, fake, NULL, fake, 1, 64, 1, NULL, fake, 1, 1, 1, 128, 64, 128, 0, fake, 64, NULL)
     assert st == dsa.DSA_ERR_INVALID_ARG    # ld_pt too small for max_ctx = 128
-    st = lib.dsa_indexer_scores(fake, fake, fake, NULL, fake, 2, 64, 1, fake, 1, 1, 128, 64, 128, 0, fake, 64, NULL)
+    st = lib.dsa_indexer_scores(fake, fake, fake, NULL, fake, 2, 64, 1, NULL, fake, 1, 1, 1, 128, 64, 128, 0, fake, 64, NULL)
     assert st == dsa.DSA_ERR_INVALID_ARG    # ld_scores < max_ctx
     mis = ctypes.c_void_p(0x1004)
-    st = lib.dsa_indexer_scores(mis, fake, fake, NULL, fake, 2, 64, 1, fake, 1, 1, 128, 64, 128, 0, fake, 128, NULL)
+    st = lib.dsa_indexer_scores(mis, fake, fake, NULL, fake, 2, 64, 1, NULL, fake, 1, 1, 1, 128, 64, 128, 0, fake, 128, NULL)
     assert st == dsa.DSA_ERR_INVALID_ARG and b"aligned" in lib.dsa_last_error()
 
 
@@ -80,7 +80,7 @@ def test_fused_indexer_topk_workspace_and_arguments(lib):
     assert long_rows == 256 + 4 * (8 + 1) * 2048 * 4 + lib.dsa_topk_workspace_size(4, 131072, 2048)
     assert size(0, 16384, 2048) == 0
     fake = ctypes.c_void_p(0x1000)
-    args = (fake, fake, fake, fake, fake, 256, 64, 256, fake, 64, 2, 16384, 64, 128, 0, fake, 16384)
+    args = (fake, fake, fake, fake, fake, 256, 64, 256, NULL, fake, 128, 64, 2, 16384, 64, 128, 0, fake, 16384)
     assert lib.dsa_indexer_topk(*args, 2048, fake, 2048, NULL, 0, NULL) == dsa.DSA_ERR_WORKSPACE
     assert lib.dsa_indexer_topk(*args, 2048, fake, 2048, fake, one - 1, NULL) == dsa.DSA_ERR_WORKSPACE
     assert lib.dsa_indexer_topk(*args, 0, fake, 2048, fake, one, NULL) == dsa.DSA_ERR_INVALID_ARG
@@ -90,19 +90,37 @@ def test_fused_indexer_topk_workspace_and_arguments(lib):
 def test_attention_rejects_unsupported_and_inconsistent(lib):
     fake = ctypes.c_void_p(0x1000)
     # v_col0 + Dv beyond the row
-    st = lib.dsa_sparse_mla_decode(fake, fake, fake, 1, 64, 1, fake, 1, 1, fake, 8, 8, 128, 576, 512, 576, 65,
+    st = lib.dsa_sparse_mla_decode(fake, fake, fake, 1, 64, 1, NULL, fake, 1, 1, 1, fake, 8, 8, 128, 576, 512, 576, 65,
                                    ctypes.c_float(0.1), fake, NULL, NULL, 0, NULL)
     assert st == dsa.DSA_ERR_INVALID_ARG
     # a shape no kernel handles is reported, never substituted
-    st = lib.dsa_sparse_mla_decode(fake, fake, fake, 1, 64, 1, fake, 1, 1, fake, 8, 8, 4, 2048, 64, 2048, 0,
+    st = lib.dsa_sparse_mla_decode(fake, fake, fake, 1, 64, 1, NULL, fake, 1, 1, 1, fake, 8, 8, 4, 2048, 64, 2048, 0,
                                    ctypes.c_float(0.1), fake, NULL, NULL, 0, NULL)
     assert st == dsa.DSA_ERR_UNSUPPORTED
     # the tuned decode path needs its split workspace for small batches
     need = lib.dsa_sparse_mla_workspace_size(4, 128, 512, 2048)
     assert need > 0
-    st = lib.dsa_sparse_mla_decode(fake, fake, fake, 64, 64, 64, fake, 4, 1, fake, 2048, 2048, 128, 576, 512, 576, 0,
+    st = lib.dsa_sparse_mla_decode(fake, fake, fake, 64, 64, 64, NULL, fake, 4, 4, 1, fake, 2048, 2048, 128, 576, 512,
+                                   576, 0,
                                    ctypes.c_float(0.1), fake, NULL, NULL, 0, NULL)
     assert st == dsa.DSA_ERR_WORKSPACE
-    st = lib.dsa_dense_mla_prefill(fake, fake, fake, 1, 64, 1, fake, 1, 4, 0, 128, 576, 512, 576, 0,
+    st = lib.dsa_dense_mla_prefill(fake, fake, fake, 1, 64, 1, NULL, fake, 4, 1, 4, 0, 128, 576, 512, 576, 0,
                                    ctypes.c_float(0.1), fake, NULL, NULL, 0, NULL)
     assert st == dsa.DSA_ERR_INVALID_ARG    # max_ctx = 0
+
+
+def test_row_descriptor_checks(lib):
+    """rows must equal n_seq * q_per_seq without q_seq; with q_seq, q_per_seq must be 1 and rows need
+    a sequence; the binding rejects a q_seq of the wrong length."""
+    fake = ctypes.c_void_p(0x1000)
+    args = (fake, fake, fake, NULL, fake, 1, 64, 1)
+    tail = (64, 64, 128, 0, fake, 64, NULL)
+    assert lib.dsa_indexer_scores(*args, NULL, fake, 5, 2, 2, *tail) == dsa.DSA_ERR_INVALID_ARG
+    assert b"n_seq * q_per_seq" in lib.dsa_last_error()
+    assert lib.dsa_indexer_scores(*args, fake, fake, 4, 2, 2, *tail) == dsa.DSA_ERR_INVALID_ARG
+    assert b"q_per_seq must be 1" in lib.dsa_last_error()
+    assert lib.dsa_indexer_scores(*args, fake, fake, 4, 0, 1, *tail) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_indexer_scores(*args, fake, fake, 0, 3, 1, *tail) == dsa.DSA_OK      # no rows: nothing to do
+    st = lib.dsa_sparse_mla_prefill(fake, fake, fake, 1, 64, 1, fake, fake, 3, 2, 2, fake, 8, 8, 128, 576, 512, 576,
+                                    0, ctypes.c_float(0.1), fake, NULL, NULL, 0, NULL)
+    assert st == dsa.DSA_ERR_INVALID_ARG
