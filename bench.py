@@ -487,8 +487,14 @@ def run_prefill_bench(args):
     step = DecodeStep(w, copies=1)
     # a prefill block takes milliseconds: a few warm-up and timed blocks suffice
     steps, warmup = min(args.steps, 20), min(args.warmup, 5)
-    ms_step, wall = time_graph_steps(step, steps, warmup)
-    ms = [time_call(step, fn, steps, reps=2) for fn in (step.call_indexer, step.call_topk, step.call_mla)]
+    if args.no_graph:
+        # eager blocks with events between the calls (for profiler runs that do not follow graphs)
+        wall, per = time_steps(step, steps, warmup)
+        ms = [float(x) for x in per.mean(axis=0)[:3]]
+        ms_step = float(per.mean(axis=0)[3])
+    else:
+        ms_step, wall = time_graph_steps(step, steps, warmup)
+        ms = [time_call(step, fn, steps, reps=2) for fn in (step.call_indexer, step.call_topk, step.call_mla)]
     ctx = w.q_pos.astype(np.int64) + 1
     sel = np.minimum(ctx, w.topk)
     flops = {"indexer": float(np.sum(ctx)) * 2 * w.Hi * w.Di,

@@ -57,5 +57,21 @@ def build(jobs: int = 4) -> str:
     return LIB
 
 
+PRECISION_SRC = os.path.join(ROOT, "tests", "precision", "fp8_mfma_precision.hip")
+PRECISION_BIN = os.path.join(ROOT, "tests", "precision", "fp8_mfma_precision.bin")
+
+
+def build_precision_check() -> str:
+    """The test program that measures the matrix cores' FP8 and f16 dot-product error (a test
+    input, not part of the library)."""
+    cmd = [HIPCC, "-O2", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", PRECISION_SRC, "-o", PRECISION_BIN + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for the FP8 precision check:\n" + r.stdout + r.stderr)
+    os.replace(PRECISION_BIN + ".tmp", PRECISION_BIN)
+    return PRECISION_BIN
+
+
 if __name__ == "__main__":
     print(build())
