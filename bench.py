@@ -676,6 +676,66 @@ def run_cache_bench(args):
     print(json.dumps({"cache_write": res, "tokens": n, "query_rows": 4096}), flush=True)
 
 
+def run_projection_bench(args):
+    """The indexer's projections at the pages' hidden size d = 7168 (query latent 1536, 64 heads x
+    128 dims): the key projection of a 131072-token prefix into the paged cache, and the query
+    projection (codes and head weights) of a 4096-row prefill chunk and of the 128 rows of the
+    decode step. TFLOP/s against the bf16 peak; the decode-sized call also as GB/s of weights and
+    activations read (it streams 25 MB of w_q for 128 rows)."""
+    import torch
+
+    from sparse_attention_06_amd import dsa
+
+    d, d_cq, Hi, Di, page = 7168, 1536, 64, 128, 64
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0xD5A0 + 9)
+    w_k = (torch.randn(Di, d, generator=g, device="cuda") / d ** 0.5).to(torch.bfloat16)
+    w_q = (torch.randn(Hi * Di, d_cq, generator=g, device="cuda") / d_cq ** 0.5).to(torch.bfloat16)
+    w_w = (torch.randn(Hi, d, generator=g, device="cuda") / d ** 0.5).to(torch.bfloat16)
+    n = 131072
+    h = torch.randn(n, d, generator=g, device="cuda").to(torch.bfloat16)
+    pt = torch.randperm(n // page, generator=g, device="cuda").to(torch.int32).view(1, -1)
+    seq = torch.zeros(n, dtype=torch.int32, device="cuda")
+    pos = torch.arange(n, dtype=torch.int32, device="cuda")
+    kc = torch.empty(n // page, page, Di, dtype=torch.uint8, device="cuda")
+    ks = torch.empty(n // page, page, dtype=torch.float32, device="cuda")
+    res = {}
+
+    def timed(name, fn, flops, nbytes, reps=8):
+        # a graph of `reps` calls replayed `steps` times: the calls' GPU time without host gaps
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(reps):
+                fn()
+        torch.cuda.synchronize()
+        ms = time_replays(torch, [gr], args.steps)[0] / reps
+        res[name] = {"us": ms * 1e3, "TFLOPs": flops / (ms * 1e-3) / 1e12,
+                     "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                     "GBps": nbytes / (ms * 1e-3) / 1e9}
+        log(f"[proj] {name}: {res[name]}")
+
+    timed("key_project_131072", lambda: dsa.indexer_key_project(h, w_k, seq, pos, pt, kc, ks, ws=False),
+          2.0 * n * Di * d, n * d * 2 + Di * d * 2 + n * (Di + 4), reps=2)
+    # the decode step's new keys: one per query row (128 rows)
+    ws = torch.empty(max(16, dsa.indexer_projection_workspace_size(128, d)), dtype=torch.uint8, device="cuda")
+    timed("key_project_128", lambda: dsa.indexer_key_project(h[:128], w_k, seq[:128], pos[:128], pt, kc, ks, ws=ws),
+          2.0 * 128 * Di * d, 128 * d * 2 + Di * d * 2 + 128 * (Di + 4))
+    for rows in (4096, 128):
+        c_q = torch.randn(rows, d_cq, generator=g, device="cuda").to(torch.bfloat16)
+        hr = h[:rows]
+        q8 = torch.empty(rows, Hi, Di, dtype=torch.uint8, device="cuda")
+        wo = torch.empty(rows, Hi, dtype=torch.float32, device="cuda")
+        wsq = torch.empty(max(16, dsa.indexer_projection_workspace_size(rows, d)), dtype=torch.uint8, device="cuda")
+        timed(f"query_project_{rows}",
+              lambda: dsa.indexer_query_project(c_q, w_q, hr, w_w, Hi, Di, q8=q8, w=wo, ws=wsq),
+              2.0 * rows * (Hi * Di * d_cq + Hi * d),
+              rows * (d_cq + d) * 2 + (Hi * Di * d_cq + Hi * d) * 2 + rows * (Hi * Di + 4 * Hi))
+    print(json.dumps({"projections": res, "d": d, "d_cq": d_cq, "heads": Hi, "head_dim": Di}), flush=True)
+
+
 def run_copy_calibration(args):
     """A plain device copy of known size (1 GiB read + 1 GiB written per launch): the reference
     for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -711,6 +771,7 @@ def main():
                     help="prefix lengths of the crossover sweep")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--cache-write", action="store_true", help="time the cache writes and query quantisation")
+    ap.add_argument("--projections", action="store_true", help="time the indexer's q / w / k projections")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -721,6 +782,8 @@ def main():
         run_copy_calibration(args)
     elif args.cache_write:
         run_cache_bench(args)
+    elif args.projections:
+        run_projection_bench(args)
     elif args.crossover:
         run_crossover(args)
     elif args.workload.startswith("prefill"):

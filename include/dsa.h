@@ -87,7 +87,8 @@ enum {
   DSA_PATH_MHA_MFMA = 30,             /* expanded attention, dense causal: bf16 MFMA */
   DSA_PATH_MHA_MFMA_MASKED = 31,      /* as 30, restricted to the index sets (bitmap in ws) */
   DSA_PATH_CACHE_WRITE = 40,          /* quantise / place rows into a paged cache */
-  DSA_PATH_QUANTIZE = 41              /* elementwise E4M3 quantisation */
+  DSA_PATH_QUANTIZE = 41,             /* elementwise E4M3 quantisation */
+  DSA_PATH_PROJECT = 42               /* indexer projections: bf16 MFMA GEMM + quantise / place */
 };
 
 const char* dsa_status_string(dsa_status_t status);
@@ -304,6 +305,41 @@ dsa_status_t dsa_latent_cache_write(const uint16_t* rows, int n_tok, int kv_dim,
                                     const int32_t* pos, int n_seq, const int32_t* page_table, int64_t ld_pt, int page_size,
                                     int num_pages, uint16_t* kv_cache, void* stream);
 dsa_status_t dsa_e4m3_quantize(const float* x, int64_t n, uint8_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * The indexer's projections ([DSA-blog] "Lightning Indexer", the first step of its figure: the
+ * current token's hidden state h_t gives the head weights w_t; the query path takes the MLA query
+ * latent and applies an indexer projection to get the n_h^I query heads; every position's hidden
+ * state h_j gives the one key k_j all heads share, stored in the Indexer Key Cache), as bf16
+ * matrix-core GEMMs with fp32 accumulation, their results quantised and placed in the same kernel.
+ * Weights are in the [out, in] layout of a linear layer (each output's weights contiguous). The
+ * pages give no normalisation, rotary part or extra scale in these projections, and none is applied.
+ *
+ * dsa_indexer_key_project -- k[t, :] = h[t, :] . w_k^T for n_tok tokens, then per token the key
+ * format of dsa_indexer_cache_write (s = max_c |k| / 448, codes E4M3(k / s), float operations,
+ * round to nearest even, saturating; all codes 0 when s = 0) written to the token's physical row
+ * (sequence seq[t], position pos[t]) of k_cache / k_scale; tokens without a valid page are skipped.
+ *   h   [n_tok, d] bf16 bits;  w_k [Di, d] bf16 bits;  Di = 128, d a multiple of 64.
+ * dsa_indexer_query_project -- q8[r, :] = E4M3(c_q[r, :] . w_q^T) (Hi * Di codes, no scale: the
+ * pages give the indexer query none) and w[r, :] = h[r, :] . w_w^T in fp32, for `rows` rows.
+ *   c_q [rows, d_cq] bf16 bits (the MLA query latent); w_q [Hi * Di, d_cq]; h [rows, d];
+ *   w_w [Hi, d]; q8 [rows, Hi, Di] bytes out; w [rows, Hi] f32 out. d_cq and d multiples of 64,
+ *   Hi * Di a multiple of 16.
+ * Workspace (both calls): with at least dsa_indexer_projection_workspace_size(rows, d) bytes at ws
+ * (16-byte aligned, contents not preserved; rows = n_tok for the keys), a small batch whose output
+ * tiles would leave most of the GPU idle splits K over workgroups (fp32 partial sums, then an
+ * in-order reduction that applies the coding); with ws NULL or smaller the same results come from
+ * one unsplit launch.
+ * Errors as for the cache writes; other shapes return DSA_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------------------------- */
+size_t dsa_indexer_projection_workspace_size(int rows, int d);
+dsa_status_t dsa_indexer_key_project(const uint16_t* h, const uint16_t* w_k, int n_tok, int d, int Di,
+                                     const int32_t* seq, const int32_t* pos, int n_seq, const int32_t* page_table,
+                                     int64_t ld_pt, int page_size, int num_pages, uint8_t* k_cache, float* k_scale,
+                                     void* ws, size_t ws_bytes, void* stream);
+dsa_status_t dsa_indexer_query_project(const uint16_t* c_q, const uint16_t* w_q, const uint16_t* h,
+                                       const uint16_t* w_w, int rows, int d_cq, int d, int Hi, int Di, uint8_t* q8,
+                                       float* w, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

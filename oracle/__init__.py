@@ -18,4 +18,6 @@ from .ref import (  # noqa: F401
     e4m3_quantize,
     indexer_cache_write,
     latent_cache_write,
+    indexer_key_project,
+    indexer_query_project,
 )

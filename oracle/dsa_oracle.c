@@ -416,3 +416,55 @@ int oracle_latent_cache_write(const uint16_t* rows, int kv_dim, const int32_t* s
   if (skipped) *skipped = skip;
   return 0;
 }
+
+/* ---- the indexer's projections --------------------------------------------------------- */
+
+/* out[i, o] = sum_c x[i, c] * wt[o, c] over c < K in double, rounded once to float: a linear layer
+ * with its weights in the [out, in] layout, on bf16 inputs. */
+static void linear_bf16(const uint16_t* x, const uint16_t* wt, int rows, int K, int N, float* out) {
+  for (int i = 0; i < rows; ++i)
+    for (int o = 0; o < N; ++o) {
+      double acc = 0.0;
+      for (int c = 0; c < K; ++c)
+        acc += oracle_bf16_to_double(x[(int64_t)i * K + c]) * oracle_bf16_to_double(wt[(int64_t)o * K + c]);
+      out[(int64_t)i * N + o] = (float)acc;
+    }
+}
+
+/* [DSA-blog] "Lightning Indexer", the first step of its figure: every position's hidden state h_j
+ * gives the one indexer key k_j all heads share, kept in the Indexer Key Cache. k = h w_k^T, then
+ * the key format of oracle_indexer_cache_write (per token s = max|k| / 448, codes E4M3(k / s)).
+ * The keys before quantisation go to k_out [n_tok, Di] when it is not NULL. */
+int oracle_indexer_key_project(const uint16_t* h, const uint16_t* w_k, int n_tok, int d, int Di, const int32_t* seq,
+                               const int32_t* pos, int n_seq, const int32_t* page_table, int64_t ld_pt, int page_size,
+                               int num_pages, uint8_t* k_cache, float* k_scale, float* k_out, int* skipped) {
+  if (n_tok < 0 || d < 1 || Di < 1) return 1;
+  float* k = (float*)malloc(sizeof(float) * (size_t)(n_tok > 0 ? n_tok : 1) * (size_t)Di);
+  if (!k) return 2;
+  linear_bf16(h, w_k, n_tok, d, Di, k);
+  int rc = oracle_indexer_cache_write(k, ORACLE_F32, Di, seq, pos, n_tok, n_seq, page_table, ld_pt, page_size,
+                                      num_pages, k_cache, k_scale, skipped);
+  if (k_out) memcpy(k_out, k, sizeof(float) * (size_t)n_tok * (size_t)Di);
+  free(k);
+  return rc;
+}
+
+/* [DSA-blog] "Lightning Indexer", the first step of its figure: the query path takes the MLA query
+ * latent c_q and applies the indexer projection to get the n_h^I query heads, and the current
+ * token's hidden state h gives the head weights. q = c_q w_q^T coded E4M3 without a scale (the pages
+ * give the indexer query none), w = h w_w^T in float. q_out [rows, Hi * Di] receives q before its
+ * coding when not NULL. */
+int oracle_indexer_query_project(const uint16_t* c_q, const uint16_t* w_q, const uint16_t* h, const uint16_t* w_w,
+                                 int rows, int d_cq, int d, int Hi, int Di, uint8_t* q8, float* w, float* q_out) {
+  if (rows < 0 || d_cq < 1 || d < 1 || Hi < 1 || Di < 1) return 1;
+  const int64_t n = (int64_t)rows * Hi * Di;
+  float* q = (float*)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+  if (!q) return 2;
+  linear_bf16(c_q, w_q, rows, d_cq, Hi * Di, q);
+  int rc = oracle_e4m3_quantize(q, n, q8);
+  if (q_out) memcpy(q_out, q, sizeof(float) * (size_t)n);
+  free(q);
+  if (rc) return rc;
+  linear_bf16(h, w_w, rows, d, Hi, w);
+  return 0;
+}

@@ -114,6 +114,20 @@ int oracle_latent_cache_write(const uint16_t* rows, int kv_dim, const int32_t* s
                               int n_tok, int n_seq, const int32_t* page_table, int64_t ld_pt, int page_size,
                               int num_pages, uint16_t* kv_cache, int* skipped);
 
+/* The indexer's projections ([DSA-blog] "Lightning Indexer", the first step of its figure), linear
+ * layers with weights in the [out, in] layout on bf16 inputs, each output summed in double and
+ * rounded once to float:
+ *   oracle_indexer_key_project    k = h w_k^T (h [n_tok, d], w_k [Di, d]), then the key format and
+ *                                 placement of oracle_indexer_cache_write; k_out (or NULL) gets k
+ *   oracle_indexer_query_project  q8 = E4M3(c_q w_q^T) (c_q [rows, d_cq], w_q [Hi*Di, d_cq]; no
+ *                                 scale) and w = h w_w^T (h [rows, d], w_w [Hi, d]) in float; q_out
+ *                                 (or NULL) gets q before its coding */
+int oracle_indexer_key_project(const uint16_t* h, const uint16_t* w_k, int n_tok, int d, int Di, const int32_t* seq,
+                               const int32_t* pos, int n_seq, const int32_t* page_table, int64_t ld_pt, int page_size,
+                               int num_pages, uint8_t* k_cache, float* k_scale, float* k_out, int* skipped);
+int oracle_indexer_query_project(const uint16_t* c_q, const uint16_t* w_q, const uint16_t* h, const uint16_t* w_w,
+                                 int rows, int d_cq, int d, int Hi, int Di, uint8_t* q8, float* w, float* q_out);
+
 #ifdef __cplusplus
 }
 #endif

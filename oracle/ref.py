@@ -68,6 +68,11 @@ def _load():
             lib.oracle_indexer_cache_write.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, i64, i32, i32, vp, vp, vp]
             lib.oracle_latent_cache_write.restype = i32
             lib.oracle_latent_cache_write.argtypes = [vp, i32, vp, vp, i32, i32, vp, i64, i32, i32, vp, vp]
+            lib.oracle_indexer_key_project.restype = i32
+            lib.oracle_indexer_key_project.argtypes = [vp, vp, i32, i32, i32, vp, vp, i32, vp, i64, i32, i32, vp,
+                                                       vp, vp, vp]
+            lib.oracle_indexer_query_project.restype = i32
+            lib.oracle_indexer_query_project.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
             lib.oracle_mha.restype = i32
             lib.oracle_mha.argtypes = [vp, vp, vp, vp, i64, vp, i32, i32, vp, i64, i32, i32, i32, i32, i32,
                                        dbl, vp, vp, i32, i32]
@@ -293,3 +298,44 @@ def latent_cache_write(rows, seq, pos, page_table, page_size, kv_cache):
     if rc != 0:
         raise ValueError(f"oracle call failed with code {rc}")
     return skipped.value
+
+
+def indexer_key_project(h, w_k, seq, pos, page_table, page_size, k_cache, k_scale, threads=1):
+    """k = h w_k^T (h uint16 bf16 bits [n_tok, d], w_k [Di, d]) quantised per token into k_cache
+    (uint8 [P, page, Di]) / k_scale (float32 [P, page]) in place. Returns (k float32 [n_tok, Di]
+    before quantisation, skipped-token count)."""
+    h, w_k = _c(h, np.uint16), _c(w_k, np.uint16)
+    seq, pos, pt = _c(seq, np.int32), _c(pos, np.int32), _c(page_table, np.int32)
+    n_tok, d = h.shape
+    Di = w_k.shape[0]
+    assert k_cache.flags.c_contiguous and k_scale.flags.c_contiguous
+    k = np.empty((n_tok, Di), np.float32)
+    skipped = ctypes.c_int(0)
+    rc = _load().oracle_indexer_key_project(_ptr(h), _ptr(w_k), n_tok, d, Di, _ptr(seq), _ptr(pos), pt.shape[0],
+                                            _ptr(pt), pt.shape[1], page_size, k_cache.shape[0], _ptr(k_cache),
+                                            _ptr(k_scale), _ptr(k), ctypes.byref(skipped))
+    if rc != 0:
+        raise ValueError(f"oracle call failed with code {rc}")
+    return k, skipped.value
+
+
+def indexer_query_project(c_q, w_q, h, w_w, Hi, Di, threads=1):
+    """q8 = E4M3(c_q w_q^T) [rows, Hi, Di] and w = h w_w^T [rows, Hi] (float32); also q before its
+    coding [rows, Hi, Di]. Rows are split over `threads` host threads."""
+    c_q, w_q, h, w_w = (_c(x, np.uint16) for x in (c_q, w_q, h, w_w))
+    rows, d_cq = c_q.shape
+    d = h.shape[1]
+    q8 = np.empty((rows, Hi, Di), np.uint8)
+    w = np.empty((rows, Hi), np.float32)
+    q = np.empty((rows, Hi, Di), np.float32)
+    lib = _load()
+
+    def fn(b, e):
+        n = e - b
+        return lib.oracle_indexer_query_project(_ptr(c_q[b:e]), _ptr(w_q), _ptr(h[b:e]), _ptr(w_w), n, d_cq, d, Hi, Di,
+                                                q8[b:e].ctypes.data_as(ctypes.c_void_p),
+                                                w[b:e].ctypes.data_as(ctypes.c_void_p),
+                                                q[b:e].ctypes.data_as(ctypes.c_void_p))
+
+    _run_rows(fn, rows, threads)
+    return q8, w, q

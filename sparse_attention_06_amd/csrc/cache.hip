@@ -16,24 +16,6 @@
 
 namespace dsa {
 
-// float -> OCP E4M3FN, round to nearest even, saturating to +-448 (finite input). Normal values:
-// round the 23-bit mantissa to 3 bits by adding half an output ulp minus one plus the kept LSB
-// (a carry moves into the exponent); below 2^-6 the value is a count of 2^-9 quanta.
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  if (a >= 0x43E00000u) return sign | 0x7Eu;  // |f| >= 448
-  if (a < 0x3C800000u) {                      // |f| < 2^-6: subnormal codes 0..8 (8 = 2^-6)
-    const float q = __uint_as_float(a) * 512.0f;  // exact
-    return sign | (uint32_t)__builtin_rintf(q);
-  }
-  const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-  const uint32_t e = (r >> 23) - 127u + 7u;  // 1 .. 15
-  const uint32_t code = (e << 3) | ((r >> 20) & 7u);
-  return sign | (code > 0x7Eu ? 0x7Eu : code);
-}
-
 // Sixteen lanes per token (four tokens per wave), Di = 128: lane j of a token's group holds
 // elements 8j .. 8j+7. The key row is loaded first, so its latency overlaps the page lookup.
 template <bool kF32>

@@ -426,6 +426,55 @@ dsa_status_t dsa_latent_cache_write(const uint16_t* rows, int n_tok, int kv_dim,
   return s == DSA_OK ? ok(DSA_PATH_CACHE_WRITE) : s;
 }
 
+size_t dsa_indexer_projection_workspace_size(int rows, int d) {
+  if (rows <= 0 || d < 64) return 0;
+  const size_t k = dsa::proj_ws_bytes(rows, 128, d), w = dsa::proj_ws_bytes(rows, 64, d);
+  return k > w ? k : w;
+}
+
+dsa_status_t dsa_indexer_key_project(const uint16_t* h, const uint16_t* w_k, int n_tok, int d, int Di,
+                                     const int32_t* seq, const int32_t* pos, int n_seq, const int32_t* page_table,
+                                     int64_t ld_pt, int page_size, int num_pages, uint8_t* k_cache, float* k_scale,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(n_tok >= 0 && d >= 1, "need n_tok >= 0 and d >= 1 (got %d, %d)", n_tok, d);
+  if (n_tok == 0) return ok(DSA_PATH_NONE);
+  REQUIRE(h && w_k && seq && pos && page_table && k_cache && k_scale, "a required pointer is NULL");
+  REQUIRE(!misaligned(h) && !misaligned(w_k) && !misaligned(k_cache) && ((uintptr_t)k_scale & 3u) == 0,
+          "h, w_k and k_cache must be 16-byte aligned, k_scale 4-byte aligned");
+  REQUIRE(n_seq >= 1, "n_seq must be >= 1 (got %d)", n_seq);
+  REQUIRE(page_size >= 1 && num_pages >= 1 && ld_pt >= 1, "bad paging (page_size %d, num_pages %d, ld_pt %lld)",
+          page_size, num_pages, (long long)ld_pt);
+  REQUIRE((int64_t)num_pages * page_size < ((int64_t)1 << 31), "cache larger than 2^31 rows");
+  if (Di != 128 || d % 64 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "the key projection takes Di = 128 and d a multiple of 64 (got Di %d, d %d)", Di, d);
+  dsa::PagedCache kc{k_cache, page_table, ld_pt, page_size, num_pages};
+  REQUIRE(!ws || ((uintptr_t)ws & 15u) == 0, "ws must be 16-byte aligned");
+  dsa_status_t s = hip_status(dsa::launch_indexer_key_project(h, w_k, n_tok, d, n_seq, seq, pos, kc, k_cache, k_scale,
+                                                               ws, ws_bytes, (hipStream_t)stream),
+                              "key projection launch");
+  return s == DSA_OK ? ok(DSA_PATH_PROJECT) : s;
+}
+
+dsa_status_t dsa_indexer_query_project(const uint16_t* c_q, const uint16_t* w_q, const uint16_t* h,
+                                       const uint16_t* w_w, int rows, int d_cq, int d, int Hi, int Di, uint8_t* q8,
+                                       float* w, void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(rows >= 0 && d_cq >= 1 && d >= 1 && Hi >= 1 && Di >= 1, "need rows >= 0 and positive dims");
+  if (rows == 0) return ok(DSA_PATH_NONE);
+  REQUIRE(c_q && w_q && h && w_w && q8 && w, "a required pointer is NULL");
+  REQUIRE(!misaligned(c_q) && !misaligned(w_q) && !misaligned(h) && !misaligned(w_w) && !misaligned(q8) &&
+              ((uintptr_t)w & 3u) == 0,
+          "c_q, w_q, h, w_w and q8 must be 16-byte aligned, w 4-byte aligned");
+  REQUIRE((int64_t)Hi * Di < (1 << 30), "Hi * Di too large");
+  if (d_cq % 64 != 0 || d % 64 != 0 || (Hi * Di) % 16 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "the query projection takes d_cq and d multiples of 64 and Hi * Di a multiple of 16 "
+                                     "(got %d, %d, %d)", d_cq, d, Hi * Di);
+  REQUIRE(!ws || ((uintptr_t)ws & 15u) == 0, "ws must be 16-byte aligned");
+  dsa_status_t s = hip_status(dsa::launch_indexer_query_project(c_q, w_q, h, w_w, rows, d_cq, d, Hi * Di, Hi, q8, w,
+                                                                 ws, ws_bytes, (hipStream_t)stream),
+                              "query projection launch");
+  return s == DSA_OK ? ok(DSA_PATH_PROJECT) : s;
+}
+
 dsa_status_t dsa_e4m3_quantize(const float* x, int64_t n, uint8_t* out, void* stream) {
   REQUIRE(n >= 0, "n must be >= 0");
   if (n == 0) return ok(DSA_PATH_NONE);

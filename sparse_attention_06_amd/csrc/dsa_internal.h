@@ -46,6 +46,24 @@ __device__ __forceinline__ void e4m3x16_to_f16(i32x4 raw, f16x8& lo, f16x8& hi) 
   hi = f16x8{e[0], e[1], f[0], f[1], g[0], g[1], h[0], h[1]};
 }
 
+// float -> OCP E4M3FN, round to nearest even, saturating to +-448 (finite input). Normal values:
+// round the 23-bit mantissa to 3 bits by adding half an output ulp minus one plus the kept LSB
+// (a carry moves into the exponent); below 2^-6 the value is a count of 2^-9 quanta.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x43E00000u) return sign | 0x7Eu;  // |f| >= 448
+  if (a < 0x3C800000u) {                      // |f| < 2^-6: subnormal codes 0..8 (8 = 2^-6)
+    const float q = __uint_as_float(a) * 512.0f;  // exact
+    return sign | (uint32_t)__builtin_rintf(q);
+  }
+  const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+  const uint32_t e = (r >> 23) - 127u + 7u;  // 1 .. 15
+  const uint32_t code = (e << 3) | ((r >> 20) & 7u);
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -162,4 +180,16 @@ hipError_t launch_indexer_cache_write(const void* k, bool f32, int n_tok, int n_
 hipError_t launch_latent_cache_write(const uint16_t* rows, int n_tok, int n_seq, int kv_dim, const int32_t* seq,
                                      const int32_t* pos, PagedCache kc, uint16_t* kv_cache, hipStream_t stream);
 hipError_t launch_e4m3_quantize(const float* x, int64_t n, uint8_t* out, hipStream_t stream);
+// The indexer's projections (bf16 MFMA GEMMs, operands K-contiguous, K a multiple of 64): keys
+// k = h w_k^T quantised per token into the paged cache (128 output columns); queries q = c_q w_q^T
+// as unscaled E4M3 codes (n_q columns, a multiple of 16) and head weights w = h w_w^T in fp32.
+// Small batches split K over workgroups when a workspace of proj_ws_bytes(M, N, K) is given (fp32
+// partial sums, then an in-order reduction with the epilogue); without one they run unsplit.
+size_t proj_ws_bytes(int M, int N, int K);
+hipError_t launch_indexer_key_project(const uint16_t* h, const uint16_t* w_k, int n_tok, int d, int n_seq,
+                                      const int32_t* seq, const int32_t* pos, PagedCache kc, uint8_t* k_cache,
+                                      float* k_scale, void* ws, size_t ws_bytes, hipStream_t stream);
+hipError_t launch_indexer_query_project(const uint16_t* c_q, const uint16_t* w_q, const uint16_t* h,
+                                        const uint16_t* w_w, int rows, int d_cq, int d, int n_q, int n_w, uint8_t* q8,
+                                        float* w, void* ws, size_t ws_bytes, hipStream_t stream);
 }  // namespace dsa

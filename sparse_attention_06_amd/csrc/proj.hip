@@ -1,0 +1,327 @@
+// proj.hip -- the Lightning Indexer's projections on gfx950, fused with the FP8 quantisation and
+// the paged key-cache write.
+//
+// Page references:
+//   [DSA-blog]  "DeepSeek Sparse Attention：从 SWA 到稀疏 Attention 计算" (kevinye.org), section
+//               "Lightning Indexer", its figure's first step: the current token's hidden state h_t
+//               gives the head weights w_t; the query path reuses the MLA query latent and applies
+//               an indexer projection to get the n_h^I query heads q_{t,r}; every position's own
+//               hidden state h_j gives one key k_j shared by all heads, kept in the Indexer Key Cache
+//   [Handbook]  "MTP 与稀疏注意力：NSA 与 DSA" (anrans.github.io): 64 indexer heads of 128 dims,
+//               scored in FP8; the key cache stores 128 FP8 codes plus a float scale per token
+//
+// One GEMM kernel, C[M x N] = A[M x K] . B[N x K]^T with bf16 operands (both K-contiguous: the
+// activations row-major, the weights in the [out, in] layout of a linear layer) on
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation, and three epilogues:
+//   key    N = 128: per row (token) s = max|c| / 448 and codes E4M3(c / s), written to the token's
+//          physical row of the paged key cache (the format dsa_indexer_cache_write writes)
+//   query  codes E4M3(c) without a scale, row-major [M, N] bytes
+//   f32    c as fp32, row-major [M, N]
+// Workgroup: 4 waves, a 128 x 128 output tile, K in blocks of 64 staged through LDS (rows padded to
+// 144 bytes, so the 16-byte operand reads of 8 consecutive rows hit distinct banks), the next block
+// loaded into registers while the current one is multiplied. Wave w owns rows 32w..32w+31 of the
+// tile and all 128 columns (four 32 x 32 accumulator blocks). Within a block of 64 the K order is
+// permuted the same way for both operands (lane half h supplies elements 32h + 8j .. +8 as its
+// part of MFMA j), which leaves every dot product unchanged.
+#include "dsa_internal.h"
+
+namespace dsa {
+
+constexpr int kPM = 128, kPN = 128, kPK = 64;
+constexpr int kPRowBytes = 2 * kPK + 16;                 // 144: padded LDS row of a K block
+constexpr int kPTileBytes = kPM * kPRowBytes;            // 18432 per operand
+constexpr int kPStageBytes = 32 * kPN;                   // one wave's 32 x 128 byte codes
+
+// kEpiPartial: fp32 sums over one K range (blockIdx.z) to ws[z][M][N], for the split-K path
+enum { kEpiKey = 0, kEpiQuery = 1, kEpiF32 = 2, kEpiPartial = 3 };
+
+struct ProjArgs {
+  const uint16_t* a;  // [M, K] bf16
+  const uint16_t* b;  // [N, K] bf16
+  int M, N, K;
+  // key epilogue
+  const int32_t* seq;
+  const int32_t* pos;
+  int n_seq;
+  PagedCache kc;
+  uint8_t* k_cache;
+  float* k_scale;
+  // query / f32 epilogues
+  uint8_t* q8;
+  float* f32;
+  // split-K: K range of blockIdx.z is [z * k_split, (z + 1) * k_split); partials in ws
+  int k_split;
+  float* ws;
+};
+
+// kTM: rows per tile. 128: wave w owns rows 32w.. and all 128 columns; 32 (small batches, so the
+// grid covers the GPU): the 4 waves share the 32 rows and wave w owns columns 32w..32w+31.
+template <int kEpi, int kTM>
+__global__ void __launch_bounds__(256) proj_gemm_kernel(ProjArgs p) {
+  static_assert(kTM == 128 || kTM == 32, "row tile");
+  constexpr int kCB = kTM == 128 ? 4 : 1;  // 32-column accumulator blocks per wave
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kPTileBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane & 31, half = lane >> 5;
+  const int m0 = blockIdx.x * kTM, n0 = blockIdx.y * kPN;
+  const int kbeg = kEpi == kEpiPartial ? blockIdx.z * p.k_split : 0;
+  const int kend = kEpi == kEpiPartial ? min(p.K, kbeg + p.k_split) : p.K;
+  const int wrow = kTM == 128 ? 32 * wave : 0;       // the wave's first row within the tile
+  const int wcb0 = kTM == 128 ? 0 : wave;            // the wave's first column block
+  uint8_t* lds_a = smem;
+  uint8_t* lds_b = smem + kPTileBytes;
+
+  // global -> register staging: thread tid moves chunks c = tid + 256 i (i < 4) of each operand's
+  // 128 rows x 128 bytes (row c / 8, 16-byte chunk c % 8); rows past M or N load zeros
+  // (A: kTM rows, so kTM / 32 chunks per thread; B: 128 rows, 4 chunks per thread)
+  constexpr int kAC = kTM / 32;
+  i32x4 ra[kAC], rb[4];
+  auto load_block = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < kAC; ++i) {
+      const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
+      ra[i] = (m0 + row < p.M) ? *(const i32x4*)(p.a + (int64_t)(m0 + row) * p.K + k0 + 8 * ch) : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
+      rb[i] = (n0 + row < p.N) ? *(const i32x4*)(p.b + (int64_t)(n0 + row) * p.K + k0 + 8 * ch) : i32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_block = [&]() {
+#pragma unroll
+    for (int i = 0; i < kAC; ++i) {
+      const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
+      *(i32x4*)(lds_a + row * kPRowBytes + 16 * ch) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
+      *(i32x4*)(lds_b + row * kPRowBytes + 16 * ch) = rb[i];
+    }
+  };
+
+  f32x16 acc[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) acc[cb] = f32x16{};
+  if (kbeg < kend) load_block(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += kPK) {
+    __syncthreads();  // the previous block's operand reads are done
+    store_block();
+    __syncthreads();
+    if (k0 + kPK < kend) load_block(k0 + kPK);
+    bf16x8 a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = *(const bf16x8*)(lds_a + (wrow + hl) * kPRowBytes + 64 * half + 16 * j);
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      bf16x8 b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = *(const bf16x8*)(lds_b + (32 * (wcb0 + cb) + hl) * kPRowBytes + 64 * half + 16 * j);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[j], acc[cb], 0, 0, 0);
+    }
+  }
+
+  // acc[cb][e]: row wrow + 8 (e / 4) + 4 half + e % 4 of the tile, column 32 (wcb0 + cb) + hl
+  if (kEpi == kEpiF32 || kEpi == kEpiPartial) {
+    float* dst = kEpi == kEpiF32 ? p.f32 : p.ws + (int64_t)blockIdx.z * p.M * p.N;
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      const int n = n0 + 32 * (wcb0 + cb) + hl;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wrow + 8 * (e >> 2) + 4 * half + (e & 3);
+        if (m < p.M && n < p.N) dst[(int64_t)m * p.N + n] = acc[cb][e];
+      }
+    }
+    return;
+  }
+  // Coded epilogues: the tile's codes staged as [row][128] bytes in LDS (the operand tiles are
+  // done); with 128-row tiles each wave stages its own 32 rows, with 32-row tiles (query only) the
+  // four waves stage their column blocks of the same 32 rows.
+  static_assert(kEpi != kEpiKey || kTM == 128, "the key epilogue takes 128-row tiles");
+  __syncthreads();
+  uint8_t* stage = smem + (kTM == 128 ? wave * kPStageBytes : 0);
+  float sc[16];  // key epilogue: the row's scale s (the code is E4M3(c / s), an IEEE division)
+#pragma unroll
+  for (int e = 0; e < 16; ++e) sc[e] = 1.f;
+  if (kEpi == kEpiKey) {
+    // per row: the largest |c| over its 128 columns (4 blocks in this lane, 32 lanes of its half)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float m = 0.f;
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) m = fmaxf(m, fabsf(acc[cb][e]));
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      sc[e] = m / 448.0f;
+    }
+  }
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = 8 * (e >> 2) + 4 * half + (e & 3);
+      uint32_t code;
+      if (kEpi == kEpiKey) code = sc[e] > 0.f ? e4m3_rne_sat(acc[cb][e] / sc[e]) : 0u;
+      else code = e4m3_rne_sat(acc[cb][e]);
+      stage[r * kPN + 32 * (wcb0 + cb) + hl] = (uint8_t)code;
+    }
+  __syncthreads();
+  // 32 rows x 8 chunks of 16 bytes: 4 per lane of each wave (128-row tiles) or 1 per thread
+  constexpr int kStores = kTM == 128 ? 4 : 1;
+#pragma unroll
+  for (int i = 0; i < kStores; ++i) {
+    const int c = kTM == 128 ? lane + 64 * i : tid, r = c >> 3, ch = c & 7;
+    const int m = m0 + wrow + r;
+    if (m >= p.M) continue;
+    const i32x4 v = *(const i32x4*)(stage + r * kPN + 16 * ch);
+    if (kEpi == kEpiQuery) {
+      if (n0 + 16 * ch < p.N) *(i32x4*)(p.q8 + (int64_t)m * p.N + n0 + 16 * ch) = v;
+    } else {
+      const int sq = p.seq[m];
+      const int64_t row = (sq >= 0 && sq < p.n_seq)
+                              ? phys_row(p.kc.page_table, p.kc.ld_pt, p.kc.page_size, p.kc.num_pages, sq, p.pos[m])
+                              : -1;
+      if (row >= 0) *(i32x4*)(p.k_cache + row * 128 + 16 * ch) = v;
+    }
+  }
+  if (kEpi == kEpiKey && hl == 0) {
+    // the lane of each half that holds column 0 writes its rows' scales
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = m0 + wrow + 8 * (e >> 2) + 4 * half + (e & 3);
+      if (m >= p.M) continue;
+      const int sq = p.seq[m];
+      const int64_t row = (sq >= 0 && sq < p.n_seq)
+                              ? phys_row(p.kc.page_table, p.kc.ld_pt, p.kc.page_size, p.kc.num_pages, sq, p.pos[m])
+                              : -1;
+      if (row >= 0) p.k_scale[row] = sc[e];
+    }
+  }
+}
+
+// The split-K path's second step: the kz partial blocks ws[z][M][N] summed in order of z, then the
+// key epilogue (N = 128: 16 lanes per token, 8 columns per lane) or fp32 stores.
+template <int kEpi>
+__global__ void __launch_bounds__(256) proj_reduce_kernel(ProjArgs p, int kz) {
+  const int64_t MN = (int64_t)p.M * p.N;
+  if (kEpi == kEpiF32) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= MN) return;
+    float sum = 0.f;
+    for (int z = 0; z < kz; ++z) sum += p.ws[z * MN + i];
+    p.f32[i] = sum;
+    return;
+  }
+  static_assert(kEpi == kEpiKey || kEpi == kEpiF32, "reduce epilogues");
+  const int j = threadIdx.x & 15;
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool live = t < p.M;
+  const int tc = live ? t : p.M - 1;  // idle groups re-read the last token and store nothing
+  float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int z = 0; z < kz; ++z) {
+    const float4* src = (const float4*)(p.ws + z * MN + (int64_t)tc * 128 + 8 * j);
+    const float4 a = src[0], b = src[1];
+    x[0] += a.x; x[1] += a.y; x[2] += a.z; x[3] += a.w; x[4] += b.x; x[5] += b.y; x[6] += b.z; x[7] += b.w;
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));  // within the 16-lane group
+  const int sq = p.seq[tc];
+  const int64_t row = live && sq >= 0 && sq < p.n_seq
+                          ? phys_row(p.kc.page_table, p.kc.ld_pt, p.kc.page_size, p.kc.num_pages, sq, p.pos[tc])
+                          : -1;
+  if (row < 0) return;
+  const float s = m / 448.0f;
+  uint32_t lo = 0, hi = 0;
+  if (s > 0.f) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo |= e4m3_rne_sat(x[e] / s) << (8 * e);
+      hi |= e4m3_rne_sat(x[4 + e] / s) << (8 * e);
+    }
+  }
+  ((uint2*)(p.k_cache + row * 128))[j] = make_uint2(lo, hi);
+  if (j == 0) p.k_scale[row] = s;
+}
+
+// Split-K is taken when the output tiles alone would fill less than half the GPU: the K blocks of
+// 64 are dealt out so that about 256 workgroups run (32-row tiles). Returns the number of K ranges
+// and sets *k_split (a multiple of 64); 1 means no split.
+static int proj_plan(int M, int N, int K, int* k_split) {
+  const int tiles = ((M + 31) / 32) * ((N + kPN - 1) / kPN);
+  const int kb = K / kPK;
+  *k_split = K;
+  if (tiles >= 128 || kb < 2) return 1;
+  const int want = 256 / tiles < kb ? 256 / tiles : kb;
+  if (want < 2) return 1;
+  const int per = (kb + want - 1) / want;  // K blocks per range
+  *k_split = per * kPK;
+  return (kb + per - 1) / per;
+}
+
+size_t proj_ws_bytes(int M, int N, int K) {
+  int ks = 0;
+  const int kz = proj_plan(M, N, K, &ks);
+  return kz > 1 ? (size_t)kz * M * N * 4 : 0;
+}
+
+hipError_t launch_indexer_key_project(const uint16_t* h, const uint16_t* w_k, int n_tok, int d, int n_seq,
+                                      const int32_t* seq, const int32_t* pos, PagedCache kc, uint8_t* k_cache,
+                                      float* k_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  ProjArgs p{};
+  p.a = h; p.b = w_k; p.M = n_tok; p.N = 128; p.K = d;
+  p.seq = seq; p.pos = pos; p.n_seq = n_seq; p.kc = kc; p.k_cache = k_cache; p.k_scale = k_scale;
+  int ks = 0;
+  const int kz = proj_plan(n_tok, 128, d, &ks);
+  if (kz > 1 && ws && ws_bytes >= proj_ws_bytes(n_tok, 128, d)) {
+    p.k_split = ks; p.ws = (float*)ws;
+    hipLaunchKernelGGL((proj_gemm_kernel<kEpiPartial, 32>), dim3((n_tok + 31) / 32, 1, kz), dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(proj_reduce_kernel<kEpiKey>, dim3((n_tok + 15) / 16), dim3(256), 0, stream, p, kz);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((proj_gemm_kernel<kEpiKey, 128>), dim3((n_tok + kPM - 1) / kPM, 1), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_query_project(const uint16_t* c_q, const uint16_t* w_q, const uint16_t* h,
+                                        const uint16_t* w_w, int rows, int d_cq, int d, int n_q, int n_w, uint8_t* q8,
+                                        float* w, void* ws, size_t ws_bytes, hipStream_t stream) {
+  ProjArgs p{};
+  p.a = c_q; p.b = w_q; p.M = rows; p.N = n_q; p.K = d_cq; p.q8 = q8;
+  // small batches take 32-row tiles, so that the column tiles spread over the GPU
+  if (rows <= 512)
+    hipLaunchKernelGGL((proj_gemm_kernel<kEpiQuery, 32>), dim3((rows + 31) / 32, (n_q + kPN - 1) / kPN), dim3(256), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((proj_gemm_kernel<kEpiQuery, 128>), dim3((rows + kPM - 1) / kPM, (n_q + kPN - 1) / kPN),
+                       dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  ProjArgs pw{};
+  pw.a = h; pw.b = w_w; pw.M = rows; pw.N = n_w; pw.K = d; pw.f32 = w;
+  int ks = 0;
+  const int kz = proj_plan(rows, n_w, d, &ks);
+  if (kz > 1 && ws && ws_bytes >= proj_ws_bytes(rows, n_w, d)) {
+    pw.k_split = ks; pw.ws = (float*)ws;
+    hipLaunchKernelGGL((proj_gemm_kernel<kEpiPartial, 32>), dim3((rows + 31) / 32, (n_w + kPN - 1) / kPN, kz),
+                       dim3(256), 0, stream, pw);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)rows * n_w;
+    hipLaunchKernelGGL(proj_reduce_kernel<kEpiF32>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, pw, kz);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((proj_gemm_kernel<kEpiF32, 128>), dim3((rows + kPM - 1) / kPM, (n_w + kPN - 1) / kPN), dim3(256),
+                     0, stream, pw);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -19,7 +19,7 @@ DSA_E4M3, DSA_F32, DSA_BF16 = 0, 1, 2
 PATHS = {
     0: "none", 1: "indexer_generic", 2: "indexer_scan_mfma", 3: "indexer_prefill_mfma", 4: "indexer_topk_fused",
     10: "topk_copy", 11: "topk_radix", 12: "topk_radix_reg", 13: "topk_radix_staged", 20: "mla_generic", 21: "mla_mfma", 22: "mla_mfma_split",
-    30: "mha_mfma", 31: "mha_mfma_masked", 40: "cache_write", 41: "quantize",
+    30: "mha_mfma", 31: "mha_mfma_masked", 40: "cache_write", 41: "quantize", 42: "project",
 }
 
 EXPORTS = [
@@ -31,6 +31,7 @@ EXPORTS = [
     "dsa_dense_mla_workspace_size", "dsa_dense_mla_prefill",
     "dsa_expanded_mha_workspace_size", "dsa_expanded_mha_prefill",
     "dsa_indexer_cache_write", "dsa_latent_cache_write", "dsa_e4m3_quantize",
+    "dsa_indexer_key_project", "dsa_indexer_query_project", "dsa_indexer_projection_workspace_size",
 ]
 
 
@@ -101,6 +102,13 @@ def load():
     lib.dsa_latent_cache_write.argtypes = [vp, i32, i32, vp, vp, i32, vp, i64, i32, i32, vp, vp]
     lib.dsa_e4m3_quantize.restype = i32
     lib.dsa_e4m3_quantize.argtypes = [vp, i64, vp, vp]
+    lib.dsa_indexer_key_project.restype = i32
+    lib.dsa_indexer_key_project.argtypes = [vp, vp, i32, i32, i32, vp, vp, i32, vp, i64, i32, i32, vp, vp, vp, sz,
+                                            vp]
+    lib.dsa_indexer_query_project.restype = i32
+    lib.dsa_indexer_query_project.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.dsa_indexer_projection_workspace_size.restype = sz
+    lib.dsa_indexer_projection_workspace_size.argtypes = [i32, i32]
     _lib = lib
     return lib
 
@@ -401,3 +409,62 @@ def e4m3_quantize(x, out=None, stream=None):
     st = load().dsa_e4m3_quantize(_p(x), x.numel(), _p(out), _stream(stream))
     _check("dsa_e4m3_quantize", st)
     return out
+
+
+def indexer_projection_workspace_size(rows, d) -> int:
+    return int(load().dsa_indexer_projection_workspace_size(rows, d))
+
+
+def _proj_ws(rows, d, ws, device):
+    if ws is False:
+        return None   # no workspace: the unsplit launch
+    if ws is None:
+        need = indexer_projection_workspace_size(rows, d)
+        ws = torch.empty(need, dtype=torch.uint8, device=device) if need else None
+    return ws
+
+
+def indexer_key_project(h, w_k, seq, pos, page_table, k_cache, k_scale, ws=None, stream=None):
+    """Keys k = h w_k^T (h [n_tok, d] bf16, w_k [128, d] bf16, the [out, in] layout of a linear
+    layer), quantised per token into the paged key cache (k_cache [P, page, 128] uint8, k_scale
+    [P, page] f32) at the tokens' (seq, pos) (int32 [n_tok]). ws: uint8 workspace (allocated here
+    when None; False runs the unsplit launch)."""
+    _need(h, "h", torch.bfloat16, 2)
+    _need(w_k, "w_k", torch.bfloat16, 2)
+    _need(seq, "seq", torch.int32, 1)
+    _need(pos, "pos", torch.int32, 1)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(k_cache, "k_cache", torch.uint8, 3)
+    _need(k_scale, "k_scale", torch.float32, 2)
+    n_tok, d = h.shape
+    if w_k.shape[1] != d or seq.numel() != n_tok or pos.numel() != n_tok:
+        raise ValueError("inconsistent key projection shapes")
+    ws = _proj_ws(n_tok, d, ws, h.device)
+    st = load().dsa_indexer_key_project(_p(h), _p(w_k), n_tok, d, w_k.shape[0], _p(seq), _p(pos), page_table.shape[0],
+                                        _p(page_table), page_table.shape[1], k_cache.shape[1], k_cache.shape[0],
+                                        _p(k_cache), _p(k_scale), _p(ws), 0 if ws is None else ws.numel(),
+                                        _stream(stream))
+    _check("dsa_indexer_key_project", st)
+
+
+def indexer_query_project(c_q, w_q, h, w_w, Hi, Di, q8=None, w=None, ws=None, stream=None):
+    """Indexer queries q8 = E4M3(c_q w_q^T) [rows, Hi, Di] (uint8 codes, no scale) and head weights
+    w = h w_w^T [rows, Hi] f32. c_q [rows, d_cq], w_q [Hi * Di, d_cq], h [rows, d], w_w [Hi, d], all
+    bf16. Returns (q8, w)."""
+    for t, name in ((c_q, "c_q"), (w_q, "w_q"), (h, "h"), (w_w, "w_w")):
+        _need(t, name, torch.bfloat16, 2)
+    rows, d_cq = c_q.shape
+    d = h.shape[1]
+    if h.shape[0] != rows or w_q.shape != (Hi * Di, d_cq) or w_w.shape != (Hi, d):
+        raise ValueError("inconsistent query projection shapes")
+    if q8 is None:
+        q8 = torch.empty(rows, Hi, Di, dtype=torch.uint8, device=c_q.device)
+    if w is None:
+        w = torch.empty(rows, Hi, dtype=torch.float32, device=c_q.device)
+    _need(q8, "q8", torch.uint8, 3)
+    _need(w, "w", torch.float32, 2)
+    ws = _proj_ws(rows, d, ws, c_q.device)
+    st = load().dsa_indexer_query_project(_p(c_q), _p(w_q), _p(h), _p(w_w), rows, d_cq, d, Hi, Di, _p(q8), _p(w),
+                                          _p(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check("dsa_indexer_query_project", st)
+    return q8, w

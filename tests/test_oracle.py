@@ -650,3 +650,59 @@ def test_latent_cache_write_places_rows(oracle_lib):
         r = pt[seq[t], pos[t] // 64] * 64 + pos[t] % 64
         np.testing.assert_array_equal(flat[r], rows[t])
     assert np.count_nonzero(flat.any(axis=1)) == 5
+
+
+# ---------------------------------------------------------------- the indexer's projections
+
+
+def _bf16_rand(rng, *shape, scale=1.0):
+    return workloads.bf16_bits(torch.from_numpy((rng.standard_normal(shape) * scale).astype(np.float32)))
+
+
+def _f64_linear(x_bits, w_bits):
+    # a linear layer with [out, in] weights, in float64 (a library matmul), rounded once to float32
+    return (_dec_bf16(x_bits) @ _dec_bf16(w_bits).T).to(torch.float32).numpy()
+
+
+def test_key_projection_is_a_linear_layer_then_the_cache_write(oracle_lib):
+    """[DSA-blog] "Lightning Indexer": k_j from h_j. The oracle's keys equal torch's float64 matmul
+    rounded to float32 (within one ulp: the two sum in different orders), and what lands in the
+    paged cache equals the oracle's cache write of those keys (pinned against torch's FP8 codes)."""
+    rng = np.random.default_rng(31)
+    n_tok, d = 37, 192
+    h = _bf16_rand(rng, n_tok, d)
+    w_k = _bf16_rand(rng, 128, d, scale=1 / math.sqrt(d))
+    seq = np.zeros(n_tok, np.int32)
+    pos = rng.permutation(n_tok).astype(np.int32)
+    pt = np.array([[2, 0, 1]], np.int32)
+    kc = np.full((3, 64, 128), 0xAA, np.uint8)
+    ks = np.full((3, 64), -1.0, np.float32)
+    k, skipped = oracle_lib.indexer_key_project(h, w_k, seq, pos, pt, 64, kc, ks)
+    assert skipped == 0
+    ref = _f64_linear(h, w_k)
+    np.testing.assert_array_max_ulp(k, ref, maxulp=1)
+    kc2 = np.full_like(kc, 0xAA)
+    ks2 = np.full_like(ks, -1.0)
+    oracle_lib.indexer_cache_write(k, seq, pos, pt, 64, kc2, ks2)
+    np.testing.assert_array_equal(kc, kc2)
+    np.testing.assert_array_equal(ks, ks2)
+    # a transposed weight or a dropped term would move the keys far beyond one ulp
+    assert not np.allclose(k, _f64_linear(h[:, ::-1].copy(), w_k), rtol=1e-3)
+
+
+def test_query_projection_codes_and_head_weights(oracle_lib):
+    """[DSA-blog] "Lightning Indexer": the query heads from the MLA query latent, the head weights
+    from h_t. q before coding and w equal torch's float64 matmuls rounded to float32 (one ulp), and
+    the codes equal torch's float8_e4m3fn conversion of q (every |q| here is below 448)."""
+    rng = np.random.default_rng(32)
+    rows, d_cq, d, Hi, Di = 9, 128, 192, 4, 32
+    c_q = _bf16_rand(rng, rows, d_cq)
+    w_q = _bf16_rand(rng, Hi * Di, d_cq, scale=1 / math.sqrt(d_cq))
+    h = _bf16_rand(rng, rows, d)
+    w_w = _bf16_rand(rng, Hi, d, scale=1 / math.sqrt(d))
+    q8, w, q = oracle_lib.indexer_query_project(c_q, w_q, h, w_w, Hi, Di)
+    np.testing.assert_array_max_ulp(q.reshape(rows, -1), _f64_linear(c_q, w_q), maxulp=1)
+    np.testing.assert_array_max_ulp(w, _f64_linear(h, w_w), maxulp=1)
+    assert np.abs(q).max() < 448
+    codes = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(q8, codes)
