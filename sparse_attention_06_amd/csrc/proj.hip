@@ -52,7 +52,18 @@ struct ProjArgs {
   // split-K: K range of blockIdx.z is [z * k_split, (z + 1) * k_split); partials in ws
   int k_split;
   float* ws;
+  int tiles_m, tiles;  // output tiles (row tiles fastest), dealt out per XCD by tile_of()
 };
+
+// Workgroups are dispatched to the 8 XCDs round robin. The padded 1-D grid gives each XCD a
+// contiguous range of tiles, row tiles fastest, so the row tiles that share a weight (column)
+// tile run on one XCD and read it once through its L2. -1 for the padding.
+__device__ __forceinline__ int tile_of(const ProjArgs& p) {
+  const int per = (int)gridDim.x >> 3;
+  const int t = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  return t < p.tiles ? t : -1;
+}
+static inline dim3 tile_grid(int tiles, int z = 1) { return dim3(8 * ((tiles + 7) / 8), 1, z); }
 
 // kTM: rows per tile. 128: wave w owns rows 32w.. and all 128 columns; 32 (small batches, so the
 // grid covers the GPU): the 4 waves share the 32 rows and wave w owns columns 32w..32w+31.
@@ -63,7 +74,9 @@ __global__ void __launch_bounds__(256) proj_gemm_kernel(ProjArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kPTileBytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane & 31, half = lane >> 5;
-  const int m0 = blockIdx.x * kTM, n0 = blockIdx.y * kPN;
+  const int tile = tile_of(p);
+  if (tile < 0) return;
+  const int m0 = (tile % p.tiles_m) * kTM, n0 = (tile / p.tiles_m) * kPN;
   const int kbeg = kEpi == kEpiPartial ? blockIdx.z * p.k_split : 0;
   const int kend = kEpi == kEpiPartial ? min(p.K, kbeg + p.k_split) : p.K;
   const int wrow = kTM == 128 ? 32 * wave : 0;       // the wave's first row within the tile
@@ -212,7 +225,14 @@ __global__ void __launch_bounds__(256) proj_reduce_kernel(ProjArgs p, int kz) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= MN) return;
     float sum = 0.f;
-    for (int z = 0; z < kz; ++z) sum += p.ws[z * MN + i];
+    for (int z0 = 0; z0 < kz; z0 += 4) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = z0 + u < kz ? p.ws[(z0 + u) * MN + i] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (z0 + u < kz) sum += v[u];
+    }
     p.f32[i] = sum;
     return;
   }
@@ -222,10 +242,22 @@ __global__ void __launch_bounds__(256) proj_reduce_kernel(ProjArgs p, int kz) {
   const bool live = t < p.M;
   const int tc = live ? t : p.M - 1;  // idle groups re-read the last token and store nothing
   float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int z = 0; z < kz; ++z) {
-    const float4* src = (const float4*)(p.ws + z * MN + (int64_t)tc * 128 + 8 * j);
-    const float4 a = src[0], b = src[1];
-    x[0] += a.x; x[1] += a.y; x[2] += a.z; x[3] += a.w; x[4] += b.x; x[5] += b.y; x[6] += b.z; x[7] += b.w;
+  for (int z0 = 0; z0 < kz; z0 += 4) {
+    // four partial blocks' loads issued together, then added in order of z
+    float4 a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int z = z0 + u < kz ? z0 + u : kz - 1;
+      const float4* src = (const float4*)(p.ws + z * MN + (int64_t)tc * 128 + 8 * j);
+      a[u] = src[0];
+      b[u] = src[1];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (z0 + u >= kz) break;
+      x[0] += a[u].x; x[1] += a[u].y; x[2] += a[u].z; x[3] += a[u].w;
+      x[4] += b[u].x; x[5] += b[u].y; x[6] += b[u].z; x[7] += b[u].w;
+    }
   }
   float m = 0.f;
 #pragma unroll
@@ -258,7 +290,8 @@ static int proj_plan(int M, int N, int K, int* k_split) {
   const int kb = K / kPK;
   *k_split = K;
   if (tiles >= 128 || kb < 2) return 1;
-  const int want = 256 / tiles < kb ? 256 / tiles : kb;
+  int want = 256 / tiles < kb ? 256 / tiles : kb;
+  want = want > 16 ? 16 : want;  // at most 16 partial blocks: their write and re-read stay small
   if (want < 2) return 1;
   const int per = (kb + want - 1) / want;  // K blocks per range
   *k_split = per * kPK;
@@ -281,13 +314,15 @@ hipError_t launch_indexer_key_project(const uint16_t* h, const uint16_t* w_k, in
   const int kz = proj_plan(n_tok, 128, d, &ks);
   if (kz > 1 && ws && ws_bytes >= proj_ws_bytes(n_tok, 128, d)) {
     p.k_split = ks; p.ws = (float*)ws;
-    hipLaunchKernelGGL((proj_gemm_kernel<kEpiPartial, 32>), dim3((n_tok + 31) / 32, 1, kz), dim3(256), 0, stream, p);
+    p.tiles_m = (n_tok + 31) / 32; p.tiles = p.tiles_m;
+    hipLaunchKernelGGL((proj_gemm_kernel<kEpiPartial, 32>), tile_grid(p.tiles, kz), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(proj_reduce_kernel<kEpiKey>, dim3((n_tok + 15) / 16), dim3(256), 0, stream, p, kz);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((proj_gemm_kernel<kEpiKey, 128>), dim3((n_tok + kPM - 1) / kPM, 1), dim3(256), 0, stream, p);
+  p.tiles_m = (n_tok + kPM - 1) / kPM; p.tiles = p.tiles_m;
+  hipLaunchKernelGGL((proj_gemm_kernel<kEpiKey, 128>), tile_grid(p.tiles), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -297,12 +332,12 @@ hipError_t launch_indexer_query_project(const uint16_t* c_q, const uint16_t* w_q
   ProjArgs p{};
   p.a = c_q; p.b = w_q; p.M = rows; p.N = n_q; p.K = d_cq; p.q8 = q8;
   // small batches take 32-row tiles, so that the column tiles spread over the GPU
-  if (rows <= 512)
-    hipLaunchKernelGGL((proj_gemm_kernel<kEpiQuery, 32>), dim3((rows + 31) / 32, (n_q + kPN - 1) / kPN), dim3(256), 0,
-                       stream, p);
+  const int tm = rows <= 512 ? 32 : kPM;
+  p.tiles_m = (rows + tm - 1) / tm; p.tiles = p.tiles_m * ((n_q + kPN - 1) / kPN);
+  if (tm == 32)
+    hipLaunchKernelGGL((proj_gemm_kernel<kEpiQuery, 32>), tile_grid(p.tiles), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((proj_gemm_kernel<kEpiQuery, 128>), dim3((rows + kPM - 1) / kPM, (n_q + kPN - 1) / kPN),
-                       dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((proj_gemm_kernel<kEpiQuery, 128>), tile_grid(p.tiles), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   ProjArgs pw{};
@@ -311,16 +346,16 @@ hipError_t launch_indexer_query_project(const uint16_t* c_q, const uint16_t* w_q
   const int kz = proj_plan(rows, n_w, d, &ks);
   if (kz > 1 && ws && ws_bytes >= proj_ws_bytes(rows, n_w, d)) {
     pw.k_split = ks; pw.ws = (float*)ws;
-    hipLaunchKernelGGL((proj_gemm_kernel<kEpiPartial, 32>), dim3((rows + 31) / 32, (n_w + kPN - 1) / kPN, kz),
-                       dim3(256), 0, stream, pw);
+    pw.tiles_m = (rows + 31) / 32; pw.tiles = pw.tiles_m * ((n_w + kPN - 1) / kPN);
+    hipLaunchKernelGGL((proj_gemm_kernel<kEpiPartial, 32>), tile_grid(pw.tiles, kz), dim3(256), 0, stream, pw);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n = (int64_t)rows * n_w;
     hipLaunchKernelGGL(proj_reduce_kernel<kEpiF32>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, pw, kz);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((proj_gemm_kernel<kEpiF32, 128>), dim3((rows + kPM - 1) / kPM, (n_w + kPN - 1) / kPN), dim3(256),
-                     0, stream, pw);
+  pw.tiles_m = (rows + kPM - 1) / kPM; pw.tiles = pw.tiles_m * ((n_w + kPN - 1) / kPN);
+  hipLaunchKernelGGL((proj_gemm_kernel<kEpiF32, 128>), tile_grid(pw.tiles), dim3(256), 0, stream, pw);
   return hipGetLastError();
 }
 
