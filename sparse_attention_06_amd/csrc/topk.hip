@@ -301,18 +301,21 @@ __device__ __forceinline__ void reg_select(const uint32_t (&key)[kRegE], uint32_
 // Stage the selected keys in input order: every valid key above tau and the first `remaining`
 // keys equal to tau (every valid key when take_all). Their positions (pos_of(e) for this thread's
 // key e) and, with_keys, their order keys land in sh.cand_pos / sh.cand_key at their output
-// slots; returns how many were selected.
-template <class PosOf>
+// slots; returns how many were selected. Each thread first forms two 16-bit masks of its keys
+// (above tau, equal to tau); without keys to stage it then visits only the set bits of its
+// selection (about one key in eight at k = 2048 over 16384), not all sixteen keys.
+template <bool with_keys, class PosOf>
 __device__ __forceinline__ uint32_t stage_selected(const uint32_t (&key)[kRegE], PosOf pos_of, uint32_t vmask, bool take_all,
-                                   uint32_t tau, uint32_t remaining, bool with_keys, TopkLds& sh, int wave,
-                                   int lane) {
-  uint32_t gt = 0, eq = 0;
+                                   uint32_t tau, uint32_t remaining, TopkLds& sh, int wave, int lane) {
+  uint32_t gtm = 0, eqm = 0;
 #pragma unroll
   for (int e = 0; e < kRegE; ++e) {
-    const bool v = (vmask >> e) & 1u;
-    gt += (v && (take_all || key[e] > tau)) ? 1u : 0u;
-    eq += (v && !take_all && key[e] == tau) ? 1u : 0u;
+    gtm |= (key[e] > tau ? 1u : 0u) << e;
+    eqm |= (key[e] == tau ? 1u : 0u) << e;
   }
+  gtm = take_all ? vmask : (gtm & vmask);
+  eqm = take_all ? 0u : (eqm & vmask);
+  const uint32_t gt = (uint32_t)__builtin_popcount(gtm), eq = (uint32_t)__builtin_popcount(eqm);
   const uint32_t gi = wave_incl_scan(gt), ei = wave_incl_scan(eq);
   __syncthreads();  // the selection may still read the candidate buffers and the wave totals
   if (lane == 63) { sh.wtot[wave][0] = gi; sh.wtot[wave][1] = ei; }
@@ -323,18 +326,30 @@ __device__ __forceinline__ uint32_t stage_selected(const uint32_t (&key)[kRegE],
     gall += sh.wtot[w][0];
     eall += sh.wtot[w][1];
   }
-  uint32_t slot = gb + min(eb, remaining), eq_rank = eb;
+  // the keys equal to tau this thread takes: the first (remaining - eb) of them, in key order
+  const uint32_t allow = remaining > eb ? remaining - eb : 0u;
+  uint32_t eqt = eqm;
+  if (allow < eq) {
+    eqt = 0u;
+    uint32_t m = eqm;
+    for (uint32_t i = 0; i < allow; ++i) {
+      eqt |= m & (0u - m);  // lowest set bit
+      m &= m - 1u;
+    }
+  }
+  const uint32_t sel = gtm | eqt;
+  uint32_t slot = gb + min(eb, remaining);
+  if (with_keys) {
 #pragma unroll
-  for (int e = 0; e < kRegE; ++e) {
-    if ((vmask >> e) & 1u) {
-      bool take = take_all || key[e] > tau;
-      if (!take_all && key[e] == tau) { take = eq_rank < remaining; ++eq_rank; }
-      if (take) {
+    for (int e = 0; e < kRegE; ++e) {
+      if ((sel >> e) & 1u) {
         sh.cand_pos[slot] = pos_of(e);
-        if (with_keys) sh.cand_key[slot] = key[e];
+        sh.cand_key[slot] = key[e];
         ++slot;
       }
     }
+  } else {
+    for (uint32_t m = sel; m; m &= m - 1u) sh.cand_pos[slot++] = pos_of(__builtin_ctz(m));
   }
   __syncthreads();
   return gall + min(eall, remaining);
@@ -374,10 +389,11 @@ __global__ void __launch_bounds__(kTopkThreads) topk_stage_kernel(TopkStageArgs 
   uint32_t key[kRegE], vmask = 0;
   uint32_t* const hist0 = kSrcScores ? (a.hist0 ? a.hist0 + ((int64_t)r * gridDim.x + c) * kRegBins : nullptr)
                                      : (a.mhist ? a.mhist + (int64_t)r * kRegBins : nullptr);
-  reg_select_init(sh, tid, hist0);
   if (kSrcScores) {
     // this thread's positions: base .. base + 15. The row is read before q_pos is known (every
-    // position below max_ctx lies inside the row), so the two memory latencies overlap.
+    // position below max_ctx lies inside the row), and both before the first-digit histogram is
+    // staged, so the memory latencies overlap.
+    int n = a.q_pos[r] + 1;
     const float* row = a.scores + (int64_t)r * a.ld_scores;
     const int base = kRegKeys * c + kRegE * tid;
     float f[kRegE];
@@ -391,7 +407,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_stage_kernel(TopkStageArgs 
 #pragma unroll
       for (int e = 0; e < kRegE; ++e) f[e] = base + e < a.max_ctx ? row[base + e] : 0.f;
     }
-    int n = a.q_pos[r] + 1;
+    reg_select_init(sh, tid, hist0);
     n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
 #pragma unroll
     for (int e = 0; e < kRegE; ++e) {
@@ -417,8 +433,10 @@ __global__ void __launch_bounds__(kTopkThreads) topk_stage_kernel(TopkStageArgs 
       for (int e = 0; e < kRegE; ++e) key[e] = g0 + e < total ? a.in_key[rb + g0 + e] : 0u;
     }
     const int ch0 = g0 / a.k, ch1 = (g0 + kRegE - 1) / a.k;
+    const int n0 = (ch0 == ch1 && ch0 < a.in_chunks) ? cnt[ch0] : 0;
+    reg_select_init(sh, tid, hist0);
     if (ch0 == ch1) {  // the thread's slots share one chunk (always when k is a multiple of 16)
-      const int n0 = ch0 < a.in_chunks ? cnt[ch0] : 0, e_end = ch0 * a.k + n0 - g0;
+      const int e_end = ch0 * a.k + n0 - g0;
 #pragma unroll
       for (int e = 0; e < kRegE; ++e) vmask |= (e < e_end ? 1u : 0u) << e;
     } else {
@@ -468,8 +486,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_stage_kernel(TopkStageArgs 
   int obase = kSrcScores ? kRegKeys * c + kRegE * tid : kRegE * tid;
   asm volatile("" : "+v"(obase));  // opaque: the 16 values are formed when they are stored
   const int64_t rb = (int64_t)r * a.in_chunks * a.k;
-  const uint32_t nsel = stage_selected(key, [&](int e) { return (uint32_t)(obase + e); }, vmask, take_all, tau,
-                                       remaining, !kFinal, sh, wave, lane);
+  const uint32_t nsel = stage_selected<!kFinal>(key, [&](int e) { return (uint32_t)(obase + e); }, vmask, take_all, tau,
+                                                remaining, sh, wave, lane);
   auto pos_at = [&](int i) { return kSrcScores ? (int32_t)sh.cand_pos[i] : a.in_pos[rb + sh.cand_pos[i]]; };
   if (kFinal) {
     // all of a thread's (at most kCandCap / kTopkThreads) reads are issued before its stores
