@@ -124,7 +124,11 @@ constexpr int kLdsBytes = kFlagOff + 16;
 // Positions per pass of the repeat filter: a bitmap of 128 KB in the tile buffers, which are idle
 // while a list chunk is resolved.
 constexpr int kDedupWindow = 1 << 20;
+// Staged prologue: an index row of at most kListCap entries and a page-table row of at most
+// kStagePages pages are copied to the start of the tile buffers before any gather is issued.
+constexpr int kStagePages = 2048;
 static_assert(kDedupWindow / 8 <= kNBuf * kTileBytes, "repeat filter bitmap in the tile buffers");
+static_assert(4 * (kListCap + kStagePages) <= kTileBytes, "staged index and page-table rows in tile buffer 0");
 static_assert(kH * kDv * 2 <= kLdsBytes, "output staging");
 static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
 constexpr float kLog2e = 1.4426950408889634f;
@@ -400,31 +404,104 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
                     32 * (G & 1) + 8 * (j & 3);
   }
 
-  // The query is loaded first, so that its latency overlaps the index-list resolve (two dependent
-  // loads) below: the latent part as this wave's B operands in registers, the rope part of all
-  // heads into LDS (head h keeps chunk c at c ^ rope_swz(h) of its 128-byte row).
-  {
-    const uint16_t* qh = a.q + ((int64_t)r * kH + 32 * wave + hl) * kDqk + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < kDv / 16; ++ks) qf[ks] = *(const bf16x8*)(qh + 16 * ks);
-    const int tid = 64 * wave + lane;
-#pragma unroll
-    for (int j = 0; j < kH * 8 / 256; ++j) {
-      const int i = tid + 256 * j, h = i >> 3, c = i & 7;
-      const i32x4 v = *(const i32x4*)(a.q + ((int64_t)r * kH + h) * kDqk + kDv + 8 * c);
-      *(__attribute__((address_space(3))) i32x4*)(lds + kQRopeOff + h * kRopeBytes + 16 * (c ^ rope_swz(h))) = v;
-    }
-  }
   // S_t is a set: only lists that are not a strictly ascending run of visible entries from entry 0
   // up to this split's end can repeat a position into this split; those go through the filter.
   const int* irow = a.idx ? a.idx + (int64_t)r * a.ld_idx : nullptr;
-  const bool dedupe = irow && block_needs_dedupe(irow, t, 1, e_end, (int*)(smem + kFlagOff), wave, lane);
+  const int tid = 64 * wave + lane;
+  const int ps = a.kv.page_size;
+  // page-table entries a visible position of this row can use
+  const int np = (seq >= 0 && t >= 0) ? min(a.kv.ld_pt, t / ps + 1) : 0;
+  // Staged prologue (index lists of at most kListCap entries over at most kStagePages pages):
+  // the index row up to this split's end, the sequence's page-table row and the rope part of the
+  // query are loaded first, then the latent part of the query; the first three are staged in
+  // LDS as soon as they land (vector loads complete in issue order, so their wait leaves the
+  // query's 128 KB in flight), and the repeat check and the resolve below run from LDS while the
+  // query arrives. Otherwise the query is loaded first and the resolve reads the index list and
+  // the page table from memory (any load issued after the query's 147 KB waits for all of it).
+  const bool staged = irow && e_end <= kListCap && np <= kStagePages;
+  int* st_raw = (int*)smem;                  // staged index row [0, e_end)
+  int* st_pt = (int*)(smem + 4 * kListCap);  // staged page-table row [0, np)
+  auto load_query_latent = [&]() {
+    const uint16_t* qh = a.q + ((int64_t)r * kH + 32 * wave + hl) * kDqk + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < kDv / 16; ++ks) qf[ks] = *(const bf16x8*)(qh + 16 * ks);
+  };
+  // the rope part of all heads into LDS: head h keeps chunk c at c ^ rope_swz(h) of its 128-byte row
+  auto rope_src = [&](int j) {
+    const int i = tid + 256 * j, h = i >> 3, c = i & 7;
+    return (const i32x4*)(a.q + ((int64_t)r * kH + h) * kDqk + kDv + 8 * c);
+  };
+  auto rope_dst = [&](int j) {
+    const int i = tid + 256 * j, h = i >> 3, c = i & 7;
+    return (__attribute__((address_space(3))) i32x4*)(lds + kQRopeOff + h * kRopeBytes + 16 * (c ^ rope_swz(h)));
+  };
+  bool dedupe = false;
+  if (staged) {
+    int raw[kListCap / 256], ptv[kStagePages / 256];
+    i32x4 qr[kH * 8 / 256];
+#pragma unroll
+    for (int u = 0; u < kListCap / 256; ++u) {
+      const int e = tid + 256 * u;
+      raw[u] = e < e_end ? irow[e] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kStagePages / 256; ++u) {
+      const int pg = tid + 256 * u;
+      ptv[u] = pg < np ? a.kv.page_table[(int64_t)seq * a.kv.ld_pt + pg] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kH * 8 / 256; ++j) qr[j] = *rope_src(j);
+    load_query_latent();
+#pragma unroll
+    for (int u = 0; u < kListCap / 256; ++u)
+      if (tid + 256 * u < e_end) st_raw[tid + 256 * u] = raw[u];
+#pragma unroll
+    for (int u = 0; u < kStagePages / 256; ++u)
+      if (tid + 256 * u < np) st_pt[tid + 256 * u] = ptv[u];
+#pragma unroll
+    for (int j = 0; j < kH * 8 / 256; ++j) *rope_dst(j) = qr[j];
+    __syncthreads();
+    // the repeat check of block_needs_dedupe, over the staged row
+    bool bad = false;
+#pragma unroll
+    for (int u = 0; u < kListCap / 256; ++u) {
+      const int e = tid + 256 * u;
+      if (e >= 1 && e < e_end) {
+        const int c = st_raw[e], pv = st_raw[e - 1];
+        const bool vc = c >= 0 && c <= t, vp = pv >= 0 && pv <= t;
+        bad |= vc && !(vp && pv < c);
+      }
+    }
+    int* flags = (int*)(smem + kFlagOff);
+    const bool any = __any(bad);
+    if (lane == 0) flags[wave] = any ? 1 : 0;
+    __syncthreads();
+    dedupe = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
+  } else {
+    load_query_latent();
+#pragma unroll
+    for (int j = 0; j < kH * 8 / 256; ++j) *rope_dst(j) = *rope_src(j);
+    dedupe = irow && block_needs_dedupe(irow, t, 1, e_end, (int*)(smem + kFlagOff), wave, lane);
+  }
   for (int cb = e_begin; cb < e_end; cb += kListCap) {
     const int ce = min(e_end, cb + kListCap);
     __syncthreads();  // the previous chunk is done with the list and the buffers
+    if (staged) {
+      // the whole list is one chunk: resolve it from the staged rows. A position j <= t with
+      // j / ps < ld_pt has j / ps < np, so it lies on a staged page; np = 0 (nothing staged) for a
+      // row without a page-table row.
+      for (int e = cb + (int)threadIdx.x; e < ce; e += 256) {
+        const int j = st_raw[e];
+        const bool vis = j >= 0 && j <= t && j / ps < np;
+        const int pg = vis ? st_pt[j / ps] : -1;
+        list[e - cb] = (pg >= 0 && pg < a.kv.num_pages) ? pg * ps + j % ps : -1;
+      }
+      // the repeat filter's bitmap overwrites the staged rows
+      if (dedupe) __syncthreads();
+    }
     // eight entries per thread at a time: all their index loads, then all their page-table
     // loads, so the resolve costs two memory latencies rather than two per entry
-    for (int e0 = cb + threadIdx.x; e0 < ce; e0 += 8 * 256) {
+    for (int e0 = cb + (int)threadIdx.x; !staged && e0 < ce; e0 += 8 * 256) {
       int jj[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -471,6 +548,12 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
       }
     }
     __syncthreads();
+    // Settle every vector-memory operation the compiler issued so far (the query loads are
+    // already consumed; register spills of the prologue may still be in flight) before the first
+    // gathers: its wait-count pass then sees nothing pending, and inserts no wait inside the tile
+    // loop that would also drain the gathers in flight (a store's data register rewritten in the
+    // loop would otherwise take one).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt left at their maxima
     // vm[d] = valid-entry mask of tile it + d (0 past the end); only constant indices, so the
     // masks stay in scalar registers
     uint32_t vm[kNBuf];

@@ -33,6 +33,7 @@ PAGE = 64
 ROW_BYTES = 1152
 NK = 32            # positions per tile
 LIST_CAP = 2048    # resolved entries per chunk
+STAGE_PAGES = 2048 # page-table entries the staged prologue copies to LDS
 NBUF = 3           # tile buffers: two tiles in flight
 
 
@@ -61,15 +62,31 @@ def model_workgroup(row, t, seq, page_table, num_pages, k, splits, sp, check_pag
     e_end = min(k, e_begin + per)
     cache_bytes = num_pages * PAGE * ROW_BYTES
     dedupe = needs_dedupe(row, t, e_end)
+    # staged prologue: the index row [0, e_end) and the page-table entries a visible position can
+    # use ([0, n_pt)) are copied to LDS first, when they fit; the resolve then reads only those
+    n_pt = min(ld_pt, t // PAGE + 1) if (seq >= 0 and t >= 0) else 0
+    staged = e_end <= LIST_CAP and n_pt <= STAGE_PAGES
+    if staged:
+        assert e_end <= LIST_CAP and 4 * (LIST_CAP + STAGE_PAGES) <= 45056
+        st_raw = [int(row[e]) for e in range(e_end)]
+        st_pt = [int(page_table[seq, p]) for p in range(n_pt)]
     kept = []
     for cb in range(e_begin, e_end, LIST_CAP):
         ce = min(e_end, cb + LIST_CAP)
         n_list = ce - cb
         lst = np.full(LIST_CAP, -(10 ** 9), np.int64)   # stale LDS: never a valid row id
         for e in range(cb, ce):
-            j = int(row[e])
-            vis = 0 <= j <= t and j // PAGE < ld_pt
-            pg = int(page_table[seq, j // PAGE]) if vis else -1
+            if staged:
+                assert cb == e_begin and 0 <= e < e_end
+                j = st_raw[e]
+                vis = 0 <= j <= t and j // PAGE < n_pt
+                if vis:
+                    assert 0 <= j // PAGE < len(st_pt)
+                pg = st_pt[j // PAGE] if vis else -1
+            else:
+                j = int(row[e])
+                vis = seq >= 0 and 0 <= j <= t and j // PAGE < ld_pt
+                pg = int(page_table[seq, j // PAGE]) if vis else -1
             ok = 0 <= pg < num_pages if check_page else pg >= 0
             lst[e - cb] = pg * PAGE + j % PAGE if ok else -1
         if dedupe:
@@ -148,6 +165,8 @@ def attended_positions(row, t, seq, page_table, num_pages, k, rows_total=1, deco
 def expected_set(row, t, seq, page_table, num_pages):
     ld_pt = page_table.shape[1]
     out = set()
+    if seq < 0:
+        return out
     for j in row:
         j = int(j)
         if 0 <= j <= t and j // PAGE < ld_pt and 0 <= page_table[seq, j // PAGE] < num_pages:
@@ -209,3 +228,31 @@ def test_model_catches_a_planted_row_id_past_the_cache():
     assert kept == [] and expected_set(row, 100, 0, page_table, 2) == set()
     with pytest.raises(AssertionError):
         model_workgroup(row, 100, 0, page_table, 2, 64, 1, 0, check_page=False)
+
+
+@pytest.mark.parametrize("t,k,decode", [(40, 2048, True), (3000, 2048, False), (4500, 4096, False), (140000, 2048, False)])
+def test_row_without_a_page_table_row_gathers_nothing(t, k, decode):
+    """A row whose sequence id lies outside the table (seq = -1): nothing is staged or read from
+    the page table and no key is kept, in the staged prologue (short lists) and the other one."""
+    rng = np.random.default_rng(t + k)
+    ld_pt = (t + 1 + PAGE - 1) // PAGE
+    page_table = rng.permutation(ld_pt).reshape(1, ld_pt).astype(np.int64)
+    row = _case(rng, t, k, "ascending", ld_pt, ld_pt)
+    kept, _ = attended_positions(row, t, -1, page_table, ld_pt, k, 1, decode)
+    assert kept == []
+
+
+@pytest.mark.parametrize("t,k,ld_pt", [(3000, 2048, 20), (3000, 2048, 47), (140000, 2048, 2188), (140000, 2048, 3000)])
+def test_positions_past_the_page_table_and_rows_over_the_staged_pages(t, k, ld_pt):
+    """Page tables narrower than the row (positions on pages past ld_pt are not visible) and rows
+    on more pages than the staged prologue copies (t / 64 + 1 > 2048: the resolve reads the page
+    table from memory)."""
+    rng = np.random.default_rng(ld_pt)
+    num_pages = ld_pt + 2
+    page_table = rng.permutation(num_pages)[:ld_pt].reshape(1, ld_pt).astype(np.int64)
+    row = _case(rng, t, k, "invisible", ld_pt, num_pages)
+    for decode in (True, False):
+        kept, _ = attended_positions(row, t, 0, page_table, num_pages, k, 1, decode)
+        pos = [int(row[e]) for e in kept]
+        assert len(pos) == len(set(pos))
+        assert set(pos) == expected_set(row, t, 0, page_table, num_pages)
