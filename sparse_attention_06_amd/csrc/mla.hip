@@ -332,6 +332,200 @@ __device__ __forceinline__ f32x2 unpack_f16x2(uint32_t v) {
   return f32x2{(float)h[0], (float)h[1]};
 }
 
+// O^T += V^T P for one tile (the asm text of the PV step); D0..D8 are spliced in after MFMAs
+// 1, 4, ..., 25: the gathers of a later tile, or nothing.
+#define MLA_PV_ASM(D0, D1, D2, D3, D4, D5, D6, D7, D8) \
+  "ds_read_b64_tr_b16 v[224:225], %[ta]\n" \
+  "ds_read_b64_tr_b16 v[226:227], %[ta] offset:10272\n" \
+  "ds_read_b64_tr_b16 v[228:229], %[ta] offset:64\n" \
+  "ds_read_b64_tr_b16 v[230:231], %[ta] offset:10336\n" \
+  "ds_read_b64_tr_b16 v[232:233], %[ta] offset:128\n" \
+  "ds_read_b64_tr_b16 v[234:235], %[ta] offset:10400\n" \
+  "ds_read_b64_tr_b16 v[236:237], %[ta] offset:192\n" \
+  "ds_read_b64_tr_b16 v[238:239], %[ta] offset:10464\n" \
+  "ds_read_b64_tr_b16 v[240:241], %[ta] offset:256\n" \
+  "ds_read_b64_tr_b16 v[242:243], %[ta] offset:10528\n" \
+  "ds_read_b64_tr_b16 v[244:245], %[ta] offset:320\n" \
+  "ds_read_b64_tr_b16 v[246:247], %[ta] offset:10592\n" \
+  "ds_read_b64_tr_b16 v[248:249], %[ta] offset:384\n" \
+  "ds_read_b64_tr_b16 v[250:251], %[ta] offset:10656\n" \
+  "ds_read_b64_tr_b16 v[252:253], %[ta] offset:448\n" \
+  "ds_read_b64_tr_b16 v[254:255], %[ta] offset:10720\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o0], v[224:227], %[p0], %[o0]\n" \
+  "ds_read_b64_tr_b16 v[224:225], %[ta] offset:512\n" \
+  "ds_read_b64_tr_b16 v[226:227], %[ta] offset:10784\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o1], v[228:231], %[p0], %[o1]\n" \
+  D0 \
+  "ds_read_b64_tr_b16 v[228:229], %[ta] offset:576\n" \
+  "ds_read_b64_tr_b16 v[230:231], %[ta] offset:10848\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o2], v[232:235], %[p0], %[o2]\n" \
+  "ds_read_b64_tr_b16 v[232:233], %[ta] offset:640\n" \
+  "ds_read_b64_tr_b16 v[234:235], %[ta] offset:10912\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o3], v[236:239], %[p0], %[o3]\n" \
+  "ds_read_b64_tr_b16 v[236:237], %[ta] offset:704\n" \
+  "ds_read_b64_tr_b16 v[238:239], %[ta] offset:10976\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o4], v[240:243], %[p0], %[o4]\n" \
+  D1 \
+  "ds_read_b64_tr_b16 v[240:241], %[ta] offset:768\n" \
+  "ds_read_b64_tr_b16 v[242:243], %[ta] offset:11040\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o5], v[244:247], %[p0], %[o5]\n" \
+  "ds_read_b64_tr_b16 v[244:245], %[ta] offset:832\n" \
+  "ds_read_b64_tr_b16 v[246:247], %[ta] offset:11104\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o6], v[248:251], %[p0], %[o6]\n" \
+  "ds_read_b64_tr_b16 v[248:249], %[ta] offset:896\n" \
+  "ds_read_b64_tr_b16 v[250:251], %[ta] offset:11168\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o7], v[252:255], %[p0], %[o7]\n" \
+  D2 \
+  "ds_read_b64_tr_b16 v[252:253], %[ta] offset:960\n" \
+  "ds_read_b64_tr_b16 v[254:255], %[ta] offset:11232\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o8], v[224:227], %[p0], %[o8]\n" \
+  "ds_read_b64_tr_b16 v[224:225], %[ta] offset:20480\n" \
+  "ds_read_b64_tr_b16 v[226:227], %[ta] offset:30752\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o9], v[228:231], %[p0], %[o9]\n" \
+  "ds_read_b64_tr_b16 v[228:229], %[ta] offset:20544\n" \
+  "ds_read_b64_tr_b16 v[230:231], %[ta] offset:30816\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o10], v[232:235], %[p0], %[o10]\n" \
+  D3 \
+  "ds_read_b64_tr_b16 v[232:233], %[ta] offset:20608\n" \
+  "ds_read_b64_tr_b16 v[234:235], %[ta] offset:30880\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o11], v[236:239], %[p0], %[o11]\n" \
+  "ds_read_b64_tr_b16 v[236:237], %[ta] offset:20672\n" \
+  "ds_read_b64_tr_b16 v[238:239], %[ta] offset:30944\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o12], v[240:243], %[p0], %[o12]\n" \
+  "ds_read_b64_tr_b16 v[240:241], %[ta] offset:20736\n" \
+  "ds_read_b64_tr_b16 v[242:243], %[ta] offset:31008\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o13], v[244:247], %[p0], %[o13]\n" \
+  D4 \
+  "ds_read_b64_tr_b16 v[244:245], %[ta] offset:20800\n" \
+  "ds_read_b64_tr_b16 v[246:247], %[ta] offset:31072\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o14], v[248:251], %[p0], %[o14]\n" \
+  "ds_read_b64_tr_b16 v[248:249], %[ta] offset:20864\n" \
+  "ds_read_b64_tr_b16 v[250:251], %[ta] offset:31136\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o15], v[252:255], %[p0], %[o15]\n" \
+  "ds_read_b64_tr_b16 v[252:253], %[ta] offset:20928\n" \
+  "ds_read_b64_tr_b16 v[254:255], %[ta] offset:31200\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o0], v[224:227], %[p1], %[o0]\n" \
+  D5 \
+  "ds_read_b64_tr_b16 v[224:225], %[ta] offset:20992\n" \
+  "ds_read_b64_tr_b16 v[226:227], %[ta] offset:31264\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o1], v[228:231], %[p1], %[o1]\n" \
+  "ds_read_b64_tr_b16 v[228:229], %[ta] offset:21056\n" \
+  "ds_read_b64_tr_b16 v[230:231], %[ta] offset:31328\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o2], v[232:235], %[p1], %[o2]\n" \
+  "ds_read_b64_tr_b16 v[232:233], %[ta] offset:21120\n" \
+  "ds_read_b64_tr_b16 v[234:235], %[ta] offset:31392\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o3], v[236:239], %[p1], %[o3]\n" \
+  D6 \
+  "ds_read_b64_tr_b16 v[236:237], %[ta] offset:21184\n" \
+  "ds_read_b64_tr_b16 v[238:239], %[ta] offset:31456\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o4], v[240:243], %[p1], %[o4]\n" \
+  "ds_read_b64_tr_b16 v[240:241], %[ta] offset:21248\n" \
+  "ds_read_b64_tr_b16 v[242:243], %[ta] offset:31520\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o5], v[244:247], %[p1], %[o5]\n" \
+  "ds_read_b64_tr_b16 v[244:245], %[ta] offset:21312\n" \
+  "ds_read_b64_tr_b16 v[246:247], %[ta] offset:31584\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o6], v[248:251], %[p1], %[o6]\n" \
+  D7 \
+  "ds_read_b64_tr_b16 v[248:249], %[ta] offset:21376\n" \
+  "ds_read_b64_tr_b16 v[250:251], %[ta] offset:31648\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o7], v[252:255], %[p1], %[o7]\n" \
+  "ds_read_b64_tr_b16 v[252:253], %[ta] offset:21440\n" \
+  "ds_read_b64_tr_b16 v[254:255], %[ta] offset:31712\n" \
+  "s_waitcnt lgkmcnt(14)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o8], v[224:227], %[p1], %[o8]\n" \
+  "s_waitcnt lgkmcnt(12)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o9], v[228:231], %[p1], %[o9]\n" \
+  D8 \
+  "s_waitcnt lgkmcnt(10)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o10], v[232:235], %[p1], %[o10]\n" \
+  "s_waitcnt lgkmcnt(8)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o11], v[236:239], %[p1], %[o11]\n" \
+  "s_waitcnt lgkmcnt(6)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o12], v[240:243], %[p1], %[o12]\n" \
+  "s_waitcnt lgkmcnt(4)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o13], v[244:247], %[p1], %[o13]\n" \
+  "s_waitcnt lgkmcnt(2)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o14], v[248:251], %[p1], %[o14]\n" \
+  "s_waitcnt lgkmcnt(0)\n" \
+  "v_mfma_f32_32x32x16_bf16 %[o15], v[252:255], %[p1], %[o15]\n"
+
+// One latent-row gather of a later tile, in the PV step, skipped when %[dma] is 0: the row's
+// per-lane address is formed in the temporary pair (row id from an SGPR times 1152, plus the
+// lane base kv + 16 * lane), M0 is the row's LDS line. SCC is tested right before each branch
+// (the M0 add overwrites it).
+#define MLA_DMA_LAT(i, off) \
+  "s_cmp_lg_u32 %[dma], 0\n" \
+  "s_cbranch_scc0 1f\n" \
+  "v_mad_u64_u32 %[ga], vcc, %[rid" #i "], %[c1152], %[kvl]\n" \
+  "s_add_u32 m0, %[lm0], " #off "\n" \
+  "s_nop 0\n" \
+  "global_load_lds_dwordx4 %[ga], off\n" \
+  "1:\n"
+#define MLA_DMA_ROPE \
+  "s_cmp_lg_u32 %[dma], 0\n" \
+  "s_cbranch_scc0 1f\n" \
+  "s_mov_b32 m0, %[rm0]\n" \
+  "s_nop 0\n" \
+  "global_load_lds_dwordx4 %[rsrc], off\n" \
+  "1:\n"
+
+// Operands of the gathers of one tile issued by MLA_DMA_LAT / MLA_DMA_ROPE: wave w loads latent
+// rows 4i + w (i = 0..7) and the rope chunks of rows 8w + lane/8, as issue_tile does. Formed
+// right before the asm that uses them (a few VALU and SALU ops), so that nothing extra stays live
+// across the tile loop.
+struct DmaOps {
+  uint64_t kvl;       // kv + 16 * lane
+  uint32_t c1152;     // the row pitch in bytes, for v_mad_u64_u32
+  uint32_t rid[kRowsPerWave];
+  uint32_t lat_m0, rope_m0;
+  uint64_t rope_src;  // this lane's rope chunk
+};
+__device__ __forceinline__ DmaOps dma_ops(const uint8_t* __restrict__ kv_base, const lds_u8* buf, TileEntries te,
+                                          int wave, int lane) {
+  asm volatile("" : "+v"(lane));  // opaque copy: the lane values are formed per tile
+  DmaOps d;
+  d.kvl = (uint64_t)(uintptr_t)(kv_base + 16 * lane);
+  d.c1152 = kRowBytes;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) d.rid[i] = (uint32_t)__builtin_amdgcn_readlane(te.ent, 4 * i + wave);
+  d.lat_m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)buf + wave * (kLatStride + 64));
+  d.rope_m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(buf + kRopeOff + kRowsPerWave * wave * kRopeBytes));
+  const int my_slot = kRowsPerWave * wave + (lane >> 3);
+  d.rope_src = (uint64_t)(uintptr_t)(kv_base + (int64_t)te.my_ent * kRowBytes + kLatBytes + 16 * ((lane & 7) ^ rope_swz(my_slot)));
+  return d;
+}
+#define MLA_DMA_INPUTS(d, m) \
+  [dma] "s"(m), [kvl] "v"(d.kvl), [c1152] "v"(d.c1152), [lm0] "s"(d.lat_m0), [rm0] "s"(d.rope_m0), \
+  [rsrc] "v"(d.rope_src), [rid0] "s"(d.rid[0]), [rid1] "s"(d.rid[1]), [rid2] "s"(d.rid[2]), [rid3] "s"(d.rid[3]), \
+  [rid4] "s"(d.rid[4]), [rid5] "s"(d.rid[5]), [rid6] "s"(d.rid[6]), [rid7] "s"(d.rid[7])
+#define MLA_DMA_ALL \
+  MLA_DMA_LAT(0, 0) MLA_DMA_LAT(1, 5136) MLA_DMA_LAT(2, 10272) MLA_DMA_LAT(3, 15408) MLA_DMA_LAT(4, 20480) \
+  MLA_DMA_LAT(5, 25616) MLA_DMA_LAT(6, 30752) MLA_DMA_LAT(7, 35888) MLA_DMA_ROPE
+
 // How a workgroup finishes: the whole row (no split), or a partial for the merge kernel.
 constexpr int kMlaNoSplit = 0, kMlaSplitCombine = 1;
 
@@ -548,48 +742,66 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
       }
     }
     __syncthreads();
+    // Only tiles with a valid key are gathered and computed (padding past a short row's end,
+    // tiles of holes): bit t of `act` is set for tile t (ntiles <= 64), and `pend` holds the
+    // active tiles not gathered yet, lowest first.
+    static_assert(kListCap / kNK <= 64, "a chunk's tiles fit one wave-wide mask");
+    const uint64_t act = __ballot(lane < ntiles && tmask[lane] != 0);
+    const int nact = __builtin_popcountll(act);
+    uint64_t pend = act;
+    auto next_tile = [&]() {
+      const int t = __builtin_ctzll(pend);
+      pend &= pend - 1;
+      return t;
+    };
     // Settle every vector-memory operation the compiler issued so far (the query loads are
     // already consumed; register spills of the prologue may still be in flight) before the first
     // gathers: its wait-count pass then sees nothing pending, and inserts no wait inside the tile
     // loop that would also drain the gathers in flight (a store's data register rewritten in the
     // loop would otherwise take one).
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt left at their maxima
-    // vm[d] = valid-entry mask of tile it + d (0 past the end); only constant indices, so the
-    // masks stay in scalar registers
+    // vm[d] = valid-entry mask of active tile j + d (0 past the end); only constant indices, so
+    // the masks stay in scalar registers. Active tiles 0 .. kNBuf - 2 are gathered here, active
+    // tile j + kNBuf - 1 during active tile j's PV step.
     uint32_t vm[kNBuf];
 #pragma unroll
     for (int pt = 0; pt < kNBuf; ++pt) {
       vm[pt] = 0u;
-      if (pt < kNBuf - 1 && pt < ntiles)
-        vm[pt] = issue_tile(kv_base, lds + pt * kTileBytes, read_entries(list, tmask, pt, ntiles, wave, lane), wave, lane);
+      if (pt < kNBuf - 1 && pt < nact)
+        vm[pt] = issue_tile(kv_base, lds + pt * kTileBytes, read_entries(list, tmask, next_tile(), ntiles, wave, lane), wave, lane);
     }
     // entries of the next tile to gather, read one iteration before they are needed
-    TileEntries nxt = read_entries(list, tmask, kNBuf - 1, ntiles, wave, lane);
-    int b = 0;  // buffer of tile it (it % kNBuf, kept as a rotating counter)
-    for (int it = 0; it < ntiles; ++it) {
+    TileEntries nxt = kNBuf - 1 < nact ? read_entries(list, tmask, next_tile(), ntiles, wave, lane) : TileEntries{0, 0, 0};
+    int b = 0;  // buffer of active tile j (j % kNBuf, kept as a rotating counter)
+    for (int j = 0; j < nact; ++j) {
       int younger = 0;  // later tiles whose gathers are in flight
 #pragma unroll
       for (int d = 1; d + 1 < kNBuf; ++d) younger += vm[d] != 0u ? 1 : 0;
       wait_gathers(younger);
-      // Every wave's share of tile `it` has landed once all waves pass this barrier, and every
-      // wave has consumed its reads of tile it-1 (into MFMAs). A bare s_barrier: the fence of
+      // Every wave's share of tile j has landed once all waves pass this barrier, and every wave
+      // has consumed its reads of tile j - 1 (into MFMAs). A bare s_barrier: the fence of
       // __syncthreads would also drain the younger tiles' loads that are meant to stay in flight.
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       const int b_cur = b;
       b = b + 1 == kNBuf ? 0 : b + 1;
-      if (it + kNBuf - 1 < ntiles) {
-        // tile it + kNBuf - 1 goes to the buffer tile it - 1 used
-        const int nt = it + kNBuf - 1, nb = b_cur == 0 ? kNBuf - 1 : b_cur - 1;
-        vm[kNBuf - 1] = issue_tile(kv_base, lds + nb * kTileBytes, nxt, wave, lane);
-        nxt = read_entries(list, tmask, nt + 1, ntiles, wave, lane);
+      // active tile j + kNBuf - 1 goes to the buffer tile j - 1 used (every wave is done with it);
+      // its gathers are issued in this iteration's PV step
+      const TileEntries te2 = nxt;
+      uint32_t mask2 = 0u;
+      lds_u8* buf2 = lds;
+      if (j + kNBuf - 1 < nact) {
+        const int nb = b_cur == 0 ? kNBuf - 1 : b_cur - 1;
+        mask2 = (uint32_t)__builtin_amdgcn_readfirstlane(te2.mask);  // nonzero: an active tile
+        buf2 = lds + nb * kTileBytes;
+        vm[kNBuf - 1] = mask2;
+        nxt = j + kNBuf < nact ? read_entries(list, tmask, next_tile(), ntiles, wave, lane) : TileEntries{0, 0, 0};
       }
       const uint32_t valid = vm[0];
 #pragma unroll
       for (int q = 0; q + 1 < kNBuf; ++q) vm[q] = vm[q + 1];
       vm[kNBuf - 1] = 0u;
-      if (valid == 0u) continue;  // uniform across the workgroup
       const lds_u8* tile = lds + b_cur * kTileBytes;
 
       // ---- S^T = K Q^T: lane holds head lane%32, keys 8*(i/4) + 4*(lane/32) + i%4, i = 0..15
@@ -784,138 +996,24 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
       //      stay in AGPRs; their readers after the tile loop are separated by s_nops.
       {
         const uint32_t ta = (uint32_t)(uintptr_t)(tile + tr_base[0]);
-        asm volatile(
-          "ds_read_b64_tr_b16 v[224:225], %[ta]\n"
-          "ds_read_b64_tr_b16 v[226:227], %[ta] offset:10272\n"
-          "ds_read_b64_tr_b16 v[228:229], %[ta] offset:64\n"
-          "ds_read_b64_tr_b16 v[230:231], %[ta] offset:10336\n"
-          "ds_read_b64_tr_b16 v[232:233], %[ta] offset:128\n"
-          "ds_read_b64_tr_b16 v[234:235], %[ta] offset:10400\n"
-          "ds_read_b64_tr_b16 v[236:237], %[ta] offset:192\n"
-          "ds_read_b64_tr_b16 v[238:239], %[ta] offset:10464\n"
-          "ds_read_b64_tr_b16 v[240:241], %[ta] offset:256\n"
-          "ds_read_b64_tr_b16 v[242:243], %[ta] offset:10528\n"
-          "ds_read_b64_tr_b16 v[244:245], %[ta] offset:320\n"
-          "ds_read_b64_tr_b16 v[246:247], %[ta] offset:10592\n"
-          "ds_read_b64_tr_b16 v[248:249], %[ta] offset:384\n"
-          "ds_read_b64_tr_b16 v[250:251], %[ta] offset:10656\n"
-          "ds_read_b64_tr_b16 v[252:253], %[ta] offset:448\n"
-          "ds_read_b64_tr_b16 v[254:255], %[ta] offset:10720\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o0], v[224:227], %[p0], %[o0]\n"
-          "ds_read_b64_tr_b16 v[224:225], %[ta] offset:512\n"
-          "ds_read_b64_tr_b16 v[226:227], %[ta] offset:10784\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o1], v[228:231], %[p0], %[o1]\n"
-          "ds_read_b64_tr_b16 v[228:229], %[ta] offset:576\n"
-          "ds_read_b64_tr_b16 v[230:231], %[ta] offset:10848\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o2], v[232:235], %[p0], %[o2]\n"
-          "ds_read_b64_tr_b16 v[232:233], %[ta] offset:640\n"
-          "ds_read_b64_tr_b16 v[234:235], %[ta] offset:10912\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o3], v[236:239], %[p0], %[o3]\n"
-          "ds_read_b64_tr_b16 v[236:237], %[ta] offset:704\n"
-          "ds_read_b64_tr_b16 v[238:239], %[ta] offset:10976\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o4], v[240:243], %[p0], %[o4]\n"
-          "ds_read_b64_tr_b16 v[240:241], %[ta] offset:768\n"
-          "ds_read_b64_tr_b16 v[242:243], %[ta] offset:11040\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o5], v[244:247], %[p0], %[o5]\n"
-          "ds_read_b64_tr_b16 v[244:245], %[ta] offset:832\n"
-          "ds_read_b64_tr_b16 v[246:247], %[ta] offset:11104\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o6], v[248:251], %[p0], %[o6]\n"
-          "ds_read_b64_tr_b16 v[248:249], %[ta] offset:896\n"
-          "ds_read_b64_tr_b16 v[250:251], %[ta] offset:11168\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o7], v[252:255], %[p0], %[o7]\n"
-          "ds_read_b64_tr_b16 v[252:253], %[ta] offset:960\n"
-          "ds_read_b64_tr_b16 v[254:255], %[ta] offset:11232\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o8], v[224:227], %[p0], %[o8]\n"
-          "ds_read_b64_tr_b16 v[224:225], %[ta] offset:20480\n"
-          "ds_read_b64_tr_b16 v[226:227], %[ta] offset:30752\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o9], v[228:231], %[p0], %[o9]\n"
-          "ds_read_b64_tr_b16 v[228:229], %[ta] offset:20544\n"
-          "ds_read_b64_tr_b16 v[230:231], %[ta] offset:30816\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o10], v[232:235], %[p0], %[o10]\n"
-          "ds_read_b64_tr_b16 v[232:233], %[ta] offset:20608\n"
-          "ds_read_b64_tr_b16 v[234:235], %[ta] offset:30880\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o11], v[236:239], %[p0], %[o11]\n"
-          "ds_read_b64_tr_b16 v[236:237], %[ta] offset:20672\n"
-          "ds_read_b64_tr_b16 v[238:239], %[ta] offset:30944\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o12], v[240:243], %[p0], %[o12]\n"
-          "ds_read_b64_tr_b16 v[240:241], %[ta] offset:20736\n"
-          "ds_read_b64_tr_b16 v[242:243], %[ta] offset:31008\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o13], v[244:247], %[p0], %[o13]\n"
-          "ds_read_b64_tr_b16 v[244:245], %[ta] offset:20800\n"
-          "ds_read_b64_tr_b16 v[246:247], %[ta] offset:31072\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o14], v[248:251], %[p0], %[o14]\n"
-          "ds_read_b64_tr_b16 v[248:249], %[ta] offset:20864\n"
-          "ds_read_b64_tr_b16 v[250:251], %[ta] offset:31136\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o15], v[252:255], %[p0], %[o15]\n"
-          "ds_read_b64_tr_b16 v[252:253], %[ta] offset:20928\n"
-          "ds_read_b64_tr_b16 v[254:255], %[ta] offset:31200\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o0], v[224:227], %[p1], %[o0]\n"
-          "ds_read_b64_tr_b16 v[224:225], %[ta] offset:20992\n"
-          "ds_read_b64_tr_b16 v[226:227], %[ta] offset:31264\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o1], v[228:231], %[p1], %[o1]\n"
-          "ds_read_b64_tr_b16 v[228:229], %[ta] offset:21056\n"
-          "ds_read_b64_tr_b16 v[230:231], %[ta] offset:31328\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o2], v[232:235], %[p1], %[o2]\n"
-          "ds_read_b64_tr_b16 v[232:233], %[ta] offset:21120\n"
-          "ds_read_b64_tr_b16 v[234:235], %[ta] offset:31392\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o3], v[236:239], %[p1], %[o3]\n"
-          "ds_read_b64_tr_b16 v[236:237], %[ta] offset:21184\n"
-          "ds_read_b64_tr_b16 v[238:239], %[ta] offset:31456\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o4], v[240:243], %[p1], %[o4]\n"
-          "ds_read_b64_tr_b16 v[240:241], %[ta] offset:21248\n"
-          "ds_read_b64_tr_b16 v[242:243], %[ta] offset:31520\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o5], v[244:247], %[p1], %[o5]\n"
-          "ds_read_b64_tr_b16 v[244:245], %[ta] offset:21312\n"
-          "ds_read_b64_tr_b16 v[246:247], %[ta] offset:31584\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o6], v[248:251], %[p1], %[o6]\n"
-          "ds_read_b64_tr_b16 v[248:249], %[ta] offset:21376\n"
-          "ds_read_b64_tr_b16 v[250:251], %[ta] offset:31648\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o7], v[252:255], %[p1], %[o7]\n"
-          "ds_read_b64_tr_b16 v[252:253], %[ta] offset:21440\n"
-          "ds_read_b64_tr_b16 v[254:255], %[ta] offset:31712\n"
-          "s_waitcnt lgkmcnt(14)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o8], v[224:227], %[p1], %[o8]\n"
-          "s_waitcnt lgkmcnt(12)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o9], v[228:231], %[p1], %[o9]\n"
-          "s_waitcnt lgkmcnt(10)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o10], v[232:235], %[p1], %[o10]\n"
-          "s_waitcnt lgkmcnt(8)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o11], v[236:239], %[p1], %[o11]\n"
-          "s_waitcnt lgkmcnt(6)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o12], v[240:243], %[p1], %[o12]\n"
-          "s_waitcnt lgkmcnt(4)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o13], v[244:247], %[p1], %[o13]\n"
-          "s_waitcnt lgkmcnt(2)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o14], v[248:251], %[p1], %[o14]\n"
-          "s_waitcnt lgkmcnt(0)\n"
-          "v_mfma_f32_32x32x16_bf16 %[o15], v[252:255], %[p1], %[o15]\n"
-          : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]), [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]), [o10] "+a"(o[10]), [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]), [o14] "+a"(o[14]), [o15] "+a"(o[15])
-          : [ta] "v"(ta), [p0] "v"(pk[0]), [p1] "v"(pk[1])
-          : "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
+        {
+          // the nine gathers of tile it + kNBuf - 1 (when it has a valid key) ride in the MFMA
+          // stream: a wave stalled at a gather's issue would otherwise hold its MFMAs back (rows
+          // 4i + w as in issue_tile; without a tile to gather the row ids are not used)
+          const DmaOps d = dma_ops(kv_base, buf2, te2, wave, lane);
+          uint64_t ga;
+          uint32_t sv;
+          asm volatile(
+            "s_mov_b32 %[sv], m0\n"
+            MLA_PV_ASM(MLA_DMA_LAT(0, 0), MLA_DMA_LAT(1, 5136), MLA_DMA_LAT(2, 10272), MLA_DMA_LAT(3, 15408),
+                       MLA_DMA_LAT(4, 20480), MLA_DMA_LAT(5, 25616), MLA_DMA_LAT(6, 30752), MLA_DMA_LAT(7, 35888),
+                       MLA_DMA_ROPE)
+            "s_mov_b32 m0, %[sv]\n"
+            : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]), [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]), [o10] "+a"(o[10]), [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]), [o14] "+a"(o[14]), [o15] "+a"(o[15]), [ga] "=&v"(ga), [sv] "=&s"(sv)
+            : [ta] "v"(ta), [p0] "v"(pk[0]), [p1] "v"(pk[1]),
+              MLA_DMA_INPUTS(d, mask2)
+            : "vcc", "scc", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
+        }
       }
     }
   }

@@ -14,9 +14,9 @@ cache, for the inputs that make it take every branch:
   repeat filter an entry whose position an earlier entry of the row holds becomes -1
   tile masks    per tile of 32 entries (the tail past the chunk counts as -1): the mask of entries
                 >= 0; in a tile with a nonzero mask every -1 takes the tile's first valid row id
-  tile loop     tiles 0 and 1 issued up front, then tile it + 2 at iteration it; the entries of the
-                next tile are read one iteration ahead and read as "no tile" past the last one;
-                a tile whose mask is 0 issues no load
+  tile loop     only tiles whose mask is nonzero (active tiles) are gathered and computed: the
+                first two active tiles are issued up front, active tile j + 2 during active tile
+                j's PV product; the entries of the next tile are read one iteration ahead
   gather        wave w (0..3), lane l (0..63): latent loads of tile rows 4i + w (i = 0..7) at
                 row * 1152 + 16 l, and the rope load of tile row 8w + l / 8 at row * 1152 + 1024 +
                 16 ((l % 8) ^ ((8w + l / 8) / 2 % 8))
@@ -111,19 +111,16 @@ def model_workgroup(row, t, seq, page_table, num_pages, k, splits, sp, check_pag
             tmask[tt] = m
 
         def read_entries(tt):
-            if tt >= ntiles:
-                return None
-            assert 0 <= tt * NK and tt * NK + NK <= LIST_CAP
+            assert 0 <= tt < ntiles and tt * NK + NK <= LIST_CAP
             return tt, lst[tt * NK: tt * NK + NK].copy(), int(tmask[tt])
 
         issued = []
+        act = [tt for tt in range(ntiles) if tmask[tt]]   # the 64-bit mask of active tiles
+        assert ntiles <= 64
 
         def issue(te):
-            if te is None:
-                return
             tt, ent, m = te
-            if m == 0:
-                return
+            assert m != 0
             issued.append(tt)
             for w in range(4):
                 for lane in range(64):
@@ -139,16 +136,17 @@ def model_workgroup(row, t, seq, page_table, num_pages, k, splits, sp, check_pag
                 if (m >> h) & 1:
                     kept.append(cb + tt * NK + h)
 
+        pend = list(act)
         for pt in range(NBUF - 1):
-            if pt < ntiles:
-                issue(read_entries(pt))
-        nxt = read_entries(NBUF - 1)
-        for it in range(ntiles):
-            if it + NBUF - 1 < ntiles:
-                assert nxt is not None and nxt[0] == it + NBUF - 1
+            if pt < len(act):
+                issue(read_entries(pend.pop(0)))
+        nxt = read_entries(pend.pop(0)) if NBUF - 1 < len(act) else None
+        for j in range(len(act)):
+            if j + NBUF - 1 < len(act):
+                assert nxt is not None and nxt[0] == act[j + NBUF - 1]
                 issue(nxt)
-                nxt = read_entries(it + NBUF)
-        assert issued == [tt for tt in range(ntiles) if tmask[tt]]
+                nxt = read_entries(pend.pop(0)) if j + NBUF < len(act) else None
+        assert issued == act and not pend
     return kept
 
 
