@@ -678,10 +678,11 @@ def run_cache_bench(args):
 
 def run_projection_bench(args):
     """The indexer's projections at the pages' hidden size d = 7168 (query latent 1536, 64 heads x
-    128 dims): the key projection of a 131072-token prefix into the paged cache, and the query
-    projection (codes and head weights) of a 4096-row prefill chunk and of the 128 rows of the
-    decode step. TFLOP/s against the bf16 peak; the decode-sized call also as GB/s of weights and
-    activations read (it streams 25 MB of w_q for 128 rows)."""
+    128 dims): the key projection of a 131072-token prefix into the paged cache, of a 4096-token
+    prefill chunk and of the decode step's 128 new keys, and the query projection (codes and head
+    weights) of a 4096-row prefill chunk and of the decode step's 128 rows. TFLOP/s against the
+    bf16 peak; also GB/s of weights and activations read (the decode-sized query projection
+    streams 25 MB of w_q for 128 rows)."""
     import torch
 
     from sparse_attention_06_amd import dsa
@@ -719,10 +720,12 @@ def run_projection_bench(args):
 
     timed("key_project_131072", lambda: dsa.indexer_key_project(h, w_k, seq, pos, pt, kc, ks, ws=False),
           2.0 * n * Di * d, n * d * 2 + Di * d * 2 + n * (Di + 4), reps=2)
-    # the decode step's new keys: one per query row (128 rows)
-    ws = torch.empty(max(16, dsa.indexer_projection_workspace_size(128, d)), dtype=torch.uint8, device="cuda")
-    timed("key_project_128", lambda: dsa.indexer_key_project(h[:128], w_k, seq[:128], pos[:128], pt, kc, ks, ws=ws),
-          2.0 * 128 * Di * d, 128 * d * 2 + Di * d * 2 + 128 * (Di + 4))
+    # a 4096-token prefill chunk's keys, and the decode step's new keys (one per query row, 128)
+    for nk in (4096, 128):
+        ws = torch.empty(max(16, dsa.indexer_projection_workspace_size(nk, d)), dtype=torch.uint8, device="cuda")
+        timed(f"key_project_{nk}",
+              lambda: dsa.indexer_key_project(h[:nk], w_k, seq[:nk], pos[:nk], pt, kc, ks, ws=ws),
+              2.0 * nk * Di * d, nk * d * 2 + Di * d * 2 + nk * (Di + 4))
     for rows in (4096, 128):
         c_q = torch.randn(rows, d_cq, generator=g, device="cuda").to(torch.bfloat16)
         hr = h[:rows]

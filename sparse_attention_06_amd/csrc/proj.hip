@@ -282,15 +282,18 @@ __global__ void __launch_bounds__(256) proj_reduce_kernel(ProjArgs p, int kz) {
   if (j == 0) p.k_scale[row] = s;
 }
 
-// Split-K is taken when the output tiles alone would fill less than half the GPU: the K blocks of
-// 64 are dealt out so that about 256 workgroups run (32-row tiles). Returns the number of K ranges
-// and sets *k_split (a multiple of 64); 1 means no split.
+// Split-K is taken when the unsplit launch (128-row tiles) would give fewer than two workgroups
+// per CU: the K blocks of 64 are dealt out over 32-row tiles so that about 1024 workgroups run
+// (a projection of a few thousand rows onto 64 or 128 columns over d = 7168 otherwise runs on a
+// few dozen CUs). Returns the number of K ranges and sets *k_split (a multiple of 64); 1 means
+// no split.
 static int proj_plan(int M, int N, int K, int* k_split) {
-  const int tiles = ((M + 31) / 32) * ((N + kPN - 1) / kPN);
+  const int n_tiles = (N + kPN - 1) / kPN;
+  const int tiles = ((M + 31) / 32) * n_tiles;
   const int kb = K / kPK;
   *k_split = K;
-  if (tiles >= 128 || kb < 2) return 1;
-  int want = 256 / tiles < kb ? 256 / tiles : kb;
+  if (((M + kPM - 1) / kPM) * n_tiles >= 512 || kb < 2) return 1;
+  int want = 1024 / tiles < kb ? 1024 / tiles : kb;
   want = want > 16 ? 16 : want;  // at most 16 partial blocks: their write and re-read stay small
   if (want < 2) return 1;
   const int per = (kb + want - 1) / want;  // K blocks per range

@@ -61,10 +61,12 @@ def _case(seed, rows, d, d_cq, Hi=64, Di=128):
 
 
 @pytest.mark.parametrize("split", [True, False])
-@pytest.mark.parametrize("rows,d,d_cq", [(131, 7168, 1536), (64, 128, 64), (1, 7168, 1536), (600, 7168, 1536)])
+@pytest.mark.parametrize("rows,d,d_cq", [(131, 7168, 1536), (64, 128, 64), (1, 7168, 1536), (600, 7168, 1536),
+                                         (3900, 7168, 512)])
 def test_query_projection(oracle_lib, rows, d, d_cq, split):
     """Small batches take 32-row tiles and, with a workspace, a split-K head-weight projection;
-    600 rows take 128-row tiles."""
+    600 and 3900 rows take 128-row tiles (the last one ragged); 3900 rows with a workspace split
+    the head-weight projection's K eight ways."""
     print(f"case: query projection rows={rows} d={d} d_cq={d_cq} split={split}", flush=True)
     h, c_q, w_k, w_q, w_w = _case(300 + rows, rows, d, d_cq)
     q8, w = dsa.indexer_query_project(c_q, w_q, h, w_w, 64, 128, ws=None if split else False)
