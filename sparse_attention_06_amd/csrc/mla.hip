@@ -10,10 +10,12 @@
 // Tuned kernel (H=128, Dqk=576, Dv=512): one workgroup = 4 waves per (row, split); wave w owns
 // heads [32w, 32w+32). Per tile of 32 selected positions:
 //   gather   the 32 latent rows (1152 B each) go straight from HBM into LDS with
-//            global_load_lds_dwordx4 (no VGPR staging), three tiles in flight; rows sit at a
-//            1168-byte stride so both LDS read patterns below are bank-conflict free
+//            global_load_lds_dwordx4 (no VGPR staging), two tiles in flight; each latent row's
+//            16-byte chunks are rotated within a 1280-byte line so both LDS read patterns below
+//            are bank-conflict free
 //   QK^T     S[32 keys x 32 heads] on v_mfma_f32_32x32x16_bf16: the key tile is the A operand
-//            (read from LDS), the wave's 32 query heads the B operand (resident in 144 VGPRs)
+//            (read from LDS), the wave's 32 query heads the B operand (latent dims resident in
+//            128 VGPRs, rope dims from LDS)
 //   softmax  fp32, in the log2 domain, with a lazily moved reference maximum: the running
 //            output is rescaled only when a head's maximum grows by more than 2^8
 //   PV       O^T[512 x 32 heads] += V^T P: the probabilities stay in registers as the B operand
@@ -522,10 +524,6 @@ __device__ __forceinline__ DmaOps dma_ops(const uint8_t* __restrict__ kv_base, c
   [dma] "s"(m), [kvl] "v"(d.kvl), [c1152] "v"(d.c1152), [lm0] "s"(d.lat_m0), [rm0] "s"(d.rope_m0), \
   [rsrc] "v"(d.rope_src), [rid0] "s"(d.rid[0]), [rid1] "s"(d.rid[1]), [rid2] "s"(d.rid[2]), [rid3] "s"(d.rid[3]), \
   [rid4] "s"(d.rid[4]), [rid5] "s"(d.rid[5]), [rid6] "s"(d.rid[6]), [rid7] "s"(d.rid[7])
-#define MLA_DMA_ALL \
-  MLA_DMA_LAT(0, 0) MLA_DMA_LAT(1, 5136) MLA_DMA_LAT(2, 10272) MLA_DMA_LAT(3, 15408) MLA_DMA_LAT(4, 20480) \
-  MLA_DMA_LAT(5, 25616) MLA_DMA_LAT(6, 30752) MLA_DMA_LAT(7, 35888) MLA_DMA_ROPE
-
 // How a workgroup finishes: the whole row (no split), or a partial for the merge kernel.
 constexpr int kMlaNoSplit = 0, kMlaSplitCombine = 1;
 

@@ -246,6 +246,36 @@ def test_sparse_mla_tuned(oracle_lib, entry, q_pos, qps, k):
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=1e-4)
 
 
+@pytest.mark.parametrize("rows,k", [(130, 128), (70, 256)])
+def test_sparse_mla_decode_two_and_four_way_splits(oracle_lib, rows, k):
+    """Decode batches whose rows split 2 ways (130 rows, k = 128; the headline batch's split) or
+    4 ways (70 rows, k = 256), as MTP pairs of positions t, t + 1. Tiny rows leave their later
+    splits without a valid key, which the merge must skip. Two calls in a row give identical
+    bits."""
+    _say(f"case: sparse mla decode 2/4-way splits rows={rows} k={k}")
+    rng = np.random.default_rng(rows)
+    n_seq = rows // 2
+    base = rng.integers(0, 700, n_seq)
+    base[:3] = [0, 30, 100]
+    q_pos = np.stack([base, base + 1], 1).reshape(-1)
+    w = workloads.make_random(n_seq, 2, q_pos, 702, seed=60 + rows, permute_pages=True, extra_pages=2)
+    d = gpu_inputs(w)
+    idx = _rand_idx(w.q_pos, k, seed=9)
+    d_idx = torch.from_numpy(idx).cuda()
+    outs = []
+    for _ in range(2):
+        lse = torch.empty(w.rows, w.H, dtype=torch.float32, device="cuda")
+        out = dsa.sparse_mla_decode(d["q"], d["kv"], d["page_table"], d["q_pos"], w.n_seq, w.q_per_seq, d_idx, w.Dqk,
+                                    w.Dv, w.v_col0, w.sm_scale, lse=lse)
+        assert dsa.last_path() == "mla_mfma_split"
+        outs.append((out, lse))
+    torch.cuda.synchronize()
+    ref, ref_lse = _attn_ref(w, idx)
+    check_attn(outs[0][0].float().cpu().numpy(), ref)
+    np.testing.assert_allclose(outs[0][1].cpu().numpy(), ref_lse, rtol=0, atol=1e-4)
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 def _lists_with_repeats(q_pos, k, seed):
     """Index lists that are sets only after removing repeats ([DSA-blog] "Sparse Attention": S_t
     is a set), one kind per row: shuffled with repeats spread over the whole list (so over the
