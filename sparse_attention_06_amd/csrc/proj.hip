@@ -17,12 +17,16 @@
 //          physical row of the paged key cache (the format dsa_indexer_cache_write writes)
 //   query  codes E4M3(c) without a scale, row-major [M, N] bytes
 //   f32    c as fp32, row-major [M, N]
-// Workgroup: 4 waves, a 128 x 128 output tile, K in blocks of 64 staged through LDS (rows padded to
-// 144 bytes, so the 16-byte operand reads of 8 consecutive rows hit distinct banks), the next block
-// loaded into registers while the current one is multiplied. Wave w owns rows 32w..32w+31 of the
-// tile and all 128 columns (four 32 x 32 accumulator blocks). Within a block of 64 the K order is
-// permuted the same way for both operands (lane half h supplies elements 32h + 8j .. +8 as its
-// part of MFMA j), which leaves every dot product unchanged.
+// Workgroup: 4 waves, a 128 x 128 output tile, K in blocks of 64. Wave w owns rows 32w..32w+31 of
+// the tile and all 128 columns (four 32 x 32 accumulator blocks). Within a block of 64 the K order
+// is permuted the same way for both operands (lane half h supplies elements 32h + 8j .. +8 as its
+// part of MFMA j), which leaves every dot product unchanged. The K blocks go straight from global
+// memory into a ring of kPStages LDS stages (global_load_lds_dwordx4, no register staging), issued
+// kPStages - 1 blocks ahead, one workgroup barrier per block; an LDS row of a block is its 128
+// bytes, 16-byte chunk c of row r stored at c ^ (r % 8), so the operand reads of 8 consecutive
+// rows hit distinct banks. Small batches (32-row tiles, and the split-K partials) stage through
+// registers instead: the next block is loaded into registers while the current one is
+// multiplied, LDS rows padded to 144 bytes.
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -31,6 +35,8 @@ constexpr int kPM = 128, kPN = 128, kPK = 64;
 constexpr int kPRowBytes = 2 * kPK + 16;                 // 144: padded LDS row of a K block
 constexpr int kPTileBytes = kPM * kPRowBytes;            // 18432 per operand
 constexpr int kPStageBytes = 32 * kPN;                   // one wave's 32 x 128 byte codes
+constexpr int kPStages = 2;                              // LDS stages of the 128-row tiles' ring
+constexpr int kPBlockBytes = 2 * kPM * 2 * kPK;          // 32768: one K block of A and B
 
 // kEpiPartial: fp32 sums over one K range (blockIdx.z) to ws[z][M][N], for the split-K path
 enum { kEpiKey = 0, kEpiQuery = 1, kEpiF32 = 2, kEpiPartial = 3 };
@@ -52,12 +58,12 @@ struct ProjArgs {
   // split-K: K range of blockIdx.z is [z * k_split, (z + 1) * k_split); partials in ws
   int k_split;
   float* ws;
-  int tiles_m, tiles;  // output tiles (row tiles fastest), dealt out per XCD by tile_of()
+  int tiles_m, tiles;  // output tiles (tiles_m row tiles x tiles / tiles_m column tiles)
 };
 
 // Workgroups are dispatched to the 8 XCDs round robin. The padded 1-D grid gives each XCD a
-// contiguous range of tiles, row tiles fastest, so the row tiles that share a weight (column)
-// tile run on one XCD and read it once through its L2. -1 for the padding.
+// contiguous range of tiles (tile_origin orders them), so the tiles that share operand panels run
+// on one XCD and read them through its L2. -1 for the padding.
 __device__ __forceinline__ int tile_of(const ProjArgs& p) {
   const int per = (int)gridDim.x >> 3;
   const int t = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
@@ -65,24 +71,118 @@ __device__ __forceinline__ int tile_of(const ProjArgs& p) {
 }
 static inline dim3 tile_grid(int tiles, int z = 1) { return dim3(8 * ((tiles + 7) / 8), 1, z); }
 
+// Tile t's first row and column. Tiles come in groups of 8 row tiles by all column tiles, row
+// tiles fastest within a group: the workgroups an XCD runs at once then cover about 8 row tiles x
+// 8 column tiles, each operand panel shared through its L2 eight ways.
+__device__ __forceinline__ void tile_origin(const ProjArgs& p, int t, int tm, int* m0, int* n0) {
+  constexpr int kGroup = 8;
+  const int n_tiles = p.tiles / p.tiles_m;
+  const int g = t / (kGroup * n_tiles), first = kGroup * g;
+  const int gs = min(p.tiles_m - first, kGroup), r = t - g * kGroup * n_tiles;
+  *m0 = (first + r % gs) * tm;
+  *n0 = (r / gs) * kPN;
+}
+
+// The K loop of a 128 x 128 tile over the whole K, through the LDS ring. Wave w moves rows
+// 32w..32w+31 of both operands: four global_load_lds_dwordx4 per operand and block, each 8 rows x
+// 128 bytes, lane l taking row 8i + l/8 and the global chunk (l % 8) ^ (l / 8), which lands at LDS
+// chunk l % 8 of its row (the swizzle above). Rows past M or N re-read the last row; their results
+// are never stored. The loads are inline asm (LDS address in M0, saved and restored), so their
+// completion is awaited with explicit vmcnt counts: at block kb the wave's own loads of block kb
+// are done once at most 8 (loads of one block) times the blocks issued after it are in flight;
+// the barrier after that wait makes every wave's loads of the block visible and also frees the
+// stage that the next issue overwrites (its last reader is the previous block's multiply).
+__device__ __forceinline__ void gemm_loop_lds_ring(const ProjArgs& p, int m0, int n0, int wave, int lane,
+                                                   uint8_t* smem, f32x16 (&acc)[4]) {
+  const int hl = lane & 31, half = lane >> 5;
+  const int nkb = p.K / kPK;
+  const uint32_t k_bytes = 2u * (uint32_t)p.K;
+  const uint32_t chunk = 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+  const int max_ra = p.M - 1 - m0, max_rb = p.N - 1 - n0;
+  uint32_t va[4], vb[4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const int r = 32 * wave + 8 * ii + (lane >> 3);
+    va[ii] = (uint32_t)min(r, max_ra) * k_bytes + chunk;
+    vb[ii] = (uint32_t)min(r, max_rb) * k_bytes + chunk;
+  }
+  const uint8_t* ga = (const uint8_t*)(p.a + (int64_t)m0 * p.K);
+  const uint8_t* gb = (const uint8_t*)(p.b + (int64_t)n0 * p.K);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  auto issue = [&](int kb, int st) {
+    const uint64_t sa = (uint64_t)(uintptr_t)(ga + 2 * kPK * kb), sb = (uint64_t)(uintptr_t)(gb + 2 * kPK * kb);
+    const uint32_t la = __builtin_amdgcn_readfirstlane(lds0 + st * kPBlockBytes + 4096 * wave);
+    const uint32_t lb = la + kPBlockBytes / 2;
+    uint32_t sv;
+    asm volatile(
+        "s_mov_b32 %[sv], m0\n"
+        "s_mov_b32 m0, %[la]\n s_nop 0\n global_load_lds_dwordx4 %[a0], %[sa]\n"
+        "s_add_u32 m0, %[la], 1024\n s_nop 0\n global_load_lds_dwordx4 %[a1], %[sa]\n"
+        "s_add_u32 m0, %[la], 2048\n s_nop 0\n global_load_lds_dwordx4 %[a2], %[sa]\n"
+        "s_add_u32 m0, %[la], 3072\n s_nop 0\n global_load_lds_dwordx4 %[a3], %[sa]\n"
+        "s_mov_b32 m0, %[lb]\n s_nop 0\n global_load_lds_dwordx4 %[b0], %[sb]\n"
+        "s_add_u32 m0, %[lb], 1024\n s_nop 0\n global_load_lds_dwordx4 %[b1], %[sb]\n"
+        "s_add_u32 m0, %[lb], 2048\n s_nop 0\n global_load_lds_dwordx4 %[b2], %[sb]\n"
+        "s_add_u32 m0, %[lb], 3072\n s_nop 0\n global_load_lds_dwordx4 %[b3], %[sb]\n"
+        "s_mov_b32 m0, %[sv]\n"
+        : [sv] "=&s"(sv)
+        : [sa] "s"(sa), [sb] "s"(sb), [la] "s"(la), [lb] "s"(lb), [a0] "v"(va[0]), [a1] "v"(va[1]),
+          [a2] "v"(va[2]), [a3] "v"(va[3]), [b0] "v"(vb[0]), [b1] "v"(vb[1]), [b2] "v"(vb[2]), [b3] "v"(vb[3])
+        : "scc", "memory");
+  };
+  // per-lane byte offsets of the four operand chunks 4 half + j of an LDS row (row % 8 = hl % 8)
+  uint32_t co[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) co[j] = 16u * (uint32_t)((4 * half + j) ^ (hl & 7));
+#pragma unroll
+  for (int kb = 0; kb < kPStages - 1; ++kb)
+    if (kb < nkb) issue(kb, kb);
+  int st = 0;
+  for (int kb = 0; kb < nkb; ++kb) {
+    // the wave's loads of block kb: done once those of later blocks are all that is in flight
+    const int later = min(kPStages - 2, nkb - 1 - kb);
+    if (later <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0)
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    else __builtin_amdgcn_s_waitcnt(0x4F70);                  // vmcnt(16)
+    __syncthreads();
+    if (kb + kPStages - 1 < nkb) issue(kb + kPStages - 1, st == 0 ? kPStages - 1 : st - 1);
+    const uint8_t* sa = smem + st * kPBlockBytes;
+    const uint8_t* sb = sa + kPBlockBytes / 2;
+    bf16x8 a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = *(const bf16x8*)(sa + (32 * wave + hl) * 128 + co[j]);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      bf16x8 b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8*)(sb + (32 * cb + hl) * 128 + co[j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[j], acc[cb], 0, 0, 0);
+    }
+    st = st == kPStages - 1 ? 0 : st + 1;
+  }
+}
+
 // kTM: rows per tile. 128: wave w owns rows 32w.. and all 128 columns; 32 (small batches, so the
 // grid covers the GPU): the 4 waves share the 32 rows and wave w owns columns 32w..32w+31.
 template <int kEpi, int kTM>
 __global__ void __launch_bounds__(256) proj_gemm_kernel(ProjArgs p) {
   static_assert(kTM == 128 || kTM == 32, "row tile");
+  static_assert(kTM == 32 || kEpi != kEpiPartial, "split-K partials take 32-row tiles");
   constexpr int kCB = kTM == 128 ? 4 : 1;  // 32-column accumulator blocks per wave
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kPTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kTM == 128 ? kPStages * kPBlockBytes : (kTM + kPN) * kPRowBytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane & 31, half = lane >> 5;
   const int tile = tile_of(p);
   if (tile < 0) return;
-  const int m0 = (tile % p.tiles_m) * kTM, n0 = (tile / p.tiles_m) * kPN;
+  int m0, n0;
+  tile_origin(p, tile, kTM, &m0, &n0);
   const int kbeg = kEpi == kEpiPartial ? blockIdx.z * p.k_split : 0;
   const int kend = kEpi == kEpiPartial ? min(p.K, kbeg + p.k_split) : p.K;
   const int wrow = kTM == 128 ? 32 * wave : 0;       // the wave's first row within the tile
   const int wcb0 = kTM == 128 ? 0 : wave;            // the wave's first column block
   uint8_t* lds_a = smem;
-  uint8_t* lds_b = smem + kPTileBytes;
+  uint8_t* lds_b = smem + kTM * kPRowBytes;
 
   // global -> register staging: thread tid moves chunks c = tid + 256 i (i < 4) of each operand's
   // 128 rows x 128 bytes (row c / 8, 16-byte chunk c % 8); rows past M or N load zeros
@@ -117,6 +217,9 @@ __global__ void __launch_bounds__(256) proj_gemm_kernel(ProjArgs p) {
   f32x16 acc[kCB];
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) acc[cb] = f32x16{};
+  if constexpr (kTM == 128) {
+    gemm_loop_lds_ring(p, m0, n0, wave, lane, smem, acc);
+  } else {
   if (kbeg < kend) load_block(kbeg);
   for (int k0 = kbeg; k0 < kend; k0 += kPK) {
     __syncthreads();  // the previous block's operand reads are done
@@ -135,6 +238,7 @@ __global__ void __launch_bounds__(256) proj_gemm_kernel(ProjArgs p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[j], acc[cb], 0, 0, 0);
     }
+  }
   }
 
   // acc[cb][e]: row wrow + 8 (e / 4) + 4 half + e % 4 of the tile, column 32 (wcb0 + cb) + hl
