@@ -33,7 +33,6 @@ namespace dsa {
 
 constexpr int kPM = 128, kPN = 128, kPK = 64;
 constexpr int kPRowBytes = 2 * kPK + 16;                 // 144: padded LDS row of a K block
-constexpr int kPTileBytes = kPM * kPRowBytes;            // 18432 per operand
 constexpr int kPStageBytes = 32 * kPN;                   // one wave's 32 x 128 byte codes
 constexpr int kPStages = 2;                              // LDS stages of the 128-row tiles' ring
 constexpr int kPBlockBytes = 2 * kPM * 2 * kPK;          // 32768: one K block of A and B
@@ -92,6 +91,10 @@ __device__ __forceinline__ void tile_origin(const ProjArgs& p, int t, int tm, in
 // are done once at most 8 (loads of one block) times the blocks issued after it are in flight;
 // the barrier after that wait makes every wave's loads of the block visible and also frees the
 // stage that the next issue overwrites (its last reader is the previous block's multiply).
+// kSq: wave w owns rows 64 (w / 2) .. +63 and columns 64 (w % 2) .. +63 (acc[2 mi + ci]: rows
+// 64 (w / 2) + 32 mi, columns 64 (w % 2) + 32 ci), so a K step reads 2 + 2 operands for 4 MFMAs;
+// otherwise rows 32w .. +31 and all 128 columns (acc[cb]: columns 32 cb), 1 + 4 operands.
+template <bool kSq>
 __device__ __forceinline__ void gemm_loop_lds_ring(const ProjArgs& p, int m0, int n0, int wave, int lane,
                                                    uint8_t* smem, f32x16 (&acc)[4]) {
   const int hl = lane & 31, half = lane >> 5;
@@ -148,22 +151,42 @@ __device__ __forceinline__ void gemm_loop_lds_ring(const ProjArgs& p, int m0, in
     if (kb + kPStages - 1 < nkb) issue(kb + kPStages - 1, st == 0 ? kPStages - 1 : st - 1);
     const uint8_t* sa = smem + st * kPBlockBytes;
     const uint8_t* sb = sa + kPBlockBytes / 2;
-    bf16x8 a[4];
+    if constexpr (kSq) {
+      const int wm = wave >> 1, wn = wave & 1;
+      bf16x8 a[2][4], b[2][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] = *(const bf16x8*)(sa + (32 * wave + hl) * 128 + co[j]);
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      bf16x8 b[4];
+        for (int j = 0; j < 4; ++j) {
+          a[i][j] = *(const bf16x8*)(sa + (64 * wm + 32 * i + hl) * 128 + co[j]);
+          b[i][j] = *(const bf16x8*)(sb + (64 * wn + 32 * i + hl) * 128 + co[j]);
+        }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8*)(sb + (32 * cb + hl) * 128 + co[j]);
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[j], acc[cb], 0, 0, 0);
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ci = 0; ci < 2; ++ci)
+            acc[2 * mi + ci] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi][j], b[ci][j], acc[2 * mi + ci], 0, 0, 0);
+    } else {
+      bf16x8 a[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = *(const bf16x8*)(sa + (32 * wave + hl) * 128 + co[j]);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        bf16x8 b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8*)(sb + (32 * cb + hl) * 128 + co[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[j], acc[cb], 0, 0, 0);
+      }
     }
     st = st == kPStages - 1 ? 0 : st + 1;
   }
 }
 
-// kTM: rows per tile. 128: wave w owns rows 32w.. and all 128 columns; 32 (small batches, so the
+// kTM: rows per tile. 128: wave w owns a 64 x 64 quarter of the tile (query and fp32 outputs) or
+// rows 32w.. and all 128 columns (keys, whose scale needs a whole row); 32 (small batches, so the
 // grid covers the GPU): the 4 waves share the 32 rows and wave w owns columns 32w..32w+31.
 template <int kEpi, int kTM>
 __global__ void __launch_bounds__(256) proj_gemm_kernel(ProjArgs p) {
@@ -179,8 +202,12 @@ __global__ void __launch_bounds__(256) proj_gemm_kernel(ProjArgs p) {
   tile_origin(p, tile, kTM, &m0, &n0);
   const int kbeg = kEpi == kEpiPartial ? blockIdx.z * p.k_split : 0;
   const int kend = kEpi == kEpiPartial ? min(p.K, kbeg + p.k_split) : p.K;
-  const int wrow = kTM == 128 ? 32 * wave : 0;       // the wave's first row within the tile
-  const int wcb0 = kTM == 128 ? 0 : wave;            // the wave's first column block
+  constexpr bool kSq = kTM == 128 && kEpi != kEpiKey;
+  const int wrow = kTM == 128 ? 32 * wave : 0;       // first row of the wave's stored rows
+  const int wcb0 = kTM == 128 ? 0 : wave;            // the wave's first column block (not kSq)
+  // accumulator block k: its first row and column within the tile
+  auto blk_row = [&](int k) { return kSq ? 64 * (wave >> 1) + 32 * (k >> 1) : wrow; };
+  auto blk_col = [&](int k) { return kSq ? 64 * (wave & 1) + 32 * (k & 1) : 32 * (wcb0 + k); };
   uint8_t* lds_a = smem;
   uint8_t* lds_b = smem + kTM * kPRowBytes;
 
@@ -218,7 +245,7 @@ __global__ void __launch_bounds__(256) proj_gemm_kernel(ProjArgs p) {
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) acc[cb] = f32x16{};
   if constexpr (kTM == 128) {
-    gemm_loop_lds_ring(p, m0, n0, wave, lane, smem, acc);
+    gemm_loop_lds_ring<kSq>(p, m0, n0, wave, lane, smem, acc);
   } else {
   if (kbeg < kend) load_block(kbeg);
   for (int k0 = kbeg; k0 < kend; k0 += kPK) {
@@ -241,23 +268,23 @@ __global__ void __launch_bounds__(256) proj_gemm_kernel(ProjArgs p) {
   }
   }
 
-  // acc[cb][e]: row wrow + 8 (e / 4) + 4 half + e % 4 of the tile, column 32 (wcb0 + cb) + hl
+  // acc[cb][e]: row blk_row(cb) + 8 (e / 4) + 4 half + e % 4 of the tile, column blk_col(cb) + hl
   if (kEpi == kEpiF32 || kEpi == kEpiPartial) {
     float* dst = kEpi == kEpiF32 ? p.f32 : p.ws + (int64_t)blockIdx.z * p.M * p.N;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
-      const int n = n0 + 32 * (wcb0 + cb) + hl;
+      const int n = n0 + blk_col(cb) + hl;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wrow + 8 * (e >> 2) + 4 * half + (e & 3);
+        const int m = m0 + blk_row(cb) + 8 * (e >> 2) + 4 * half + (e & 3);
         if (m < p.M && n < p.N) dst[(int64_t)m * p.N + n] = acc[cb][e];
       }
     }
     return;
   }
   // Coded epilogues: the tile's codes staged as [row][128] bytes in LDS (the operand tiles are
-  // done); with 128-row tiles each wave stages its own 32 rows, with 32-row tiles (query only) the
-  // four waves stage their column blocks of the same 32 rows.
+  // done), each wave writing its accumulator blocks; then wave w stores rows 32w..32w+31
+  // (128-row tiles) or the block stores the 32 rows (32-row tiles, query only).
   static_assert(kEpi != kEpiKey || kTM == 128, "the key epilogue takes 128-row tiles");
   __syncthreads();
   uint8_t* stage = smem + (kTM == 128 ? wave * kPStageBytes : 0);
@@ -284,7 +311,7 @@ __global__ void __launch_bounds__(256) proj_gemm_kernel(ProjArgs p) {
       uint32_t code;
       if (kEpi == kEpiKey) code = sc[e] > 0.f ? e4m3_rne_sat(acc[cb][e] / sc[e]) : 0u;
       else code = e4m3_rne_sat(acc[cb][e]);
-      stage[r * kPN + 32 * (wcb0 + cb) + hl] = (uint8_t)code;
+      smem[(blk_row(cb) + r) * kPN + blk_col(cb) + hl] = (uint8_t)code;
     }
   __syncthreads();
   // 32 rows x 8 chunks of 16 bytes: 4 per lane of each wave (128-row tiles) or 1 per thread
