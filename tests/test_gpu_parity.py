@@ -246,10 +246,10 @@ def test_sparse_mla_tuned(oracle_lib, entry, q_pos, qps, k):
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=1e-4)
 
 
-@pytest.mark.parametrize("rows,k", [(130, 128), (70, 256)])
+@pytest.mark.parametrize("rows,k", [(130, 256), (70, 512)])
 def test_sparse_mla_decode_two_and_four_way_splits(oracle_lib, rows, k):
-    """Decode batches whose rows split 2 ways (130 rows, k = 128; the headline batch's split) or
-    4 ways (70 rows, k = 256), as MTP pairs of positions t, t + 1. Tiny rows leave their later
+    """Decode batches whose rows split 2 ways (130 rows, k = 256; the headline batch's split) or
+    4 ways (70 rows, k = 512), as MTP pairs of positions t, t + 1. Tiny rows leave their later
     splits without a valid key, which the merge must skip. Two calls in a row give identical
     bits."""
     _say(f"case: sparse mla decode 2/4-way splits rows={rows} k={k}")

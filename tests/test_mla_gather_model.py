@@ -39,7 +39,7 @@ NBUF = 3           # tile buffers: two tiles in flight
 
 def pick_splits(rows, k):
     s = 1
-    while rows * s < 256 and (k // (s * 2)) >= 2 * NK:
+    while rows * s < 256 and (k // (s * 2)) >= 4 * NK:
         s *= 2
     return s
 

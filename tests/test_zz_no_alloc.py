@@ -3,7 +3,7 @@
 It runs the same kernels as dsa_sparse_mla_decode, with the split-merge workspace taken from the
 library's own device array instead of the caller's buffer, so its outputs must equal that entry
 point's bit for bit. Two calls in a row on the shared array, the second with a smaller input: a
-128-row batch (two splits per row, 256 units: most of the array) and then a 5-row one (32 splits
+128-row batch (two splits per row, 256 units: most of the array) and then a 5-row one (16 splits
 per row), so the second call runs over what the first left there. Also: a shape that needs no
 workspace (one split per row) and the rejection of a missing output tensor.
 """
