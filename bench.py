@@ -361,9 +361,9 @@ def _src_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was taken on the
-    current kernel source (else None)."""
+def measured_traffic(kernel_key, workload):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was taken on this
+    workload and the current kernel source (else None)."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
@@ -372,7 +372,7 @@ def measured_traffic(kernel_key):
     except Exception:
         return None
     ent = t.get(kernel_key)
-    if not ent or ent.get("source_hash") != _src_hash():
+    if not ent or ent.get("source_hash") != _src_hash() or ent.get("workload") != workload:
         return None
     return ent.get("bytes_per_launch")
 
@@ -446,7 +446,7 @@ def run_decode_bench(args):
     mla_bytes = by["mla"]
     achieved = mla_bytes / (ms[2] * 1e-3) / 1e9
     # the call's two launches: the attention kernel and the merge of its key splits
-    tr = [measured_traffic(key) for key in ("sparse_mla_decode", "sparse_mla_combine")]
+    tr = [measured_traffic(key, args.workload) for key in ("sparse_mla_decode", "sparse_mla_combine")]
     traffic = None if None in tr else sum(tr)
     roof = {"bound": "hbm", "kernel": "dsa_sparse_mla_decode (mla_mfma_kernel + mla_combine_kernel)",
             "achieved": round(achieved, 1),

@@ -55,3 +55,15 @@ def test_decode_step_model_uses_the_same_unit_costs():
     q_out = 128 * 576 * 2 + 128 * 512 * 2
     q8_w = 64 * 128 + 64 * 4
     assert by["step"] == c["decode_bytes"][1] + q_out + q8_w
+
+
+def test_measured_traffic_only_for_the_measured_workload_and_source():
+    """The bench's roofline takes HBM bytes from the committed counter summary only for the
+    workload and kernel source the counters were taken on."""
+    with open(os.path.join(HERE, "..", "profiles", "traffic.json")) as f:
+        t = json.load(f)
+    ent = t["sparse_mla_decode"]
+    got = bench.measured_traffic("sparse_mla_decode", ent["workload"])
+    assert got == (ent["bytes_per_launch"] if ent["source_hash"] == bench._src_hash() else None)
+    assert bench.measured_traffic("sparse_mla_decode", "decode_b16_4k") is None
+    assert bench.measured_traffic("no_such_kernel", ent["workload"]) is None
