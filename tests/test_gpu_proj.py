@@ -131,3 +131,72 @@ def test_key_projection_into_paged_cache(oracle_lib, n_tok, d, split):
     delta = 1.001 * (bound[toks] / s_ref[:, None] + np.abs(x) * (kmax_bound / kmax)[:, None]) + np.abs(x) * 2.0 ** -22
     same = _codes_within(kc_h.reshape(-1, 128)[rows], x, delta)
     print(f"key codes equal to the oracle's: {same:.6f}", flush=True)
+
+
+def _check_key_rows(kc_h, ks_h, rows, h_bits, w_bits, ref_k, ref_ks_rows):
+    """The scale and codes the GPU wrote at `rows` (one per sampled token, in order) against the
+    oracle's values for those tokens, within the fp32 summation bound (see the module notes)."""
+    d = h_bits.shape[1]
+    bound = d * 2.0 ** -24 * _sum_abs(h_bits, w_bits)
+    kmax_bound = bound.max(axis=1)
+    kmax = np.maximum(np.abs(ref_k).max(axis=1), 1e-30)
+    s_ref = ref_ks_rows.astype(np.float64)
+    s_gpu = ks_h.reshape(-1)[rows].astype(np.float64)
+    assert (np.abs(s_gpu - s_ref) <= kmax_bound / 448 + 2.0 ** -23 * s_ref).all()
+    x = ref_k / s_ref[:, None]
+    delta = 1.001 * (bound / s_ref[:, None] + np.abs(x) * (kmax_bound / kmax)[:, None]) + np.abs(x) * 2.0 ** -22
+    return _codes_within(kc_h.reshape(-1, 128)[rows], x, delta)
+
+
+def test_projections_at_the_benchmark_sizes(oracle_lib):
+    """The launch configurations the projection benchmark times, at its sizes, on sampled rows:
+    the key projection of a 131072-token prefix (128-row tiles, no workspace) and of a
+    4096-token chunk (K split eight ways), through a permuted 64-token page table, and the query
+    projection of a 4096-row chunk (query codes on 128-row tiles, head weights split eight ways).
+    Sampled: the first and last tokens / rows and seeded ones between."""
+    print("case: projections at the benchmark sizes", flush=True)
+    d, d_cq, Hi, Di, page, n = 7168, 1536, 64, 128, 64, 131072
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0xD5A1)
+    w_k = (torch.randn(Di, d, generator=g, device="cuda") / d ** 0.5).to(torch.bfloat16)
+    w_q = (torch.randn(Hi * Di, d_cq, generator=g, device="cuda") / d_cq ** 0.5).to(torch.bfloat16)
+    w_w = (torch.randn(Hi, d, generator=g, device="cuda") / d ** 0.5).to(torch.bfloat16)
+    h = torch.randn(n, d, generator=g, device="cuda").to(torch.bfloat16)
+    pt = torch.randperm(n // page, generator=g, device="cuda").to(torch.int32).view(1, -1)
+    seq = torch.zeros(n, dtype=torch.int32, device="cuda")
+    pos = torch.arange(n, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(7)
+    pt_h = pt.cpu().numpy()
+    wk_bits = _bits(w_k)
+    for nk, ws in ((n, False), (4096, None)):
+        kc = torch.full((n // page, page, Di), 0xAA, dtype=torch.uint8, device="cuda")
+        ks = torch.full((n // page, page), -1.0, dtype=torch.float32, device="cuda")
+        dsa.indexer_key_project(h[:nk], w_k, seq[:nk], pos[:nk], pt, kc, ks, ws=ws)
+        torch.cuda.synchronize()
+        toks = np.unique(np.concatenate([np.arange(4), np.arange(nk - 4, nk), rng.integers(0, nk, 40)]))
+        h_bits = _bits(h[torch.from_numpy(toks).cuda()])
+        ref_kc = np.zeros((n // page, page, Di), np.uint8)
+        ref_ks = np.full((n // page, page), -1.0, np.float32)
+        ref_k, skipped = oracle.indexer_key_project(h_bits, wk_bits, np.zeros(toks.size, np.int32),
+                                                    toks.astype(np.int32), pt_h, page, ref_kc, ref_ks)
+        assert skipped == 0
+        rows = [int(pt_h[0, t // page]) * page + t % page for t in toks]
+        kc_h, ks_h = kc.cpu().numpy(), ks.cpu().numpy()
+        same = _check_key_rows(kc_h, ks_h, rows, h_bits, wk_bits, ref_k, ref_ks.reshape(-1)[rows])
+        assert int((ks_h != -1.0).sum()) == nk  # every token has a page: one scale written per token
+        print(f"key projection of {nk} tokens: codes equal to the oracle's {same:.6f}", flush=True)
+    rows_q = 4096
+    c_q = torch.randn(rows_q, d_cq, generator=g, device="cuda").to(torch.bfloat16)
+    q8, w = dsa.indexer_query_project(c_q, w_q, h[:rows_q], w_w, Hi, Di)
+    assert dsa.last_path() == "project"
+    torch.cuda.synchronize()
+    r = np.unique(np.concatenate([np.arange(4), np.arange(rows_q - 4, rows_q), rng.integers(0, rows_q, 24)]))
+    ri = torch.from_numpy(r).cuda()
+    cq_bits, h_bits = _bits(c_q[ri]), _bits(h[:rows_q][ri])
+    ref_q8, ref_w, ref_q = oracle.indexer_query_project(cq_bits, _bits(w_q), h_bits, _bits(w_w), Hi, Di, threads=THREADS)
+    bound_w = d * 2.0 ** -24 * _sum_abs(h_bits, _bits(w_w))
+    err_w = np.abs(w[ri].cpu().numpy().astype(np.float64) - ref_w)
+    assert (err_w <= bound_w).all(), f"w: max err / bound {np.max(err_w / bound_w):.3f}"
+    bound_q = d_cq * 2.0 ** -24 * _sum_abs(cq_bits, _bits(w_q)).reshape(r.size, Hi, Di)
+    same = _codes_within(q8[ri].cpu().numpy(), ref_q, bound_q)
+    print(f"query projection of {rows_q} rows: codes equal to the oracle's {same:.6f}", flush=True)
