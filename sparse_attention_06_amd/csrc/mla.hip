@@ -803,19 +803,19 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
       const lds_u8* tile = lds + b_cur * kTileBytes;
 
       // ---- S^T = K Q^T: lane holds head lane%32, keys 8*(i/4) + 4*(lane/32) + i%4, i = 0..15
-      // S^T for this tile: the 4 rope k-steps (both operands from LDS) and the 32 latent k-steps,
-      // alternating between two accumulation chains, with 8 operand fetches in flight ahead of
-      // the MFMAs (into v224..v255); when a gather is due, its loads are issued between the
-      // MFMAs. Written as one asm block so that S stays in VGPRs (the AGPRs hold the output) and
-      // the fetches are not reordered. LDS reads complete in order, so each wait counts only the
-      // younger reads of this block; the trailing s_nops cover the MFMA-result to VALU-read
-      // latency of the softmax that follows.
+      // S^T for this tile: the 4 rope k-steps (both operands from LDS) and the 32 latent k-steps
+      // in one accumulation chain (back-to-back MFMAs on one accumulator measured slightly faster
+      // than two interleaved chains, with 16 fewer VGPRs), 8 operand fetches in flight ahead of
+      // the MFMAs (into v224..v255). Written as one asm block so that S stays in VGPRs (the AGPRs
+      // hold the output) and the fetches are not reordered. LDS reads complete in order, so each
+      // wait counts only the younger reads of this block; the trailing s_nops cover the
+      // MFMA-result to VALU-read latency of the softmax that follows.
       f32x16 s;
       {
         const uint32_t al = (uint32_t)(uintptr_t)(tile + g1_base);
         const uint32_t kb = (uint32_t)(uintptr_t)(tile + rope_base), qb = (uint32_t)(uintptr_t)(lds + qr_base);
         const uint32_t x0 = 32 * (0 ^ rope_x), x1 = 32 * (1 ^ rope_x), x2 = 32 * (2 ^ rope_x), x3 = 32 * (3 ^ rope_x);
-        f32x16 s0, s1;
+        f32x16 s0;
         asm volatile(
           "ds_read_b128 v[224:227], %[k0]\n"
           "ds_read_b128 v[228:231], %[r0]\n"
@@ -830,7 +830,7 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
           "ds_read_b128 v[224:227], %[al]\n"
           "ds_read_b128 v[228:231], %[al] offset:32\n"
           "s_waitcnt lgkmcnt(6)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[232:235], v[236:239], 0\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[232:235], v[236:239], %[s0]\n"
           "ds_read_b128 v[232:235], %[al] offset:64\n"
           "ds_read_b128 v[236:239], %[al] offset:96\n"
           "s_waitcnt lgkmcnt(6)\n"
@@ -838,106 +838,106 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
           "ds_read_b128 v[240:243], %[al] offset:128\n"
           "ds_read_b128 v[244:247], %[al] offset:160\n"
           "s_waitcnt lgkmcnt(6)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[248:251], v[252:255], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[248:251], v[252:255], %[s0]\n"
           "ds_read_b128 v[248:251], %[al] offset:192\n"
           "ds_read_b128 v[252:255], %[al] offset:224\n"
           "s_waitcnt lgkmcnt(7)\n"
           "v_mfma_f32_32x32x16_bf16 %[s0], v[224:227], %[q0], %[s0]\n"
           "ds_read_b128 v[224:227], %[al] offset:256\n"
           "s_waitcnt lgkmcnt(7)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[228:231], %[q1], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[228:231], %[q1], %[s0]\n"
           "ds_read_b128 v[228:231], %[al] offset:288\n"
           "s_waitcnt lgkmcnt(7)\n"
           "v_mfma_f32_32x32x16_bf16 %[s0], v[232:235], %[q2], %[s0]\n"
           "ds_read_b128 v[232:235], %[al] offset:320\n"
           "s_waitcnt lgkmcnt(7)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[236:239], %[q3], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[236:239], %[q3], %[s0]\n"
           "ds_read_b128 v[236:239], %[al] offset:352\n"
           "s_waitcnt lgkmcnt(7)\n"
           "v_mfma_f32_32x32x16_bf16 %[s0], v[240:243], %[q4], %[s0]\n"
           "ds_read_b128 v[240:243], %[al] offset:384\n"
           "s_waitcnt lgkmcnt(7)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[244:247], %[q5], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[244:247], %[q5], %[s0]\n"
           "ds_read_b128 v[244:247], %[al] offset:416\n"
           "s_waitcnt lgkmcnt(7)\n"
           "v_mfma_f32_32x32x16_bf16 %[s0], v[248:251], %[q6], %[s0]\n"
           "ds_read_b128 v[248:251], %[al] offset:448\n"
           "s_waitcnt lgkmcnt(7)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[252:255], %[q7], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[252:255], %[q7], %[s0]\n"
           "ds_read_b128 v[252:255], %[al] offset:480\n"
           "s_waitcnt lgkmcnt(7)\n"
           "v_mfma_f32_32x32x16_bf16 %[s0], v[224:227], %[q8], %[s0]\n"
           "ds_read_b128 v[224:227], %[al] offset:512\n"
           "s_waitcnt lgkmcnt(7)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[228:231], %[q9], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[228:231], %[q9], %[s0]\n"
           "ds_read_b128 v[228:231], %[al] offset:544\n"
           "s_waitcnt lgkmcnt(7)\n"
           "v_mfma_f32_32x32x16_bf16 %[s0], v[232:235], %[q10], %[s0]\n"
           "ds_read_b128 v[232:235], %[al] offset:576\n"
           "s_waitcnt lgkmcnt(7)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[236:239], %[q11], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[236:239], %[q11], %[s0]\n"
           "ds_read_b128 v[236:239], %[al] offset:608\n"
           "s_waitcnt lgkmcnt(7)\n"
           "v_mfma_f32_32x32x16_bf16 %[s0], v[240:243], %[q12], %[s0]\n"
           "ds_read_b128 v[240:243], %[al] offset:640\n"
           "s_waitcnt lgkmcnt(7)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[244:247], %[q13], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[244:247], %[q13], %[s0]\n"
           "ds_read_b128 v[244:247], %[al] offset:672\n"
           "s_waitcnt lgkmcnt(7)\n"
           "v_mfma_f32_32x32x16_bf16 %[s0], v[248:251], %[q14], %[s0]\n"
           "ds_read_b128 v[248:251], %[al] offset:704\n"
           "s_waitcnt lgkmcnt(7)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[252:255], %[q15], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[252:255], %[q15], %[s0]\n"
           "ds_read_b128 v[252:255], %[al] offset:736\n"
           "s_waitcnt lgkmcnt(7)\n"
           "v_mfma_f32_32x32x16_bf16 %[s0], v[224:227], %[q16], %[s0]\n"
           "ds_read_b128 v[224:227], %[al] offset:768\n"
           "s_waitcnt lgkmcnt(7)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[228:231], %[q17], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[228:231], %[q17], %[s0]\n"
           "ds_read_b128 v[228:231], %[al] offset:800\n"
           "s_waitcnt lgkmcnt(7)\n"
           "v_mfma_f32_32x32x16_bf16 %[s0], v[232:235], %[q18], %[s0]\n"
           "ds_read_b128 v[232:235], %[al] offset:832\n"
           "s_waitcnt lgkmcnt(7)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[236:239], %[q19], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[236:239], %[q19], %[s0]\n"
           "ds_read_b128 v[236:239], %[al] offset:864\n"
           "s_waitcnt lgkmcnt(7)\n"
           "v_mfma_f32_32x32x16_bf16 %[s0], v[240:243], %[q20], %[s0]\n"
           "ds_read_b128 v[240:243], %[al] offset:896\n"
           "s_waitcnt lgkmcnt(7)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[244:247], %[q21], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[244:247], %[q21], %[s0]\n"
           "ds_read_b128 v[244:247], %[al] offset:928\n"
           "s_waitcnt lgkmcnt(7)\n"
           "v_mfma_f32_32x32x16_bf16 %[s0], v[248:251], %[q22], %[s0]\n"
           "ds_read_b128 v[248:251], %[al] offset:960\n"
           "s_waitcnt lgkmcnt(7)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[252:255], %[q23], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[252:255], %[q23], %[s0]\n"
           "ds_read_b128 v[252:255], %[al] offset:992\n"
           "s_waitcnt lgkmcnt(7)\n"
           "v_mfma_f32_32x32x16_bf16 %[s0], v[224:227], %[q24], %[s0]\n"
           "s_waitcnt lgkmcnt(6)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[228:231], %[q25], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[228:231], %[q25], %[s0]\n"
           "s_waitcnt lgkmcnt(5)\n"
           "v_mfma_f32_32x32x16_bf16 %[s0], v[232:235], %[q26], %[s0]\n"
           "s_waitcnt lgkmcnt(4)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[236:239], %[q27], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[236:239], %[q27], %[s0]\n"
           "s_waitcnt lgkmcnt(3)\n"
           "v_mfma_f32_32x32x16_bf16 %[s0], v[240:243], %[q28], %[s0]\n"
           "s_waitcnt lgkmcnt(2)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[244:247], %[q29], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[244:247], %[q29], %[s0]\n"
           "s_waitcnt lgkmcnt(1)\n"
           "v_mfma_f32_32x32x16_bf16 %[s0], v[248:251], %[q30], %[s0]\n"
           "s_waitcnt lgkmcnt(0)\n"
-          "v_mfma_f32_32x32x16_bf16 %[s1], v[252:255], %[q31], %[s1]\n"
+          "v_mfma_f32_32x32x16_bf16 %[s0], v[252:255], %[q31], %[s0]\n"
           "s_nop 7\n"
           "s_nop 7\n"
           "s_nop 7\n"
-          : [s0] "=&v"(s0), [s1] "=&v"(s1)
+          : [s0] "=&v"(s0)
           : [al] "v"(al), [k0] "v"(kb + x0), [k1] "v"(kb + x1), [k2] "v"(kb + x2), [k3] "v"(kb + x3),
             [r0] "v"(qb + x0), [r1] "v"(qb + x1), [r2] "v"(qb + x2), [r3] "v"(qb + x3),
             [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]), [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]), [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]), [q14] "v"(qf[14]), [q15] "v"(qf[15]), [q16] "v"(qf[16]), [q17] "v"(qf[17]), [q18] "v"(qf[18]), [q19] "v"(qf[19]), [q20] "v"(qf[20]), [q21] "v"(qf[21]), [q22] "v"(qf[22]), [q23] "v"(qf[23]), [q24] "v"(qf[24]), [q25] "v"(qf[25]), [q26] "v"(qf[26]), [q27] "v"(qf[27]), [q28] "v"(qf[28]), [q29] "v"(qf[29]), [q30] "v"(qf[30]), [q31] "v"(qf[31])
           : "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255", "memory");
-        s = s0 + s1;
+        s = s0;
       }
       // ---- softmax bookkeeping in the log2 domain; the two lanes of a head see all 32 keys.
       //      c_scale > 0, so the largest raw score gives the largest logit.
