@@ -381,8 +381,12 @@ struct TopkStageArgs {
                     // chunk stage adds its selection's counts, the merge starts from them
 };
 
-template <bool kSrcScores, bool kFinal>
-__global__ void __launch_bounds__(kTopkThreads) topk_stage_kernel(TopkStageArgs a) {
+// kPacked: two workgroups per CU (at most 64 VGPRs, a few spilled), for grids of many rows or
+// chunks, where a second workgroup's work overlaps the first's barrier-bound phases; one
+// workgroup per CU otherwise (no spills).
+template <bool kSrcScores, bool kFinal, bool kPacked>
+__global__ void __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(kPacked ? 8 : 4, 8)))
+topk_stage_kernel(TopkStageArgs a) {
   __shared__ __attribute__((aligned(16))) TopkLds sh;
   const int r = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -518,6 +522,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_stage_kernel(TopkStageArgs 
 // then position), and the candidates stay in ascending position order, so ties still go to the
 // smaller position. Usable while every row's candidates fit one block.
 static_assert(kRegKeys == kTopkChunkKeys, "chunks of the first-digit counts");
+// Stage grids of at least this many workgroups (two per CU) take the packed stage kernel.
+constexpr int kTopkPackedGrid = 512;
 int topk_reg_max_ctx() { return kRegKeys; }
 int topk_reg_max_k() { return kCandCap; }
 int topk_chunks(int max_ctx) { return (max_ctx + kRegKeys - 1) / kRegKeys; }
@@ -539,7 +545,10 @@ hipError_t launch_topk(const float* scores, int64_t ld_scores, const int32_t* q_
   if (max_ctx <= kRegKeys && k <= kCandCap) {
     a.hist0 = hist0;
     *path = (max_ctx <= k) ? DSA_PATH_TOPK_COPY : DSA_PATH_TOPK_RADIX_REG;
-    hipLaunchKernelGGL((topk_stage_kernel<true, true>), dim3(1, rows), dim3(kTopkThreads), 0, stream, a);
+    if (rows >= kTopkPackedGrid)
+      hipLaunchKernelGGL((topk_stage_kernel<true, true, true>), dim3(1, rows), dim3(kTopkThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((topk_stage_kernel<true, true, false>), dim3(1, rows), dim3(kTopkThreads), 0, stream, a);
     return hipGetLastError();
   }
   const size_t need = topk_staged_ws_bytes(rows, max_ctx, k);
@@ -555,14 +564,20 @@ hipError_t launch_topk(const float* scores, int64_t ld_scores, const int32_t* q_
     a.hist0 = hist0;
     // with the chunks' counts given, the merge's candidate counts follow the chunks' histograms
     a.mhist = hist0 ? hist0 + (size_t)rows * C * kRegBins : nullptr;
-    hipLaunchKernelGGL((topk_stage_kernel<true, false>), dim3(C, rows), dim3(kTopkThreads), 0, stream, a);
+    if ((int64_t)C * rows >= kTopkPackedGrid)
+      hipLaunchKernelGGL((topk_stage_kernel<true, false, true>), dim3(C, rows), dim3(kTopkThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((topk_stage_kernel<true, false, false>), dim3(C, rows), dim3(kTopkThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     TopkStageArgs b = a;
     b.in_key = a.out_key; b.in_pos = a.out_pos; b.in_cnt = a.out_cnt; b.in_chunks = C;
     b.out_key = nullptr; b.out_pos = nullptr; b.out_cnt = nullptr; b.out_chunks = 0;
     b.hist0 = nullptr;
-    hipLaunchKernelGGL((topk_stage_kernel<false, true>), dim3(1, rows), dim3(kTopkThreads), 0, stream, b);
+    if (rows >= kTopkPackedGrid)
+      hipLaunchKernelGGL((topk_stage_kernel<false, true, true>), dim3(1, rows), dim3(kTopkThreads), 0, stream, b);
+    else
+      hipLaunchKernelGGL((topk_stage_kernel<false, true, false>), dim3(1, rows), dim3(kTopkThreads), 0, stream, b);
     return hipGetLastError();
   }
   const int cap = max_ctx < kTopkLdsCap ? max_ctx : kTopkLdsCap;

@@ -119,6 +119,24 @@ def test_topk_matches_oracle_exactly(oracle_lib, n, k):
     np.testing.assert_array_equal(g, r)
 
 
+@pytest.mark.parametrize("rows,n", [(520, 5000), (512, 20000), (64, 131072)])
+def test_topk_many_rows_two_workgroups_per_cu(oracle_lib, rows, n):
+    """Grids of 512 or more workgroups run the stage kernel at two workgroups per CU (register
+    budget halved): 520 short rows (one stage), 512 rows of 20000 (two chunks each, then a
+    512-row merge) and 64 rows of 131072 (8 chunks each: 512 chunk workgroups, then a 64-row
+    merge at one workgroup per CU). Row lengths vary from k - 1 to the full width; bit-exact
+    against the oracle."""
+    _say(f"case: topk packed rows={rows} n={n}")
+    rng = np.random.default_rng(rows + n)
+    k = 2048
+    sc = rng.standard_normal((rows, n)).astype(np.float32)
+    sc[:, rng.integers(0, n, 64)] = 0.5  # some equal scores across each row
+    q_pos = rng.integers(k // 2, n, rows).astype(np.int32)
+    q_pos[:3] = [n - 1, k - 1, k]
+    g, r = _topk_case(sc, q_pos, k)
+    np.testing.assert_array_equal(g, r)
+
+
 @pytest.mark.parametrize("n", [20000, 16000])
 def test_topk_ties_and_signed_zeros(oracle_lib, n):
     _say(f"case: topk ties n={n}")
