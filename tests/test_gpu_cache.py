@@ -126,3 +126,37 @@ def test_written_cache_feeds_the_indexer(oracle_lib):
     ref = oracle_lib.indexer_scores(q8.cpu().numpy(), w, ref_c, ref_s, pt, page, q_pos, n_seq, qps, oracle_lib.E4M3, L,
                                     threads=8)
     check_scores(scores.cpu().numpy(), ref, q_pos)
+
+
+def test_cache_writes_at_the_benchmark_sizes(oracle_lib):
+    """The calls the cache-write benchmark times, at its sizes and launch shapes, bit for bit: the
+    indexer keys of a 131072-token sequence (f32, per-token scale) and its latent rows written
+    through a permuted 64-token page table, and a 4096-row block of indexer queries quantised."""
+    print("case: cache writes at the benchmark sizes", flush=True)
+    n, page = 131072, 64
+    pages = n // page
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0xD5A2)
+    pt = torch.randperm(pages, generator=g, device="cuda").to(torch.int32).view(1, pages)
+    seq = torch.zeros(n, dtype=torch.int32, device="cuda")
+    pos = torch.arange(n, dtype=torch.int32, device="cuda")
+    k = torch.randn(n, 128, generator=g, device="cuda")
+    rows = torch.randn(n, 576, generator=g, device="cuda").to(torch.bfloat16)
+    kc = torch.full((pages, page, 128), 0x5A, dtype=torch.uint8, device="cuda")
+    ks = torch.full((pages, page), -2.0, dtype=torch.float32, device="cuda")
+    kv = torch.zeros(pages, page, 576, dtype=torch.bfloat16, device="cuda")
+    q = torch.randn(4096, 64, 128, generator=g, device="cuda")
+    dsa.indexer_cache_write(k, seq, pos, pt, kc, ks)
+    dsa.latent_cache_write(rows, seq, pos, pt, kv)
+    q8 = dsa.e4m3_quantize(q)
+    torch.cuda.synchronize()
+    pt_h, seq_h, pos_h = pt.cpu().numpy(), seq.cpu().numpy(), pos.cpu().numpy()
+    ref_c = np.full((pages, page, 128), 0x5A, np.uint8)
+    ref_s = np.full((pages, page), -2.0, np.float32)
+    assert oracle_lib.indexer_cache_write(k.cpu().numpy(), seq_h, pos_h, pt_h, page, ref_c, ref_s) == 0
+    np.testing.assert_array_equal(kc.cpu().numpy(), ref_c)
+    np.testing.assert_array_equal(ks.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+    ref_kv = np.zeros((pages, page, 576), np.uint16)
+    oracle_lib.latent_cache_write(rows.view(torch.int16).cpu().numpy().view(np.uint16), seq_h, pos_h, pt_h, page, ref_kv)
+    np.testing.assert_array_equal(kv.view(torch.int16).cpu().numpy().view(np.uint16), ref_kv)
+    np.testing.assert_array_equal(q8.cpu().numpy().reshape(-1), oracle_lib.e4m3_quantize(q.cpu().numpy().reshape(-1)))
