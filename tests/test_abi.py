@@ -124,3 +124,51 @@ def test_row_descriptor_checks(lib):
     st = lib.dsa_sparse_mla_prefill(fake, fake, fake, 1, 64, 1, fake, fake, 3, 2, 2, fake, 8, 8, 128, 576, 512, 576,
                                     0, ctypes.c_float(0.1), fake, NULL, NULL, 0, NULL)
     assert st == dsa.DSA_ERR_INVALID_ARG
+
+
+def _attention_splits(rows, k, nk=32):
+    """The decode split rule restated: double while fewer than 256 workgroups and each split keeps
+    at least 4 tiles of nk keys."""
+    s = 1
+    while rows * s < 256 and k // (s * 2) >= 4 * nk:
+        s *= 2
+    return s
+
+
+def _align256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("rows,k", [(1, 2048), (4, 2048), (16, 2048), (64, 2048), (128, 2048), (130, 256), (255, 2048),
+                                    (256, 2048), (3, 128), (5, 100)])
+def test_attention_split_workspace_follows_the_split_rule(lib, rows, k):
+    """Workspace bytes of the decode split: fp16 partials [units, 128, 512] and (max, sum) pairs
+    [units, 128], each part 256-byte aligned, for units = rows x splits; none without a split."""
+    s = _attention_splits(rows, k)
+    want = 0 if s == 1 else _align256(rows * s * 128 * 512 * 2) + _align256(rows * s * 128 * 8)
+    assert lib.dsa_sparse_mla_workspace_size(rows, 128, 512, k) == want
+
+
+def _projection_ws(M, N, K):
+    """The projection split-K plan restated: split only when 128-row tiles give fewer than 512
+    workgroups; then deal K blocks of 64 so that about 1024 32-row workgroups run, at most 16 ways."""
+    n_tiles = (N + 127) // 128
+    tiles = (M + 31) // 32 * n_tiles
+    kb = K // 64
+    if (M + 127) // 128 * n_tiles >= 512 or kb < 2:
+        return 0
+    want = min(1024 // tiles, kb, 16)
+    if want < 2:
+        return 0
+    per = (kb + want - 1) // want
+    kz = (kb + per - 1) // per
+    return kz * M * N * 4 if kz > 1 else 0
+
+
+@pytest.mark.parametrize("rows,d", [(1, 7168), (128, 7168), (600, 7168), (3900, 7168), (4096, 7168), (16384, 7168),
+                                    (65536, 7168), (131072, 7168), (300, 128), (37, 64)])
+def test_projection_workspace_follows_the_split_plan(lib, rows, d):
+    """The projection workspace covers the split-K partials of both calls' GEMMs (keys: N = 128;
+    head weights: N = 64)."""
+    want = max(_projection_ws(rows, 128, d), _projection_ws(rows, 64, d))
+    assert lib.dsa_indexer_projection_workspace_size(rows, d) == want
