@@ -73,13 +73,13 @@ static inline dim3 tile_grid(int tiles, int z = 1) { return dim3(8 * ((tiles + 7
 // Tile t's first row and column. Tiles come in groups of 8 row tiles by all column tiles, row
 // tiles fastest within a group: the workgroups an XCD runs at once then cover about 8 row tiles x
 // 8 column tiles, each operand panel shared through its L2 eight ways.
-__device__ __forceinline__ void tile_origin(const ProjArgs& p, int t, int tm, int* m0, int* n0) {
+__device__ __forceinline__ void tile_origin(const ProjArgs& p, int t, int tm, int* m0, int* n0, int tn = kPN) {
   constexpr int kGroup = 8;
   const int n_tiles = p.tiles / p.tiles_m;
   const int g = t / (kGroup * n_tiles), first = kGroup * g;
   const int gs = min(p.tiles_m - first, kGroup), r = t - g * kGroup * n_tiles;
   *m0 = (first + r % gs) * tm;
-  *n0 = (r / gs) * kPN;
+  *n0 = (r / gs) * tn;
 }
 
 // The K loop of a 128 x 128 tile over the whole K, through the LDS ring. Wave w moves rows
@@ -413,6 +413,112 @@ __global__ void __launch_bounds__(256) proj_reduce_kernel(ProjArgs p, int kz) {
   if (j == 0) p.k_scale[row] = s;
 }
 
+// Query codes of prefill-sized batches: 8 waves, a 256 x 256 output tile, K blocks of 64 in a
+// two-stage LDS ring (64 KB a stage, one workgroup per CU), loaded and swizzled as in
+// gemm_loop_lds_ring (wave w moves rows 32w..32w+31 of each operand). Wave w owns rows
+// 64 (w / 2) .. +63 and columns 128 (w % 2) .. +127 (acc[4 mi + ci]: rows 64 (w / 2) + 32 mi,
+// columns 128 (w % 2) + 32 ci), so a K step reads 2 + 4 operands for 8 MFMAs; and a K block
+// loads 64 KB for 8.4 MFLOP, half the bytes per FLOP of a 128 x 128 tile, whose loop is bound by
+// its loads' issue. The codes are staged as [row][256] bytes in LDS and stored 16 bytes a lane.
+constexpr int kBT = 256;                       // tile edge
+constexpr int kBStage = 2 * kBT * 2 * kPK;     // 65536: one K block of A and B
+__global__ void __launch_bounds__(512) proj_query_big_kernel(ProjArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kBStage];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane & 31, half = lane >> 5;
+  const int tile = tile_of(p);
+  if (tile < 0) return;
+  int m0, n0;
+  tile_origin(p, tile, kBT, &m0, &n0, kBT);
+  const int nkb = p.K / kPK;
+  const uint32_t k_bytes = 2u * (uint32_t)p.K;
+  const uint32_t chunk = 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+  const int max_ra = p.M - 1 - m0, max_rb = p.N - 1 - n0;
+  uint32_t va[4], vb[4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const int r = 32 * wave + 8 * ii + (lane >> 3);
+    va[ii] = (uint32_t)min(r, max_ra) * k_bytes + chunk;
+    vb[ii] = (uint32_t)min(r, max_rb) * k_bytes + chunk;
+  }
+  const uint8_t* ga = (const uint8_t*)(p.a + (int64_t)m0 * p.K);
+  const uint8_t* gb = (const uint8_t*)(p.b + (int64_t)n0 * p.K);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  auto issue = [&](int kb, int st) {
+    const uint64_t sa = (uint64_t)(uintptr_t)(ga + 2 * kPK * kb), sb = (uint64_t)(uintptr_t)(gb + 2 * kPK * kb);
+    const uint32_t la = __builtin_amdgcn_readfirstlane(lds0 + st * kBStage + 4096 * wave);
+    const uint32_t lb = la + kBStage / 2;
+    uint32_t sv;
+    asm volatile(
+        "s_mov_b32 %[sv], m0\n"
+        "s_mov_b32 m0, %[la]\n s_nop 0\n global_load_lds_dwordx4 %[a0], %[sa]\n"
+        "s_add_u32 m0, %[la], 1024\n s_nop 0\n global_load_lds_dwordx4 %[a1], %[sa]\n"
+        "s_add_u32 m0, %[la], 2048\n s_nop 0\n global_load_lds_dwordx4 %[a2], %[sa]\n"
+        "s_add_u32 m0, %[la], 3072\n s_nop 0\n global_load_lds_dwordx4 %[a3], %[sa]\n"
+        "s_mov_b32 m0, %[lb]\n s_nop 0\n global_load_lds_dwordx4 %[b0], %[sb]\n"
+        "s_add_u32 m0, %[lb], 1024\n s_nop 0\n global_load_lds_dwordx4 %[b1], %[sb]\n"
+        "s_add_u32 m0, %[lb], 2048\n s_nop 0\n global_load_lds_dwordx4 %[b2], %[sb]\n"
+        "s_add_u32 m0, %[lb], 3072\n s_nop 0\n global_load_lds_dwordx4 %[b3], %[sb]\n"
+        "s_mov_b32 m0, %[sv]\n"
+        : [sv] "=&s"(sv)
+        : [sa] "s"(sa), [sb] "s"(sb), [la] "s"(la), [lb] "s"(lb), [a0] "v"(va[0]), [a1] "v"(va[1]),
+          [a2] "v"(va[2]), [a3] "v"(va[3]), [b0] "v"(vb[0]), [b1] "v"(vb[1]), [b2] "v"(vb[2]), [b3] "v"(vb[3])
+        : "scc", "memory");
+  };
+  uint32_t co[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) co[j] = 16u * (uint32_t)((4 * half + j) ^ (hl & 7));
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x16 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
+  issue(0, 0);
+  int st = 0;
+  for (int kb = 0; kb < nkb; ++kb) {
+    // the wave's loads of block kb are the only ones in flight; the barrier then makes every
+    // wave's visible and frees the other stage (its last reader was the previous block)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (kb + 1 < nkb) issue(kb + 1, st ^ 1);
+    const uint8_t* sa = smem + st * kBStage;
+    const uint8_t* sb = sa + kBStage / 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8 a[2], b[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = *(const bf16x8*)(sa + (64 * wm + 32 * i + hl) * 128 + co[j]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) b[c] = *(const bf16x8*)(sb + (128 * wn + 32 * c + hl) * 128 + co[j]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[4 * i + c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[c], acc[4 * i + c], 0, 0, 0);
+    }
+    st ^= 1;
+  }
+  // codes staged [row][256] in LDS (the ring is done once every wave passes the barrier)
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = 64 * wm + 32 * i + 8 * (e >> 2) + 4 * half + (e & 3);
+        smem[r * kBT + 128 * wn + 32 * c + hl] = (uint8_t)e4m3_rne_sat(acc[4 * i + c][e]);
+      }
+  __syncthreads();
+  // wave w stores rows 32w..32w+31: 16 chunks of 16 bytes a row, 8 a lane
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = lane + 64 * i, r = c >> 4, ch = c & 15;
+    const int m = m0 + 32 * wave + r;
+    if (m >= p.M || n0 + 16 * ch >= p.N) continue;
+    *(i32x4*)(p.q8 + (int64_t)m * p.N + n0 + 16 * ch) = *(const i32x4*)(smem + (32 * wave + r) * kBT + 16 * ch);
+  }
+}
+
 // Split-K is taken when the unsplit launch (128-row tiles) would give fewer than two workgroups
 // per CU: the K blocks of 64 are dealt out over 32-row tiles so that about 1024 workgroups run
 // (a projection of a few thousand rows onto 64 or 128 columns over d = 7168 otherwise runs on a
@@ -465,10 +571,15 @@ hipError_t launch_indexer_query_project(const uint16_t* c_q, const uint16_t* w_q
                                         float* w, void* ws, size_t ws_bytes, hipStream_t stream) {
   ProjArgs p{};
   p.a = c_q; p.b = w_q; p.M = rows; p.N = n_q; p.K = d_cq; p.q8 = q8;
-  // small batches take 32-row tiles, so that the column tiles spread over the GPU
+  // small batches take 32-row tiles, so that the column tiles spread over the GPU; batches that
+  // give every CU a 256 x 256 tile take those
+  const int big_tiles = ((rows + kBT - 1) / kBT) * ((n_q + kBT - 1) / kBT);
   const int tm = rows <= 512 ? 32 : kPM;
   p.tiles_m = (rows + tm - 1) / tm; p.tiles = p.tiles_m * ((n_q + kPN - 1) / kPN);
-  if (tm == 32)
+  if (big_tiles >= 256) {
+    p.tiles_m = (rows + kBT - 1) / kBT; p.tiles = big_tiles;
+    hipLaunchKernelGGL(proj_query_big_kernel, tile_grid(p.tiles), dim3(512), 0, stream, p);
+  } else if (tm == 32)
     hipLaunchKernelGGL((proj_gemm_kernel<kEpiQuery, 32>), tile_grid(p.tiles), dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((proj_gemm_kernel<kEpiQuery, 128>), tile_grid(p.tiles), dim3(256), 0, stream, p);
