@@ -10,23 +10,25 @@
 //   [Handbook]  "MTP 与稀疏注意力：NSA 与 DSA" (anrans.github.io): 64 indexer heads of 128 dims,
 //               scored in FP8; the key cache stores 128 FP8 codes plus a float scale per token
 //
-// One GEMM kernel, C[M x N] = A[M x K] . B[N x K]^T with bf16 operands (both K-contiguous: the
-// activations row-major, the weights in the [out, in] layout of a linear layer) on
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation, and three epilogues:
+// GEMMs C[M x N] = A[M x K] . B[N x K]^T with bf16 operands (both K-contiguous: the activations
+// row-major, the weights in the [out, in] layout of a linear layer) on v_mfma_f32_32x32x16_bf16
+// with fp32 accumulation, and three epilogues:
 //   key    N = 128: per row (token) s = max|c| / 448 and codes E4M3(c / s), written to the token's
 //          physical row of the paged key cache (the format dsa_indexer_cache_write writes)
 //   query  codes E4M3(c) without a scale, row-major [M, N] bytes
 //   f32    c as fp32, row-major [M, N]
-// Workgroup: 4 waves, a 128 x 128 output tile, K in blocks of 64. Wave w owns rows 32w..32w+31 of
-// the tile and all 128 columns (four 32 x 32 accumulator blocks). Within a block of 64 the K order
-// is permuted the same way for both operands (lane half h supplies elements 32h + 8j .. +8 as its
+// proj_gemm_kernel: 4 waves, a 128 x 128 output tile, K in blocks of 64; each wave owns four 32 x 32
+// accumulator blocks (a 64 x 64 quarter of the tile, or for keys rows 32w..32w+31 and all 128
+// columns, so that a row's scale stays within a wave). Within a block of 64 the K order is
+// permuted the same way for both operands (lane half h supplies elements 32h + 8j .. +8 as its
 // part of MFMA j), which leaves every dot product unchanged. The K blocks go straight from global
 // memory into a ring of kPStages LDS stages (global_load_lds_dwordx4, no register staging), issued
 // kPStages - 1 blocks ahead, one workgroup barrier per block; an LDS row of a block is its 128
 // bytes, 16-byte chunk c of row r stored at c ^ (r % 8), so the operand reads of 8 consecutive
 // rows hit distinct banks. Small batches (32-row tiles, and the split-K partials) stage through
 // registers instead: the next block is loaded into registers while the current one is
-// multiplied, LDS rows padded to 144 bytes.
+// multiplied, LDS rows padded to 144 bytes. proj_query_big_kernel: query codes of large batches
+// on 256 x 256 tiles with 8 waves, the same ring and swizzle.
 #include "dsa_internal.h"
 
 namespace dsa {
