@@ -200,3 +200,39 @@ def test_projections_at_the_benchmark_sizes(oracle_lib):
     bound_q = d_cq * 2.0 ** -24 * _sum_abs(cq_bits, _bits(w_q)).reshape(r.size, Hi, Di)
     same = _codes_within(q8[ri].cpu().numpy(), ref_q, bound_q)
     print(f"query projection of {rows_q} rows: codes equal to the oracle's {same:.6f}", flush=True)
+
+
+@pytest.mark.parametrize("rows,Hi,Di", [(5, 3, 16), (700, 3, 16), (300, 5, 32)])
+def test_query_projection_narrow_heads(oracle_lib, rows, Hi, Di):
+    """Query widths that end inside a 128-column tile (48 and 160 columns): the tile's missing
+    columns re-read the last weight row and are never stored; head-weight widths of 3 and 5."""
+    print(f"case: narrow query projection rows={rows} Hi={Hi} Di={Di}", flush=True)
+    d, d_cq = 192, 128
+    h, c_q, _, w_q, w_w = _case(700 + rows + Hi, rows, d, d_cq, Hi=Hi, Di=Di)
+    q8 = torch.full((rows, Hi, Di), 0x5A, dtype=torch.uint8, device="cuda")
+    q8, w = dsa.indexer_query_project(c_q, w_q, h, w_w, Hi, Di, q8=q8)
+    torch.cuda.synchronize()
+    ref_q8, ref_w, ref_q = oracle.indexer_query_project(_bits(c_q), _bits(w_q), _bits(h), _bits(w_w), Hi, Di,
+                                                        threads=THREADS)
+    bound_w = d * 2.0 ** -24 * _sum_abs(_bits(h), _bits(w_w))
+    assert (np.abs(w.cpu().numpy().astype(np.float64) - ref_w) <= bound_w).all()
+    bound_q = d_cq * 2.0 ** -24 * _sum_abs(_bits(c_q), _bits(w_q)).reshape(rows, Hi, Di)
+    _codes_within(q8.cpu().numpy(), ref_q, bound_q)
+
+
+def test_key_projection_with_every_token_skipped(oracle_lib):
+    """Tokens with no sequence row or past the page table write nothing: the caches keep their
+    contents, with and without the split-K workspace; zero tokens is a no-op."""
+    print("case: key projection, all tokens skipped", flush=True)
+    h, _, w_k, _, _ = _case(991, 200, 256, 64)
+    pt = torch.arange(4, dtype=torch.int32, device="cuda").view(1, 4)
+    seq = torch.full((200,), -1, dtype=torch.int32, device="cuda")
+    seq[100:] = 0
+    pos = torch.arange(200, dtype=torch.int32, device="cuda") + 256   # rows 100.. are past the 4 pages
+    for ws in (None, False):
+        kc = torch.full((4, 64, 128), 0x77, dtype=torch.uint8, device="cuda")
+        ks = torch.full((4, 64), 3.0, dtype=torch.float32, device="cuda")
+        dsa.indexer_key_project(h, w_k, seq, pos, pt, kc, ks, ws=ws)
+        dsa.indexer_key_project(h[:0], w_k, seq[:0], pos[:0], pt, kc, ks, ws=ws)
+        torch.cuda.synchronize()
+        assert bool((kc == 0x77).all()) and bool((ks == 3.0).all())
