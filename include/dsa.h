@@ -323,8 +323,8 @@ dsa_status_t dsa_e4m3_quantize(const float* x, int64_t n, uint8_t* out, void* st
  * dsa_indexer_query_project -- q8[r, :] = E4M3(c_q[r, :] . w_q^T) (Hi * Di codes, no scale: the
  * pages give the indexer query none) and w[r, :] = h[r, :] . w_w^T in fp32, for `rows` rows.
  *   c_q [rows, d_cq] bf16 bits (the MLA query latent); w_q [Hi * Di, d_cq]; h [rows, d];
- *   w_w [Hi, d]; q8 [rows, Hi, Di] bytes out; w [rows, Hi] f32 out. d_cq and d multiples of 64,
- *   Hi * Di a multiple of 16.
+ *   w_w [Hi, d]; q8 [rows, Hi, Di] bytes out; w [rows, Hi] f32 out. d_cq and d multiples of 64
+ *   up to 65536 (both calls), Hi * Di a multiple of 16.
  * Workspace (both calls): with at least dsa_indexer_projection_workspace_size(rows, d) bytes at ws
  * (16-byte aligned, contents not preserved; rows = n_tok for the keys), a small batch whose output
  * tiles would leave most of the GPU idle splits K over workgroups (fp32 partial sums, then an

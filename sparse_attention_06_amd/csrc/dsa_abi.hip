@@ -426,6 +426,9 @@ dsa_status_t dsa_latent_cache_write(const uint16_t* rows, int n_tok, int kv_dim,
   return s == DSA_OK ? ok(DSA_PATH_CACHE_WRITE) : s;
 }
 
+// The projections' widest K: a 256-row tile's per-lane byte offsets (row x 2K) stay in 32 bits.
+constexpr int kProjMaxK = 65536;
+
 size_t dsa_indexer_projection_workspace_size(int rows, int d) {
   if (rows <= 0 || d < 64) return 0;
   const size_t k = dsa::proj_ws_bytes(rows, 128, d), w = dsa::proj_ws_bytes(rows, 64, d);
@@ -445,8 +448,9 @@ dsa_status_t dsa_indexer_key_project(const uint16_t* h, const uint16_t* w_k, int
   REQUIRE(page_size >= 1 && num_pages >= 1 && ld_pt >= 1, "bad paging (page_size %d, num_pages %d, ld_pt %lld)",
           page_size, num_pages, (long long)ld_pt);
   REQUIRE((int64_t)num_pages * page_size < ((int64_t)1 << 31), "cache larger than 2^31 rows");
-  if (Di != 128 || d % 64 != 0)
-    return fail(DSA_ERR_UNSUPPORTED, "the key projection takes Di = 128 and d a multiple of 64 (got Di %d, d %d)", Di, d);
+  if (Di != 128 || d % 64 != 0 || d > kProjMaxK)
+    return fail(DSA_ERR_UNSUPPORTED, "the key projection takes Di = 128 and d a multiple of 64 up to %d (got Di %d, d %d)",
+                kProjMaxK, Di, d);
   dsa::PagedCache kc{k_cache, page_table, ld_pt, page_size, num_pages};
   REQUIRE(!ws || ((uintptr_t)ws & 15u) == 0, "ws must be 16-byte aligned");
   dsa_status_t s = hip_status(dsa::launch_indexer_key_project(h, w_k, n_tok, d, n_seq, seq, pos, kc, k_cache, k_scale,
@@ -465,9 +469,9 @@ dsa_status_t dsa_indexer_query_project(const uint16_t* c_q, const uint16_t* w_q,
               ((uintptr_t)w & 3u) == 0,
           "c_q, w_q, h, w_w and q8 must be 16-byte aligned, w 4-byte aligned");
   REQUIRE((int64_t)Hi * Di < (1 << 30), "Hi * Di too large");
-  if (d_cq % 64 != 0 || d % 64 != 0 || (Hi * Di) % 16 != 0)
-    return fail(DSA_ERR_UNSUPPORTED, "the query projection takes d_cq and d multiples of 64 and Hi * Di a multiple of 16 "
-                                     "(got %d, %d, %d)", d_cq, d, Hi * Di);
+  if (d_cq % 64 != 0 || d % 64 != 0 || d_cq > kProjMaxK || d > kProjMaxK || (Hi * Di) % 16 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "the query projection takes d_cq and d multiples of 64 up to %d and Hi * Di a "
+                                     "multiple of 16 (got %d, %d, %d)", kProjMaxK, d_cq, d, Hi * Di);
   REQUIRE(!ws || ((uintptr_t)ws & 15u) == 0, "ws must be 16-byte aligned");
   dsa_status_t s = hip_status(dsa::launch_indexer_query_project(c_q, w_q, h, w_w, rows, d_cq, d, Hi * Di, Hi, q8, w,
                                                                  ws, ws_bytes, (hipStream_t)stream),

@@ -172,3 +172,15 @@ def test_projection_workspace_follows_the_split_plan(lib, rows, d):
     head weights: N = 64)."""
     want = max(_projection_ws(rows, 128, d), _projection_ws(rows, 64, d))
     assert lib.dsa_indexer_projection_workspace_size(rows, d) == want
+
+
+def test_projection_rejects_oversized_reduction_dims(lib):
+    """d and d_cq above 65536 are reported as unsupported before any launch."""
+    fake = ctypes.c_void_p(0x1000)
+    st = lib.dsa_indexer_key_project(fake, fake, 4, 65536 + 64, 128, fake, fake, 1, fake, 1, 64, 1, fake, fake, NULL, 0,
+                                     NULL)
+    assert st == dsa.DSA_ERR_UNSUPPORTED
+    st = lib.dsa_indexer_query_project(fake, fake, fake, fake, 4, 65536 + 64, 128, 64, 128, fake, fake, NULL, 0, NULL)
+    assert st == dsa.DSA_ERR_UNSUPPORTED
+    st = lib.dsa_indexer_query_project(fake, fake, fake, fake, 4, 128, 65536 + 64, 64, 128, fake, fake, NULL, 0, NULL)
+    assert st == dsa.DSA_ERR_UNSUPPORTED
