@@ -188,8 +188,9 @@ __device__ __forceinline__ void hist_add_keys(uint32_t* hist, const uint32_t (&k
 
 // Wave 0 picks the digit of the remaining-th largest key from a 2048-bin histogram (digits in
 // descending order): 64 coarse bins of 32 digits first, then the 32 digits of the chosen one.
-// Publishes {digit, keys with larger digits, keys with that digit} in pub.
-__device__ __forceinline__ void pick_digit_wave(const uint32_t* hist, uint32_t remaining, uint32_t* pub, int lane) {
+// Publishes {digit, keys with larger digits, keys with that digit} in pub and returns the digit
+// (the same in every lane). The histogram must hold at least `remaining` keys.
+__device__ __forceinline__ uint32_t pick_digit_wave(const uint32_t* hist, uint32_t remaining, uint32_t* pub, int lane) {
   // lane l owns coarse bin 63 - l: digits 32 * (63 - l) .. + 31
   const int c = 63 - lane;
   uint32_t csum = 0;
@@ -213,13 +214,27 @@ __device__ __forceinline__ void pick_digit_wave(const uint32_t* hist, uint32_t r
     pub[1] = fincl - f;
     pub[2] = f;
   }
+  return (uint32_t)(32 * cc + 31 - fl);
+}
+
+// Keys of `hist` (2048 bins) whose digit is at least d, summed over wave 0 (same in every lane).
+__device__ __forceinline__ uint32_t count_at_or_above_wave(const uint32_t* hist, uint32_t d, int lane) {
+  uint32_t s = 0;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int b0 = 32 * lane + 4 * v;
+    const uint4 q4 = *(const uint4*)(hist + b0);
+    s += ((uint32_t)b0 >= d ? q4.x : 0u) + ((uint32_t)b0 + 1 >= d ? q4.y : 0u) + ((uint32_t)b0 + 2 >= d ? q4.z : 0u) +
+         ((uint32_t)b0 + 3 >= d ? q4.w : 0u);
+  }
+  return __builtin_amdgcn_readlane(wave_incl_scan(s), 63);
 }
 
 struct TopkLds {
   uint32_t hist[3][kRegBins];  // one histogram per pass
   uint32_t cand_key[kCandCap], cand_pos[kCandCap];
   uint32_t wtot[kTopkWaves][2];
-  uint32_t pub[3][3];
+  uint32_t pub[4][4];
   uint32_t ncand;
 };
 
@@ -237,6 +252,30 @@ __device__ __forceinline__ void reg_select_init(TopkLds& sh, int tid, uint32_t* 
       ((uint4*)hist0)[i] = make_uint4(0u, 0u, 0u, 0u);
     }
     ((uint4*)&sh.hist[0][0])[i] = v;
+  }
+  if (tid == 0) sh.ncand = 0;
+}
+
+// The chunk stage of a long row whose chunks' first-digit counts are all given (hist_row: the row's
+// nchunks chunks of 2048 bins each, nchunks <= kTopkFilterChunks): sh.hist[0] takes this chunk's
+// counts, sh.hist[1] the row's (their sum), sh.hist[2] is zeroed. The counts stay in place, since
+// every chunk of the row reads them; the merge clears them.
+constexpr int kTopkFilterChunks = 8;
+__device__ __forceinline__ void filter_init(TopkLds& sh, int tid, const uint32_t* hist_row, int nchunks, int c) {
+  for (int i = tid; i < kRegBins / 4; i += kTopkThreads) {
+    uint4 v[kTopkFilterChunks];
+#pragma unroll
+    for (int ch = 0; ch < kTopkFilterChunks; ++ch)
+      v[ch] = ch < nchunks ? ((const uint4*)(hist_row + (size_t)ch * kRegBins))[i] : make_uint4(0u, 0u, 0u, 0u);
+    uint4 sum = make_uint4(0u, 0u, 0u, 0u), own = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int ch = 0; ch < kTopkFilterChunks; ++ch) {
+      sum.x += v[ch].x; sum.y += v[ch].y; sum.z += v[ch].z; sum.w += v[ch].w;
+      if (ch == c) own = v[ch];
+    }
+    ((uint4*)&sh.hist[0][0])[i] = own;
+    ((uint4*)&sh.hist[1][0])[i] = sum;
+    ((uint4*)&sh.hist[2][0])[i] = make_uint4(0u, 0u, 0u, 0u);
   }
   if (tid == 0) sh.ncand = 0;
 }
@@ -379,6 +418,9 @@ struct TopkStageArgs {
   uint32_t* hist0;  // score rows: per row and chunk, the first-digit histogram (or null)
   uint32_t* mhist;  // per row, the first-digit histogram of the merge's candidates (or null): the
                     // chunk stage adds its selection's counts, the merge starts from them
+  int row_filter;   // chunk stage with hist0 and mhist over at most kTopkFilterChunks chunks: each
+                    // chunk passes on its keys whose first digit reaches the row's threshold digit
+                    // (from the sum of the row's chunk counts), and the merge clears those counts
 };
 
 // kPacked: two workgroups per CU (at most 64 VGPRs, a few spilled), for grids of many rows or
@@ -393,6 +435,7 @@ topk_stage_kernel(TopkStageArgs a) {
   uint32_t key[kRegE], vmask = 0;
   uint32_t* const hist0 = kSrcScores ? (a.hist0 ? a.hist0 + ((int64_t)r * gridDim.x + c) * kRegBins : nullptr)
                                      : (a.mhist ? a.mhist + (int64_t)r * kRegBins : nullptr);
+  const bool row_filter = kSrcScores && !kFinal && a.row_filter;
   if (kSrcScores) {
     // this thread's positions: base .. base + 15. The row is read before q_pos is known (every
     // position below max_ctx lies inside the row), and both before the first-digit histogram is
@@ -411,7 +454,8 @@ topk_stage_kernel(TopkStageArgs a) {
 #pragma unroll
       for (int e = 0; e < kRegE; ++e) f[e] = base + e < a.max_ctx ? row[base + e] : 0.f;
     }
-    reg_select_init(sh, tid, hist0);
+    if (row_filter) filter_init(sh, tid, a.hist0 + (int64_t)r * gridDim.x * kRegBins, gridDim.x, c);
+    else reg_select_init(sh, tid, hist0);
     n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
 #pragma unroll
     for (int e = 0; e < kRegE; ++e) {
@@ -470,18 +514,51 @@ topk_stage_kernel(TopkStageArgs a) {
   const uint32_t k = (uint32_t)a.k;
   const bool take_all = nvalid <= k;
   uint32_t tau = 0, remaining = k;
-  if (!take_all) reg_select(key, vmask, k, hist0 != nullptr, sh, tid, wave, lane, tau, remaining);
+  // Row filter: every key of the row's top k has a first digit of at least dstar, the first digit
+  // of the row's k-th largest key. A chunk with at most k such keys passes on all of them (a
+  // superset of its share of the row's top k, like its own top k), with no selection of its own;
+  // a chunk with more selects its own top k.
+  bool filt = false;
+  uint32_t dstar = 0;
+  if (row_filter) {
+    int n = a.q_pos[r] + 1;
+    n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+    if ((uint32_t)n > k) {  // else every chunk keeps every key
+      __syncthreads();      // publishes filter_init
+      if (wave == 0) {
+        const uint32_t d = pick_digit_wave(sh.hist[1], k, sh.pub[3], lane);  // the row holds n > k keys
+        const uint32_t own = count_at_or_above_wave(sh.hist[0], d, lane);
+        if (lane == 0) sh.pub[3][3] = own;
+      }
+      __syncthreads();
+      dstar = sh.pub[3][0];
+      filt = sh.pub[3][3] <= k;  // block-uniform
+      if (filt) {
+        tau = dstar == 0 ? 0u : (dstar << 21) - 1u;  // keys above tau: first digit >= dstar
+        remaining = 0;
+      } else {
+        // reg_select counts its second digit into sh.hist[1]; its first barrier publishes this
+        for (int i = tid; i < kRegBins / 4; i += kTopkThreads) ((uint4*)&sh.hist[1][0])[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+  if (!take_all && !filt) reg_select(key, vmask, k, hist0 != nullptr, sh, tid, wave, lane, tau, remaining);
+  // keys staged without a selection: all valid ones (a chunk that keeps every key, or a filter
+  // threshold of digit 0), else those above tau and the first `remaining` equal to it
+  const bool stage_all = filt ? dstar == 0 : take_all;
   if (kSrcScores && !kFinal && hist0 && a.mhist) {
     // this chunk's selection by first digit, from its full counts (still in the first LDS
-    // histogram): every bin above the k-th key's, and k - (keys above) from its bin; all of
-    // them when the chunk keeps every key
+    // histogram): with the row filter every bin from dstar up; otherwise every bin above the k-th
+    // key's, and k - (keys above) from its bin; all of them when the chunk keeps every key
     // A chunk that keeps every key skipped reg_select and its barriers: publish the histogram
     // reg_select_init wrote (each thread wrote other bins than it reads here) before reading it.
     if (take_all) __syncthreads();  // block-uniform
     const uint32_t d0 = sh.pub[0][0], above0 = sh.pub[0][1];
     uint32_t* mh = a.mhist + (int64_t)r * kRegBins;
     for (int b = tid; b < kRegBins; b += kTopkThreads) {
-      const uint32_t n = take_all || (uint32_t)b > d0 ? sh.hist[0][b] : ((uint32_t)b == d0 ? k - above0 : 0u);
+      uint32_t n;
+      if (filt) n = (uint32_t)b >= dstar ? sh.hist[0][b] : 0u;
+      else n = take_all || (uint32_t)b > d0 ? sh.hist[0][b] : ((uint32_t)b == d0 ? k - above0 : 0u);
       if (n) __hip_atomic_fetch_add(mh + b, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -490,7 +567,7 @@ topk_stage_kernel(TopkStageArgs a) {
   int obase = kSrcScores ? kRegKeys * c + kRegE * tid : kRegE * tid;
   asm volatile("" : "+v"(obase));  // opaque: the 16 values are formed when they are stored
   const int64_t rb = (int64_t)r * a.in_chunks * a.k;
-  const uint32_t nsel = stage_selected<!kFinal>(key, [&](int e) { return (uint32_t)(obase + e); }, vmask, take_all, tau,
+  const uint32_t nsel = stage_selected<!kFinal>(key, [&](int e) { return (uint32_t)(obase + e); }, vmask, stage_all, tau,
                                                 remaining, sh, wave, lane);
   auto pos_at = [&](int i) { return kSrcScores ? (int32_t)sh.cand_pos[i] : a.in_pos[rb + sh.cand_pos[i]]; };
   if (kFinal) {
@@ -507,6 +584,11 @@ topk_stage_kernel(TopkStageArgs a) {
       const int i = tid + j * kTopkThreads;
       if (i < a.k) out[i] = v[j];
     }
+    if (!kSrcScores && a.row_filter) {
+      // the chunk stage left the row's chunk counts in place: clear them for the producer's next use
+      uint4* h = (uint4*)(a.hist0 + (int64_t)r * a.in_chunks * kRegBins);
+      for (int i = tid; i < a.in_chunks * kRegBins / 4; i += kTopkThreads) h[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
   } else {
     const int64_t ob = ((int64_t)r * a.out_chunks + c) * a.k;
     for (int i = tid; i < (int)nsel; i += kTopkThreads) {
@@ -520,7 +602,10 @@ topk_stage_kernel(TopkStageArgs a) {
 // Long rows: candidates per chunk of kRegKeys positions (at most k each), then one selection over
 // them. The union of the chunks' top-k sets holds the row's top-k under the same order (value,
 // then position), and the candidates stay in ascending position order, so ties still go to the
-// smaller position. Usable while every row's candidates fit one block.
+// smaller position. Usable while every row's candidates fit one block. With every chunk's
+// first-digit counts given, a chunk with at most k keys whose first digit reaches the row's
+// threshold digit passes on those instead of its own top-k: they too hold its share of the row's
+// top-k.
 static_assert(kRegKeys == kTopkChunkKeys, "chunks of the first-digit counts");
 // Stage grids of at least this many workgroups (two per CU) take the packed stage kernel.
 constexpr int kTopkPackedGrid = 512;
@@ -564,6 +649,7 @@ hipError_t launch_topk(const float* scores, int64_t ld_scores, const int32_t* q_
     a.hist0 = hist0;
     // with the chunks' counts given, the merge's candidate counts follow the chunks' histograms
     a.mhist = hist0 ? hist0 + (size_t)rows * C * kRegBins : nullptr;
+    a.row_filter = hist0 && C <= kTopkFilterChunks ? 1 : 0;
     if ((int64_t)C * rows >= kTopkPackedGrid)
       hipLaunchKernelGGL((topk_stage_kernel<true, false, true>), dim3(C, rows), dim3(kTopkThreads), 0, stream, a);
     else
@@ -573,7 +659,7 @@ hipError_t launch_topk(const float* scores, int64_t ld_scores, const int32_t* q_
     TopkStageArgs b = a;
     b.in_key = a.out_key; b.in_pos = a.out_pos; b.in_cnt = a.out_cnt; b.in_chunks = C;
     b.out_key = nullptr; b.out_pos = nullptr; b.out_cnt = nullptr; b.out_chunks = 0;
-    b.hist0 = nullptr;
+    b.hist0 = a.row_filter ? a.hist0 : nullptr;  // the chunk counts the merge clears
     if (rows >= kTopkPackedGrid)
       hipLaunchKernelGGL((topk_stage_kernel<false, true, true>), dim3(1, rows), dim3(kTopkThreads), 0, stream, b);
     else

@@ -143,6 +143,39 @@ def test_fused_ragged_long_rows_equal_separate_calls(oracle_lib):
     np.testing.assert_array_equal(runs[0], oracle.topk(s_h, w.q_pos, w.topk, threads=8))
 
 
+def test_fused_long_rows_row_threshold_and_own_selection(oracle_lib):
+    """Rows over 16384 positions whose chunks take both chunk-stage forms: a chunk passes on its
+    keys at or above the row's threshold first digit when there are at most k of them, else it
+    selects its own top k. Row 0: random scores. Row 1: the first chunk's key scales times 1000,
+    so the row's top k lies in that chunk (which selects its own) and the other chunks pass on
+    nothing. Row 2: zero head weights, every score ties (every chunk selects its own; the k
+    smallest positions win). Row 3: no longer than k (every key kept). Index lists bit for bit
+    equal to the separate calls and to the oracle's top-k of the same scores."""
+    print("case: fused long rows, row threshold and own selection", flush=True)
+    q_pos = [131071, 100000, 70000, 2047]
+    w = workloads.make_random(4, 1, q_pos, 131072, H=2, Dqk=16, Dv=8, seed=95, permute_pages=True, extra_pages=2)
+    pages = w.page_table[1, : 16384 // w.page_size]
+    w.iks[pages] *= 1000.0
+    w.iw[2] = 0.0
+    d = gpu_inputs(w)
+    ws = torch.zeros(dsa.indexer_topk_workspace_size(w.rows, w.max_ctx, w.topk), dtype=torch.uint8, device="cuda")
+    runs = []
+    for _ in range(2):
+        s, idx = _fused(w, d, ws)
+        torch.cuda.synchronize()
+        assert dsa.last_path() == "indexer_topk_fused"
+        assert _hist_part_zero(ws, w.rows * _nh(w.max_ctx))
+        runs.append(idx.cpu().numpy())
+    np.testing.assert_array_equal(runs[0], runs[1])
+    s_h = s.cpu().numpy()
+    idx_sep = dsa.topk(s, d["q_pos"], w.max_ctx, w.topk).cpu().numpy()
+    np.testing.assert_array_equal(runs[0], idx_sep)
+    np.testing.assert_array_equal(runs[0], oracle.topk(s_h, w.q_pos, w.topk, threads=8))
+    assert (runs[0][1] < 16384).all()                                   # row 1: all from the first chunk
+    np.testing.assert_array_equal(runs[0][2], np.arange(w.topk))         # row 2: ties, smallest positions
+    np.testing.assert_array_equal(runs[0][3], np.arange(w.topk))         # row 3: every key
+
+
 def test_fused_rejects_small_workspace():
     w = workloads.make_random(1, 2, [300, 301], 320, H=2, Dqk=16, Dv=8, seed=3)
     d = gpu_inputs(w)
