@@ -7,7 +7,9 @@ the separate calls); and the index lists bit for bit against dsa_topk on the sam
 own parity with the oracle is exact. Repeated calls on one workspace (the histogram is left
 zero by each call), rows of both unit widths (two MTP rows per scan unit, or one), rows no
 longer than k, rows whose scores all tie (zero head weights) or are all <= 0 with signed zeros
-(negative head weights), and the full-size decode batches.
+(negative head weights), rows over one 16384-position chunk (whose chunk stages either pass on
+the keys at or above the row's threshold first digit or select their own top k), and the
+full-size decode batches.
 """
 import numpy as np
 import pytest
