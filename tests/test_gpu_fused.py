@@ -179,6 +179,37 @@ def test_fused_long_rows_row_threshold_and_own_selection(oracle_lib):
     np.testing.assert_array_equal(runs[0][3], np.arange(w.topk))         # row 3: every key
 
 
+def test_fused_long_rows_many_chunk_workgroups(oracle_lib):
+    """64 rows (32 units of two MTP rows) over up to 131072 positions: 512 chunk-stage workgroups,
+    so the chunk stage and the merge take the two-per-CU variants, with the row-threshold filter.
+    One unit has zero head weights (every score ties). Index lists bit for bit equal to the
+    separate calls; three rows against the oracle's top-k of the same scores."""
+    print("case: fused long rows, 512 chunk-stage workgroups", flush=True)
+    lens = [131072, 100000, 40000, 16385, 2048, 70001, 131072, 65536]
+    q_pos = []
+    for u in range(32):
+        n = lens[u % len(lens)]
+        q_pos += [n - 1, n - 2]
+    w = workloads.make_random(32, 2, q_pos, 131072, H=2, Dqk=16, Dv=8, seed=97, permute_pages=True)
+    w.iw[12:14] = 0.0
+    d = gpu_inputs(w)
+    ws = torch.zeros(dsa.indexer_topk_workspace_size(w.rows, w.max_ctx, w.topk), dtype=torch.uint8, device="cuda")
+    runs = []
+    for _ in range(2):
+        s, idx = _fused(w, d, ws)
+        torch.cuda.synchronize()
+        assert dsa.last_path() == "indexer_topk_fused"
+        assert _hist_part_zero(ws, w.rows * _nh(w.max_ctx))
+        runs.append(idx.cpu().numpy())
+    np.testing.assert_array_equal(runs[0], runs[1])
+    idx_sep = dsa.topk(s, d["q_pos"], w.max_ctx, w.topk).cpu().numpy()
+    np.testing.assert_array_equal(runs[0], idx_sep)
+    rows = [0, 13, 63]
+    s_h = s.cpu().numpy()
+    np.testing.assert_array_equal(runs[0][rows], oracle.topk(s_h[rows], w.q_pos[rows], w.topk, threads=8))
+    np.testing.assert_array_equal(runs[0][12], np.arange(w.topk))
+
+
 def test_fused_rejects_small_workspace():
     w = workloads.make_random(1, 2, [300, 301], 320, H=2, Dqk=16, Dv=8, seed=3)
     d = gpu_inputs(w)
