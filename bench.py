@@ -484,7 +484,10 @@ def run_prefill_bench(args):
     w = workloads.MAKERS[args.workload]()
     log(f"[bench] workload {w.name}: {w.rows} query rows over {w.max_ctx} positions, generated in "
         f"{time.time() - t0:.1f} s")
-    step = DecodeStep(w, copies=1)
+    # rows over one 16384-position top-k chunk take the fused indexer + top-k call (its chunk stage
+    # starts from the scan's counts: faster at the 128K chunk); shorter ones the separate calls
+    # (faster at the 8K block, where the scan's counting costs more than the top-k saves)
+    step = DecodeStep(w, copies=1, fused=w.max_ctx > 16384)
     # a prefill block takes milliseconds: a few warm-up and timed blocks suffice
     steps, warmup = min(args.steps, 20), min(args.warmup, 5)
     if args.no_graph:
@@ -495,6 +498,7 @@ def run_prefill_bench(args):
     else:
         ms_step, wall = time_graph_steps(step, steps, warmup)
         ms = [time_call(step, fn, steps, reps=2) for fn in (step.call_indexer, step.call_topk, step.call_mla)]
+    ms_fused = time_call(step, step.call_indexer_topk, steps, reps=2) if step.fused and not args.no_graph else None
     ctx = w.q_pos.astype(np.int64) + 1
     sel = np.minimum(ctx, w.topk)
     flops = {"indexer": float(np.sum(ctx)) * 2 * w.Hi * w.Di,
@@ -503,7 +507,8 @@ def run_prefill_bench(args):
     dominant = "indexer" if ms[0] >= ms[2] else "mla"
     achieved = tflops["indexer_f16"] if dominant == "indexer" else tflops["sparse_mla_bf16"]
     roof = {"bound": "mfma",
-            "kernel": "indexer_prefill_kernel (dsa_indexer_scores)" if dominant == "indexer"
+            "kernel": ("indexer_scan_kernel<2> (dsa_indexer_scores)" if w.page_size == 64 else
+                       "indexer_prefill_kernel (dsa_indexer_scores)") if dominant == "indexer"
             else "mla_mfma_kernel (dsa_sparse_mla_prefill)",
             "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
@@ -518,7 +523,9 @@ def run_prefill_bench(args):
                    "page_size": w.page_size},
         "roofline": roof,
         "cpu_baseline": None,
-        "detail": {"ms": {"indexer": ms[0], "topk": ms[1], "sparse_mla": ms[2], "step": float(ms_step)},
+        "detail": {"ms": {"indexer": ms[0], "topk": ms[1], "sparse_mla": ms[2], "step": float(ms_step),
+                          "indexer_topk_fused": ms_fused},
+                   "step_calls": "indexer_topk (fused) + sparse_mla" if step.fused else "indexer + topk + sparse_mla",
                    "wall_ms_per_step": wall / steps * 1e3, "mfma_TFLOPs": tflops,
                    "TFLOP": {k: v / 1e12 for k, v in flops.items()},
                    "topk_rows_per_s": w.rows / (ms[1] * 1e-3)},
