@@ -513,6 +513,9 @@ def run_prefill_bench(args):
             "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
             "algorithmic_flops_per_launch": flops[dominant]}
+    if dominant == "indexer" and step.fused:
+        roof["note"] = ("timed as the dsa_indexer_scores call; the step's fused call runs the same scan "
+                        "with the top-k's first-digit counts added")
     line = {
         "metric": "DSA prefill queries/s (indexer + top-2048 + sparse MLA)", "value": round(w.rows / (ms_step * 1e-3), 1),
         "unit": "queries/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
