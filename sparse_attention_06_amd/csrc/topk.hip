@@ -18,7 +18,7 @@
 // rows are re-read from global memory (L2) on each pass.
 //
 // Rows of at most 16384 positions take a register-resident variant: each of the 1024 threads
-// holds 16 consecutive keys, so the row is read once. Three passes over 11-, 11- and 10-bit
+// holds 16 consecutive keys, so the row is read once (rows of at most 4096 positions: 256 threads). Three passes over 11-, 11- and 10-bit
 // digits each fill a 2048-bin LDS histogram; a lane adds its keys that repeat one digit with a
 // single atomic (the leading digit of real scores is nearly constant, and one atomic per key would
 // serialise on it), and one wave picks the digit with DPP scans over coarse then fine bins. After a pass only keys sharing the decided top bits of
@@ -230,10 +230,12 @@ __device__ __forceinline__ uint32_t count_at_or_above_wave(const uint32_t* hist,
   return __builtin_amdgcn_readlane(wave_incl_scan(s), 63);
 }
 
+// The register variant's LDS for a workgroup of kT threads (kT / 64 waves).
+template <int kT>
 struct TopkLds {
   uint32_t hist[3][kRegBins];  // one histogram per pass
   uint32_t cand_key[kCandCap], cand_pos[kCandCap];
-  uint32_t wtot[kTopkWaves][2];
+  uint32_t wtot[kT / kWave][2];
   uint32_t pub[4][4];
   uint32_t ncand;
 };
@@ -242,10 +244,11 @@ struct TopkLds {
 // reg_select's first barrier publishes it. With hist0 (the row's first-digit histogram, counted
 // by the producer of the scores) the first histogram is taken from there instead, and hist0 is
 // zeroed for the producer's next use.
-__device__ __forceinline__ void reg_select_init(TopkLds& sh, int tid, uint32_t* hist0) {
+template <int kT>
+__device__ __forceinline__ void reg_select_init(TopkLds<kT>& sh, int tid, uint32_t* hist0) {
   static_assert(kRegBins == kTopkDigit0Bins, "first digit: key bits 31..21");
   const int given = hist0 ? kRegBins / 4 : 0;
-  for (int i = tid; i < 3 * kRegBins / 4; i += kTopkThreads) {
+  for (int i = tid; i < 3 * kRegBins / 4; i += kT) {
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (i < given) {
       v = ((const uint4*)hist0)[i];
@@ -261,8 +264,9 @@ __device__ __forceinline__ void reg_select_init(TopkLds& sh, int tid, uint32_t* 
 // counts, sh.hist[1] the row's (their sum), sh.hist[2] is zeroed. The counts stay in place, since
 // every chunk of the row reads them; the merge clears them.
 constexpr int kTopkFilterChunks = 8;
-__device__ __forceinline__ void filter_init(TopkLds& sh, int tid, const uint32_t* hist_row, int nchunks, int c) {
-  for (int i = tid; i < kRegBins / 4; i += kTopkThreads) {
+template <int kT>
+__device__ __forceinline__ void filter_init(TopkLds<kT>& sh, int tid, const uint32_t* hist_row, int nchunks, int c) {
+  for (int i = tid; i < kRegBins / 4; i += kT) {
     uint4 v[kTopkFilterChunks];
 #pragma unroll
     for (int ch = 0; ch < kTopkFilterChunks; ++ch)
@@ -285,8 +289,9 @@ __device__ __forceinline__ void filter_init(TopkLds& sh, int tid, const uint32_t
 // keys and reg_select_init since the keys' arrival. Three passes over 11-, 11- and 10-bit digits;
 // once the keys still undecided fit in LDS they are compacted there and the remaining passes run
 // over them alone.
+template <int kT>
 __device__ __forceinline__ void reg_select(const uint32_t (&key)[kRegE], uint32_t vmask, uint32_t k, bool hist0_given,
-                           TopkLds& sh, int tid, int wave, int lane, uint32_t& tau_out, uint32_t& remaining_out) {
+                           TopkLds<kT>& sh, int tid, int wave, int lane, uint32_t& tau_out, uint32_t& remaining_out) {
   __syncthreads();  // publishes reg_select_init
   const int npass = 3;
   uint32_t pmask = 0u;
@@ -301,7 +306,7 @@ __device__ __forceinline__ void reg_select(const uint32_t (&key)[kRegE], uint32_
     } else if (!compacted) {
       hist_add_keys(sh.hist[pass], key, vmask, pmask, prefix, dg);
     } else {
-      for (int i = tid; i < (int)nc; i += kTopkThreads) {
+      for (int i = tid; i < (int)nc; i += kT) {
         const uint32_t kk = sh.cand_key[i];
         if ((kk & pmask) == prefix) atomicAdd(&sh.hist[pass][dg.of(kk)], 1u);
       }
@@ -343,9 +348,9 @@ __device__ __forceinline__ void reg_select(const uint32_t (&key)[kRegE], uint32_
 // slots; returns how many were selected. Each thread first forms two 16-bit masks of its keys
 // (above tau, equal to tau); without keys to stage it then visits only the set bits of its
 // selection (about one key in eight at k = 2048 over 16384), not all sixteen keys.
-template <bool with_keys, class PosOf>
+template <int kT, bool with_keys, class PosOf>
 __device__ __forceinline__ uint32_t stage_selected(const uint32_t (&key)[kRegE], PosOf pos_of, uint32_t vmask, bool take_all,
-                                   uint32_t tau, uint32_t remaining, TopkLds& sh, int wave, int lane) {
+                                   uint32_t tau, uint32_t remaining, TopkLds<kT>& sh, int wave, int lane) {
   uint32_t gtm = 0, eqm = 0;
 #pragma unroll
   for (int e = 0; e < kRegE; ++e) {
@@ -360,7 +365,7 @@ __device__ __forceinline__ uint32_t stage_selected(const uint32_t (&key)[kRegE],
   if (lane == 63) { sh.wtot[wave][0] = gi; sh.wtot[wave][1] = ei; }
   __syncthreads();
   uint32_t gb = gi - gt, eb = ei - eq, gall = 0, eall = 0;
-  for (int w = 0; w < kTopkWaves; ++w) {
+  for (int w = 0; w < kT / kWave; ++w) {
     if (w < wave) { gb += sh.wtot[w][0]; eb += sh.wtot[w][1]; }
     gall += sh.wtot[w][0];
     eall += sh.wtot[w][1];
@@ -425,11 +430,13 @@ struct TopkStageArgs {
 
 // kPacked: two workgroups per CU (at most 64 VGPRs, a few spilled), for grids of many rows or
 // chunks, where a second workgroup's work overlaps the first's barrier-bound phases; one
-// workgroup per CU otherwise (no spills).
-template <bool kSrcScores, bool kFinal, bool kPacked>
-__global__ void __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(kPacked ? 8 : 4, 8)))
+// workgroup per CU otherwise (no spills). kT: threads per workgroup (1024: 16384 keys; 256: 4096
+// keys, two workgroups per CU as LDS allows).
+template <bool kSrcScores, bool kFinal, bool kPacked, int kT = kTopkThreads>
+__global__ void __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kPacked ? 8 : kT / 256, 8)))
 topk_stage_kernel(TopkStageArgs a) {
-  __shared__ __attribute__((aligned(16))) TopkLds sh;
+  constexpr int kKeys = kT * kRegE;  // keys a workgroup holds: one chunk of a row
+  __shared__ __attribute__((aligned(16))) TopkLds<kT> sh;
   const int r = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t key[kRegE], vmask = 0;
@@ -442,7 +449,7 @@ topk_stage_kernel(TopkStageArgs a) {
     // staged, so the memory latencies overlap.
     int n = a.q_pos[r] + 1;
     const float* row = a.scores + (int64_t)r * a.ld_scores;
-    const int base = kRegKeys * c + kRegE * tid;
+    const int base = kKeys * c + kRegE * tid;
     float f[kRegE];
     if (base + kRegE <= a.max_ctx && ((uintptr_t)(row + base) & 15) == 0) {
 #pragma unroll
@@ -503,8 +510,8 @@ topk_stage_kernel(TopkStageArgs a) {
   if (kSrcScores) {
     int n = a.q_pos[r] + 1;
     n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
-    const int len = n - kRegKeys * c;
-    nvalid = len < 0 ? 0u : (uint32_t)min(len, kRegKeys);
+    const int len = n - kKeys * c;
+    nvalid = len < 0 ? 0u : (uint32_t)min(len, kKeys);
   } else {
     // lanes load the counts side by side (a loop of dependent loads would serialise them)
     uint32_t part = 0;
@@ -538,7 +545,7 @@ topk_stage_kernel(TopkStageArgs a) {
         remaining = 0;
       } else {
         // reg_select counts its second digit into sh.hist[1]; its first barrier publishes this
-        for (int i = tid; i < kRegBins / 4; i += kTopkThreads) ((uint4*)&sh.hist[1][0])[i] = make_uint4(0u, 0u, 0u, 0u);
+        for (int i = tid; i < kRegBins / 4; i += kT) ((uint4*)&sh.hist[1][0])[i] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
   }
@@ -555,7 +562,7 @@ topk_stage_kernel(TopkStageArgs a) {
     if (take_all) __syncthreads();  // block-uniform
     const uint32_t d0 = sh.pub[0][0], above0 = sh.pub[0][1];
     uint32_t* mh = a.mhist + (int64_t)r * kRegBins;
-    for (int b = tid; b < kRegBins; b += kTopkThreads) {
+    for (int b = tid; b < kRegBins; b += kT) {
       uint32_t n;
       if (filt) n = (uint32_t)b >= dstar ? sh.hist[0][b] : 0u;
       else n = take_all || (uint32_t)b > d0 ? sh.hist[0][b] : ((uint32_t)b == d0 ? k - above0 : 0u);
@@ -564,34 +571,34 @@ topk_stage_kernel(TopkStageArgs a) {
   }
   // staged per selected key: its position for a score row, its input slot for candidates (the
   // slot's position is read when the result is written, by every thread at once)
-  int obase = kSrcScores ? kRegKeys * c + kRegE * tid : kRegE * tid;
+  int obase = kSrcScores ? kKeys * c + kRegE * tid : kRegE * tid;
   asm volatile("" : "+v"(obase));  // opaque: the 16 values are formed when they are stored
   const int64_t rb = (int64_t)r * a.in_chunks * a.k;
-  const uint32_t nsel = stage_selected<!kFinal>(key, [&](int e) { return (uint32_t)(obase + e); }, vmask, stage_all, tau,
+  const uint32_t nsel = stage_selected<kT, !kFinal>(key, [&](int e) { return (uint32_t)(obase + e); }, vmask, stage_all, tau,
                                                 remaining, sh, wave, lane);
   auto pos_at = [&](int i) { return kSrcScores ? (int32_t)sh.cand_pos[i] : a.in_pos[rb + sh.cand_pos[i]]; };
   if (kFinal) {
-    // all of a thread's (at most kCandCap / kTopkThreads) reads are issued before its stores
+    // all of a thread's (at most kCandCap / kT) reads are issued before its stores
     int32_t* out = a.idx + (int64_t)r * a.ld_idx;
-    int32_t v[kCandCap / kTopkThreads];
+    int32_t v[kCandCap / kT];
 #pragma unroll
-    for (int j = 0; j < kCandCap / kTopkThreads; ++j) {
-      const int i = tid + j * kTopkThreads;
+    for (int j = 0; j < kCandCap / kT; ++j) {
+      const int i = tid + j * kT;
       v[j] = i < (int)nsel ? pos_at(i) : -1;
     }
 #pragma unroll
-    for (int j = 0; j < kCandCap / kTopkThreads; ++j) {
-      const int i = tid + j * kTopkThreads;
+    for (int j = 0; j < kCandCap / kT; ++j) {
+      const int i = tid + j * kT;
       if (i < a.k) out[i] = v[j];
     }
     if (!kSrcScores && a.row_filter) {
       // the chunk stage left the row's chunk counts in place: clear them for the producer's next use
       uint4* h = (uint4*)(a.hist0 + (int64_t)r * a.in_chunks * kRegBins);
-      for (int i = tid; i < a.in_chunks * kRegBins / 4; i += kTopkThreads) h[i] = make_uint4(0u, 0u, 0u, 0u);
+      for (int i = tid; i < a.in_chunks * kRegBins / 4; i += kT) h[i] = make_uint4(0u, 0u, 0u, 0u);
     }
   } else {
     const int64_t ob = ((int64_t)r * a.out_chunks + c) * a.k;
-    for (int i = tid; i < (int)nsel; i += kTopkThreads) {
+    for (int i = tid; i < (int)nsel; i += kT) {
       a.out_key[ob + i] = sh.cand_key[i];
       a.out_pos[ob + i] = pos_at(i);
     }
@@ -609,6 +616,9 @@ topk_stage_kernel(TopkStageArgs a) {
 static_assert(kRegKeys == kTopkChunkKeys, "chunks of the first-digit counts");
 // Stage grids of at least this many workgroups (two per CU) take the packed stage kernel.
 constexpr int kTopkPackedGrid = 512;
+// Rows of at most kTopkSmallThreads * kRegE (4096) positions take 256-thread workgroups: the same
+// 16 keys per thread, a quarter of the waves to synchronise and no threads without keys.
+constexpr int kTopkSmallThreads = 256;
 int topk_reg_max_ctx() { return kRegKeys; }
 int topk_reg_max_k() { return kCandCap; }
 int topk_chunks(int max_ctx) { return (max_ctx + kRegKeys - 1) / kRegKeys; }
@@ -630,7 +640,10 @@ hipError_t launch_topk(const float* scores, int64_t ld_scores, const int32_t* q_
   if (max_ctx <= kRegKeys && k <= kCandCap) {
     a.hist0 = hist0;
     *path = (max_ctx <= k) ? DSA_PATH_TOPK_COPY : DSA_PATH_TOPK_RADIX_REG;
-    if (rows >= kTopkPackedGrid)
+    if (max_ctx <= kTopkSmallThreads * kRegE)
+      hipLaunchKernelGGL((topk_stage_kernel<true, true, false, kTopkSmallThreads>), dim3(1, rows), dim3(kTopkSmallThreads), 0,
+                         stream, a);
+    else if (rows >= kTopkPackedGrid)
       hipLaunchKernelGGL((topk_stage_kernel<true, true, true>), dim3(1, rows), dim3(kTopkThreads), 0, stream, a);
     else
       hipLaunchKernelGGL((topk_stage_kernel<true, true, false>), dim3(1, rows), dim3(kTopkThreads), 0, stream, a);

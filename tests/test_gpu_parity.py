@@ -108,7 +108,8 @@ def _topk_case(scores, q_pos, k):
     return g, r
 
 
-@pytest.mark.parametrize("n,k", [(5000, 2048), (16384, 2048), (40000, 2048), (300, 32), (100, 1), (2048, 2048), (12000, 5000)])
+@pytest.mark.parametrize("n,k", [(5000, 2048), (16384, 2048), (40000, 2048), (300, 32), (100, 1), (2048, 2048), (12000, 5000),
+                                 (4096, 2048), (4096, 4000), (4097, 2048), (3000, 1500)])
 def test_topk_matches_oracle_exactly(oracle_lib, n, k):
     _say(f"case: topk n={n} k={k}")
     rng = np.random.default_rng(n + k)
@@ -119,13 +120,13 @@ def test_topk_matches_oracle_exactly(oracle_lib, n, k):
     np.testing.assert_array_equal(g, r)
 
 
-@pytest.mark.parametrize("rows,n", [(520, 5000), (512, 20000), (64, 131072)])
+@pytest.mark.parametrize("rows,n", [(520, 5000), (512, 20000), (64, 131072), (600, 4096)])
 def test_topk_many_rows_two_workgroups_per_cu(oracle_lib, rows, n):
     """Grids of 512 or more workgroups run the stage kernel at two workgroups per CU (register
     budget halved): 520 short rows (one stage), 512 rows of 20000 (two chunks each, then a
     512-row merge) and 64 rows of 131072 (8 chunks each: 512 chunk workgroups, then a 64-row
-    merge at one workgroup per CU). Row lengths vary from k - 1 to the full width; bit-exact
-    against the oracle."""
+    merge at one workgroup per CU); 600 rows of 4096 take the 256-thread workgroups. Row lengths
+    vary from k - 1 to the full width; bit-exact against the oracle."""
     _say(f"case: topk packed rows={rows} n={n}")
     rng = np.random.default_rng(rows + n)
     k = 2048
@@ -151,13 +152,14 @@ def test_topk_ties_and_signed_zeros(oracle_lib, n):
     np.testing.assert_array_equal(g, r)
 
 
-def test_topk_register_path_special_rows(oracle_lib):
-    """Rows of at most 16384 positions: the register-resident kernel, including rows whose
+@pytest.mark.parametrize("n", [16384, 4096])
+def test_topk_register_path_special_rows(oracle_lib, n):
+    """Rows of at most 16384 positions (4096: the 256-thread workgroups): the register-resident kernel, including rows whose
     undecided keys overflow the candidate buffer (all equal), -inf entries, a threshold inside a
     run of equal scores, and scores packed into a narrow range (long shared key prefixes)."""
-    _say("case: topk register path special rows")
+    _say(f"case: topk register path special rows n={n}")
     rng = np.random.default_rng(11)
-    n, k = 16384, 2048
+    k = 2048
     sc = rng.standard_normal((6, n)).astype(np.float32)
     sc[0] = 3.0                                   # all equal: every key ties with the threshold
     sc[1, ::2] = -np.inf                          # half the row masked
@@ -165,7 +167,7 @@ def test_topk_register_path_special_rows(oracle_lib):
     sc[2, n // 2:] = rng.uniform(0.0, 0.5, n // 2)
     sc[3] = (100.0 + rng.uniform(0.0, 1e-3, n)).astype(np.float32)   # narrow range
     sc[4, 7::13] = np.inf                         # +inf above everything
-    q_pos = np.array([n - 1, n - 1, n - 1, n - 1, n - 1, 9000], np.int32)
+    q_pos = np.array([n - 1, n - 1, n - 1, n - 1, n - 1, n * 9 // 16], np.int32)
     g, r = _topk_case(sc, q_pos, k)
     assert dsa.last_path() == "topk_radix_reg"
     np.testing.assert_array_equal(g, r)
