@@ -18,7 +18,8 @@
 // rows are re-read from global memory (L2) on each pass.
 //
 // Rows of at most 16384 positions take a register-resident variant: each of the 1024 threads
-// holds 16 consecutive keys, so the row is read once (rows of at most 4096 positions: 256 threads). Three passes over 11-, 11- and 10-bit
+// holds 16 consecutive keys, so the row is read once (rows of at most 4096 / 8192 positions: 256 /
+// 512 threads). Three passes over 11-, 11- and 10-bit
 // digits each fill a 2048-bin LDS histogram; a lane adds its keys that repeat one digit with a
 // single atomic (the leading digit of real scores is nearly constant, and one atomic per key would
 // serialise on it), and one wave picks the digit with DPP scans over coarse then fine bins. After a pass only keys sharing the decided top bits of
@@ -430,8 +431,8 @@ struct TopkStageArgs {
 
 // kPacked: two workgroups per CU (at most 64 VGPRs, a few spilled), for grids of many rows or
 // chunks, where a second workgroup's work overlaps the first's barrier-bound phases; one
-// workgroup per CU otherwise (no spills). kT: threads per workgroup (1024: 16384 keys; 256: 4096
-// keys, two workgroups per CU as LDS allows).
+// workgroup per CU otherwise (no spills). kT: threads per workgroup (1024: 16384 keys; 512 / 256:
+// 8192 / 4096 keys, two workgroups per CU as LDS allows).
 template <bool kSrcScores, bool kFinal, bool kPacked, int kT = kTopkThreads>
 __global__ void __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kPacked ? 8 : kT / 256, 8)))
 topk_stage_kernel(TopkStageArgs a) {
@@ -616,8 +617,8 @@ topk_stage_kernel(TopkStageArgs a) {
 static_assert(kRegKeys == kTopkChunkKeys, "chunks of the first-digit counts");
 // Stage grids of at least this many workgroups (two per CU) take the packed stage kernel.
 constexpr int kTopkPackedGrid = 512;
-// Rows of at most kTopkSmallThreads * kRegE (4096) positions take 256-thread workgroups: the same
-// 16 keys per thread, a quarter of the waves to synchronise and no threads without keys.
+// Rows of at most 4096 (8192) positions take 256-thread (512-thread) workgroups: the same 16 keys
+// per thread, fewer waves to synchronise and no threads without keys.
 constexpr int kTopkSmallThreads = 256;
 int topk_reg_max_ctx() { return kRegKeys; }
 int topk_reg_max_k() { return kCandCap; }
@@ -643,6 +644,9 @@ hipError_t launch_topk(const float* scores, int64_t ld_scores, const int32_t* q_
     if (max_ctx <= kTopkSmallThreads * kRegE)
       hipLaunchKernelGGL((topk_stage_kernel<true, true, false, kTopkSmallThreads>), dim3(1, rows), dim3(kTopkSmallThreads), 0,
                          stream, a);
+    else if (max_ctx <= 2 * kTopkSmallThreads * kRegE)
+      hipLaunchKernelGGL((topk_stage_kernel<true, true, false, 2 * kTopkSmallThreads>), dim3(1, rows),
+                         dim3(2 * kTopkSmallThreads), 0, stream, a);
     else if (rows >= kTopkPackedGrid)
       hipLaunchKernelGGL((topk_stage_kernel<true, true, true>), dim3(1, rows), dim3(kTopkThreads), 0, stream, a);
     else

@@ -109,7 +109,8 @@ def _topk_case(scores, q_pos, k):
 
 
 @pytest.mark.parametrize("n,k", [(5000, 2048), (16384, 2048), (40000, 2048), (300, 32), (100, 1), (2048, 2048), (12000, 5000),
-                                 (4096, 2048), (4096, 4000), (4097, 2048), (3000, 1500)])
+                                 (4096, 2048), (4096, 4000), (4097, 2048), (3000, 1500), (8192, 2048), (8193, 2048),
+                                 (6000, 4096)])
 def test_topk_matches_oracle_exactly(oracle_lib, n, k):
     _say(f"case: topk n={n} k={k}")
     rng = np.random.default_rng(n + k)
@@ -152,9 +153,9 @@ def test_topk_ties_and_signed_zeros(oracle_lib, n):
     np.testing.assert_array_equal(g, r)
 
 
-@pytest.mark.parametrize("n", [16384, 4096])
+@pytest.mark.parametrize("n", [16384, 8192, 4096])
 def test_topk_register_path_special_rows(oracle_lib, n):
-    """Rows of at most 16384 positions (4096: the 256-thread workgroups): the register-resident kernel, including rows whose
+    """Rows of at most 16384 positions (8192 / 4096: the 512- / 256-thread workgroups): the register-resident kernel, including rows whose
     undecided keys overflow the candidate buffer (all equal), -inf entries, a threshold inside a
     run of equal scores, and scores packed into a narrow range (long shared key prefixes)."""
     _say(f"case: topk register path special rows n={n}")
