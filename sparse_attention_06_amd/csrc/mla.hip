@@ -1072,8 +1072,21 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
 // Merge the splits of each row from their fp16 partials: out = sum_s w_s N_s / sum_s w_s with
 // w_s = l_s 2^(m_s - M). One thread per (row, head, 8 output columns). The (m, l) pairs, then the
 // partials, of up to kBatch splits at a time are loaded together, so a row split many ways costs a
-// few memory latencies rather than one per split. A split without keys (l = 0) is skipped by
+// few memory latencies rather than one per split; with at most kBatch splits the pairs and the
+// partials are all loaded at once (one memory latency). A split without keys (l = 0) is skipped by
 // selects: whatever its partial holds never enters the sum.
+// The merged 8 columns (bf16) and, for the first column group, the lse of the row's head.
+__device__ __forceinline__ void combine_store(const AttnArgs& a, int r, int head, int cg, float M, float L,
+                                              const float (&acc)[8]) {
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t* dst = a.out + ((int64_t)r * kH + head) * kDv + 8 * cg;
+  uint32_t wd[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) wd[e] = (uint32_t)f32_to_bf16(acc[2 * e] * inv) | ((uint32_t)f32_to_bf16(acc[2 * e + 1] * inv) << 16);
+  *(i32x4*)dst = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+  if (a.lse && cg == 0) a.lse[(int64_t)r * kH + head] = L > 0.f ? (M + __log2f(L)) / kLog2e : -INFINITY;
+}
+
 template <int kBatch>
 __global__ void __launch_bounds__(256) mla_combine_kernel(AttnArgs a, int splits, int units, void* __restrict__ ws) {
   const int r = blockIdx.y;
@@ -1083,6 +1096,38 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(AttnArgs a, int splits
   MlaSplitWs w = mla_split_ws(ws, units);
   const int64_t u0 = (int64_t)r * splits * kH + head;  // split s2 at u0 + s2 * kH
   float M = -INFINITY;
+  if (splits <= kBatch) {
+    f32x2 ml[kBatch];
+    i32x4 v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (j < splits) {  // uniform
+        const int64_t u = u0 + (int64_t)j * kH;
+        ml[j] = w.ml[u];
+        v[j] = *(const i32x4*)(w.part + u * kDv + 8 * cg);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (j < splits && ml[j][1] > 0.f) M = fmaxf(M, ml[j][0]);
+    float L = 0.f, acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const bool use = j < splits && ml[j][1] > 0.f;
+      const float f = use ? ml[j][1] * exp2f(ml[j][0] - M) : 0.f;
+      L += f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 x = unpack_f16x2((uint32_t)v[j][e]);
+        acc[2 * e] = use ? fmaf(f, x[0], acc[2 * e]) : acc[2 * e];
+        acc[2 * e + 1] = use ? fmaf(f, x[1], acc[2 * e + 1]) : acc[2 * e + 1];
+      }
+    }
+    combine_store(a, r, head, cg, M, L, acc);
+    return;
+  }
   for (int s0 = 0; s0 < splits; s0 += kBatch) {
     f32x2 ml[kBatch];
 #pragma unroll
@@ -1119,13 +1164,7 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(AttnArgs a, int splits
       }
     }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint16_t* dst = a.out + ((int64_t)r * kH + head) * kDv + 8 * cg;
-  uint32_t wd[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) wd[e] = (uint32_t)f32_to_bf16(acc[2 * e] * inv) | ((uint32_t)f32_to_bf16(acc[2 * e + 1] * inv) << 16);
-  *(i32x4*)dst = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
-  if (a.lse && cg == 0) a.lse[(int64_t)r * kH + head] = L > 0.f ? (M + __log2f(L)) / kLog2e : -INFINITY;
+  combine_store(a, r, head, cg, M, L, acc);
 }
 
 size_t mla_mfma_ws_bytes(int rows, int splits) {
@@ -1159,6 +1198,8 @@ hipError_t launch_mla_mfma(const AttnArgs& a, int splits, void* ws, hipStream_t 
   const dim3 cgrid((kH * (kDv / 8) + 255) / 256, rows);
   if (splits <= 2)
     hipLaunchKernelGGL(mla_combine_kernel<2>, cgrid, dim3(256), 0, stream, a, splits, units, ws);
+  else if (splits <= 16)
+    hipLaunchKernelGGL(mla_combine_kernel<16>, cgrid, dim3(256), 0, stream, a, splits, units, ws);
   else
     hipLaunchKernelGGL(mla_combine_kernel<8>, cgrid, dim3(256), 0, stream, a, splits, units, ws);
   return hipGetLastError();
