@@ -565,11 +565,12 @@ hipError_t launch_indexer_scan(const uint8_t* q, const float* w, PagedCache kc, 
                                RowSeq rs, const int32_t* q_pos, int rows, int max_ctx,
                                float* scores, int64_t ld_scores, uint32_t* hist0, hipStream_t stream) {
   // units of NQ query rows of one sequence; about 2048 waves (8 per CU) per launch for a decode
-  // batch, each a whole number of pages (at most 64 of them)
+  // batch of two-row units, 1024 for one-row units (half the work per key, so twice the keys per
+  // wave balance its fixed query load and ring fill), each a whole number of pages (at most 64)
   const int nq = indexer_scan_rows_per_wave(rs);
   const int units = rows / nq;
   const int64_t total = (int64_t)units * max_ctx;
-  int kpw = (int)((total / 2048 + kScanPage - 1) / kScanPage * kScanPage);
+  int kpw = (int)((total / (nq == 1 ? 1024 : 2048) + kScanPage - 1) / kScanPage * kScanPage);
   kpw = kpw < kScanPage ? kScanPage : (kpw > 64 * kScanPage ? 64 * kScanPage : kpw);
   if (hist0) {
     // counted per top-k chunk: a workgroup's range (4 kpw) must not straddle one, so kpw is a
