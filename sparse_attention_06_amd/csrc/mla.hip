@@ -549,10 +549,22 @@ mla_mfma_kernel(AttnArgs a, int splits, int entries_per_split, int units, int pe
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Workgroups are dispatched to the 8 XCDs round robin; give each XCD a contiguous range of
-  // units, so the rows of one sequence share that XCD's L2.
-  const int unit = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (unit >= units) return;
+  // Workgroups are dispatched to the 8 XCDs round robin. Split rows: each XCD takes a contiguous
+  // range of units, so the splits of a row and the rows of a request share that XCD's L2. Unsplit
+  // rows (prefill blocks, large decode batches): rows in pairs, the pairs dealt round robin over the
+  // XCDs, the two rows of a pair one after the other on one XCD (MTP rows, neighbouring prefill
+  // rows), and the last rows first; a causal block's rows differ in length, so contiguous row
+  // ranges per XCD would give the XCDs uneven work.
+  int unit;
+  if (kMode == kMlaNoSplit) {
+    const int slot = blockIdx.x >> 3;
+    const int fwd = 2 * ((slot >> 1) * 8 + (int)(blockIdx.x & 7)) + (slot & 1);
+    if (fwd >= units) return;
+    unit = units - 1 - fwd;
+  } else {
+    unit = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (unit >= units) return;
+  }
   const int r = unit / splits, sp = unit % splits;
   const int seq = a.rs.of(r);  // -1: no page-table row, every entry resolves to no row
   const int t = a.q_pos[r];
@@ -1188,7 +1200,10 @@ hipError_t launch_mla_mfma(const AttnArgs& a, int splits, void* ws, hipStream_t 
   const int blocks = 8 * per_xcd;
   if (splits <= 1) {
     const int per = a.idx ? a.k : 1 << 30;
-    hipLaunchKernelGGL(mla_mfma_kernel<kMlaNoSplit>, dim3(blocks), dim3(256), 0, stream, a, 1, per, units, per_xcd, nullptr);
+    // pair p of rows takes slots 2 (p / 8) and 2 (p / 8) + 1 of XCD p % 8
+    const int pair_blocks = 16 * (((units + 1) / 2 + 7) / 8);
+    hipLaunchKernelGGL(mla_mfma_kernel<kMlaNoSplit>, dim3(pair_blocks), dim3(256), 0, stream, a, 1, per, units, per_xcd,
+                       nullptr);
     return hipGetLastError();
   }
   const int per = ((a.k + splits - 1) / splits + kNK - 1) / kNK * kNK;
