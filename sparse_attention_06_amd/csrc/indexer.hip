@@ -572,6 +572,9 @@ hipError_t launch_indexer_scan(const uint8_t* q, const float* w, PagedCache kc, 
   const int64_t total = (int64_t)units * max_ctx;
   int kpw = (int)((total / (nq == 1 ? 1024 : 2048) + kScanPage - 1) / kScanPage * kScanPage);
   kpw = kpw < kScanPage ? kScanPage : (kpw > 64 * kScanPage ? 64 * kScanPage : kpw);
+  // at least 8 ranges per row: in a causal prefill block the rows' prefixes differ in length, and
+  // ranges as long as the row leave most of a workgroup's waves without keys
+  while (kpw > kScanPage && 8 * kpw > max_ctx) kpw = kpw / 2 / kScanPage * kScanPage;  // whole pages
   if (hist0) {
     // counted per top-k chunk: a workgroup's range (4 kpw) must not straddle one, so kpw is a
     // power of two (64 .. 4096 keys) and 4 kpw divides the chunk
