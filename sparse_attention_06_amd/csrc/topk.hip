@@ -400,9 +400,10 @@ __device__ __forceinline__ uint32_t stage_selected(const uint32_t (&key)[kRegE],
   return gall + min(eall, remaining);
 }
 
-// One selection over up to 16384 keys per block. With kSrcScores the keys are the scores of row
-// blockIdx.y at positions [16384 * blockIdx.x, ...) below the row's length; otherwise they are the
-// candidate slots of row blockIdx.y written by a previous stage (in_chunks chunks of k slots, the
+// One selection over up to 16384 keys per block. With kSrcScores the keys are the scores of row r
+// at positions [16384 * c, ...) below the row's length (r = blockIdx.y, c = blockIdx.x; chunk
+// stages: a 1-D grid whose block b is chunk c of row r as chunk_stage_of maps it); otherwise they
+// are the candidate slots of row r = blockIdx.y written by a previous stage (in_chunks chunks of k slots, the
 // first in_cnt of each valid, in ascending position order). With kFinal the block writes the row's
 // index list (positions ascending, -1 padded to k); otherwise this chunk's candidates (at most k
 // order keys with their positions, ascending by position) and their count.
@@ -424,6 +425,7 @@ struct TopkStageArgs {
   uint32_t* hist0;  // score rows: per row and chunk, the first-digit histogram (or null)
   uint32_t* mhist;  // per row, the first-digit histogram of the merge's candidates (or null): the
                     // chunk stage adds its selection's counts, the merge starts from them
+  int rows;         // rows of the launch (chunk stages: the 1-D grid covers 8 * out_chunks * ceil(rows / 8))
   int row_filter;   // chunk stage with hist0 and mhist over at most kTopkFilterChunks chunks: each
                     // chunk passes on its keys whose first digit reaches the row's threshold digit
                     // (from the sum of the row's chunk counts), and the merge clears those counts
@@ -438,10 +440,20 @@ __global__ void __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kPacked
 topk_stage_kernel(TopkStageArgs a) {
   constexpr int kKeys = kT * kRegE;  // keys a workgroup holds: one chunk of a row
   __shared__ __attribute__((aligned(16))) TopkLds<kT> sh;
-  const int r = blockIdx.y, c = blockIdx.x;
+  int r = blockIdx.y, c = blockIdx.x;
+  if (kSrcScores && !kFinal) {
+    // Workgroups go to the 8 XCDs round robin: the chunks of a row run on one XCD, one after the
+    // other, so the row's chunk counts that each of them reads (the row filter) come from that
+    // XCD's L2 after the first
+    const int slot = blockIdx.x >> 3;
+    r = (slot / a.out_chunks) * 8 + (int)(blockIdx.x & 7);
+    c = slot % a.out_chunks;
+    if (r >= a.rows) return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t key[kRegE], vmask = 0;
-  uint32_t* const hist0 = kSrcScores ? (a.hist0 ? a.hist0 + ((int64_t)r * gridDim.x + c) * kRegBins : nullptr)
+  const int nchunks = kFinal ? 1 : a.out_chunks;  // score chunks of a row in this launch
+  uint32_t* const hist0 = kSrcScores ? (a.hist0 ? a.hist0 + ((int64_t)r * nchunks + c) * kRegBins : nullptr)
                                      : (a.mhist ? a.mhist + (int64_t)r * kRegBins : nullptr);
   const bool row_filter = kSrcScores && !kFinal && a.row_filter;
   if (kSrcScores) {
@@ -462,7 +474,7 @@ topk_stage_kernel(TopkStageArgs a) {
 #pragma unroll
       for (int e = 0; e < kRegE; ++e) f[e] = base + e < a.max_ctx ? row[base + e] : 0.f;
     }
-    if (row_filter) filter_init(sh, tid, a.hist0 + (int64_t)r * gridDim.x * kRegBins, gridDim.x, c);
+    if (row_filter) filter_init(sh, tid, a.hist0 + (int64_t)r * nchunks * kRegBins, nchunks, c);
     else reg_select_init(sh, tid, hist0);
     n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
 #pragma unroll
@@ -667,10 +679,12 @@ hipError_t launch_topk(const float* scores, int64_t ld_scores, const int32_t* q_
     // with the chunks' counts given, the merge's candidate counts follow the chunks' histograms
     a.mhist = hist0 ? hist0 + (size_t)rows * C * kRegBins : nullptr;
     a.row_filter = hist0 && C <= kTopkFilterChunks ? 1 : 0;
+    a.rows = rows;
+    const dim3 cgrid((unsigned)(8 * C * ((rows + 7) / 8)));
     if ((int64_t)C * rows >= kTopkPackedGrid)
-      hipLaunchKernelGGL((topk_stage_kernel<true, false, true>), dim3(C, rows), dim3(kTopkThreads), 0, stream, a);
+      hipLaunchKernelGGL((topk_stage_kernel<true, false, true>), cgrid, dim3(kTopkThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL((topk_stage_kernel<true, false, false>), dim3(C, rows), dim3(kTopkThreads), 0, stream, a);
+      hipLaunchKernelGGL((topk_stage_kernel<true, false, false>), cgrid, dim3(kTopkThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     TopkStageArgs b = a;
