@@ -1186,8 +1186,8 @@ size_t mla_mfma_ws_bytes(int rows, int splits) {
 
 int mla_mfma_pick_splits(int rows, int k) {
   // aim for >= 256 workgroups (one per (row, split)), at least 4 tiles per split (a split's fixed
-  // cost, its query load and partial, outweighs two tiles: 4 rows of 2048 keys run 3% faster in
-  // 16 splits than in 32, while 16 rows keep 16 splits, 8 being slower)
+  // cost, its query load and partial, is worth about two tiles: 4 rows of 2048 keys run as fast in
+  // 16 splits as in 32, and 16 rows run slower in 8 splits than in 16)
   int s = 1;
   while (rows * s < 256 && (k / (s * 2)) >= 4 * kNK) s *= 2;
   return s;
