@@ -215,31 +215,36 @@ __global__ void __launch_bounds__(256) proj_gemm_kernel(ProjArgs p) {
 
   // global -> register staging: thread tid moves chunks c = tid + 256 i (i < 4) of each operand's
   // 128 rows x 128 bytes (row c / 8, 16-byte chunk c % 8); rows past M or N load zeros
-  // (A: kTM rows, so kTM / 32 chunks per thread; B: 128 rows, 4 chunks per thread)
+  // (A: kTM rows, so kTM / 32 chunks per thread; B: 128 rows, 4 chunks per thread). The query's
+  // 32-row tiles (one workgroup per CU at decode sizes) keep kDepth K blocks in flight in
+  // registers: a block's multiply is a few MFMAs, far shorter than its load, so one block of
+  // lookahead leaves the loop waiting on memory. The split-K partials run several workgroups per
+  // CU, which hide the loads instead, and keep the registers for that occupancy.
   constexpr int kAC = kTM / 32;
-  i32x4 ra[kAC], rb[4];
-  auto load_block = [&](int k0) {
+  constexpr int kDepth = kTM == 32 && kEpi == kEpiQuery ? 6 : 1;
+  i32x4 ra[kDepth][kAC], rb[kDepth][4];
+  auto load_block = [&](int k0, int s) {
 #pragma unroll
     for (int i = 0; i < kAC; ++i) {
       const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-      ra[i] = (m0 + row < p.M) ? *(const i32x4*)(p.a + (int64_t)(m0 + row) * p.K + k0 + 8 * ch) : i32x4{0, 0, 0, 0};
+      ra[s][i] = (m0 + row < p.M) ? *(const i32x4*)(p.a + (int64_t)(m0 + row) * p.K + k0 + 8 * ch) : i32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-      rb[i] = (n0 + row < p.N) ? *(const i32x4*)(p.b + (int64_t)(n0 + row) * p.K + k0 + 8 * ch) : i32x4{0, 0, 0, 0};
+      rb[s][i] = (n0 + row < p.N) ? *(const i32x4*)(p.b + (int64_t)(n0 + row) * p.K + k0 + 8 * ch) : i32x4{0, 0, 0, 0};
     }
   };
-  auto store_block = [&]() {
+  auto store_block = [&](int s) {
 #pragma unroll
     for (int i = 0; i < kAC; ++i) {
       const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-      *(i32x4*)(lds_a + row * kPRowBytes + 16 * ch) = ra[i];
+      *(i32x4*)(lds_a + row * kPRowBytes + 16 * ch) = ra[s][i];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-      *(i32x4*)(lds_b + row * kPRowBytes + 16 * ch) = rb[i];
+      *(i32x4*)(lds_b + row * kPRowBytes + 16 * ch) = rb[s][i];
     }
   };
 
@@ -249,23 +254,33 @@ __global__ void __launch_bounds__(256) proj_gemm_kernel(ProjArgs p) {
   if constexpr (kTM == 128) {
     gemm_loop_lds_ring<kSq>(p, m0, n0, wave, lane, smem, acc);
   } else {
-  if (kbeg < kend) load_block(kbeg);
-  for (int k0 = kbeg; k0 < kend; k0 += kPK) {
-    __syncthreads();  // the previous block's operand reads are done
-    store_block();
-    __syncthreads();
-    if (k0 + kPK < kend) load_block(k0 + kPK);
-    bf16x8 a[4];
+  // block k0 + s kPK sits in register slot s (mod kDepth); each slot is refilled with the block
+  // kDepth blocks later as soon as it is in LDS
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] = *(const bf16x8*)(lds_a + (wrow + hl) * kPRowBytes + 64 * half + 16 * j);
+  for (int s = 0; s < kDepth; ++s)
+    if (kbeg + s * kPK < kend) load_block(kbeg + s * kPK, s);
+  for (int k00 = kbeg; k00 < kend; k00 += kDepth * kPK) {
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-      bf16x8 b[4];
+    for (int s = 0; s < kDepth; ++s) {
+      const int k0 = k00 + s * kPK;
+      if (k0 < kend) {  // uniform
+        __syncthreads();  // the previous block's operand reads are done
+        store_block(s);
+        __syncthreads();
+        if (k0 + kDepth * kPK < kend) load_block(k0 + kDepth * kPK, s);
+        bf16x8 a[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *(const bf16x8*)(lds_b + (32 * (wcb0 + cb) + hl) * kPRowBytes + 64 * half + 16 * j);
+        for (int j = 0; j < 4; ++j) a[j] = *(const bf16x8*)(lds_a + (wrow + hl) * kPRowBytes + 64 * half + 16 * j);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[j], acc[cb], 0, 0, 0);
+        for (int cb = 0; cb < kCB; ++cb) {
+          bf16x8 b[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            b[j] = *(const bf16x8*)(lds_b + (32 * (wcb0 + cb) + hl) * kPRowBytes + 64 * half + 16 * j);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[j], acc[cb], 0, 0, 0);
+        }
+      }
     }
   }
   }
