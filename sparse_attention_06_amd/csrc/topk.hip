@@ -426,6 +426,8 @@ struct TopkStageArgs {
   uint32_t* mhist;  // per row, the first-digit histogram of the merge's candidates (or null): the
                     // chunk stage adds its selection's counts, the merge starts from them
   int rows;         // rows of the launch (chunk stages: the 1-D grid covers 8 * out_chunks * ceil(rows / 8))
+  int len_first;    // score rows: read the row's length before its scores and load only positions
+                    // below it (grids of many rows, bound by bytes); else load the whole chunk at once
   int row_filter;   // chunk stage with hist0 and mhist over at most kTopkFilterChunks chunks: each
                     // chunk passes on its keys whose first digit reaches the row's threshold digit
                     // (from the sum of the row's chunk counts), and the merge clears those counts
@@ -464,15 +466,29 @@ topk_stage_kernel(TopkStageArgs a) {
     const float* row = a.scores + (int64_t)r * a.ld_scores;
     const int base = kKeys * c + kRegE * tid;
     float f[kRegE];
-    if (base + kRegE <= a.max_ctx && ((uintptr_t)(row + base) & 15) == 0) {
+    auto load_keys = [&]() {
+      if (base + kRegE <= a.max_ctx && ((uintptr_t)(row + base) & 15) == 0) {
 #pragma unroll
-      for (int v = 0; v < kRegE / 4; ++v) {
-        const float4 x = *(const float4*)(row + base + 4 * v);
-        f[4 * v] = x.x; f[4 * v + 1] = x.y; f[4 * v + 2] = x.z; f[4 * v + 3] = x.w;
+        for (int v = 0; v < kRegE / 4; ++v) {
+          const float4 x = *(const float4*)(row + base + 4 * v);
+          f[4 * v] = x.x; f[4 * v + 1] = x.y; f[4 * v + 2] = x.z; f[4 * v + 3] = x.w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < kRegE; ++e) f[e] = base + e < a.max_ctx ? row[base + e] : 0.f;
+      }
+    };
+    if (a.len_first) {
+      // a thread whose positions all lie past the row's end loads nothing (its keys are masked
+      // off below)
+      if (base < n) {
+        load_keys();
+      } else {
+#pragma unroll
+        for (int e = 0; e < kRegE; ++e) f[e] = 0.f;
       }
     } else {
-#pragma unroll
-      for (int e = 0; e < kRegE; ++e) f[e] = base + e < a.max_ctx ? row[base + e] : 0.f;
+      load_keys();
     }
     if (row_filter) filter_init(sh, tid, a.hist0 + (int64_t)r * nchunks * kRegBins, nchunks, c);
     else reg_select_init(sh, tid, hist0);
@@ -652,6 +668,8 @@ hipError_t launch_topk(const float* scores, int64_t ld_scores, const int32_t* q_
   a.idx = idx; a.ld_idx = ld_idx;
   if (max_ctx <= kRegKeys && k <= kCandCap) {
     a.hist0 = hist0;
+    // many rows (prefill blocks): bound by the bytes read, so causal rows skip their tails
+    a.len_first = rows >= kTopkPackedGrid ? 1 : 0;
     *path = (max_ctx <= k) ? DSA_PATH_TOPK_COPY : DSA_PATH_TOPK_RADIX_REG;
     if (max_ctx <= kTopkSmallThreads * kRegE)
       hipLaunchKernelGGL((topk_stage_kernel<true, true, false, kTopkSmallThreads>), dim3(1, rows), dim3(kTopkSmallThreads), 0,
