@@ -139,6 +139,26 @@ def test_topk_many_rows_two_workgroups_per_cu(oracle_lib, rows, n):
     np.testing.assert_array_equal(g, r)
 
 
+@pytest.mark.parametrize("rows,n", [(600, 8192), (520, 16384), (100, 8192)])
+def test_topk_ignores_scores_past_the_row(oracle_lib, rows, n):
+    """Positions past a row's q_pos hold +inf, NaN and huge values, which the top-k must never
+    rank: causal prefill rows of every length (-1, 0, k - 1, k, up to the full width) at 512+ rows
+    (the grids that read each row's length first and skip the positions past it) and at 100 rows
+    (which load the whole row and mask it); bit-exact against the oracle, which reads j <= t only."""
+    _say(f"case: topk poisoned tails rows={rows} n={n}")
+    rng = np.random.default_rng(rows * 7 + n)
+    k = 2048
+    sc = rng.standard_normal((rows, n)).astype(np.float32)
+    q_pos = rng.integers(-1, n, rows).astype(np.int32)
+    q_pos[:6] = [-1, 0, k - 1, k, n - 1, n - 2]
+    poison = np.array([np.inf, np.nan, 3.0e38], dtype=np.float32)
+    for i, t in enumerate(q_pos):
+        tail = sc[i, t + 1:]
+        tail[:] = poison[rng.integers(0, 3, tail.size)]
+    g, r = _topk_case(sc, q_pos, k)
+    np.testing.assert_array_equal(g, r)
+
+
 @pytest.mark.parametrize("n", [20000, 16000])
 def test_topk_ties_and_signed_zeros(oracle_lib, n):
     _say(f"case: topk ties n={n}")
