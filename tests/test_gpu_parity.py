@@ -317,6 +317,45 @@ def test_sparse_mla_decode_two_and_four_way_splits(oracle_lib, rows, k):
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+def test_sparse_mla_decode_headline_split_with_empty_rows_and_halves(oracle_lib):
+    """The headline decode launch (128 rows as 64 MTP pairs, k = 2048: two splits of 1024 entries
+    per row, then the two-way merge) with rows whose lists hold no visible entry (all -1, or all
+    past t), a row at t = 0 with its one key, and rows whose only valid entries lie in one split
+    (the other split has no key and must not enter the merge). Empty rows give zero output and
+    lse = -inf, as the oracle does for an empty set."""
+    _say("case: sparse mla decode headline split, empty rows and halves")
+    rng = np.random.default_rng(128)
+    n_seq, k = 64, 2048
+    base = rng.integers(2100, 2400, n_seq)
+    base[2] = 0
+    q_pos = np.stack([base, base + 1], 1).reshape(-1).astype(np.int32)
+    w = workloads.make_random(n_seq, 2, q_pos, 2402, seed=128, permute_pages=True, extra_pages=2)
+    d = gpu_inputs(w)
+    idx = _rand_idx(w.q_pos, k, seed=11)
+    for r, t in enumerate(w.q_pos):
+        kind = r % 8
+        if kind == 0:
+            idx[r] = -1                                            # nothing listed
+        elif kind == 1:
+            idx[r] = rng.integers(t + 1, t + 5000, k)              # every entry past t
+        elif kind == 3:
+            idx[r, :k // 2] = -1                                   # first split empty
+        elif kind == 5:
+            idx[r, k // 2:] = rng.integers(t + 1, t + 9, k // 2)   # second split invisible only
+    d_idx = torch.from_numpy(idx).cuda()
+    lse = torch.empty(w.rows, w.H, dtype=torch.float32, device="cuda")
+    out = dsa.sparse_mla_decode(d["q"], d["kv"], d["page_table"], d["q_pos"], w.n_seq, w.q_per_seq, d_idx, w.Dqk,
+                                w.Dv, w.v_col0, w.sm_scale, lse=lse)
+    assert dsa.last_path() == "mla_mfma_split"
+    ref, ref_lse = _attn_ref(w, idx)
+    o = out.float().cpu().numpy()
+    check_attn(o, ref)
+    g_lse = lse.cpu().numpy()
+    np.testing.assert_allclose(g_lse, ref_lse, rtol=0, atol=1e-4)
+    empty = [r for r in range(w.rows) if r % 8 in (0, 1)]
+    assert (o[empty] == 0).all() and np.isneginf(g_lse[empty]).all()
+
+
 def _lists_with_repeats(q_pos, k, seed):
     """Index lists that are sets only after removing repeats ([DSA-blog] "Sparse Attention": S_t
     is a set), one kind per row: shuffled with repeats spread over the whole list (so over the
