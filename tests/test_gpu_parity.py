@@ -60,7 +60,7 @@ def test_indexer_scan(oracle_lib, qps, q_pos, max_ctx, permute):
 @pytest.mark.parametrize("T,offset", [(300, 0), (64, 700), (517, 1531), (1100, 0)])
 def test_indexer_prefill(oracle_lib, T, offset):
     """A prefill block: the key scan takes its rows two at a time (one at a time for odd T); T = 1100
-    is 550 row pairs whose prefixes span 1 to 18 pages (ranges of one to three pages per wave)."""
+    is 550 row pairs with prefixes of 1 to 1100 keys, scanned in two-page ranges."""
     _say(f"case: indexer prefill T={T} offset={offset}")
     q_pos = np.arange(offset, offset + T, dtype=np.int32)
     w = workloads.make_random(1, T, q_pos, offset + T, H=2, Dqk=16, Dv=8, seed=41 + T, permute_pages=True)
