@@ -462,6 +462,34 @@ def test_dense_equals_sparse_with_full_sets_bitwise(oracle_lib):
     check_attn(dense.float().cpu().numpy(), ref)
 
 
+def test_lists_longer_than_one_chunk(oracle_lib):
+    """Rows whose position list exceeds the 2048 entries the tuned kernel resolves at a time: the
+    dense causal fallback at t = 2047 .. 5000 (one to three chunks of the key loop over [0, t]),
+    and sparse prefill over lists of k = 3000 entries with holes (two chunks; the repeat check
+    then spans both), against the oracle."""
+    _say("case: attention lists longer than one chunk")
+    q_pos = np.array([2047, 2048, 2049, 3071, 4095, 5000], np.int32)
+    w = workloads.make_random(1, len(q_pos), q_pos, 5001, seed=67, permute_pages=True, extra_pages=2)
+    d = gpu_inputs(w)
+    lse = torch.empty(w.rows, w.H, dtype=torch.float32, device="cuda")
+    dense = dsa.dense_mla_prefill(d["q"], d["kv"], d["page_table"], d["q_pos"], 1, w.rows, w.max_ctx, w.Dqk, w.Dv,
+                                  w.v_col0, w.sm_scale, lse=lse)
+    assert dsa.last_path().startswith("mla_mfma")
+    ref, ref_lse = oracle.dense_mla(w.q, w.kv, w.page_table, 64, w.q_pos, 1, w.rows, w.Dqk, w.Dv, w.v_col0,
+                                    w.sm_scale, threads=8)
+    check_attn(dense.float().cpu().numpy(), ref)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=1e-4)
+    k = 3000
+    idx = _rand_idx(w.q_pos, k, seed=13)
+    lse_s = torch.empty_like(lse)
+    sparse = dsa.sparse_mla_prefill(d["q"], d["kv"], d["page_table"], d["q_pos"], 1, w.rows,
+                                    torch.from_numpy(idx).cuda(), w.Dqk, w.Dv, w.v_col0, w.sm_scale, lse=lse_s)
+    assert dsa.last_path().startswith("mla_mfma")
+    ref_s, ref_s_lse = _attn_ref(w, idx)
+    check_attn(sparse.float().cpu().numpy(), ref_s)
+    np.testing.assert_allclose(lse_s.cpu().numpy(), ref_s_lse, rtol=0, atol=1e-4)
+
+
 def test_sparse_mla_never_reads_unselected_rows(oracle_lib):
     """Poison every latent row outside the selected sets with NaN: the output stays finite and
     bit-identical."""
