@@ -490,6 +490,45 @@ def test_lists_longer_than_one_chunk(oracle_lib):
     np.testing.assert_allclose(lse_s.cpu().numpy(), ref_s_lse, rtol=0, atol=1e-4)
 
 
+def test_attention_page_size_invariance(oracle_lib):
+    """The same latent cache seen as 32-token pages (each 64-token page split in halves, the page
+    table doubled): decode (two-way split), prefill and the dense fallback gather the same rows in
+    the same order, so their outputs and lse are bit-identical to the 64-token-page calls; the
+    64-token results are checked against the oracle."""
+    _say("case: attention page-size invariance")
+    rng = np.random.default_rng(71)
+    n_seq = 64
+    base = rng.integers(100, 2600, n_seq)
+    q_pos = np.stack([base, base + 1], 1).reshape(-1).astype(np.int32)
+    w = workloads.make_random(n_seq, 2, q_pos, 2602, H=128, seed=71, permute_pages=True, extra_pages=3)
+    d = gpu_inputs(w)
+    idx = torch.from_numpy(_rand_idx(w.q_pos, 2048, seed=17)).cuda()
+    P = d["kv"].shape[0]
+    kv32 = d["kv"].reshape(2 * P, 32, d["kv"].shape[2]).contiguous()
+    pt = d["page_table"].long()
+    pt32 = torch.stack([2 * pt, 2 * pt + 1], dim=2).reshape(pt.shape[0], -1).to(torch.int32).contiguous()
+    results = {}
+    for name, kv, table in (("64", d["kv"], d["page_table"]), ("32", kv32, pt32)):
+        for entry in ("decode", "prefill", "dense"):
+            lse = torch.empty(w.rows, w.H, dtype=torch.float32, device="cuda")
+            if entry == "dense":
+                lse = lse[:8]  # a few rows: the dense key loop runs over each whole prefix
+                o = dsa.dense_mla_prefill(d["q"][:8].contiguous(), kv, table, d["q_pos"][:8].contiguous(), 4, 2,
+                                          w.max_ctx, w.Dqk, w.Dv, w.v_col0, w.sm_scale, lse=lse)
+            else:
+                fn = dsa.sparse_mla_decode if entry == "decode" else dsa.sparse_mla_prefill
+                o = fn(d["q"], kv, table, d["q_pos"], w.n_seq, w.q_per_seq, idx, w.Dqk, w.Dv, w.v_col0, w.sm_scale,
+                       lse=lse)
+            assert dsa.last_path().startswith("mla_mfma"), (name, entry, dsa.last_path())
+            results[(name, entry)] = (o.view(torch.int16).cpu(), lse.cpu())
+    for entry in ("decode", "prefill", "dense"):
+        assert torch.equal(results[("64", entry)][0], results[("32", entry)][0]), entry
+        assert torch.equal(results[("64", entry)][1], results[("32", entry)][1]), entry
+    ref, _ = _attn_ref(w, idx.cpu().numpy(), rows=np.arange(0, w.rows, 9))
+    got = results[("64", "decode")][0].view(torch.bfloat16).float().numpy()[::9]
+    check_attn(got, ref[::9])
+
+
 def test_sparse_mla_never_reads_unselected_rows(oracle_lib):
     """Poison every latent row outside the selected sets with NaN: the output stays finite and
     bit-identical."""
